@@ -1,0 +1,522 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: published
+generator outputs, a library routine (numpy's IEEE half conversion, scipy's
+normal distribution and quadrature, scipy's Hadamard matrix, torch's SDPA), a
+closed form or bound, an invariant stated by the pages ("no changed symbol
+moves by more than one reconstruction level", "D-Quant: Entropy Coding Meets
+KV Cache at 2.26 Bits", Drift: Bending Variable Back to Fixed), or brute force
+on tiny inputs.  The readings they pin are the ones documented in
+oracle/dq_oracle.c.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy import integrate
+from scipy.linalg import hadamard
+from scipy.stats import norm as N01
+
+import synth
+
+D = 128
+H128 = hadamard(D).astype(np.float64)
+DEFAULTS = [(8, 34), (6, 34), (8, 29), (6, 29)]
+
+
+def bits_bf16(a):
+    return synth.bf16_bits(torch.as_tensor(np.asarray(a, np.float32)).to(torch.bfloat16))
+
+
+def f32_of_bf16(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------------ SplitMix64
+def test_splitmix64_published_outputs(oracle_lib):
+    O = oracle_lib
+    # Published outputs of the SplitMix64 reference generator (Steele, Lea &
+    # Flood 2014; the seed-0 and seed-1234567 streams are the standard checks).
+    assert [O.splitmix64(0, n) for n in range(4)] == [
+        0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F, 0xF88BB8A8724C81EC]
+    assert [O.splitmix64(1234567, n) for n in range(3)] == [
+        6457827717110365317, 3203168211198807973, 9817491932198370423]
+
+
+# ------------------------------------------------------------------ fp16
+def test_f16_conversion_matches_numpy(oracle_lib):
+    O = oracle_lib
+    rng = np.random.default_rng(1)
+    vals = list(rng.standard_normal(3000) * 10.0 ** rng.uniform(-9, 5, 3000))
+    # exact ties, subnormal edge, overflow edge, signed zeros, specials
+    for k in range(1, 2000, 7):
+        vals.append((k + 0.5) * 2.0 ** -24)
+        vals.append((1024 + k + 0.5) * 2.0 ** -10)
+    vals += [0.0, -0.0, 2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -24, 65504.0, 65519.99,
+             65520.0, -65520.0, 1e30, math.inf, -math.inf, 6.1e-5, 6.0975552e-05]
+    for v in vals:
+        with np.errstate(over="ignore"):
+            want = int(np.array([v], np.float64).astype(np.float16).view(np.uint16)[0])
+        assert O.f16_from_f64(v) == want, v
+    assert O.f16_from_f64(math.nan) == 0x7E00
+
+
+def test_f16_to_f64_all_patterns(oracle_lib):
+    O = oracle_lib
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = allh.view(np.float16).astype(np.float64)
+    got = np.array([O.f64_from_f16(int(h)) for h in allh])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+# ------------------------------------------------------------------ tables
+@pytest.mark.parametrize("levels,C", DEFAULTS)
+def test_table_closed_forms(oracle_lib, levels, C):
+    O = oracle_lib
+    codec = O.Codec(levels, C, seed=0, hkv=1)
+    t = codec.tables()
+    f, cum, rec, mass = t["freq"], t["cum"], t["recon_f16"], t["mass"]
+    h = levels // 2
+    step = codec.step64 / 64.0
+    edges = [m * step for m in range(h)] + [math.inf]
+    # cell masses against scipy's normal CDF (closed form Phi)
+    for m in range(h):
+        P = N01.cdf(edges[m + 1]) - N01.cdf(edges[m])
+        assert mass[h + m] == pytest.approx(P, rel=1e-12, abs=1e-15)
+        assert mass[h - 1 - m] == pytest.approx(P, rel=1e-12, abs=1e-15)
+    assert mass.sum() == pytest.approx(1.0, abs=1e-12)
+    # 12-bit table: sums to 4096, symmetric, floor 16, non-floored outer cells
+    # are the nearest integer to 4096 * P
+    assert int(f.sum()) == 4096 and (f >= 16).all()
+    assert (f == f[::-1]).all()
+    assert list(cum) == [0] + list(np.cumsum(f))
+    for m in range(1, h):
+        if f[h + m] > 16:
+            assert abs(int(f[h + m]) - 4096 * mass[h + m]) <= 0.5
+    # reconstruction levels: centroid by quadrature, rounded to fp16
+    for m in range(h):
+        P = N01.cdf(edges[m + 1]) - N01.cdf(edges[m])
+        num, _ = integrate.quad(lambda z: z * N01.pdf(z), edges[m], edges[m + 1],
+                                epsabs=1e-14, epsrel=1e-12)
+        lam = num / P
+        assert edges[m] <= lam and lam < edges[m + 1]
+        want = int(np.float16(lam).view(np.uint16))
+        assert int(rec[h + m]) == want
+        assert int(rec[h - 1 - m]) == want | 0x8000
+
+
+def test_table_rejections(oracle_lib):
+    O = oracle_lib
+    assert O.codec_check(7, 64, 34) == -1        # odd level count
+    assert O.codec_check(8, 0, 34) == -1         # zero width
+    assert O.codec_check(8, 73, 4) == -1         # container too small
+    assert O.codec_check(8, 73, 133) == -1       # too large
+    assert O.codec_check(8, 84, 29) == -3        # outer frequencies too close
+    # container too small for the all-innermost vector
+    st, f, _, _, _ = O.table(6, 66)
+    bits = 128 * math.log2(4096 / f[3]) + 0.0903
+    need = 4 + math.floor(bits / 8)
+    assert O.codec_check(6, 66, need) == 0
+    assert O.codec_check(6, 66, need - 1) == -3
+
+
+def test_bits_per_value_and_memory_ratio():
+    # C bytes + 2-byte fp16 norm per 128 values; ~7x smaller than bf16 is the
+    # pages' memory figure ("D-Quant: Entropy Coding Meets KV Cache at 2.26
+    # Bits", summary and So What).
+    assert (34 + 2) * 8 / 128 == 2.25
+    assert (29 + 2) * 8 / 128 == 1.9375
+    ratio = 16.0 / ((34 + 2) * 8 / 128)
+    assert 6.5 < ratio < 7.5
+
+
+# ------------------------------------------------------------------ rANS
+def _bigint_rans(sym, f, cum):
+    """Non-streaming rANS on an unbounded integer (Duda 2013): pushes symbols
+    127..0 starting from 2^23; returns the final integer."""
+    x = 1 << 23
+    for s in reversed([int(v) for v in sym]):
+        x = (x // int(f[s])) * 4096 + (x % int(f[s])) + int(cum[s])
+    return x
+
+
+def _bigint_unrans(x, f, cum, n=D):
+    out = []
+    for _ in range(n):
+        slot = x % 4096
+        s = int(np.searchsorted(cum, slot, side="right") - 1)
+        out.append(s)
+        x = int(f[s]) * (x // 4096) + slot - int(cum[s])
+    return out, x
+
+
+def _random_symbol_sets(levels, rng):
+    h = levels // 2
+    sets = [np.full(D, h, np.uint8), np.full(D, h - 1, np.uint8),
+            np.zeros(D, np.uint8), np.full(D, levels - 1, np.uint8),
+            np.arange(D, dtype=np.uint8) % levels]
+    for _ in range(200):
+        p = rng.dirichlet(np.ones(levels) * rng.uniform(0.2, 3))
+        sets.append(rng.choice(levels, size=D, p=p).astype(np.uint8))
+    return sets
+
+
+@pytest.mark.parametrize("levels,C", DEFAULTS)
+def test_rans_roundtrip_length_bound_and_bigint(oracle_lib, levels, C):
+    O = oracle_lib
+    t = O.Codec(levels, C, seed=0, hkv=1).tables()
+    f, cum = t["freq"], t["cum"]
+    rng = np.random.default_rng(levels * 100 + C)
+    for sym in _random_symbol_sets(levels, rng):
+        stream = O.rans_encode(sym, f, cum)
+        B = len(stream) - 4
+        x_final = int.from_bytes(bytes(stream[:4]), "little")
+        assert (1 << 23) <= x_final < (1 << 31)        # state interval
+        dec, fs, cons = O.rans_decode(stream, len(stream), f, cum)
+        assert (dec == sym).all()                       # round trip
+        assert fs == (1 << 23)                          # decoder ends where encoder began
+        assert cons == len(stream)                      # consumes exactly the stream
+        # code length = sum of -log2(f/4096) up to the exact bound
+        c = float(sum(math.log2(4096.0 / f[s]) for s in sym))
+        assert 8 * B <= c + 0.0902
+        assert 8 * B > c - 8.0902 - 0.0057
+        # the unbounded-integer coder spends the same information
+        X = _bigint_rans(sym, f, cum)
+        assert abs(X.bit_length() - 1 - (8 * B + math.log2(x_final))) < 1.2
+        assert abs(math.log2(X) - 23 - c) < 0.01
+        back, x0 = _bigint_unrans(X, f, cum)
+        assert back == [int(v) for v in sym] and x0 == (1 << 23)
+
+
+def test_rans_decode_reads_past_end_as_zero(oracle_lib):
+    O = oracle_lib
+    t = O.Codec(6, 34, seed=0, hkv=1).tables()
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        junk = rng.integers(0, 256, 34).astype(np.uint8)
+        a = O.rans_decode(junk, 34, t["freq"], t["cum"])
+        # same bytes followed by explicit zeros: identical result
+        padded = np.concatenate([junk, np.zeros(200, np.uint8)])
+        b = O.rans_decode(padded, 34, t["freq"], t["cum"])
+        assert (a[0] == b[0]).all() and a[1] == b[1] and a[2] == b[2]
+
+
+# ------------------------------------------------------------------ encode
+def _vectors(rng, n=64):
+    out = []
+    for k in range(n):
+        kind = k % 4
+        z = rng.standard_normal(D)
+        if kind == 1:
+            z[rng.permutation(D)[:4]] *= 10
+        elif kind == 2:
+            z = rng.standard_t(5, D)
+        elif kind == 3:
+            z *= math.exp(rng.uniform(math.log(0.5), math.log(2)))
+        out.append(bits_bf16(z.astype(np.float32)))
+    return out
+
+
+def _signs(O, seed, g):
+    w = [O.splitmix64(seed, 2 * g), O.splitmix64(seed, 2 * g + 1)]
+    return np.array([-1.0 if (w[i // 64] >> (i % 64)) & 1 else 1.0 for i in range(D)])
+
+
+def test_rotation_is_signed_hadamard(oracle_lib):
+    O = oracle_lib
+    codec = O.Codec(8, 34, seed=12345, hkv=4)
+    rng = np.random.default_rng(7)
+    for g in range(4):
+        sig = _signs(O, 12345, g)
+        # small integers: every fp32 sum is exact, so the fast transform must
+        # equal the dense Hadamard product exactly
+        xi = rng.integers(-40, 41, D).astype(np.float32)
+        _, d = O.encode_detail(codec, bits_bf16(xi), g)
+        assert (np.array(d.y, np.float64) == H128 @ (sig * xi)).all()
+        # general bf16 data: within the fp32 rounding bound of 7 stages
+        xb = bits_bf16(rng.standard_normal(D) * 3)
+        x = f32_of_bf16(xb).astype(np.float64)
+        _, d = O.encode_detail(codec, xb, g)
+        err = np.abs(np.array(d.y, np.float64) - H128 @ (sig * x))
+        assert err.max() <= 8 * 2.0 ** -24 * np.abs(x).sum()
+
+
+def test_norm_and_quantisation_cells(oracle_lib):
+    O = oracle_lib
+    rng = np.random.default_rng(11)
+    for levels, C in DEFAULTS:
+        codec = O.Codec(levels, C, seed=99, hkv=1)
+        h = levels // 2
+        step = codec.step64 / 64.0
+        for xb in _vectors(rng, 48):
+            x = f32_of_bf16(xb).astype(np.float64)
+            _, d = O.encode_detail(codec, xb, 0)
+            nh = np.uint16(d.norm).view(np.float16).astype(np.float64)
+            # fp16 norm: within half an fp16 ulp (plus fp32 summation slack) of ||x||
+            ulp = 2.0 ** (math.floor(math.log2(nh)) - 10)
+            assert abs(nh - np.linalg.norm(x)) <= 0.5 * ulp * (1 + 1e-5) + 1e-6 * nh
+            # unit variance per coordinate after normalisation
+            y = np.array(d.y, np.float64)
+            assert np.mean((y / np.linalg.norm(x)) ** 2) == pytest.approx(1.0, rel=1e-5)
+            # every symbol's cell contains |y| / n_h, sign rule
+            for i in range(D):
+                s = d.sym0[i]
+                m = s - h if s >= h else h - 1 - s
+                a = abs(y[i])
+                assert a >= m * step * nh
+                if m < h - 1:
+                    assert a < (m + 1) * step * nh
+                assert (s >= h) == (y[i] >= 0)
+
+
+def test_integer_norm_exact(oracle_lib):
+    O = oracle_lib
+    codec = O.Codec(8, 34, seed=1, hkv=1)
+    for vals, want in [([3, 4] + [0] * 126, 5.0), ([1] * 128, math.sqrt(128)),
+                       ([2] * 64 + [0] * 64, 16.0)]:
+        _, d = O.encode_detail(codec, bits_bf16(np.array(vals, np.float32)), 0)
+        assert int(d.norm) == int(np.float16(want).view(np.uint16))
+
+
+def _drift_key_order(d, h):
+    y = np.array(d.y, np.float32)
+    cand = []
+    for i in range(D):
+        s = d.sym0[i]
+        m = s - h if s >= h else h - 1 - s
+        if m >= 1:
+            cand.append((-m, float(abs(y[i])), i))
+    return [c[2] for c in sorted(cand)]
+
+
+@pytest.mark.parametrize("levels,C", DEFAULTS)
+def test_drift_invariants(oracle_lib, levels, C):
+    """Drift moves symbols one level toward zero, only when the stream does
+    not fit, the first k candidates in the stated order, with k minimal."""
+    O = oracle_lib
+    codec = O.Codec(levels, C, seed=3, hkv=1)
+    t = codec.tables()
+    h = levels // 2
+    rng = np.random.default_rng(levels + C)
+    drifted = 0
+    for xb in _vectors(rng, 96):
+        cont, d = O.encode_detail(codec, xb, 0)
+        s0 = np.array(d.sym0, np.int32)
+        s1 = np.array(d.sym, np.int32)
+        assert d.len <= C and len(cont) == C
+        assert (cont[d.len:] == 0).all()
+        dec, fs, cons = O.rans_decode(cont, C, t["freq"], t["cum"])
+        assert (dec == s1).all() and fs == 1 << 23 and cons == d.len
+        assert d.len0 == len(O.rans_encode(s0, t["freq"], t["cum"]))
+        if d.len0 <= C:
+            assert d.moves == 0 and (s0 == s1).all()
+            continue
+        drifted += 1
+        assert d.passes == 0
+        changed = np.nonzero(s0 != s1)[0]
+        assert len(changed) == d.moves >= 1
+        for i in changed:  # one level inward, never across zero
+            assert (s1[i] == s0[i] - 1) if s0[i] >= h else (s1[i] == s0[i] + 1)
+            assert s0[i] not in (h - 1, h)
+        order = _drift_key_order(d, h)
+        k = d.moves
+        assert sorted(order[:k]) == sorted(changed.tolist())
+        # minimality: the first k-1 candidates do not fit
+        prev = s0.copy()
+        for i in order[:k - 1]:
+            prev[i] = prev[i] - 1 if prev[i] >= h else prev[i] + 1
+        assert len(O.rans_encode(prev.astype(np.uint8), t["freq"], t["cum"])) > C
+        # stream length is non-increasing along the whole candidate order
+        cur = s0.copy()
+        last = d.len0
+        for i in order:
+            cur[i] = cur[i] - 1 if cur[i] >= h else cur[i] + 1
+            n = len(O.rans_encode(cur.astype(np.uint8), t["freq"], t["cum"]))
+            assert n <= last
+            last = n
+    assert drifted > 0
+
+
+def test_degenerate_vectors(oracle_lib):
+    O = oracle_lib
+    codec = O.Codec(6, 34, seed=5, hkv=1)
+    t = codec.tables()
+    cases = {
+        "zero": (np.zeros(D, np.float32), 0x0000, 1),
+        "tiny": (np.full(D, 1e-30, np.float32), 0x0000, 1),
+        "huge": (np.full(D, 1e30, np.float32), 0x7C00, 2),
+        "inf": (np.r_[np.inf, np.zeros(D - 1)].astype(np.float32), 0x7C00, 2),
+        "nan": (np.r_[np.nan, np.ones(D - 1)].astype(np.float32), 0x7E00, 2),
+    }
+    for name, (x, want_norm, deg) in cases.items():
+        cont, d = O.encode_detail(codec, bits_bf16(x), 0)
+        assert int(d.norm) == want_norm, name
+        assert d.degenerate == deg and d.moves == 0
+        assert (np.array(d.sym) == 3).all()
+        dec, fs, _ = O.rans_decode(cont, 34, t["freq"], t["cum"])
+        assert (dec == 3).all() and fs == 1 << 23
+    # negative zero is the positive innermost level
+    x = np.zeros(D, np.float32)
+    x[0] = 1.0
+    _, d = O.encode_detail(codec, bits_bf16(x), 0)
+    assert set(np.array(d.sym0).tolist()) <= {2, 3}
+
+
+def test_batch_encode_matches_single(oracle_lib):
+    O = oracle_lib
+    codec = O.Codec(8, 34, seed=21, hkv=3)
+    x = synth.kv_tensor("outlier", 50, 3, seed=4)
+    slots = np.random.default_rng(0).permutation(80)[:50]
+    cont, norm, stats = O.encode(codec, x, slots=slots, num_slots=80)
+    xb = synth.bf16_bits(x)
+    for t in range(0, 50, 7):
+        for g in range(3):
+            c1, d = O.encode_detail(codec, xb[t, g], g)
+            assert (cont[g, slots[t]] == c1).all()
+            assert norm[g, slots[t]] == d.norm
+    s = O.stats_dict(stats)
+    assert s["vectors"] == 150 and sum(s["len_hist"]) == 150
+
+
+def test_code_length_matches_model_entropy(oracle_lib):
+    """On N(0,1) data the mean stream length before drift matches the model
+    entropy sum(-log2 p) of the quantised symbols (spec pin), and the
+    table's KL to the exact cell masses is tiny."""
+    O = oracle_lib
+    for levels, C in [(8, 34), (6, 34)]:
+        codec = O.Codec(levels, C, seed=0, hkv=1)
+        t = codec.tables()
+        x = synth.bf16_bits(synth.kv_tensor("iid", 2000, 1, seed=8))
+        bits_model, bits_stream, bits_true = 0.0, 0.0, 0.0
+        for v in range(0, 2000, 4):
+            _, d = O.encode_detail(codec, x[v, 0], 0)
+            s0 = np.array(d.sym0)
+            c = sum(math.log2(4096.0 / t["freq"][s]) for s in s0)
+            stream = O.rans_encode(s0, t["freq"], t["cum"])
+            # information held by the stream: renorm bytes plus the bits the
+            # final state gained over its starting value 2^23
+            info = 8 * (len(stream) - 4) + math.log2(
+                int.from_bytes(bytes(stream[:4]), "little")) - 23
+            assert abs(info - c) <= 0.0902 + 0.0057
+            bits_model += c
+            bits_stream += info
+            bits_true += sum(-math.log2(t["mass"][s]) for s in s0)
+        n = 500 * 128
+        assert abs(bits_stream / n - bits_model / n) < 0.002
+        # the 12-bit table costs little over the exact cell probabilities
+        assert 0 <= (bits_model - bits_true) / n < 0.02
+        p = t["mass"]
+        q = t["freq"] / 4096.0
+        kl = float(np.sum(p * np.log2(p / q)))
+        assert 0 <= kl < 0.01
+
+
+# ------------------------------------------------------------------ dequant + attention
+def test_dequant_is_inverse_rotation(oracle_lib):
+    O = oracle_lib
+    codec = O.Codec(8, 34, seed=77, hkv=2)
+    t = codec.tables()
+    x = synth.kv_tensor("iid", 20, 2, seed=9)
+    cont, norm, _ = O.encode(codec, x)
+    for g in range(2):
+        deq = O.dequant(codec, cont, norm, g, np.arange(20))
+        sig = _signs(O, 77, g)
+        sym, _, _ = O.decode_symbols(codec, cont, g, np.arange(20))
+        for j in range(20):
+            n = float(np.uint16(norm[g, j]).view(np.float16))
+            r = n * t["recon_f16"][sym[j]].view(np.float16).astype(np.float64)
+            want = sig * (H128 @ r) / 128.0
+            assert np.allclose(deq[j], want, rtol=0, atol=1e-12 * max(1.0, np.abs(want).max()))
+        # reconstruction error close to the quantiser's analytic distortion
+        xd = synth.bf16_bits(x)[:, g]
+        xf = f32_of_bf16(xd).astype(np.float64)
+        rel = np.sum((deq - xf) ** 2) / np.sum(xf ** 2)
+        assert rel < 0.15
+
+
+def _tiny_attention_case(O, B=2, Hq=4, hkv=2, lens=(3, 5), seed=0):
+    ck = O.Codec(8, 34, seed=seed + 1, hkv=hkv)
+    cv = O.Codec(6, 34, seed=seed + 2, hkv=hkv)
+    S = sum(lens) + 3
+    K = synth.kv_tensor("outlier", S, hkv, seed=seed + 3)
+    V = synth.kv_tensor("iid_scaled", S, hkv, seed=seed + 4)
+    q = synth.q_tensor(B, Hq, seed=seed + 5)
+    kc, kn, _ = O.encode(ck, K)
+    vc, vn, _ = O.encode(cv, V)
+    starts = np.array([0, lens[0] + 2][:B], np.int64)
+    return ck, cv, q, kc, kn, vc, vn, starts, np.array(lens[:B], np.int32)
+
+
+def test_attention_brute_force_loops(oracle_lib):
+    O = oracle_lib
+    ck, cv, q, kc, kn, vc, vn, starts, lens = _tiny_attention_case(O)
+    out = O.attention(ck, cv, q, kc, kn, vc, vn, starts, lens)
+    qf = q.float().numpy().astype(np.float64)
+    B, Hq, _ = qf.shape
+    hkv = kc.shape[0]
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // hkv)
+            slots = np.arange(starts[b], starts[b] + lens[b])
+            kh = O.dequant(ck, kc, kn, g, slots)
+            vh = O.dequant(cv, vc, vn, g, slots)
+            sc = [sum(qf[b, h, i] * kh[t, i] for i in range(D)) / math.sqrt(D)
+                  for t in range(lens[b])]
+            mx = max(sc)
+            w = [math.exp(s - mx) for s in sc]
+            den = sum(w)
+            ref = [sum(w[t] * vh[t, i] for t in range(lens[b])) / den for i in range(D)]
+            assert np.allclose(out[b, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_matches_torch_sdpa_fp64(oracle_lib):
+    O = oracle_lib
+    ck, cv, q, kc, kn, vc, vn, starts, lens = _tiny_attention_case(
+        O, B=2, Hq=8, hkv=2, lens=(37, 70), seed=3)
+    out = O.attention(ck, cv, q, kc, kn, vc, vn, starts, lens, sm_scale=0.3)
+    qf = q.double()
+    for b in range(2):
+        slots = np.arange(starts[b], starts[b] + lens[b])
+        for g in range(2):
+            kh = torch.from_numpy(O.dequant(ck, kc, kn, g, slots))
+            vh = torch.from_numpy(O.dequant(cv, vc, vn, g, slots))
+            qq = qf[b, g * 4:(g + 1) * 4][None, :, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qq, kh[None, None].expand(1, 4, -1, -1), vh[None, None].expand(1, 4, -1, -1),
+                scale=0.3)
+            assert torch.allclose(torch.from_numpy(out[b, g * 4:(g + 1) * 4]), ref[0, :, 0],
+                                  rtol=1e-11, atol=1e-12)
+
+
+def test_attention_special_cases(oracle_lib):
+    O = oracle_lib
+    ck, cv, q, kc, kn, vc, vn, starts, lens = _tiny_attention_case(
+        O, B=2, Hq=4, hkv=2, lens=(1, 9), seed=7)
+    out = O.attention(ck, cv, q, kc, kn, vc, vn, starts, lens)
+    # one token: output is that token's dequantised value
+    for h in range(4):
+        vh = O.dequant(cv, vc, vn, h // 2, [starts[0]])
+        assert np.allclose(out[0, h], vh[0], rtol=0, atol=1e-12)
+    # zero query: equal scores, output is the mean of the values
+    qz = torch.zeros_like(q)
+    outz = O.attention(ck, cv, qz, kc, kn, vc, vn, starts, lens)
+    for h in range(4):
+        vh = O.dequant(cv, vc, vn, h // 2, np.arange(starts[1], starts[1] + 9))
+        assert np.allclose(outz[1, h], vh.mean(0), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ golden
+def test_golden_fixtures_unchanged(oracle_lib):
+    """The oracle still reproduces the stored fixtures byte for byte."""
+    import os
+    import importlib.util
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    spec = importlib.util.spec_from_file_location("make_golden", os.path.join(here, "make_golden.py"))
+    mg = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mg)
+    with open(os.path.join(here, "codec_tables.txt")) as f:
+        assert f.read() == mg.tables_text()
+    with open(os.path.join(here, "small_encode.txt")) as f:
+        assert f.read() == mg.small_encode_text()
