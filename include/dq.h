@@ -1,0 +1,178 @@
+/*
+ * dq.h -- C ABI of the D-Quant hot path on MI355X (gfx950).
+ *
+ * D-Quant ("D-Quant: Driftable Entropy Coding for KV Cache Quantization",
+ * abstract; "D-Quant: Entropy Coding Meets KV Cache at 2.26 Bits", sections
+ * "Why Fixed Width Is a Ceiling" and "Drift: Bending Variable Back to Fixed")
+ * stores each token's K or V vector as an rANS-coded stream of quantised
+ * symbols inside a fixed-size byte container, so attention can address the
+ * compressed cache at a fixed stride and dequantise in parallel.
+ *
+ * Conventions for every call:
+ *  - Return value: DQ_OK (0) or a negative DQ_ERR_* code.  Calls never abort
+ *    and never print.  Argument errors are detected synchronously, before
+ *    anything is launched.
+ *  - "device" pointers are HIP device allocations owned by the caller; the
+ *    library never allocates, frees or synchronises in dq_encode,
+ *    dq_decode_symbols or dq_attn_decode.  Work is enqueued on `stream`
+ *    (a hipStream_t; NULL means the default stream).  Faults inside a kernel
+ *    surface at the caller's next synchronisation, as usual in HIP.
+ *  - Codec objects are host-only, immutable after creation and safe to share
+ *    between threads.  Creating one needs no GPU.
+ *  - Layouts: head_dim is 128.  The compressed cache of one stream (K or V)
+ *    is a pool of `num_slots` slots per kv head:
+ *        cont[Hkv][num_slots][C]   uint8   (one C-byte container per vector)
+ *        norm[Hkv][num_slots]      uint16  (fp16 bits of the vector norm)
+ *    `cont` must be 16-byte aligned and num_slots * C a multiple of 16.
+ */
+#ifndef DQ_H_
+#define DQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DQ_OK = 0,
+  DQ_ERR_INVALID = -1,     /* bad argument (null, range, shape, alignment)  */
+  DQ_ERR_UNSUPPORTED = -2, /* valid but not supported (head_dim != 128, ...) */
+  DQ_ERR_BUDGET = -3,      /* the table cannot meet the container budget    */
+  DQ_ERR_WORKSPACE = -4,   /* workspace too small                           */
+  DQ_ERR_HIP = -5          /* a HIP runtime call failed                     */
+};
+
+typedef void *dq_stream_t; /* hipStream_t */
+
+/* Human-readable text for a status code (static storage). */
+const char *dq_status_string(int status);
+
+/* ABI version: 100 * major + minor. */
+int dq_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Codec: the parameters of one coded stream (K or V).
+ *
+ * The probability model is the analytic N(0,1) mass of each quantiser cell
+ * (no calibration data), per "Drift: Bending Variable Back to Fixed"; keys use
+ * 8 levels and values 6 there.  Cells are symmetric, uniform of width
+ * step64/64 (in units of the per-coordinate standard deviation after
+ * normalisation), the outermost cell open; masses are quantised to a 12-bit
+ * rANS table with every frequency >= 16; the reconstruction level of a cell is
+ * its centroid rounded to fp16.  The rotation is a randomized Walsh-Hadamard
+ * transform whose signs for kv head g are the bits of SplitMix64 outputs
+ * 2g and 2g+1 of the stream seeded with `seed`. */
+typedef struct dq_codec *dq_codec_t;
+
+typedef struct {
+  int32_t head_dim;        /* must be 128, else DQ_ERR_UNSUPPORTED           */
+  int32_t levels;          /* even, 2..16 (keys 8, values 6)                 */
+  int32_t container_bytes; /* C in [5, 132]: 34 -> 2.25 bits/value with norm */
+  int32_t num_kv_heads;    /* 1..1024; one sign vector per kv head           */
+  uint64_t seed;           /* rotation seed                                  */
+  int32_t step64;          /* cell width * 64, 1..1023; 0 = default for
+                              (levels, C) where one exists, else DQ_ERR_INVALID */
+  int32_t reserved;        /* must be 0                                      */
+} dq_codec_desc;
+
+/* Validates `desc`, builds the tables (host memory only) and returns a new
+ * codec in *out.  DQ_ERR_BUDGET when a frequency would fall below 16, when
+ * adjacent magnitude cells are not at least 1.15x apart in probability, or
+ * when the all-innermost vector cannot fit C bytes. */
+int dq_codec_create(const dq_codec_desc *desc, dq_codec_t *out);
+int dq_codec_destroy(dq_codec_t codec); /* NULL is accepted */
+
+/* The resolved parameters (step64 filled in). */
+int dq_codec_info(dq_codec_t codec, dq_codec_desc *out);
+
+/* Host copies of the tables, any pointer may be NULL:
+ *   freq[levels], cum[levels + 1] (12-bit rANS table in symbol order, symbol
+ *   0 = outermost negative cell), recon_f16[levels] (fp16 bits of the
+ *   reconstruction levels), sign_words[2 * num_kv_heads] (bit i % 64 of word
+ *   2g + i / 64 set means coordinate i of kv head g is negated). */
+int dq_codec_tables(dq_codec_t codec, uint16_t *freq, uint16_t *cum,
+                    uint16_t *recon_f16, uint64_t *sign_words);
+
+/* ------------------------------------------------------------------------ */
+/* Encode statistics, accumulated (atomically) by dq_encode into a
+ * caller-zeroed device struct.  Drift rate = drifted_symbols / (128 *
+ * vectors); the pages report 0.75% for keys and 5.00% for values
+ * ("Drift: Bending Variable Back to Fixed"). */
+#define DQ_MAX_CONTAINER 132
+typedef struct {
+  uint64_t vectors;           /* vectors encoded                          */
+  uint64_t drifted_vectors;   /* vectors that needed at least one move    */
+  uint64_t drifted_symbols;   /* one-level symbol moves                   */
+  uint64_t multilevel_events; /* extra drift passes (expected 0)          */
+  uint64_t bad_norms;         /* norm inf or NaN: coded as all-innermost  */
+  uint64_t zero_norms;        /* norm rounds to 0: coded as all-innermost */
+  uint64_t len_hist[DQ_MAX_CONTAINER + 1]; /* final stream length counts  */
+} dq_stats;
+
+/* dq_encode: rotate, normalise, quantise, rANS-code and drift T x Hkv
+ * vectors into their containers ("Drift: Bending Variable Back to Fixed").
+ *   x         device bf16, element (t, g, i) at x[t*stride_t + g*stride_h + i]
+ *   slots     device int64[T]: pool slot of token t (0 <= slot < num_slots)
+ *   cont      device uint8[Hkv][num_slots][C]   (written at the given slots)
+ *   norm      device uint16[Hkv][num_slots]     (fp16 bits)
+ *   stats     device dq_stats, may be NULL
+ * Vectors with a zero, inf or NaN norm are coded as all innermost-positive
+ * symbols (norm stored as 0, inf or 0x7E00).  Duplicate slots race.
+ * T = 0 is a no-op. */
+int dq_encode(dq_codec_t codec, const void *x, int64_t T, int64_t stride_t,
+              int64_t stride_h, const int64_t *slots, int64_t num_slots,
+              uint8_t *cont, uint16_t *norm, dq_stats *stats,
+              dq_stream_t stream);
+
+/* dq_decode_symbols: container -> the 128 symbols, for kv head `head` at n
+ * slots (inspection and checking; attention decodes inside its own kernel).
+ *   sym_out      device uint8[n][128]
+ *   final_state  device uint32[n] or NULL: decoder state after 128 symbols
+ *                (2^23 for every container dq_encode wrote)
+ *   consumed     device int32[n] or NULL: container bytes read
+ * Bytes past the C-byte container read as 0 and are never fetched. */
+int dq_decode_symbols(dq_codec_t codec, const uint8_t *cont, int64_t num_slots,
+                      int32_t head, const int64_t *slots, int64_t n,
+                      uint8_t *sym_out, uint32_t *final_state,
+                      int32_t *consumed, dq_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over the compressed cache ("D-Quant: Driftable Entropy
+ * Coding for KV Cache Quantization", abstract: fixed-size streams give
+ * regular memory access and parallel dequantisation inside attention; "D-Quant:
+ * Entropy Coding Meets KV Cache at 2.26 Bits", So What: the entropy decoder
+ * sits inside the attention kernel).
+ *
+ * One query token per sequence; GQA with query head h reading kv head
+ * h / (Hq / Hkv); Hq / Hkv must be 1, 2 or 4.  Sequence b occupies pool
+ * slots [seq_start[b], seq_start[b] + seq_len[b]).  Split-K: the context is
+ * cut into chunks decoded in parallel and merged by a log-sum-exp combine.
+ * The result is computed in the rotated basis and rotated back before the
+ * store.
+ *   q          device bf16 [B][Hq][128]
+ *   seq_start  device int64[B]; seq_len device int32[B], 1 <= len <= max_len
+ *   max_len    host: upper bound of seq_len, used to plan the split
+ *   sm_scale   softmax scale (e.g. 1/sqrt(128))
+ *   out_dtype  0: fp32, 1: bf16
+ *   out        device [B][Hq][128]
+ *   workspace  device scratch of at least the size reported by
+ *              dq_attn_decode_workspace for the same (B, Hq, Hkv, max_len)
+ * The two codecs must have the same num_kv_heads. */
+int dq_attn_decode_workspace(int32_t B, int32_t Hq, int32_t Hkv,
+                             int64_t max_len, size_t *bytes);
+
+int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B,
+                   int32_t Hq, const uint8_t *k_cont, const uint16_t *k_norm,
+                   const uint8_t *v_cont, const uint16_t *v_norm,
+                   int64_t num_slots, const int64_t *seq_start,
+                   const int32_t *seq_len, int64_t max_len, float sm_scale,
+                   int32_t out_dtype, void *out, void *workspace,
+                   size_t ws_bytes, dq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DQ_H_ */

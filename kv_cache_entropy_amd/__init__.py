@@ -1,0 +1,217 @@
+"""D-Quant hot path on MI355X: driftable rANS KV-cache coding and decode
+attention over the coded cache.
+
+Thin binding over the C ABI in include/dq.h (libdq.so, built by
+``python -m kv_cache_entropy_amd.build``).  This module only checks and
+marshals arguments: every step of the computation runs in the HIP kernels.
+torch is used for device memory and the current stream.  If libdq.so is
+missing or fails to load, every entry point raises; there is no fallback.
+
+    ck = Codec(levels=8, container_bytes=34, seed=1, kv_heads=8)
+    cont, norm = alloc_pool(ck, num_slots, device="cuda")
+    encode(ck, k_bf16, slots, cont, norm)
+    out = attn_decode(ck, cv, q, kc, kn, vc, vn, seq_start, seq_len, max_len)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import _lib
+
+HEAD_DIM = 128
+MAX_CONTAINER = 132
+NSTATS = 6 + MAX_CONTAINER + 1
+
+__all__ = ["Codec", "alloc_pool", "encode", "decode_symbols", "attn_decode",
+           "attn_workspace_bytes", "new_stats", "stats_dict", "DQError", "library_path"]
+
+
+class DQError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _lib.LIB
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = _lib.lib().dq_status_string(status).decode()
+        raise DQError(f"{what}: {msg} ({status})")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_cuda(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise DQError(f"{name} must be a CUDA/HIP tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise DQError(f"{name} must have dtype {dtype}, got {t.dtype}")
+
+
+class Codec:
+    """One coded stream (K or V): level count, container bytes, rotation
+    seed, kv heads and cell width (step64 / 64 sigma; 0 = default)."""
+
+    def __init__(self, levels: int, container_bytes: int, seed: int, kv_heads: int,
+                 step64: int = 0):
+        L = _lib.lib()
+        desc = _lib.CodecDesc(HEAD_DIM, levels, container_bytes, kv_heads,
+                              seed & (2**64 - 1), step64, 0)
+        h = ctypes.c_void_p()
+        _check(L.dq_codec_create(ctypes.byref(desc), ctypes.byref(h)), "dq_codec_create")
+        self._h = h
+        info = _lib.CodecDesc()
+        _check(L.dq_codec_info(h, ctypes.byref(info)), "dq_codec_info")
+        self.levels = info.levels
+        self.C = info.container_bytes
+        self.seed = info.seed
+        self.kv_heads = info.num_kv_heads
+        self.step64 = info.step64
+
+    @property
+    def handle(self):
+        return self._h
+
+    def tables(self) -> dict:
+        import numpy as np
+        L = self.levels
+        f = np.zeros(L, np.uint16)
+        c = np.zeros(L + 1, np.uint16)
+        r = np.zeros(L, np.uint16)
+        w = np.zeros(2 * self.kv_heads, np.uint64)
+        _check(_lib.lib().dq_codec_tables(
+            self._h, f.ctypes.data_as(ctypes.c_void_p), c.ctypes.data_as(ctypes.c_void_p),
+            r.ctypes.data_as(ctypes.c_void_p), w.ctypes.data_as(ctypes.c_void_p)),
+            "dq_codec_tables")
+        return {"freq": f, "cum": c, "recon_f16": r, "sign_words": w}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                _lib.lib().dq_codec_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+
+def pool_slots(num_slots: int, C: int) -> int:
+    """Smallest slot count >= num_slots with num_slots * C a multiple of 16."""
+    n = num_slots
+    while (n * C) % 16:
+        n += 1
+    return n
+
+
+def alloc_pool(codec: Codec, num_slots: int, device="cuda"):
+    """Zeroed (cont uint8 [Hkv, S, C], norm fp16 [Hkv, S]) with S padded so the
+    plane size is a multiple of 16 bytes."""
+    S = pool_slots(num_slots, codec.C)
+    cont = torch.zeros((codec.kv_heads, S, codec.C), dtype=torch.uint8, device=device)
+    norm = torch.zeros((codec.kv_heads, S), dtype=torch.float16, device=device)
+    return cont, norm
+
+
+def new_stats(device="cuda") -> torch.Tensor:
+    return torch.zeros(NSTATS, dtype=torch.int64, device=device)
+
+
+def stats_dict(stats: torch.Tensor) -> dict:
+    s = [int(v) for v in stats.cpu().tolist()]
+    return {"vectors": s[0], "drifted_vectors": s[1], "drifted_symbols": s[2],
+            "multilevel_events": s[3], "bad_norms": s[4], "zero_norms": s[5],
+            "len_hist": s[6:]}
+
+
+def encode(codec: Codec, x: torch.Tensor, slots: torch.Tensor, cont: torch.Tensor,
+           norm: torch.Tensor, stats: torch.Tensor | None = None):
+    """x: bf16 [T, Hkv, 128] (last dim contiguous); slots: int64 [T];
+    cont/norm: the pool from alloc_pool; stats: int64 [NSTATS] or None."""
+    _need_cuda("x", x, torch.bfloat16)
+    _need_cuda("slots", slots, torch.int64)
+    _need_cuda("cont", cont, torch.uint8)
+    _need_cuda("norm", norm, torch.float16)
+    if x.dim() != 3 or x.shape[1] != codec.kv_heads or x.shape[2] != HEAD_DIM or x.stride(2) != 1:
+        raise DQError(f"x must be [T, {codec.kv_heads}, 128] with unit inner stride")
+    if slots.dim() != 1 or slots.shape[0] != x.shape[0] or not slots.is_contiguous():
+        raise DQError("slots must be a contiguous int64 [T]")
+    if (cont.dim() != 3 or cont.shape[0] != codec.kv_heads or cont.shape[2] != codec.C
+            or not cont.is_contiguous()):
+        raise DQError("cont must be a contiguous uint8 [Hkv, S, C]")
+    if norm.shape != cont.shape[:2] or not norm.is_contiguous():
+        raise DQError("norm must be a contiguous fp16 [Hkv, S]")
+    if stats is not None:
+        _need_cuda("stats", stats, torch.int64)
+        if stats.numel() != NSTATS or not stats.is_contiguous():
+            raise DQError(f"stats must be a contiguous int64 [{NSTATS}]")
+    _check(_lib.lib().dq_encode(codec.handle, _ptr(x), x.shape[0], x.stride(0), x.stride(1),
+                                _ptr(slots), cont.shape[1], _ptr(cont), _ptr(norm),
+                                _ptr(stats), _stream(x.device)), "dq_encode")
+
+
+def decode_symbols(codec: Codec, cont: torch.Tensor, head: int, slots: torch.Tensor):
+    """Returns (symbols uint8 [n, 128], final_state int64 [n], consumed int32 [n])."""
+    _need_cuda("cont", cont, torch.uint8)
+    _need_cuda("slots", slots, torch.int64)
+    n = slots.shape[0]
+    sym = torch.empty((n, HEAD_DIM), dtype=torch.uint8, device=cont.device)
+    fs = torch.empty(n, dtype=torch.int32, device=cont.device)
+    cons = torch.empty(n, dtype=torch.int32, device=cont.device)
+    _check(_lib.lib().dq_decode_symbols(codec.handle, _ptr(cont), cont.shape[1], head,
+                                        _ptr(slots.contiguous()), n, _ptr(sym), _ptr(fs),
+                                        _ptr(cons), _stream(cont.device)), "dq_decode_symbols")
+    return sym, fs.to(torch.int64) & 0xFFFFFFFF, cons
+
+
+def attn_workspace_bytes(B: int, Hq: int, Hkv: int, max_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.lib().dq_attn_decode_workspace(B, Hq, Hkv, max_len, ctypes.byref(n)),
+           "dq_attn_decode_workspace")
+    return n.value
+
+
+def attn_decode(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_cont, v_norm,
+                seq_start: torch.Tensor, seq_len: torch.Tensor, max_len: int,
+                sm_scale: float | None = None, out: torch.Tensor | None = None,
+                out_dtype=torch.float32, workspace: torch.Tensor | None = None):
+    """q: bf16 [B, Hq, 128]; pools from alloc_pool; seq_start int64 [B];
+    seq_len int32 [B] (1 <= len <= max_len).  Returns out [B, Hq, 128]."""
+    _need_cuda("q", q, torch.bfloat16)
+    for name, t, dt in (("k_cont", k_cont, torch.uint8), ("v_cont", v_cont, torch.uint8),
+                        ("k_norm", k_norm, torch.float16), ("v_norm", v_norm, torch.float16),
+                        ("seq_start", seq_start, torch.int64), ("seq_len", seq_len, torch.int32)):
+        _need_cuda(name, t, dt)
+        if not t.is_contiguous():
+            raise DQError(f"{name} must be contiguous")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise DQError("q must be a contiguous bf16 [B, Hq, 128]")
+    if k_cont.shape[1] != v_cont.shape[1]:
+        raise DQError("K and V pools must have the same slot count")
+    B, Hq, _ = q.shape
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise DQError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, Hq, HEAD_DIM) or not out.is_contiguous():
+        raise DQError("out has the wrong shape or dtype")
+    need = attn_workspace_bytes(B, Hq, ck.kv_heads, max_len)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if sm_scale is None:
+        sm_scale = HEAD_DIM ** -0.5
+    _check(_lib.lib().dq_attn_decode(
+        ck.handle, cv.handle, _ptr(q), B, Hq, _ptr(k_cont), _ptr(k_norm), _ptr(v_cont),
+        _ptr(v_norm), k_cont.shape[1], _ptr(seq_start), _ptr(seq_len), max_len,
+        ctypes.c_float(sm_scale), 0 if out_dtype == torch.float32 else 1, _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(q.device)), "dq_attn_decode")
+    return out

@@ -1,0 +1,478 @@
+// dq_attn_decode: GQA split-K decode attention over rANS containers.
+//
+// "D-Quant: Driftable Entropy Coding for KV Cache Quantization" (abstract):
+// fixed-size per-token streams give attention regular, fixed-stride memory
+// access and let it dequantise in parallel; "D-Quant: Entropy Coding Meets KV
+// Cache at 2.26 Bits" (intro, So What): the entropy decoder runs inside the
+// attention kernel.
+//
+// Three kernels on the caller's stream:
+//  1. rotate_q: q~ = H * D_K * q in fp32 for every query head, stored as an
+//     fp16 hi/lo pair (hi + lo carries ~22 bits) in the MFMA operand layout.
+//     Because H * H = 128 I, q . khat = q~ . (n * r(s)) / 128: scores are
+//     computed directly on the decoded levels, no inverse rotation of K.
+//  2. attn_splitk: persistent waves; a work item is (sequence, kv head,
+//     context chunk).  Per 64-token tile a wave copies the tile's K and V
+//     containers (64 * C contiguous bytes each, fixed stride) into its LDS
+//     slice with 16-byte loads; every lane then rANS-decodes one token's
+//     container through an LDS table (slot -> f, slot - cum, fp16 level).
+//     K: every 4 decoded symbols form the A operand of a 4x4x4 MFMA
+//     (16 blocks = the wave's 64 tokens) against q~ (4 heads), so the decoded
+//     keys never leave registers.  Online softmax in fp32 (exp2 domain).
+//     V: decoded levels are written transposed into an LDS tile [dim][token]
+//     and contracted with p * n_v by 4x4x4 MFMAs whose 16 blocks cover 64
+//     dims.  Each item leaves (m, l, acc[4][128]) in the workspace.
+//  3. combine: log-sum-exp merge of an item's chunks, then the inverse
+//     rotation D_V * H / 128 and the store.
+#include "decode_common.h"
+
+#include <math.h>
+#include <stdlib.h>
+
+namespace dq {
+namespace {
+
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 64;
+constexpr int kVtStride = 66;    // halves per V-tile row: 33 dwords, spreads LDS banks
+constexpr int kPart = 132;       // floats per (item, head): acc[128], m, l, pad
+constexpr int kQrotPerBG = 32 * 4 * 8;  // halves per (b, kv head): [chunk][head][hi4 lo4]
+constexpr int kLutBytes = 2 * (int)kM * 8;
+
+struct AttnArgs {
+  const uint16_t *q;
+  int B, Hq, Hkv, group;
+  const uint8_t *kc;
+  const uint16_t *kn;
+  const uint8_t *vc;
+  const uint16_t *vn;
+  int64_t S;
+  const int64_t *seq_start;
+  const int32_t *seq_len;
+  float qk_scale;  // sm_scale * log2(e) / 128
+  int chunk, nc;
+  int64_t n_items;
+  float *part;
+  uint16_t *qrot;
+  void *out;
+  int out_bf16;
+  int waves_per_block;
+  int wave_bytes;
+};
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------- rotate q
+__global__ void __launch_bounds__(64) rotate_q_kernel(AttnArgs a, uint64_t kseed) {
+  const int lane = threadIdx.x;
+  const int bg = blockIdx.x >> 2, hh = blockIdx.x & 3;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  uint16_t *dst = a.qrot + (int64_t)bg * kQrotPerBG;
+  const int d0 = lane, d1 = lane + 64;
+  if (hh >= a.group) {
+    const int i0 = ((d0 >> 2) * 4 + hh) * 8 + (d0 & 3), i1 = ((d1 >> 2) * 4 + hh) * 8 + (d1 & 3);
+    dst[i0] = 0; dst[i0 + 4] = 0; dst[i1] = 0; dst[i1 + 4] = 0;
+    return;
+  }
+  const int h = g * a.group + hh;
+  const uint16_t *qp = a.q + ((int64_t)b * a.Hq + h) * kD;
+  const uint64_t w0 = dev_splitmix64(kseed, 2ull * (uint64_t)g);
+  const uint64_t w1 = dev_splitmix64(kseed, 2ull * (uint64_t)g + 1ull);
+  float v0 = __uint_as_float((uint32_t)qp[d0] << 16);
+  float v1 = __uint_as_float((uint32_t)qp[d1] << 16);
+  if ((w0 >> lane) & 1ull) v0 = -v0;
+  if ((w1 >> lane) & 1ull) v1 = -v1;
+  // width 64 pairs d with d + 64 inside the lane; widths 32..1 across lanes
+  float t0 = v0 + v1, t1 = v0 - v1;
+  v0 = t0;
+  v1 = t1;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const float p0 = __shfl_xor(v0, w), p1 = __shfl_xor(v1, w);
+    const bool hi = lane & w;
+    v0 = hi ? p0 - v0 : v0 + p0;
+    v1 = hi ? p1 - v1 : v1 + p1;
+  }
+  const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+  const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
+  const int i0 = ((d0 >> 2) * 4 + hh) * 8 + (d0 & 3), i1 = ((d1 >> 2) * 4 + hh) * 8 + (d1 & 3);
+  dst[i0] = __builtin_bit_cast(uint16_t, h0);
+  dst[i0 + 4] = __builtin_bit_cast(uint16_t, l0);
+  dst[i1] = __builtin_bit_cast(uint16_t, h1);
+  dst[i1 + 4] = __builtin_bit_cast(uint16_t, l1);
+}
+
+// Copies nbytes starting at src (inside [pool, pool_end)) into the 16-byte
+// aligned LDS buffer dst with 16-byte loads from the aligned-down address;
+// returns the offset of src's first byte inside dst.  Loads that would cross
+// pool_end are skipped (their bytes only belong to masked tokens).
+__device__ __forceinline__ int stage(uint8_t *dst, const uint8_t *src, int nbytes, const uint8_t *pool,
+                                     const uint8_t *pool_end, int lane) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src);
+  const uintptr_t a0 = a & ~(uintptr_t)15;
+  const int off = (int)(a - a0);
+  const int n16 = (off + nbytes + 15) >> 4;
+  const uintptr_t beg = reinterpret_cast<uintptr_t>(pool);
+  const uintptr_t end = reinterpret_cast<uintptr_t>(pool_end);
+  for (int i = lane; i < n16; i += 64) {
+    const uintptr_t p = a0 + 16 * (uintptr_t)i;
+    if (p >= beg && p + 16 <= end) *reinterpret_cast<uint4 *>(dst + 16 * i) = *reinterpret_cast<const uint4 *>(p);
+  }
+  return off;
+}
+
+__device__ __forceinline__ uint32_t load_le32(const uint8_t *p) {
+  return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+// ---------------------------------------------------------------- split-K
+__global__ void __launch_bounds__(256) attn_splitk_kernel(AttnArgs a, Tables tk, Tables tv) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint2 *lutk = reinterpret_cast<uint2 *>(smem);
+  uint2 *lutv = lutk + kM;
+  build_lut(lutk, tk, threadIdx.x, blockDim.x);
+  build_lut(lutv, tv, threadIdx.x, blockDim.x);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int Ck = tk.C, Cv = tv.C;
+  // per-wave LDS slice
+  uint8_t *base = smem + kLutBytes + (size_t)wave * a.wave_bytes;
+  const int kst_bytes = ((kTile * Ck + 31) & ~15);
+  const int vst_bytes = ((kTile * Cv + 31) & ~15);
+  uint8_t *kst = base;
+  uint8_t *vst = kst + kst_bytes;
+  uint16_t *knl = reinterpret_cast<uint16_t *>(vst + vst_bytes);
+  uint16_t *vnl = knl + kTile;
+  uint4 *qr = reinterpret_cast<uint4 *>(vnl + kTile);          // [32][4] x 16 B
+  uint16_t *pl = reinterpret_cast<uint16_t *>(qr + 32 * 4);     // [4][64]
+  uint16_t *vt = pl + 4 * kTile;                                // [128][kVtStride]
+
+  const uint8_t *kpool_end = a.kc + (size_t)a.Hkv * a.S * Ck;
+  const uint8_t *vpool_end = a.vc + (size_t)a.Hkv * a.S * Cv;
+  const int64_t W = (int64_t)gridDim.x * a.waves_per_block;
+  const int hl = lane & 3;       // head of this lane's score column
+  const int tq = lane >> 2;      // token quad of this lane's score column
+
+  for (int64_t item = (int64_t)blockIdx.x * a.waves_per_block + wave; item < a.n_items; item += W) {
+    const int c = (int)(item % a.nc);
+    const int64_t bg = item / a.nc;
+    const int b = (int)(bg / a.Hkv), g = (int)(bg - (int64_t)b * a.Hkv);
+    const int len = a.seq_len[b];
+    const int t0 = c * a.chunk;
+    if (t0 >= len) continue;
+    const int t1 = min(t0 + a.chunk, len);
+    const int64_t start = a.seq_start[b];
+
+    // rotated query of this (b, g): 2 KB into LDS
+    const uint4 *qsrc = reinterpret_cast<const uint4 *>(a.qrot + bg * kQrotPerBG);
+    qr[lane] = qsrc[lane];
+    qr[lane + 64] = qsrc[lane + 64];
+
+    float m_run = -__builtin_inff(), l_run = 0.0f;
+    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+
+    for (int ts = t0; ts < t1; ts += kTile) {
+      const int64_t slot0 = start + ts;
+      wave_sync();  // previous tile's LDS reads are done
+      const int koff = stage(kst, a.kc + ((int64_t)g * a.S + slot0) * Ck, kTile * Ck, a.kc, kpool_end, lane);
+      const int voff = stage(vst, a.vc + ((int64_t)g * a.S + slot0) * Cv, kTile * Cv, a.vc, vpool_end, lane);
+      const int64_t ns = slot0 + lane;
+      const bool in_pool = ns >= 0 && ns < a.S;
+      knl[lane] = in_pool ? a.kn[(int64_t)g * a.S + ns] : (uint16_t)0;
+      vnl[lane] = in_pool ? a.vn[(int64_t)g * a.S + ns] : (uint16_t)0;
+      wave_sync();
+
+      // ---- K: decode + QK^T on MFMA, 4 dims per step
+      floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+      {
+        const uint8_t *pb = kst + koff + lane * Ck;
+        uint32_t x = load_le32(pb);
+        pb += 4;
+        for (int cc = 0; cc < 32; ++cc) {
+          uint32_t lv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint2 e = rans_step(x, lutk);
+            const uint32_t byte = *pb;
+            const bool need = x < kLow;
+            x = need ? ((x << 8) | byte) : x;
+            pb += need ? 1 : 0;
+            lv[j] = e.y;
+          }
+          const uint32_t a01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
+          const uint32_t a23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
+          const half4 A = __builtin_bit_cast(half4, make_uint2(a01, a23));
+          const uint4 qv = qr[cc * 4 + hl];
+          const half4 Qh = __builtin_bit_cast(half4, make_uint2(qv.x, qv.y));
+          const half4 Ql = __builtin_bit_cast(half4, make_uint2(qv.z, qv.w));
+          sc = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Qh, sc, 0, 0, 0);
+          sc = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Ql, sc, 0, 0, 0);
+        }
+      }
+      // this lane holds scores of tokens 4*tq + r (r = 0..3) for head hl
+      const uint2 kn4 = *reinterpret_cast<const uint2 *>(knl + 4 * tq);
+      const uint2 vn4 = *reinterpret_cast<const uint2 *>(vnl + 4 * tq);
+      const uint32_t knw[2] = {kn4.x, kn4.y}, vnw[2] = {vn4.x, vn4.y};
+      float s[4], mt = -__builtin_inff();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t kh = (knw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu;
+        const float nk = (float)__builtin_bit_cast(_Float16, (uint16_t)kh);
+        const bool valid = ts + 4 * tq + r < t1;
+        s[r] = valid ? sc[r] * nk * a.qk_scale : -__builtin_inff();
+        mt = fmaxf(mt, s[r]);
+      }
+#pragma unroll
+      for (int w = 4; w < 64; w <<= 1) mt = fmaxf(mt, __shfl_xor(mt, w));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);
+      float psum = 0.0f;
+      uint32_t pw[2] = {0u, 0u};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool valid = ts + 4 * tq + r < t1;
+        const float p = valid ? exp2f(s[r] - m_new) : 0.0f;
+        psum += p;
+        const uint32_t vh = (vnw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu;
+        const float nv = (float)__builtin_bit_cast(_Float16, (uint16_t)vh);
+        const float pv = valid ? p * nv : 0.0f;
+        pw[r >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)pv) << (16 * (r & 1));
+      }
+#pragma unroll
+      for (int w = 4; w < 64; w <<= 1) psum += __shfl_xor(psum, w);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      *reinterpret_cast<uint2 *>(pl + hl * kTile + 4 * tq) = make_uint2(pw[0], pw[1]);
+      {
+        const float a0 = __shfl(alpha, 0), a1 = __shfl(alpha, 1), a2 = __shfl(alpha, 2), a3 = __shfl(alpha, 3);
+        acc0[0] *= a0; acc0[1] *= a1; acc0[2] *= a2; acc0[3] *= a3;
+        acc1[0] *= a0; acc1[1] *= a1; acc1[2] *= a2; acc1[3] *= a3;
+      }
+
+      // ---- V: decode into the transposed LDS tile
+      {
+        const uint8_t *pb = vst + voff + lane * Cv;
+        uint32_t x = load_le32(pb);
+        pb += 4;
+        uint16_t *col = vt + lane;
+        for (int i = 0; i < kD; i += 4) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint2 e = rans_step(x, lutv);
+            const uint32_t byte = *pb;
+            const bool need = x < kLow;
+            x = need ? ((x << 8) | byte) : x;
+            pb += need ? 1 : 0;
+            col[(i + j) * kVtStride] = (uint16_t)(e.y >> 16);
+          }
+        }
+      }
+      wave_sync();
+      // ---- PV on MFMA: blocks cover 64 dims, k = 4 tokens per step
+#pragma unroll 4
+      for (int cc = 0; cc < 16; ++cc) {
+        const half4 P = *reinterpret_cast<const half4 *>(pl + hl * kTile + 4 * cc);
+        // rows are 33 dwords apart (4-byte aligned): two 4-byte reads each
+        const uint32_t *r0 = reinterpret_cast<const uint32_t *>(vt) + lane * (kVtStride / 2) + 2 * cc;
+        const uint32_t *r1 = r0 + 64 * (kVtStride / 2);
+        const half4 V0 = __builtin_bit_cast(half4, make_uint2(r0[0], r0[1]));
+        const half4 V1 = __builtin_bit_cast(half4, make_uint2(r1[0], r1[1]));
+        acc0 = __builtin_amdgcn_mfma_f32_4x4x4f16(P, V0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_4x4x4f16(P, V1, acc1, 0, 0, 0);
+      }
+    }
+
+    // partial for this item: acc[h][d] for d = lane, 64 + lane; (m, l) per head
+    float *dst = a.part + item * 4 * kPart;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      dst[h * kPart + lane] = acc0[h];
+      dst[h * kPart + 64 + lane] = acc1[h];
+    }
+    if (lane < 4) {
+      dst[lane * kPart + 128] = m_run;
+      dst[lane * kPart + 129] = l_run;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+__global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed) {
+  __shared__ float buf[kD];
+  const int d = threadIdx.x;
+  const int b = blockIdx.x / a.Hq, h = blockIdx.x - b * a.Hq;
+  const int g = h / a.group, hh = h - g * a.group;
+  const int len = a.seq_len[b];
+  const int n = min((len + a.chunk - 1) / a.chunk, a.nc);
+  const float *src = a.part + (((int64_t)b * a.Hkv + g) * a.nc) * 4 * kPart + hh * kPart;
+  float M = -__builtin_inff();
+  for (int c = 0; c < n; ++c) M = fmaxf(M, src[(int64_t)c * 4 * kPart + 128]);
+  float L = 0.0f, o = 0.0f;
+  for (int c = 0; c < n; ++c) {
+    const float *p = src + (int64_t)c * 4 * kPart;
+    const float w = exp2f(p[128] - M);
+    L += w * p[129];
+    o += w * p[d];
+  }
+  buf[d] = o / L;
+  // inverse rotation: o = D_V * H * o' / 128 (H * H = 128 I)
+#pragma unroll
+  for (int w = 1; w < kD; w <<= 1) {
+    __syncthreads();
+    const float v = buf[d], pv = buf[d ^ w];
+    __syncthreads();
+    buf[d] = (d & w) ? pv - v : v + pv;
+  }
+  __syncthreads();
+  const uint64_t sw = dev_splitmix64(vseed, 2ull * (uint64_t)g + (uint64_t)(d >> 6));
+  float r = buf[d] * 0.0078125f;
+  if ((sw >> (d & 63)) & 1ull) r = -r;
+  const int64_t oi = ((int64_t)b * a.Hq + h) * kD + d;
+  if (a.out_bf16) {
+    const uint32_t u = __float_as_uint(r);
+    const uint32_t rb = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
+    reinterpret_cast<uint16_t *>(a.out)[oi] = (r != r) ? (uint16_t)0x7FC0u : (uint16_t)rb;
+  } else {
+    reinterpret_cast<float *>(a.out)[oi] = r;
+  }
+}
+
+// ---------------------------------------------------------------- planning
+struct Plan {
+  int chunk, nc, waves_per_block, blocks, wave_bytes;
+  int64_t n_items;
+  size_t lds, qrot_bytes, part_bytes, total;
+};
+
+int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  }
+  return cus;
+}
+
+int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl) {
+  (void)Hq;
+  const int cus = device_cus();
+  if (cus <= 0) return DQ_ERR_HIP;
+  const int kst = (kTile * Ck + 31) & ~15, vst = (kTile * Cv + 31) & ~15;
+  const int wave_bytes = kst + vst + 2 * kTile * 2 + 32 * 4 * 16 + 4 * kTile * 2 + kD * kVtStride * 2;
+  const int wb = (wave_bytes + 15) & ~15;
+  const int lds_cap = 160 * 1024;
+  int wpb = 4;
+  while (wpb > 1 && kLutBytes + wpb * wb > lds_cap) wpb >>= 1;
+  if (kLutBytes + wpb * wb > lds_cap) return DQ_ERR_UNSUPPORTED;
+  // chunk: aim for ~8 items per resident wave (4 per CU) if every sequence
+  // were max_len; independent of C so the workspace size is too
+  const int64_t waves = (int64_t)cus * 4;
+  int64_t chunk = (max_len * (int64_t)B * Hkv + 8 * waves - 1) / (8 * waves);
+  chunk = ((chunk + kTile - 1) / kTile) * kTile;
+  if (chunk < 256) chunk = 256;
+  if (chunk > 1024) chunk = 1024;
+  if (const char *e = getenv("DQ_SPLIT_TOKENS")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= kTile && v % kTile == 0) chunk = v;
+  }
+  const int64_t nc = (max_len + chunk - 1) / chunk;
+  pl->chunk = (int)chunk;
+  pl->nc = (int)nc;
+  pl->waves_per_block = wpb;
+  pl->wave_bytes = wb;
+  pl->n_items = (int64_t)B * Hkv * nc;
+  pl->lds = (size_t)kLutBytes + (size_t)wpb * wb;
+  const int64_t want_blocks = (pl->n_items + wpb - 1) / wpb;
+  pl->blocks = (int)(want_blocks < cus ? want_blocks : cus);
+  pl->qrot_bytes = ((size_t)B * Hkv * kQrotPerBG * 2 + 255) & ~(size_t)255;
+  pl->part_bytes = (size_t)pl->n_items * 4 * kPart * sizeof(float);
+  pl->total = pl->qrot_bytes + pl->part_bytes;
+  return DQ_OK;
+}
+
+}  // namespace
+}  // namespace dq
+
+extern "C" int dq_attn_decode_workspace(int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, size_t *bytes) {
+  if (!bytes || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_len < 1) return DQ_ERR_INVALID;
+  // the plan depends on C only through the LDS split, not the workspace size
+  dq::Plan pl;
+  const int st = dq::make_plan(B, Hq, Hkv, max_len, 34, 34, &pl);
+  if (st) return st;
+  *bytes = pl.total;
+  return DQ_OK;
+}
+
+extern "C" int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,
+                              const uint8_t *k_cont, const uint16_t *k_norm, const uint8_t *v_cont,
+                              const uint16_t *v_norm, int64_t num_slots, const int64_t *seq_start,
+                              const int32_t *seq_len, int64_t max_len, float sm_scale, int32_t out_dtype,
+                              void *out, void *workspace, size_t ws_bytes, dq_stream_t stream) {
+  if (!ck || !cv || !q || !k_cont || !k_norm || !v_cont || !v_norm || !seq_start || !seq_len || !out ||
+      !workspace)
+    return DQ_ERR_INVALID;
+  const int Hkv = ck->t.hkv;
+  if (cv->t.hkv != Hkv || B < 1 || Hq < 1 || Hq % Hkv || num_slots < 1 || max_len < 1) return DQ_ERR_INVALID;
+  const int group = Hq / Hkv;
+  if (group != 1 && group != 2 && group != 4) return DQ_ERR_UNSUPPORTED;
+  if (out_dtype != 0 && out_dtype != 1) return DQ_ERR_INVALID;
+  if (max_len > (int64_t)1 << 31) return DQ_ERR_INVALID;
+  const uintptr_t kca = reinterpret_cast<uintptr_t>(k_cont), vca = reinterpret_cast<uintptr_t>(v_cont);
+  if ((kca & 15u) || (vca & 15u) || ((num_slots * ck->t.C) & 15) || ((num_slots * cv->t.C) & 15))
+    return DQ_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(q) & 15u) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return DQ_ERR_INVALID;
+  dq::Plan pl;
+  int st = dq::make_plan(B, Hq, Hkv, max_len, ck->t.C, cv->t.C, &pl);
+  if (st) return st;
+  size_t need = 0;
+  st = dq_attn_decode_workspace(B, Hq, Hkv, max_len, &need);
+  if (st) return st;
+  if (ws_bytes < need || pl.total > need) return DQ_ERR_WORKSPACE;
+
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(dq::attn_splitk_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+      return DQ_ERR_HIP;
+    attr_set = true;
+  }
+  dq::AttnArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = group;
+  a.kc = k_cont;
+  a.kn = k_norm;
+  a.vc = v_cont;
+  a.vn = v_norm;
+  a.S = num_slots;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.qk_scale = sm_scale * 1.4426950408889634f / 128.0f;
+  a.chunk = pl.chunk;
+  a.nc = pl.nc;
+  a.n_items = pl.n_items;
+  a.qrot = static_cast<uint16_t *>(workspace);
+  a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.qrot_bytes);
+  a.out = out;
+  a.out_bf16 = out_dtype;
+  a.waves_per_block = pl.waves_per_block;
+  a.wave_bytes = pl.wave_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(dq::rotate_q_kernel, dim3((unsigned)(B * Hkv * 4)), dim3(64), 0, s, a, ck->t.seed);
+  hipLaunchKernelGGL(dq::attn_splitk_kernel, dim3((unsigned)pl.blocks), dim3(64 * pl.waves_per_block), pl.lds, s,
+                     a, ck->t, cv->t);
+  hipLaunchKernelGGL(dq::combine_kernel, dim3((unsigned)(B * Hq)), dim3(128), 0, s, a, cv->t.seed);
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}

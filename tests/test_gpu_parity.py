@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Containers, norms, decoded symbols and drift statistics must be bit-exact;
+attention output (fp32) must be within max-abs 2e-3 and relative-L2 1e-3 of
+the oracle's fp64 result on the same containers.  Inputs come from the seeded
+generator in synth/ (drawn on the GPU, copied to the host for the oracle).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_entropy_amd as dq
+import synth
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, REL_L2 = 2e-3, 1e-3
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _np_bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _codecs(O, levels, C, seed, hkv, step64=0):
+    g = dq.Codec(levels, C, seed=seed, kv_heads=hkv, step64=step64)
+    o = O.Codec(levels, C, seed=seed, hkv=hkv, step64=g.step64)
+    return g, o
+
+
+def _encode_both(O, gc, oc, x, slots, num_slots):
+    cont, norm = dq.alloc_pool(gc, num_slots, DEV)
+    st = dq.new_stats(DEV)
+    dq.encode(gc, x, slots, cont, norm, st)
+    torch.cuda.synchronize()
+    S = cont.shape[1]
+    ocont, onorm, ost = O.encode(oc, _np_bits(x), slots.cpu().numpy(), num_slots=S)
+    return cont, norm, st, ocont, onorm, ost
+
+
+def _assert_encode_equal(cont, norm, st, ocont, onorm, ost, label):
+    gcont = cont.cpu().numpy()
+    gnorm = _np_bits(norm)
+    bad = np.argwhere((gcont != ocont).any(axis=2))
+    assert len(bad) == 0, f"{label}: {len(bad)} containers differ, first {bad[:5].tolist()}"
+    assert (gnorm == onorm).all(), f"{label}: norms differ"
+    assert dq.stats_dict(st) == O_stats(ost), f"{label}: stats differ"
+
+
+def O_stats(ost):
+    import oracle
+    return oracle.stats_dict(ost)
+
+
+@pytest.mark.parametrize("levels,C", [(8, 34), (6, 34), (8, 29), (6, 29)])
+@pytest.mark.parametrize("kind", ["iid", "outlier", "student_t5", "iid_scaled"])
+def test_encode_bit_exact(oracle_lib, levels, C, kind):
+    O = oracle_lib
+    _say(f"encode {levels}/{C} {kind}")
+    T, hkv = 333, 3
+    gc, oc = _codecs(O, levels, C, seed=101 + levels, hkv=hkv)
+    x = synth.kv_tensor(kind, T, hkv, seed=7, device=DEV)
+    perm = torch.randperm(400, generator=torch.Generator().manual_seed(3))[:T]
+    slots = perm.to(DEV)
+    _assert_encode_equal(*_encode_both(O, gc, oc, x, slots, 400), f"{levels}/{C}/{kind}")
+
+
+def _adversarial_batch():
+    rows = []
+    z = np.zeros(128, np.float32)
+    rows.append(z.copy())                                  # zero vector
+    rows.append(np.full(128, 1e-30, np.float32))            # norm underflows fp16
+    rows.append(np.full(128, 1e30, np.float32))             # squares overflow fp32
+    r = z.copy(); r[5] = np.inf; rows.append(r)              # inf
+    r = np.ones(128, np.float32); r[7] = np.nan; rows.append(r)  # nan
+    r = z.copy(); r[0] = 3.3895314e38; rows.append(r)        # largest bf16
+    r = z.copy(); r[:3] = [9.2e-41, -4.6e-41, 1e-39]; rows.append(r)  # bf16 subnormals
+    r = z.copy(); r[:3] = [2048, 64, 1]; rows.append(r)      # |x| = 2049: fp16 tie -> 2048
+    r = z.copy(); r[:4] = [2048, 64, 1, 1]; rows.append(r)   # just above the tie -> 2050
+    r = z.copy(); r[:3] = [1.0, 2.0 ** -5, 2.0 ** -11]; rows.append(r)  # tie at 1 + 2^-11
+    r = z.copy(); r[0] = -0.0; r[1] = 1.0; rows.append(r)    # negative zero
+    r = z.copy(); r[3] = 1.0; rows.append(r)                 # one-hot: |y_i| all equal
+    rows.append(np.where(np.arange(128) % 2 == 0, 1.0, -1.0).astype(np.float32))
+    rows.append((np.arange(128) - 64).astype(np.float32))   # exact integer sums
+    rows.append(np.full(128, 65504.0 / 11.3, np.float32))    # norm near fp16 max
+    rng = np.random.default_rng(0)
+    for _ in range(17):
+        v = rng.standard_normal(128).astype(np.float32)
+        v[rng.integers(0, 128, 6)] *= 10 ** rng.uniform(-3, 3)
+        rows.append(v)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("levels,C,step64", [(8, 34, 0), (6, 34, 0), (8, 29, 0), (6, 29, 0),
+                                             (8, 34, 64), (6, 34, 64), (4, 24, 64), (16, 60, 50)])
+def test_encode_adversarial(oracle_lib, levels, C, step64):
+    """Degenerate norms, fp16 rounding ties, exact threshold ties (step 1.0
+    and one-hot inputs put |y| exactly on a threshold), subnormals."""
+    O = oracle_lib
+    _say(f"adversarial {levels}/{C}/{step64}")
+    rows = _adversarial_batch()
+    x = torch.from_numpy(rows).to(torch.bfloat16).reshape(-1, 1, 128).to(DEV)
+    gc, oc = _codecs(O, levels, C, seed=5, hkv=1, step64=step64)
+    slots = torch.arange(x.shape[0], dtype=torch.int64, device=DEV)
+    _assert_encode_equal(*_encode_both(O, gc, oc, x, slots, x.shape[0]), "adversarial")
+
+
+def test_encode_strided_input_and_pool_slots(oracle_lib):
+    O = oracle_lib
+    gc, oc = _codecs(O, 8, 34, seed=9, hkv=4)
+    big = synth.kv_tensor("outlier", 200, 8, seed=11, device=DEV)
+    x = big[:, 1::2]  # stride_h = 256 elements
+    assert x.stride(1) == 256
+    slots = torch.arange(1000, 1200, dtype=torch.int64, device=DEV)
+    cont, norm, st, ocont, onorm, ost = _encode_both(O, gc, oc, x, slots, 1300)
+    _assert_encode_equal(cont, norm, st, ocont, onorm, ost, "strided")
+    # untouched slots stay zero
+    assert int(cont[:, :1000].abs().sum()) == 0
+
+
+@pytest.mark.parametrize("levels,C", [(8, 34), (6, 29)])
+def test_decode_symbols_bit_exact(oracle_lib, levels, C):
+    O = oracle_lib
+    gc, oc = _codecs(O, levels, C, seed=21, hkv=2)
+    x = synth.kv_tensor("outlier", 500, 2, seed=4)
+    ocont, _, _ = O.encode(oc, _np_bits(x))
+    S = dq.pool_slots(500, C)
+    pool = np.zeros((2, S, C), np.uint8)
+    pool[:, :500] = ocont
+    # corrupted containers: random bytes in slots 500..S-1 and a few overwritten
+    rng = np.random.default_rng(1)
+    pool[:, 500:] = rng.integers(0, 256, (2, S - 500, C))
+    pool[:, 3] = rng.integers(0, 256, (2, C))
+    gpool = torch.from_numpy(pool).to(DEV)
+    for head in range(2):
+        slots = np.arange(S)
+        sym, fs, cons = dq.decode_symbols(gc, gpool, head, torch.from_numpy(slots).to(DEV))
+        osym, ofs, ocons = O.decode_symbols(oc, pool, head, slots)
+        assert (sym.cpu().numpy() == osym).all()
+        assert (fs.cpu().numpy() == ofs).all()
+        assert (cons.cpu().numpy() == ocons).all()
+        valid = [s for s in range(500) if s != 3]
+        assert (ofs[valid] == 1 << 23).all()
+
+
+def _attn_case(O, B, Hq, hkv, lens, kinds=("outlier", "outlier"), C=(34, 34), seed=0, gap=5):
+    ck, ock = _codecs(O, 8, C[0], seed=seed + 1, hkv=hkv)
+    cv, ocv = _codecs(O, 6, C[1], seed=seed + 2, hkv=hkv)
+    starts, s = [], 0
+    for L in lens:
+        starts.append(s)
+        s += L + gap
+    total = s
+    K = synth.kv_tensor(kinds[0], total, hkv, seed=seed + 3, device=DEV)
+    V = synth.kv_tensor(kinds[1], total, hkv, seed=seed + 4, device=DEV)
+    q = synth.q_tensor(B, Hq, seed=seed + 5, device=DEV)
+    slots = torch.arange(total, dtype=torch.int64, device=DEV)
+    kc, kn = dq.alloc_pool(ck, total, DEV)
+    vc, vn = dq.alloc_pool(cv, total, DEV)
+    dq.encode(ck, K, slots, kc, kn)
+    dq.encode(cv, V, slots, vc, vn)
+    ss = torch.tensor(starts, dtype=torch.int64, device=DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    return dict(ck=ck, cv=cv, ock=ock, ocv=ocv, q=q, kc=kc, kn=kn, vc=vc, vn=vn, ss=ss, sl=sl,
+                starts=np.array(starts), lens=np.array(lens, np.int32))
+
+
+def _oracle_attn(O, c, rows=None, sm_scale=None):
+    idx = np.arange(len(c["lens"])) if rows is None else np.asarray(rows)
+    return O.attention(c["ock"], c["ocv"], _np_bits(c["q"])[idx], c["kc"].cpu().numpy(),
+                       _np_bits(c["kn"]), c["vc"].cpu().numpy(), _np_bits(c["vn"]),
+                       c["starts"][idx], c["lens"][idx], sm_scale=sm_scale)
+
+
+def _gpu_attn(c, max_len=None, **kw):
+    out = dq.attn_decode(c["ck"], c["cv"], c["q"], c["kc"], c["kn"], c["vc"], c["vn"], c["ss"],
+                         c["sl"], int(max_len or c["lens"].max()), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _assert_close(got, ref, label):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    _say(f"{label}: max-abs {err.max():.3e} rel-L2 {rel:.3e} worst {worst}")
+    assert err.max() <= MAX_ABS and rel <= REL_L2, label
+
+
+@pytest.mark.parametrize("Hq,hkv", [(8, 2), (4, 4), (4, 2), (1, 1)])
+def test_attention_ragged_small(oracle_lib, Hq, hkv):
+    O = oracle_lib
+    lens = [1, 63, 64, 65, 300, 129]
+    c = _attn_case(O, len(lens), Hq, hkv, lens, seed=Hq * 10 + hkv)
+    _assert_close(_gpu_attn(c).cpu().numpy(), _oracle_attn(O, c), f"ragged Hq={Hq} hkv={hkv}")
+
+
+def test_attention_split_invariance_and_bf16(oracle_lib):
+    O = oracle_lib
+    lens = [2000, 777, 1500]
+    c = _attn_case(O, 3, 8, 2, lens, kinds=("iid_scaled", "student_t5"), C=(34, 29), seed=3)
+    ref = _oracle_attn(O, c, sm_scale=0.11)
+    outs = []
+    for split in ("64", "256", "1024", ""):
+        if split:
+            os.environ["DQ_SPLIT_TOKENS"] = split
+        else:
+            os.environ.pop("DQ_SPLIT_TOKENS", None)
+        o = _gpu_attn(c, sm_scale=0.11).cpu().numpy()
+        _assert_close(o, ref, f"split={split or 'default'}")
+        outs.append(o)
+    os.environ.pop("DQ_SPLIT_TOKENS", None)
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() < 1e-4
+    ob = _gpu_attn(c, sm_scale=0.11, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.abs(ob - outs[-1]).max() <= np.abs(outs[-1]).max() * 2 ** -8
+
+
+def test_attention_deterministic(oracle_lib):
+    O = oracle_lib
+    c = _attn_case(O, 2, 8, 2, [3000, 1234], seed=8)
+    a = _gpu_attn(c)
+    b = _gpu_attn(c)
+    assert torch.equal(a, b)
+
+
+def test_tiny_1seq_1k_config(oracle_lib):
+    """1 sequence, 1 query / 1 kv head, context 1024, per-token scaled
+    N(0,1) K/V, 34-byte containers: every container and the output."""
+    O = oracle_lib
+    w = synth.workloads()["tiny_1seq_1k"]
+    ck, ock = _codecs(O, 8, 34, seed=w.seed, hkv=1)
+    cv, ocv = _codecs(O, 6, 34, seed=w.seed + 1, hkv=1)
+    K = synth.kv_tensor(w.kind, 1024, 1, seed=w.seed + 10, device=DEV)
+    V = synth.kv_tensor(w.kind, 1024, 1, seed=w.seed + 11, device=DEV)
+    slots = torch.arange(1024, dtype=torch.int64, device=DEV)
+    for gc, oc, x in ((ck, ock, K), (cv, ocv, V)):
+        _assert_encode_equal(*_encode_both(O, gc, oc, x, slots, 1024), "tiny")
+    c = _attn_case(O, 1, 1, 1, [1024], kinds=(w.kind, w.kind), seed=w.seed)
+    _assert_close(_gpu_attn(c).cpu().numpy(), _oracle_attn(O, c), "tiny attention")
+
+
+def test_qwen3_shape_full_encode_and_sampled_attention(oracle_lib):
+    """Batch 16 x 8192 context, 32 q / 8 kv heads, outlier channels, 34-byte
+    containers: every K and V container bit-exact; attention rows of two
+    sequences against the oracle, in the launch configuration the bench uses."""
+    O = oracle_lib
+    w = synth.workloads()["qwen3_8b_b16_8k"]
+    B, Hq, hkv, ctx = w.batch, w.hq, w.hkv, w.ctx[0]
+    total = B * ctx
+    _say("qwen3-shape: encode")
+    ck, ock = _codecs(O, 8, 34, seed=w.seed, hkv=hkv)
+    cv, ocv = _codecs(O, 6, 34, seed=w.seed + 1, hkv=hkv)
+    K = synth.kv_tensor(w.kind, total, hkv, seed=w.seed + 10, device=DEV)
+    V = synth.kv_tensor(w.kind, total, hkv, seed=w.seed + 11, device=DEV)
+    slots = torch.arange(total, dtype=torch.int64, device=DEV)
+    pools = {}
+    for name, gc, oc, x in (("K", ck, ock, K), ("V", cv, ocv, V)):
+        cont, norm, st, ocont, onorm, ost = _encode_both(O, gc, oc, x, slots, total)
+        _assert_encode_equal(cont, norm, st, ocont, onorm, ost, f"qwen3 {name}")
+        s = dq.stats_dict(st)
+        _say(f"qwen3 {name}: drift rate {s['drifted_symbols'] / (128 * s['vectors']):.4%}, "
+             f"multilevel {s['multilevel_events']}")
+        pools[name] = (cont, norm)
+    _say("qwen3-shape: attention")
+    q = synth.q_tensor(B, Hq, seed=w.seed + 12, device=DEV)
+    ss = torch.arange(B, dtype=torch.int64, device=DEV) * ctx
+    sl = torch.full((B,), ctx, dtype=torch.int32, device=DEV)
+    out = dq.attn_decode(ck, cv, q, *pools["K"], *pools["V"], ss, sl, ctx)
+    torch.cuda.synchronize()
+    rows = [0, 9]
+    ref = O.attention(ock, ocv, _np_bits(q)[rows], pools["K"][0].cpu().numpy(), _np_bits(pools["K"][1]),
+                      pools["V"][0].cpu().numpy(), _np_bits(pools["V"][1]),
+                      ss.cpu().numpy()[rows], sl.cpu().numpy()[rows])
+    _assert_close(out.cpu().numpy()[rows], ref, "qwen3 attention rows 0, 9")
