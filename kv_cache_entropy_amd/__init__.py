@@ -105,12 +105,11 @@ class Codec:
             self._h = None
 
 
-def pool_slots(num_slots: int, C: int) -> int:
-    """Smallest slot count >= num_slots with num_slots * C a multiple of 16."""
-    n = num_slots
-    while (n * C) % 16:
-        n += 1
-    return n
+def pool_slots(num_slots: int, C: int = 0) -> int:
+    """num_slots rounded up to a multiple of 16, so that slots * C is a
+    multiple of 16 bytes for every container size (K and V pools with
+    different C then share slot numbering)."""
+    return (num_slots + 15) // 16 * 16
 
 
 def alloc_pool(codec: Codec, num_slots: int, device="cuda"):

@@ -51,7 +51,7 @@ def test_status_strings_and_version():
 @pytest.mark.parametrize("levels,C,step64", [
     (8, 34, 0), (6, 34, 0), (8, 29, 0), (6, 29, 0),
     (8, 34, 60), (8, 34, 80), (6, 29, 70), (4, 24, 64), (2, 20, 64),
-    (10, 40, 64), (12, 48, 60), (16, 60, 50), (6, 132, 30), (8, 64, 40)])
+    (10, 40, 64), (12, 48, 60), (16, 60, 25), (16, 60, 50), (6, 132, 30), (8, 64, 40)])
 def test_tables_match_oracle(oracle_lib, levels, C, step64):
     O = oracle_lib
     seed = 0xDEADBEEF12345 + levels

@@ -99,7 +99,7 @@ def _adversarial_batch():
 
 
 @pytest.mark.parametrize("levels,C,step64", [(8, 34, 0), (6, 34, 0), (8, 29, 0), (6, 29, 0),
-                                             (8, 34, 64), (6, 34, 64), (4, 24, 64), (16, 60, 50)])
+                                             (8, 34, 64), (6, 34, 64), (4, 30, 64), (16, 60, 25), (10, 40, 34)])
 def test_encode_adversarial(oracle_lib, levels, C, step64):
     """Degenerate norms, fp16 rounding ties, exact threshold ties (step 1.0
     and one-hot inputs put |y| exactly on a threshold), subnormals."""
@@ -191,8 +191,9 @@ def _assert_close(got, ref, label):
     err = np.abs(got - ref)
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     worst = np.unravel_index(np.argmax(err), err.shape)
-    _say(f"{label}: max-abs {err.max():.3e} rel-L2 {rel:.3e} worst {worst}")
-    assert err.max() <= MAX_ABS and rel <= REL_L2, label
+    emax = float(err.max())
+    _say(f"{label}: max-abs {emax:.3e} rel-L2 {rel:.3e} worst {tuple(int(i) for i in worst)}")
+    assert emax <= MAX_ABS and rel <= REL_L2, (label, emax, rel)
 
 
 @pytest.mark.parametrize("Hq,hkv", [(8, 2), (4, 4), (4, 2), (1, 1)])
@@ -219,9 +220,11 @@ def test_attention_split_invariance_and_bf16(oracle_lib):
         outs.append(o)
     os.environ.pop("DQ_SPLIT_TOKENS", None)
     for o in outs[1:]:
-        assert np.abs(o - outs[0]).max() < 1e-4
+        spread = float(np.abs(o - outs[0]).max())
+        assert spread < MAX_ABS / 4, spread
     ob = _gpu_attn(c, sm_scale=0.11, out_dtype=torch.bfloat16).float().cpu().numpy()
-    assert np.abs(ob - outs[-1]).max() <= np.abs(outs[-1]).max() * 2 ** -8
+    bf_err = float(np.abs(ob - outs[-1]).max())
+    assert bf_err <= float(np.abs(outs[-1]).max()) * 2 ** -8, bf_err
 
 
 def test_attention_deterministic(oracle_lib):
