@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the D-Quant hot path on one MI355X.
+
+Workload (default): Llama-3.1-8B-shaped layer at its maximum batch -- batch
+128, 32 query / 8 kv heads, head_dim 128, 8K-token prompt, 34-byte containers
+(2.25 bits/value with the fp16 norm), keys 8 levels, values 6, bf16 K/V with 4
+outlier channels per head.  Synthetic data (synth/), no model weights.
+
+Untimed setup: draw K/V, encode the whole prompt into the compressed pools
+(timed separately for encode vectors/s).  One timed step = one decode step:
+  dq_encode of the new token's K and V for every sequence (append), then
+  dq_attn_decode for every sequence over its grown context.
+`value` = compressed KV bytes (containers + fp16 norms) read by attention per
+step / wall time per step.  The roofline entry measures the attention call
+alone with HIP events on its stream inside the timed region.
+
+    python bench.py [--steps 16] [--warmup 3] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+COUNTERS = os.path.join(ROOT, "profiles", "attn_splitk_llama31_8b_b128_8k_counters.json")
+ATTN_SOURCES = ["kv_cache_entropy_amd/csrc/attention.hip", "kv_cache_entropy_amd/csrc/decode_common.h",
+                "kv_cache_entropy_amd/csrc/dq_internal.h"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attn_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(bytes_per_launch_alg):
+    """HBM bytes per attention launch from committed rocprofv3 counters, or
+    None when they were taken on a different kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha256_16") != attn_source_hash():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, ck, cv, kc, kn, vc, vn, q, starts, ctx, seconds):
+    """The oracle, as it stands, on a bounded sample: decode attention for the
+    first n sequences (n grown until ~`seconds` of CPU work), on the host
+    cores this process may use."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    ock = oracle.Codec(8, ck.C, seed=ck.seed, hkv=ck.kv_heads, step64=ck.step64)
+    ocv = oracle.Codec(6, cv.C, seed=cv.seed, hkv=cv.kv_heads, step64=cv.step64)
+    qb = synth.bf16_bits(q)
+    done_bytes, done_tokens, elapsed, n = 0, 0, 0.0, 0
+    per_tok = w.hkv * (ck.C + 2 + cv.C + 2)
+    while elapsed < seconds and n < w.batch:
+        b = n
+        lo, hi = int(starts[b]), int(starts[b]) + int(ctx[b])
+        kcs = np.ascontiguousarray(kc[:, lo:hi].cpu().numpy())
+        vcs = np.ascontiguousarray(vc[:, lo:hi].cpu().numpy())
+        kns = synth.bf16_bits(kn[:, lo:hi])
+        vns = synth.bf16_bits(vn[:, lo:hi])
+        t0 = time.perf_counter()
+        oracle.attention(ock, ocv, qb[b:b + 1], kcs, kns, vcs, vns, np.array([0]),
+                         np.array([hi - lo], np.int32), nthreads=threads)
+        elapsed += time.perf_counter() - t0
+        done_bytes += (hi - lo) * per_tok
+        done_tokens += hi - lo
+        n += 1
+    # oracle encode on one sequence's K vectors
+    xk = synth.kv_tensor(w.kind, min(2048, int(ctx[0])), w.hkv, seed=w.seed + 10)
+    t0 = time.perf_counter()
+    oracle.encode(ock, synth.bf16_bits(xk), nthreads=threads)
+    enc_s = time.perf_counter() - t0
+    return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 decode attention of {n} of {w.batch} sequences "
+                      f"({done_tokens} context tokens x {w.hkv} kv heads, {w.hq} q heads) "
+                      f"in {elapsed:.1f} s; encode of {xk.shape[0] * w.hkv} K vectors",
+            "context_tokens_per_s": done_tokens / elapsed,
+            "encode_vectors_per_s": xk.shape[0] * w.hkv / enc_s}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=16)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama31_8b_b128_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter scale for rocprofv3)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_entropy_amd as dq
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.workloads()[args.workload]
+    B, Hq, Hkv = w.batch, w.hq, w.hkv
+    ctx = np.array(w.ctx, np.int64)
+    nsteps = args.warmup + args.steps
+    cap = ctx + nsteps + w.append_tokens
+    starts = np.concatenate([[0], np.cumsum(cap)[:-1]])
+    S_total = int(cap.sum())
+    ck = dq.Codec(w.levels_k, w.container_k, seed=w.seed, kv_heads=Hkv)
+    cv = dq.Codec(w.levels_v, w.container_v, seed=w.seed + 1, kv_heads=Hkv)
+    kc, kn = dq.alloc_pool(ck, S_total, dev)
+    vc, vn = dq.alloc_pool(cv, S_total, dev)
+    log(f"[bench] workload {w.name}: B={B} Hq={Hq} Hkv={Hkv} ctx={int(ctx.min())}..{int(ctx.max())} "
+        f"pool {S_total} slots, containers {ck.C}/{cv.C} B")
+
+    # ---- prefill encode (untimed for the step; timed on its own)
+    T_pre = int(ctx.sum())
+    slots_pre = torch.from_numpy(np.concatenate([np.arange(s, s + L) for s, L in zip(starts, ctx)])).to(dev)
+    K = synth.kv_tensor(w.kind, T_pre, Hkv, seed=w.seed + 10, device=dev)
+    V = synth.kv_tensor(w.kind, T_pre, Hkv, seed=w.seed + 11, device=dev)
+    stk, stv = dq.new_stats(dev), dq.new_stats(dev)
+    torch.cuda.synchronize()
+    e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_a.record()
+    dq.encode(ck, K, slots_pre, kc, kn, stk)
+    dq.encode(cv, V, slots_pre, vc, vn, stv)
+    e_b.record()
+    torch.cuda.synchronize()
+    prefill_ms = e_a.elapsed_time(e_b)
+    prefill_vps = 2 * T_pre * Hkv / (prefill_ms / 1e3)
+    sk, sv = dq.stats_dict(stk), dq.stats_dict(stv)
+    drift_k = sk["drifted_symbols"] / (128.0 * sk["vectors"])
+    drift_v = sv["drifted_symbols"] / (128.0 * sv["vectors"])
+    log(f"[bench] prefill encode {2 * T_pre * Hkv} vectors in {prefill_ms:.2f} ms "
+        f"({prefill_vps / 1e9:.2f} G vectors/s); drift K {drift_k:.3%} V {drift_v:.3%}")
+    del K, V
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b2 = torch.empty_like(a)
+        b2.copy_(a)
+        torch.cuda.synchronize()
+        del a, b2
+
+    # ---- decode steps: inputs drawn up front
+    Kn = synth.kv_tensor(w.kind, nsteps * B, Hkv, seed=w.seed + 20, device=dev).view(nsteps, B, Hkv, 128)
+    Vn = synth.kv_tensor(w.kind, nsteps * B, Hkv, seed=w.seed + 21, device=dev).view(nsteps, B, Hkv, 128)
+    qs = [synth.q_tensor(B, Hq, seed=w.seed + 100 + s, device=dev) for s in range(nsteps)]
+    st_t = torch.from_numpy(starts).to(dev)
+    slots_s = [(st_t + torch.from_numpy(ctx).to(dev) + s).contiguous() for s in range(nsteps)]
+    lens_s = [torch.from_numpy(ctx + s + 1).to(torch.int32).to(dev) for s in range(nsteps)]
+    max_len = int(ctx.max()) + nsteps
+    ws = torch.empty(dq.attn_workspace_bytes(B, Hq, Hkv, max_len), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    per_tok = Hkv * (ck.C + 2 + cv.C + 2)
+    bytes_s = [int((ctx + s + 1).sum()) * per_tok for s in range(nsteps)]
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        dq.encode(ck, Kn[s], slots_s[s], kc, kn)
+        dq.encode(cv, Vn[s], slots_s[s], vc, vn)
+        if ev is not None:
+            ev[1].record()
+        dq.attn_decode(ck, cv, qs[s], kc, kn, vc, vn, st_t, lens_s[s], max_len, out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = [evs[k][0].elapsed_time(evs[k][1]) for k in range(args.steps)]
+    att_ms = [evs[k][1].elapsed_time(evs[k][2]) for k in range(args.steps)]
+    ev_total = evs[0][0].elapsed_time(evs[-1][2])
+    total_s = max(wall, ev_total / 1e3)
+    timed_bytes = sum(bytes_s[args.warmup:])
+    ms_per_step = total_s * 1e3 / args.steps
+    value = timed_bytes / total_s / 1e9
+    att_avg_ms = sum(att_ms) / len(att_ms)
+    alg_bytes = timed_bytes / args.steps
+    achieved = alg_bytes / (att_avg_ms / 1e3) / 1e9
+    ctx_tokens = sum(int((ctx + args.warmup + k + 1).sum()) for k in range(args.steps))
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (append encode {np.mean(enc_ms):.3f} ms, "
+        f"attention {att_avg_ms:.3f} ms), {value:.1f} GB/s step, attention {achieved:.1f} GB/s "
+        f"= {achieved / HBM_PEAK_GBPS:.1%} of HBM peak")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on host cores")
+        cpu = cpu_baseline(w, ck, cv, kc, kn, vc, vn, qs[0], starts, ctx, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']:.4f} GB/s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": "dq_attn_decode compressed-KV GB/s (decode step incl. append encode)",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32+f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": 128,
+                   "context": [int(ctx.min()), int(ctx.max())], "container_bytes": [ck.C, cv.C],
+                   "levels": [ck.levels, cv.levels], "kv_distribution": w.kind},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic(alg_bytes), "kernel": "dq_attn_decode",
+                     "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(att_avg_ms, 4)},
+        "cpu_baseline": cpu,
+        "attn_context_tokens_per_s": round(ctx_tokens / (sum(att_ms) / 1e3), 1),
+        "append_encode_ms": round(float(np.mean(enc_ms)), 4),
+        "prefill_encode_vectors_per_s": round(prefill_vps, 1),
+        "drift_rate": {"k": round(drift_k, 5), "v": round(drift_v, 5)},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

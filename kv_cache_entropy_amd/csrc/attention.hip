@@ -37,6 +37,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;
 constexpr int kVtStride = 66;    // halves per V-tile row: 33 dwords, spreads LDS banks
+constexpr int kPass = 32;        // dims per V-tile pass
 constexpr int kPart = 132;       // floats per (item, head): acc[128], m, l, pad
 constexpr int kQrotPerBG = 32 * 4 * 8;  // halves per (b, kv head): [chunk][head][hi4 lo4]
 constexpr int kLutBytes = 2 * (int)kM * 8;
@@ -59,7 +60,6 @@ struct AttnArgs {
   void *out;
   int out_bf16;
   int waves_per_block;
-  int wave_bytes;
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -108,31 +108,181 @@ __global__ void __launch_bounds__(64) rotate_q_kernel(AttnArgs a, uint64_t kseed
   dst[i1 + 4] = __builtin_bit_cast(uint16_t, l1);
 }
 
-// Copies nbytes starting at src (inside [pool, pool_end)) into the 16-byte
-// aligned LDS buffer dst with 16-byte loads from the aligned-down address;
-// returns the offset of src's first byte inside dst.  Loads that would cross
-// pool_end are skipped (their bytes only belong to masked tokens).
-__device__ __forceinline__ int stage(uint8_t *dst, const uint8_t *src, int nbytes, const uint8_t *pool,
-                                     const uint8_t *pool_end, int lane) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(src);
-  const uintptr_t a0 = a & ~(uintptr_t)15;
-  const int off = (int)(a - a0);
-  const int n16 = (off + nbytes + 15) >> 4;
-  const uintptr_t beg = reinterpret_cast<uintptr_t>(pool);
-  const uintptr_t end = reinterpret_cast<uintptr_t>(pool_end);
-  for (int i = lane; i < n16; i += 64) {
-    const uintptr_t p = a0 + 16 * (uintptr_t)i;
-    if (p >= beg && p + 16 <= end) *reinterpret_cast<uint4 *>(dst + 16 * i) = *reinterpret_cast<const uint4 *>(p);
-  }
-  return off;
-}
-
 __device__ __forceinline__ uint32_t load_le32(const uint8_t *p) {
   return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
 }
 
 // ---------------------------------------------------------------- split-K
-__global__ void __launch_bounds__(256) attn_splitk_kernel(AttnArgs a, Tables tk, Tables tv) {
+// Per-wave LDS slice (byte offsets), identical on host and device.
+struct WaveLayout {
+  int kst, vst, knl, vnl, qr, pl, vt, bytes;
+};
+__host__ __device__ inline WaveLayout wave_layout(int Ck, int Cv) {
+  WaveLayout w;
+  w.kst = 0;
+  w.vst = w.kst + ((kTile * Ck + 31) & ~15);
+  w.knl = w.vst + ((kTile * Cv + 31) & ~15);
+  w.vnl = w.knl + kTile * 2;
+  w.qr = w.vnl + kTile * 2;
+  w.pl = w.qr + 32 * 4 * 16;
+  w.vt = w.pl + 4 * kTile * 2;
+  w.bytes = w.vt + kPass * kVtStride * 2;
+  w.bytes = (w.bytes + 15) & ~15;
+  return w;
+}
+
+// Container bytes of one 64-token tile, fetched into registers one tile
+// ahead (NQ 16-byte pieces per lane) and committed to LDS when needed.
+template <int NQ>
+struct TileRegs {
+  uint4 q[NQ];
+  int off;
+};
+
+template <int NQ>
+__device__ __forceinline__ void fetch(TileRegs<NQ> &r, const uint8_t *src, int nbytes, const uint8_t *pool,
+                                      const uint8_t *pool_end, int lane) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src);
+  const uintptr_t a0 = a & ~(uintptr_t)15;
+  r.off = (int)(a - a0);
+  const int n16 = (r.off + nbytes + 15) >> 4;
+  const uintptr_t beg = reinterpret_cast<uintptr_t>(pool), end = reinterpret_cast<uintptr_t>(pool_end);
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int i = lane + 64 * k;
+    const uintptr_t p = a0 + 16 * (uintptr_t)i;
+    r.q[k] = (i < n16 && p >= beg && p + 16 <= end) ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int NQ>
+__device__ __forceinline__ void commit(const TileRegs<NQ> &r, uint8_t *dst, int nbytes, int lane) {
+  const int n16 = (r.off + nbytes + 15) >> 4;
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int i = lane + 64 * k;
+    if (i < n16) *reinterpret_cast<uint4 *>(dst + 16 * i) = r.q[k];
+  }
+}
+
+__device__ __forceinline__ void renorm(uint32_t &x, const uint8_t *&p) {
+  const uint32_t byte = *p;
+  const bool need = x < kLow;
+  x = need ? ((x << 8) | byte) : x;
+  p += need ? 1 : 0;
+}
+
+// Decodes one K tile (scores into sc) and/or one V tile (PV into acc),
+// interleaving the two independent rANS chains of each lane.  K: every 4
+// symbols feed a 4x4x4 MFMA (A = the lane's 4 fp16 levels, B = q~ hi / lo).
+// V: levels go to the transposed LDS tile, 32 dims per pass; each pass is
+// contracted with P by 8 MFMAs whose blocks are (8 dim quads) x (2 token
+// halves).
+template <bool DK, bool DV>
+__device__ __forceinline__ void tile_pass(const uint2 *lutk, const uint2 *lutv, const uint8_t *kb,
+                                          const uint8_t *vb, const uint4 *qr, const uint16_t *pl,
+                                          uint16_t *vt, floatx4 &sc, floatx4 (&acc)[4], int lane) {
+  const int hl = lane & 3, th = lane >> 5, row = lane & 31;
+  uint32_t xk = 0, xv = 0;
+  const uint8_t *pk = kb, *pv = vb;
+  if (DK) {
+    xk = load_le32(kb);
+    pk = kb + 4;
+  }
+  if (DV) {
+    xv = load_le32(vb);
+    pv = vb + 4;
+  }
+  uint16_t *col = vt + lane;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    for (int gq = 0; gq < kPass / 4; ++gq) {
+      uint32_t lv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (DK) {
+          const uint2 e = rans_step(xk, lutk);
+          renorm(xk, pk);
+          lv[j] = e.y;
+        }
+        if (DV) {
+          const uint2 e = rans_step(xv, lutv);
+          renorm(xv, pv);
+          col[(gq * 4 + j) * kVtStride] = (uint16_t)(e.y >> 16);
+        }
+      }
+      if (DK) {
+        const uint32_t a01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
+        const uint32_t a23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
+        const half4 A = __builtin_bit_cast(half4, make_uint2(a01, a23));
+        const uint4 qv = qr[(p * (kPass / 4) + gq) * 4 + hl];
+        sc = __builtin_amdgcn_mfma_f32_4x4x4f16(A, __builtin_bit_cast(half4, make_uint2(qv.x, qv.y)), sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_4x4x4f16(A, __builtin_bit_cast(half4, make_uint2(qv.z, qv.w)), sc, 0, 0, 0);
+      }
+    }
+    if (DV) {
+      wave_sync();
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const half4 P = *reinterpret_cast<const half4 *>(pl + hl * kTile + th * 32 + 4 * c);
+        const uint32_t *r = reinterpret_cast<const uint32_t *>(vt) + row * (kVtStride / 2) + th * 16 + 2 * c;
+        const half4 V = __builtin_bit_cast(half4, make_uint2(r[0], r[1]));
+        acc[p] = __builtin_amdgcn_mfma_f32_4x4x4f16(P, V, acc[p], 0, 0, 0);
+      }
+      wave_sync();
+    }
+  }
+}
+
+// Scales a tile's raw scores (lane: tokens 4*tq + r, head hl), updates the
+// running max / sum of head hl, writes P = p * n_v (fp16) to LDS and
+// rescales the V accumulators of all four heads.
+__device__ __forceinline__ void softmax_tile(const floatx4 &sc, const uint16_t *knl, const uint16_t *vnl,
+                                             int valid_tokens, float qk_scale, float &m_run, float &l_run,
+                                             uint16_t *pl, floatx4 (&acc)[4], int lane) {
+  const int hl = lane & 3, tq = lane >> 2;
+  const uint2 kn4 = *reinterpret_cast<const uint2 *>(knl + 4 * tq);
+  const uint2 vn4 = *reinterpret_cast<const uint2 *>(vnl + 4 * tq);
+  const uint32_t knw[2] = {kn4.x, kn4.y}, vnw[2] = {vn4.x, vn4.y};
+  float s[4], mt = -__builtin_inff();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float nk = (float)__builtin_bit_cast(_Float16, (uint16_t)(knw[r >> 1] >> (16 * (r & 1))));
+    s[r] = (4 * tq + r < valid_tokens) ? sc[r] * nk * qk_scale : -__builtin_inff();
+    mt = fmaxf(mt, s[r]);
+  }
+#pragma unroll
+  for (int w = 4; w < 64; w <<= 1) mt = fmaxf(mt, __shfl_xor(mt, w));
+  const float m_new = fmaxf(m_run, mt);
+  const float alpha = exp2f(m_run - m_new);
+  float psum = 0.0f;
+  uint32_t pw[2] = {0u, 0u};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool valid = 4 * tq + r < valid_tokens;
+    const float p = valid ? exp2f(s[r] - m_new) : 0.0f;
+    psum += p;
+    const float nv = (float)__builtin_bit_cast(_Float16, (uint16_t)(vnw[r >> 1] >> (16 * (r & 1))));
+    const float pv = valid ? p * nv : 0.0f;
+    pw[r >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)pv) << (16 * (r & 1));
+  }
+#pragma unroll
+  for (int w = 4; w < 64; w <<= 1) psum += __shfl_xor(psum, w);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  *reinterpret_cast<uint2 *>(pl + hl * kTile + 4 * tq) = make_uint2(pw[0], pw[1]);
+  const float a0 = __shfl(alpha, 0), a1 = __shfl(alpha, 1), a2 = __shfl(alpha, 2), a3 = __shfl(alpha, 3);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    acc[p][0] *= a0;
+    acc[p][1] *= a1;
+    acc[p][2] *= a2;
+    acc[p][3] *= a3;
+  }
+}
+
+template <int NQ>
+__global__ void __launch_bounds__(512) attn_splitk_kernel(AttnArgs a, Tables tk, Tables tv) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint2 *lutk = reinterpret_cast<uint2 *>(smem);
   uint2 *lutv = lutk + kM;
@@ -143,23 +293,19 @@ __global__ void __launch_bounds__(256) attn_splitk_kernel(AttnArgs a, Tables tk,
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int Ck = tk.C, Cv = tv.C;
-  // per-wave LDS slice
-  uint8_t *base = smem + kLutBytes + (size_t)wave * a.wave_bytes;
-  const int kst_bytes = ((kTile * Ck + 31) & ~15);
-  const int vst_bytes = ((kTile * Cv + 31) & ~15);
-  uint8_t *kst = base;
-  uint8_t *vst = kst + kst_bytes;
-  uint16_t *knl = reinterpret_cast<uint16_t *>(vst + vst_bytes);
-  uint16_t *vnl = knl + kTile;
-  uint4 *qr = reinterpret_cast<uint4 *>(vnl + kTile);          // [32][4] x 16 B
-  uint16_t *pl = reinterpret_cast<uint16_t *>(qr + 32 * 4);     // [4][64]
-  uint16_t *vt = pl + 4 * kTile;                                // [128][kVtStride]
+  const WaveLayout L = wave_layout(Ck, Cv);
+  uint8_t *base = smem + kLutBytes + (size_t)wave * L.bytes;
+  uint8_t *kst = base + L.kst;
+  uint8_t *vst = base + L.vst;
+  uint16_t *knl = reinterpret_cast<uint16_t *>(base + L.knl);
+  uint16_t *vnl = reinterpret_cast<uint16_t *>(base + L.vnl);
+  uint4 *qr = reinterpret_cast<uint4 *>(base + L.qr);
+  uint16_t *pl = reinterpret_cast<uint16_t *>(base + L.pl);
+  uint16_t *vt = reinterpret_cast<uint16_t *>(base + L.vt);
 
   const uint8_t *kpool_end = a.kc + (size_t)a.Hkv * a.S * Ck;
   const uint8_t *vpool_end = a.vc + (size_t)a.Hkv * a.S * Cv;
   const int64_t W = (int64_t)gridDim.x * a.waves_per_block;
-  const int hl = lane & 3;       // head of this lane's score column
-  const int tq = lane >> 2;      // token quad of this lane's score column
 
   for (int64_t item = (int64_t)blockIdx.x * a.waves_per_block + wave; item < a.n_items; item += W) {
     const int c = (int)(item % a.nc);
@@ -169,133 +315,85 @@ __global__ void __launch_bounds__(256) attn_splitk_kernel(AttnArgs a, Tables tk,
     const int t0 = c * a.chunk;
     if (t0 >= len) continue;
     const int t1 = min(t0 + a.chunk, len);
-    const int64_t start = a.seq_start[b];
+    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+    const int64_t pbase = (int64_t)g * a.S + a.seq_start[b] + t0;  // pool index of token t0
+    const uint8_t *kplane = a.kc + pbase * Ck;
+    const uint8_t *vplane = a.vc + pbase * Cv;
 
-    // rotated query of this (b, g): 2 KB into LDS
+    wave_sync();  // the previous item's LDS reads are done
     const uint4 *qsrc = reinterpret_cast<const uint4 *>(a.qrot + bg * kQrotPerBG);
     qr[lane] = qsrc[lane];
     qr[lane + 64] = qsrc[lane + 64];
 
+    // norms of a tile: lane t holds token t's (0 past the pool)
+    auto norms = [&](int tile, uint16_t &nk, uint16_t &nv) {
+      const int64_t idx = pbase + tile * kTile + lane;
+      const bool ok = idx >= (int64_t)g * a.S && idx < (int64_t)(g + 1) * a.S;
+      nk = ok ? a.kn[idx] : (uint16_t)0;
+      nv = ok ? a.vn[idx] : (uint16_t)0;
+    };
+    TileRegs<NQ> rk, rv;
+    uint16_t nk, nv;
+    // prologue: K of tile 0
+    fetch<NQ>(rk, kplane, kTile * Ck, a.kc, kpool_end, lane);
+    norms(0, nk, nv);
+    commit<NQ>(rk, kst, kTile * Ck, lane);
+    const int koff0 = rk.off;
+    knl[lane] = nk;
+    vnl[lane] = nv;
+    wave_sync();
+    fetch<NQ>(rv, vplane, kTile * Cv, a.vc, vpool_end, lane);
+    if (ntiles > 1) {
+      fetch<NQ>(rk, kplane + kTile * Ck, kTile * Ck, a.kc, kpool_end, lane);
+      norms(1, nk, nv);
+    }
     float m_run = -__builtin_inff(), l_run = 0.0f;
-    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    floatx4 acc[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+    tile_pass<true, false>(lutk, lutv, kst + koff0 + lane * Ck, nullptr, qr, pl, vt, sc, acc, lane);
+    softmax_tile(sc, knl, vnl, t1 - t0, a.qk_scale, m_run, l_run, pl, acc, lane);
 
-    for (int ts = t0; ts < t1; ts += kTile) {
-      const int64_t slot0 = start + ts;
-      wave_sync();  // previous tile's LDS reads are done
-      const int koff = stage(kst, a.kc + ((int64_t)g * a.S + slot0) * Ck, kTile * Ck, a.kc, kpool_end, lane);
-      const int voff = stage(vst, a.vc + ((int64_t)g * a.S + slot0) * Cv, kTile * Cv, a.vc, vpool_end, lane);
-      const int64_t ns = slot0 + lane;
-      const bool in_pool = ns >= 0 && ns < a.S;
-      knl[lane] = in_pool ? a.kn[(int64_t)g * a.S + ns] : (uint16_t)0;
-      vnl[lane] = in_pool ? a.vn[(int64_t)g * a.S + ns] : (uint16_t)0;
-      wave_sync();
-
-      // ---- K: decode + QK^T on MFMA, 4 dims per step
-      floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-      {
-        const uint8_t *pb = kst + koff + lane * Ck;
-        uint32_t x = load_le32(pb);
-        pb += 4;
-        for (int cc = 0; cc < 32; ++cc) {
-          uint32_t lv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint2 e = rans_step(x, lutk);
-            const uint32_t byte = *pb;
-            const bool need = x < kLow;
-            x = need ? ((x << 8) | byte) : x;
-            pb += need ? 1 : 0;
-            lv[j] = e.y;
-          }
-          const uint32_t a01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
-          const uint32_t a23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
-          const half4 A = __builtin_bit_cast(half4, make_uint2(a01, a23));
-          const uint4 qv = qr[cc * 4 + hl];
-          const half4 Qh = __builtin_bit_cast(half4, make_uint2(qv.x, qv.y));
-          const half4 Ql = __builtin_bit_cast(half4, make_uint2(qv.z, qv.w));
-          sc = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Qh, sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_4x4x4f16(A, Ql, sc, 0, 0, 0);
-        }
-      }
-      // this lane holds scores of tokens 4*tq + r (r = 0..3) for head hl
-      const uint2 kn4 = *reinterpret_cast<const uint2 *>(knl + 4 * tq);
-      const uint2 vn4 = *reinterpret_cast<const uint2 *>(vnl + 4 * tq);
-      const uint32_t knw[2] = {kn4.x, kn4.y}, vnw[2] = {vn4.x, vn4.y};
-      float s[4], mt = -__builtin_inff();
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t kh = (knw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu;
-        const float nk = (float)__builtin_bit_cast(_Float16, (uint16_t)kh);
-        const bool valid = ts + 4 * tq + r < t1;
-        s[r] = valid ? sc[r] * nk * a.qk_scale : -__builtin_inff();
-        mt = fmaxf(mt, s[r]);
-      }
-#pragma unroll
-      for (int w = 4; w < 64; w <<= 1) mt = fmaxf(mt, __shfl_xor(mt, w));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
-      float psum = 0.0f;
-      uint32_t pw[2] = {0u, 0u};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool valid = ts + 4 * tq + r < t1;
-        const float p = valid ? exp2f(s[r] - m_new) : 0.0f;
-        psum += p;
-        const uint32_t vh = (vnw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu;
-        const float nv = (float)__builtin_bit_cast(_Float16, (uint16_t)vh);
-        const float pv = valid ? p * nv : 0.0f;
-        pw[r >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)pv) << (16 * (r & 1));
-      }
-#pragma unroll
-      for (int w = 4; w < 64; w <<= 1) psum += __shfl_xor(psum, w);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      *reinterpret_cast<uint2 *>(pl + hl * kTile + 4 * tq) = make_uint2(pw[0], pw[1]);
-      {
-        const float a0 = __shfl(alpha, 0), a1 = __shfl(alpha, 1), a2 = __shfl(alpha, 2), a3 = __shfl(alpha, 3);
-        acc0[0] *= a0; acc0[1] *= a1; acc0[2] *= a2; acc0[3] *= a3;
-        acc1[0] *= a0; acc1[1] *= a1; acc1[2] *= a2; acc1[3] *= a3;
-      }
-
-      // ---- V: decode into the transposed LDS tile
-      {
-        const uint8_t *pb = vst + voff + lane * Cv;
-        uint32_t x = load_le32(pb);
-        pb += 4;
-        uint16_t *col = vt + lane;
-        for (int i = 0; i < kD; i += 4) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint2 e = rans_step(x, lutv);
-            const uint32_t byte = *pb;
-            const bool need = x < kLow;
-            x = need ? ((x << 8) | byte) : x;
-            pb += need ? 1 : 0;
-            col[(i + j) * kVtStride] = (uint16_t)(e.y >> 16);
-          }
-        }
+    for (int j = 0; j < ntiles; ++j) {
+      const bool next = j + 1 < ntiles;
+      wave_sync();  // every read of the staging buffers and norms is done
+      commit<NQ>(rv, vst, kTile * Cv, lane);
+      const int voff = rv.off;
+      int koff = 0;
+      if (next) {
+        commit<NQ>(rk, kst, kTile * Ck, lane);
+        koff = rk.off;
+        knl[lane] = nk;
+        vnl[lane] = nv;
       }
       wave_sync();
-      // ---- PV on MFMA: blocks cover 64 dims, k = 4 tokens per step
-#pragma unroll 4
-      for (int cc = 0; cc < 16; ++cc) {
-        const half4 P = *reinterpret_cast<const half4 *>(pl + hl * kTile + 4 * cc);
-        // rows are 33 dwords apart (4-byte aligned): two 4-byte reads each
-        const uint32_t *r0 = reinterpret_cast<const uint32_t *>(vt) + lane * (kVtStride / 2) + 2 * cc;
-        const uint32_t *r1 = r0 + 64 * (kVtStride / 2);
-        const half4 V0 = __builtin_bit_cast(half4, make_uint2(r0[0], r0[1]));
-        const half4 V1 = __builtin_bit_cast(half4, make_uint2(r1[0], r1[1]));
-        acc0 = __builtin_amdgcn_mfma_f32_4x4x4f16(P, V0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_4x4x4f16(P, V1, acc1, 0, 0, 0);
+      // prefetch the next iteration's tiles into registers
+      if (next) fetch<NQ>(rv, vplane + (j + 1) * kTile * Cv, kTile * Cv, a.vc, vpool_end, lane);
+      if (j + 2 < ntiles) {
+        fetch<NQ>(rk, kplane + (j + 2) * kTile * Ck, kTile * Ck, a.kc, kpool_end, lane);
+        norms(j + 2, nk, nv);
+      }
+      if (next) {
+        sc = floatx4{0.f, 0.f, 0.f, 0.f};
+        tile_pass<true, true>(lutk, lutv, kst + koff + lane * Ck, vst + voff + lane * Cv, qr, pl, vt, sc, acc,
+                              lane);
+        softmax_tile(sc, knl, vnl, t1 - t0 - (j + 1) * kTile, a.qk_scale, m_run, l_run, pl, acc, lane);
+      } else {
+        tile_pass<false, true>(lutk, lutv, nullptr, vst + voff + lane * Cv, qr, pl, vt, sc, acc, lane);
       }
     }
 
-    // partial for this item: acc[h][d] for d = lane, 64 + lane; (m, l) per head
+    // partial for this item: the two token halves of every dim are summed
+    // across lanes l and l ^ 32; lanes 0..31 hold dims 32p + l.
     float *dst = a.part + item * 4 * kPart;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      dst[h * kPart + lane] = acc0[h];
-      dst[h * kPart + 64 + lane] = acc1[h];
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float v = acc[p][h] + __shfl_xor(acc[p][h], 32);
+        if (lane < 32) dst[h * kPart + p * kPass + lane] = v;
+      }
     }
     if (lane < 4) {
       dst[lane * kPart + 128] = m_run;
@@ -347,7 +445,7 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
 
 // ---------------------------------------------------------------- planning
 struct Plan {
-  int chunk, nc, waves_per_block, blocks, wave_bytes;
+  int chunk, nc, waves_per_block, blocks, nq;
   int64_t n_items;
   size_t lds, qrot_bytes, part_bytes, total;
 };
@@ -366,16 +464,16 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   (void)Hq;
   const int cus = device_cus();
   if (cus <= 0) return DQ_ERR_HIP;
-  const int kst = (kTile * Ck + 31) & ~15, vst = (kTile * Cv + 31) & ~15;
-  const int wave_bytes = kst + vst + 2 * kTile * 2 + 32 * 4 * 16 + 4 * kTile * 2 + kD * kVtStride * 2;
-  const int wb = (wave_bytes + 15) & ~15;
+  const int cmax = Ck > Cv ? Ck : Cv;
+  pl->nq = cmax <= 47 ? 3 : (cmax <= 79 ? 5 : 9);  // 16-byte pieces per lane per tile
+  const int wb = wave_layout(Ck, Cv).bytes;
   const int lds_cap = 160 * 1024;
-  int wpb = 4;
+  int wpb = 8;  // two waves per SIMD when the LDS allows
   while (wpb > 1 && kLutBytes + wpb * wb > lds_cap) wpb >>= 1;
   if (kLutBytes + wpb * wb > lds_cap) return DQ_ERR_UNSUPPORTED;
-  // chunk: aim for ~8 items per resident wave (4 per CU) if every sequence
-  // were max_len; independent of C so the workspace size is too
-  const int64_t waves = (int64_t)cus * 4;
+  // chunk: aim for ~8 items per resident wave (8 waves per CU) if every
+  // sequence were max_len; independent of C so the workspace size is too
+  const int64_t waves = (int64_t)cus * 8;
   int64_t chunk = (max_len * (int64_t)B * Hkv + 8 * waves - 1) / (8 * waves);
   chunk = ((chunk + kTile - 1) / kTile) * kTile;
   if (chunk < 256) chunk = 256;
@@ -388,7 +486,6 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   pl->chunk = (int)chunk;
   pl->nc = (int)nc;
   pl->waves_per_block = wpb;
-  pl->wave_bytes = wb;
   pl->n_items = (int64_t)B * Hkv * nc;
   pl->lds = (size_t)kLutBytes + (size_t)wpb * wb;
   const int64_t want_blocks = (pl->n_items + wpb - 1) / wpb;
@@ -397,6 +494,20 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   pl->part_bytes = (size_t)pl->n_items * 4 * kPart * sizeof(float);
   pl->total = pl->qrot_bytes + pl->part_bytes;
   return DQ_OK;
+}
+
+template <int NQ>
+hipError_t launch_splitk(const Plan &pl, const AttnArgs &a, const Tables &tk, const Tables &tv, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(attn_splitk_kernel<NQ>, dim3((unsigned)pl.blocks), dim3(64 * pl.waves_per_block), pl.lds, s,
+                     a, tk, tv);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -439,13 +550,6 @@ extern "C" int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32
   if (st) return st;
   if (ws_bytes < need || pl.total > need) return DQ_ERR_WORKSPACE;
 
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(dq::attn_splitk_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-      return DQ_ERR_HIP;
-    attr_set = true;
-  }
   dq::AttnArgs a{};
   a.q = static_cast<const uint16_t *>(q);
   a.B = B;
@@ -468,11 +572,12 @@ extern "C" int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32
   a.out = out;
   a.out_bf16 = out_dtype;
   a.waves_per_block = pl.waves_per_block;
-  a.wave_bytes = pl.wave_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(dq::rotate_q_kernel, dim3((unsigned)(B * Hkv * 4)), dim3(64), 0, s, a, ck->t.seed);
-  hipLaunchKernelGGL(dq::attn_splitk_kernel, dim3((unsigned)pl.blocks), dim3(64 * pl.waves_per_block), pl.lds, s,
-                     a, ck->t, cv->t);
+  hipError_t e = pl.nq == 3   ? dq::launch_splitk<3>(pl, a, ck->t, cv->t, s)
+                 : pl.nq == 5 ? dq::launch_splitk<5>(pl, a, ck->t, cv->t, s)
+                              : dq::launch_splitk<9>(pl, a, ck->t, cv->t, s);
+  if (e != hipSuccess) return DQ_ERR_HIP;
   hipLaunchKernelGGL(dq::combine_kernel, dim3((unsigned)(B * Hq)), dim3(128), 0, s, a, cv->t.seed);
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }
