@@ -40,7 +40,7 @@ constexpr int kVtStride = 66;    // halves per V-tile row: 33 dwords, spreads LD
 constexpr int kPass = 32;        // dims per V-tile pass
 constexpr int kPart = 132;       // floats per (item, head): acc[128], m, l, pad
 constexpr int kQrotPerBG = 32 * 4 * 8;  // halves per (b, kv head): [chunk][head][hi4 lo4]
-constexpr int kLutBytes = 2 * (int)kM * 8;
+constexpr int kLutBytes = 2 * kDecodeTableBytes;  // K and V decode tables
 
 struct AttnArgs {
   const uint16_t *q;
@@ -165,11 +165,17 @@ __device__ __forceinline__ void commit(const TileRegs<NQ> &r, uint8_t *dst, int 
   }
 }
 
-__device__ __forceinline__ void renorm(uint32_t &x, const uint8_t *&p) {
-  const uint32_t byte = *p;
+// Byte renormalisation.  The next byte is loaded unconditionally (the load
+// is volatile so the compiler cannot sink it into a branch): the select then
+// stays branch-free and the load overlaps the table lookups of the step.
+__device__ __forceinline__ void renorm(uint32_t &x, const uint8_t *&p, uint32_t byte) {
   const bool need = x < kLow;
   x = need ? ((x << 8) | byte) : x;
   p += need ? 1 : 0;
+}
+typedef const volatile __attribute__((address_space(3))) uint8_t lds_byte;
+__device__ __forceinline__ uint32_t next_byte(const uint8_t *p) {
+  return *(lds_byte *)p;  // p points into LDS (a container staged by this wave)
 }
 
 // Decodes one K tile (scores into sc) and/or one V tile (PV into acc),
@@ -178,8 +184,13 @@ __device__ __forceinline__ void renorm(uint32_t &x, const uint8_t *&p) {
 // V: levels go to the transposed LDS tile, 32 dims per pass; each pass is
 // contracted with P by 8 MFMAs whose blocks are (8 dim quads) x (2 token
 // halves).
+struct DecTab {
+  const uint8_t *sym8;
+  const uint2 *symtab;
+};
+
 template <bool DK, bool DV>
-__device__ __forceinline__ void tile_pass(const uint2 *lutk, const uint2 *lutv, const uint8_t *kb,
+__device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
                                           const uint8_t *vb, const uint4 *qr, const uint16_t *pl,
                                           uint16_t *vt, floatx4 &sc, floatx4 (&acc)[4], int lane) {
   const int hl = lane & 3, th = lane >> 5, row = lane & 31;
@@ -200,14 +211,19 @@ __device__ __forceinline__ void tile_pass(const uint2 *lutk, const uint2 *lutv, 
       uint32_t lv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        uint32_t bk = 0, bv = 0;
+        if (DK) bk = next_byte(pk);
+        if (DV) bv = next_byte(pv);
         if (DK) {
-          const uint2 e = rans_step(xk, lutk);
-          renorm(xk, pk);
+          uint32_t sy;
+          const uint2 e = rans_step(xk, tk.sym8, tk.symtab, sy);
+          renorm(xk, pk, bk);
           lv[j] = e.y;
         }
         if (DV) {
-          const uint2 e = rans_step(xv, lutv);
-          renorm(xv, pv);
+          uint32_t sy;
+          const uint2 e = rans_step(xv, tv.sym8, tv.symtab, sy);
+          renorm(xv, pv, bv);
           col[(gq * 4 + j) * kVtStride] = (uint16_t)(e.y >> 16);
         }
       }
@@ -282,19 +298,22 @@ __device__ __forceinline__ void softmax_tile(const floatx4 &sc, const uint16_t *
 }
 
 template <int NQ>
-__global__ void __launch_bounds__(512) attn_splitk_kernel(AttnArgs a, Tables tk, Tables tv) {
+__global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnArgs a, Tables tk, Tables tv) {
+  // decode tables at fixed LDS addresses (static), per-wave slices after them
+  __shared__ uint8_t sym8[2][kM];
+  __shared__ uint2 symtab[2][kMaxLevels];
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint2 *lutk = reinterpret_cast<uint2 *>(smem);
-  uint2 *lutv = lutk + kM;
-  build_lut(lutk, tk, threadIdx.x, blockDim.x);
-  build_lut(lutv, tv, threadIdx.x, blockDim.x);
+  const DecTab dk{sym8[0], symtab[0]};
+  const DecTab dv{sym8[1], symtab[1]};
+  build_tables(sym8[0], symtab[0], tk, threadIdx.x, blockDim.x);
+  build_tables(sym8[1], symtab[1], tv, threadIdx.x, blockDim.x);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int Ck = tk.C, Cv = tv.C;
   const WaveLayout L = wave_layout(Ck, Cv);
-  uint8_t *base = smem + kLutBytes + (size_t)wave * L.bytes;
+  uint8_t *base = smem + (size_t)wave * L.bytes;
   uint8_t *kst = base + L.kst;
   uint8_t *vst = base + L.vst;
   uint16_t *knl = reinterpret_cast<uint16_t *>(base + L.knl);
@@ -352,7 +371,7 @@ __global__ void __launch_bounds__(512) attn_splitk_kernel(AttnArgs a, Tables tk,
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
     floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-    tile_pass<true, false>(lutk, lutv, kst + koff0 + lane * Ck, nullptr, qr, pl, vt, sc, acc, lane);
+    tile_pass<true, false>(dk, dv, kst + koff0 + lane * Ck, nullptr, qr, pl, vt, sc, acc, lane);
     softmax_tile(sc, knl, vnl, t1 - t0, a.qk_scale, m_run, l_run, pl, acc, lane);
 
     for (int j = 0; j < ntiles; ++j) {
@@ -376,11 +395,11 @@ __global__ void __launch_bounds__(512) attn_splitk_kernel(AttnArgs a, Tables tk,
       }
       if (next) {
         sc = floatx4{0.f, 0.f, 0.f, 0.f};
-        tile_pass<true, true>(lutk, lutv, kst + koff + lane * Ck, vst + voff + lane * Cv, qr, pl, vt, sc, acc,
+        tile_pass<true, true>(dk, dv, kst + koff + lane * Ck, vst + voff + lane * Cv, qr, pl, vt, sc, acc,
                               lane);
         softmax_tile(sc, knl, vnl, t1 - t0 - (j + 1) * kTile, a.qk_scale, m_run, l_run, pl, acc, lane);
       } else {
-        tile_pass<false, true>(lutk, lutv, nullptr, vst + voff + lane * Cv, qr, pl, vt, sc, acc, lane);
+        tile_pass<false, true>(dk, dv, nullptr, vst + voff + lane * Cv, qr, pl, vt, sc, acc, lane);
       }
     }
 
@@ -468,8 +487,8 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   pl->nq = cmax <= 47 ? 3 : (cmax <= 79 ? 5 : 9);  // 16-byte pieces per lane per tile
   const int wb = wave_layout(Ck, Cv).bytes;
   const int lds_cap = 160 * 1024;
-  int wpb = 8;  // two waves per SIMD when the LDS allows
-  while (wpb > 1 && kLutBytes + wpb * wb > lds_cap) wpb >>= 1;
+  int wpb = pl->nq == 3 ? 12 : 4;  // three waves per SIMD when the LDS allows (larger C: fewer)
+  while (wpb > 1 && kLutBytes + wpb * wb > lds_cap) wpb -= wpb > 4 ? 4 : 1;
   if (kLutBytes + wpb * wb > lds_cap) return DQ_ERR_UNSUPPORTED;
   // chunk: aim for ~8 items per resident wave (8 waves per CU) if every
   // sequence were max_len; independent of C so the workspace size is too
@@ -487,7 +506,7 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   pl->nc = (int)nc;
   pl->waves_per_block = wpb;
   pl->n_items = (int64_t)B * Hkv * nc;
-  pl->lds = (size_t)kLutBytes + (size_t)wpb * wb;
+  pl->lds = (size_t)wpb * wb;  // dynamic part; the decode tables are static
   const int64_t want_blocks = (pl->n_items + wpb - 1) / wpb;
   pl->blocks = (int)(want_blocks < cus ? want_blocks : cus);
   pl->qrot_bytes = ((size_t)B * Hkv * kQrotPerBG * 2 + 255) & ~(size_t)255;
@@ -501,7 +520,7 @@ hipError_t launch_splitk(const Plan &pl, const AttnArgs &a, const Tables &tk, co
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kLutBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }

@@ -22,8 +22,9 @@ struct DecodeArgs {
 };
 
 __global__ void __launch_bounds__(kThreads) decode_symbols_kernel(DecodeArgs a, Tables t) {
-  __shared__ uint2 lut[kM];
-  build_lut(lut, t, threadIdx.x, kThreads);
+  __shared__ uint8_t sym8[kM];
+  __shared__ uint2 symtab[kMaxLevels];
+  build_tables(sym8, symtab, t, threadIdx.x, kThreads);
   __syncthreads();
   const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (j >= a.n) return;
@@ -43,8 +44,9 @@ __global__ void __launch_bounds__(kThreads) decode_symbols_kernel(DecodeArgs a, 
     uint32_t packed = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint2 e = rans_step(x, lut);
-      packed |= (e.x >> 24) << (8 * q);
+      uint32_t sy;
+      rans_step(x, sym8, symtab, sy);
+      packed |= sy << (8 * q);
       if (x < kLow) {
         const uint32_t b = p < C ? (uint32_t)c[p] : 0u;
         x = (x << 8) | b;

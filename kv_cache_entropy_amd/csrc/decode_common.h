@@ -6,6 +6,13 @@
 // i: slot = x mod 4096 selects the symbol s (cum_s <= slot < cum_{s+1}),
 // x <- f_s * (x >> 12) + slot - cum_s, then one byte is shifted in if
 // x < 2^23 (every f >= 16, so one byte always restores the interval).
+//
+// Decode tables in LDS, per codec (4352 bytes):
+//   sym8[4096]   slot -> symbol (one byte, so the slot itself is the LDS
+//                address: no index arithmetic)
+//   symtab[16]   symbol -> {f, cum | fp16 level << 16}
+// The byte table is read at a random slot per lane; the symbol table has at
+// most 16 distinct entries, so its reads are mostly broadcasts.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,23 +21,28 @@
 
 namespace dq {
 
-// LUT entry for slot u (8 bytes):
-//   .x = f_s | s << 24        (mad24 reads only the low 24 bits: f_s)
-//   .y = (u - cum_s) | r_s << 16   (r_s = fp16 reconstruction level)
-__device__ __forceinline__ void build_lut(uint2 *lut, const Tables &t, int tid, int nthreads) {
+constexpr int kSymTabBytes = kMaxLevels * 8;
+constexpr int kDecodeTableBytes = (int)kM + kSymTabBytes;
+
+__device__ __forceinline__ void build_tables(uint8_t *sym8, uint2 *symtab, const Tables &t, int tid,
+                                             int nthreads) {
   for (int u = tid; u < (int)kM; u += nthreads) {
     int s = 0;
     while (s + 1 < t.levels && (int)t.cum[s + 1] <= u) ++s;
-    lut[u] = make_uint2((uint32_t)t.freq[s] | ((uint32_t)s << 24),
-                        (uint32_t)(u - (int)t.cum[s]) | ((uint32_t)t.recon[s] << 16));
+    sym8[u] = (uint8_t)s;
   }
+  if (tid < kMaxLevels)
+    symtab[tid] = tid < t.levels ? make_uint2(t.freq[tid], (uint32_t)t.cum[tid] | ((uint32_t)t.recon[tid] << 16))
+                                 : make_uint2(0u, 0u);
 }
 
-// One decode step; returns the LUT entry so callers can take the symbol
-// (e.x >> 24) or the fp16 level (e.y >> 16).
-__device__ __forceinline__ uint2 rans_step(uint32_t &x, const uint2 *lut) {
-  const uint2 e = lut[x & (kM - 1)];
-  x = __umul24(e.x, x >> kMBits) + (e.y & 0xFFFFu);
+// One decode step without the renormalisation; returns the symbol-table
+// entry (.y >> 16 = fp16 level) and the symbol.
+__device__ __forceinline__ uint2 rans_step(uint32_t &x, const uint8_t *sym8, const uint2 *symtab, uint32_t &s) {
+  const uint32_t slot = x & (kM - 1);
+  s = sym8[slot];
+  const uint2 e = symtab[s];
+  x = __umul24(e.x, x >> kMBits) + (slot - (e.y & 0xFFFFu));
   return e;
 }
 
