@@ -115,15 +115,13 @@ __device__ __forceinline__ uint32_t load_le32(const uint8_t *p) {
 // ---------------------------------------------------------------- split-K
 // Per-wave LDS slice (byte offsets), identical on host and device.
 struct WaveLayout {
-  int kst, vst, knl, vnl, qr, pl, vt, bytes;
+  int kst, vst, qr, pl, vt, bytes;
 };
 __host__ __device__ inline WaveLayout wave_layout(int Ck, int Cv) {
   WaveLayout w;
   w.kst = 0;
   w.vst = w.kst + ((kTile * Ck + 31) & ~15);
-  w.knl = w.vst + ((kTile * Cv + 31) & ~15);
-  w.vnl = w.knl + kTile * 2;
-  w.qr = w.vnl + kTile * 2;
+  w.qr = w.vst + ((kTile * Cv + 31) & ~15);
   w.pl = w.qr + 32 * 4 * 16;
   w.vt = w.pl + 4 * kTile * 2;
   w.bytes = w.vt + kPass * kVtStride * 2;
@@ -178,22 +176,27 @@ __device__ __forceinline__ uint32_t next_byte(const uint8_t *p) {
   return *(lds_byte *)p;  // p points into LDS (a container staged by this wave)
 }
 
-// Decodes one K tile (scores into sc) and/or one V tile (PV into acc),
-// interleaving the two independent rANS chains of each lane.  K: every 4
-// symbols feed a 4x4x4 MFMA (A = the lane's 4 fp16 levels, B = q~ hi / lo).
-// V: levels go to the transposed LDS tile, 32 dims per pass; each pass is
-// contracted with P by 8 MFMAs whose blocks are (8 dim quads) x (2 token
-// halves).
 struct DecTab {
   const uint8_t *sym8;
   const uint2 *symtab;
 };
 
+// Decodes one K tile (scores into sc) and/or one V tile (PV into acc),
+// interleaving the two independent rANS chains of each lane.
+// K: after every 4 symbols, sc += q~[4 heads][4 dims] x levels[4 dims]
+//   on a 4x4x4 MFMA whose A operand (the query, hi then lo) is broadcast
+//   from block 0 (cbsz 4), so only lanes 0..3 read it from LDS; the lane's
+//   own 4 levels are the B column, and the lane ends with its token's
+//   scores for the 4 heads.
+// V: levels go to the transposed LDS tile, 32 dims per pass; each pass is
+//   contracted with P by 8 MFMAs whose blocks are (8 dim quads) x (2 token
+//   halves); P is broadcast per half (cbsz 3), read by lanes 0..3, 32..35.
 template <bool DK, bool DV>
 __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
                                           const uint8_t *vb, const uint4 *qr, const uint16_t *pl,
                                           uint16_t *vt, floatx4 &sc, floatx4 (&acc)[4], int lane) {
-  const int hl = lane & 3, th = lane >> 5, row = lane & 31;
+  const int th = lane >> 5, row = lane & 31;
+  const bool qlane = lane < 4, plane = (lane & 31) < 4;
   uint32_t xk = 0, xv = 0;
   const uint8_t *pk = kb, *pv = vb;
   if (DK) {
@@ -208,6 +211,8 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     for (int gq = 0; gq < kPass / 4; ++gq) {
+      uint4 qv = make_uint4(0, 0, 0, 0);
+      if (DK && qlane) qv = qr[(p * (kPass / 4) + gq) * 4 + lane];
       uint32_t lv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -228,73 +233,63 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
         }
       }
       if (DK) {
-        const uint32_t a01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
-        const uint32_t a23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
-        const half4 A = __builtin_bit_cast(half4, make_uint2(a01, a23));
-        const uint4 qv = qr[(p * (kPass / 4) + gq) * 4 + hl];
-        sc = __builtin_amdgcn_mfma_f32_4x4x4f16(A, __builtin_bit_cast(half4, make_uint2(qv.x, qv.y)), sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_4x4x4f16(A, __builtin_bit_cast(half4, make_uint2(qv.z, qv.w)), sc, 0, 0, 0);
+        const uint32_t b01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
+        const uint32_t b23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
+        const half4 Bk = __builtin_bit_cast(half4, make_uint2(b01, b23));
+        sc = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(qv.x, qv.y)), Bk, sc, 4, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(qv.z, qv.w)), Bk, sc, 4, 0, 0);
       }
     }
     if (DV) {
       wave_sync();
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const half4 P = *reinterpret_cast<const half4 *>(pl + hl * kTile + th * 32 + 4 * c);
+        uint2 pa = make_uint2(0, 0);
+        if (plane) pa = *reinterpret_cast<const uint2 *>(pl + (lane & 3) * kTile + th * 32 + 4 * c);
         const uint32_t *r = reinterpret_cast<const uint32_t *>(vt) + row * (kVtStride / 2) + th * 16 + 2 * c;
         const half4 V = __builtin_bit_cast(half4, make_uint2(r[0], r[1]));
-        acc[p] = __builtin_amdgcn_mfma_f32_4x4x4f16(P, V, acc[p], 0, 0, 0);
+        acc[p] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, pa), V, acc[p], 3, 0, 0);
       }
       wave_sync();
     }
   }
 }
 
-// Scales a tile's raw scores (lane: tokens 4*tq + r, head hl), updates the
-// running max / sum of head hl, writes P = p * n_v (fp16) to LDS and
-// rescales the V accumulators of all four heads.
-__device__ __forceinline__ void softmax_tile(const floatx4 &sc, const uint16_t *knl, const uint16_t *vnl,
-                                             int valid_tokens, float qk_scale, float &m_run, float &l_run,
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int w = 1; w < 64; w <<= 1) v = fmaxf(v, __shfl_xor(v, w));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int w = 1; w < 64; w <<= 1) v += __shfl_xor(v, w);
+  return v;
+}
+
+// Online softmax for one tile.  Lane t holds its token's scores for the 4
+// heads (sc) and its own K and V norms; m_run is per head (same in every
+// lane), l_lane is this lane's share of the per-head sum (reduced once per
+// item).  Writes P = p * n_v (fp16) to LDS and rescales the V accumulators.
+__device__ __forceinline__ void softmax_tile(const floatx4 &sc, uint32_t nk_bits, uint32_t nv_bits, bool valid,
+                                             float qk_scale, float (&m_run)[4], float (&l_lane)[4],
                                              uint16_t *pl, floatx4 (&acc)[4], int lane) {
-  const int hl = lane & 3, tq = lane >> 2;
-  const uint2 kn4 = *reinterpret_cast<const uint2 *>(knl + 4 * tq);
-  const uint2 vn4 = *reinterpret_cast<const uint2 *>(vnl + 4 * tq);
-  const uint32_t knw[2] = {kn4.x, kn4.y}, vnw[2] = {vn4.x, vn4.y};
-  float s[4], mt = -__builtin_inff();
+  const float nk = (float)__builtin_bit_cast(_Float16, (uint16_t)nk_bits);
+  const float nv = (float)__builtin_bit_cast(_Float16, (uint16_t)nv_bits);
+  float alpha[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float nk = (float)__builtin_bit_cast(_Float16, (uint16_t)(knw[r >> 1] >> (16 * (r & 1))));
-    s[r] = (4 * tq + r < valid_tokens) ? sc[r] * nk * qk_scale : -__builtin_inff();
-    mt = fmaxf(mt, s[r]);
+  for (int h = 0; h < 4; ++h) {
+    const float s = valid ? sc[h] * nk * qk_scale : -__builtin_inff();
+    const float m_new = fmaxf(m_run[h], wave_max(s));
+    alpha[h] = exp2f(m_run[h] - m_new);
+    const float p = valid ? exp2f(s - m_new) : 0.0f;
+    l_lane[h] = l_lane[h] * alpha[h] + p;
+    m_run[h] = m_new;
+    pl[h * kTile + lane] = __builtin_bit_cast(uint16_t, (_Float16)(valid ? p * nv : 0.0f));
   }
 #pragma unroll
-  for (int w = 4; w < 64; w <<= 1) mt = fmaxf(mt, __shfl_xor(mt, w));
-  const float m_new = fmaxf(m_run, mt);
-  const float alpha = exp2f(m_run - m_new);
-  float psum = 0.0f;
-  uint32_t pw[2] = {0u, 0u};
+  for (int p = 0; p < 4; ++p)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const bool valid = 4 * tq + r < valid_tokens;
-    const float p = valid ? exp2f(s[r] - m_new) : 0.0f;
-    psum += p;
-    const float nv = (float)__builtin_bit_cast(_Float16, (uint16_t)(vnw[r >> 1] >> (16 * (r & 1))));
-    const float pv = valid ? p * nv : 0.0f;
-    pw[r >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)pv) << (16 * (r & 1));
-  }
-#pragma unroll
-  for (int w = 4; w < 64; w <<= 1) psum += __shfl_xor(psum, w);
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-  *reinterpret_cast<uint2 *>(pl + hl * kTile + 4 * tq) = make_uint2(pw[0], pw[1]);
-  const float a0 = __shfl(alpha, 0), a1 = __shfl(alpha, 1), a2 = __shfl(alpha, 2), a3 = __shfl(alpha, 3);
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    acc[p][0] *= a0;
-    acc[p][1] *= a1;
-    acc[p][2] *= a2;
-    acc[p][3] *= a3;
-  }
+    for (int h = 0; h < 4; ++h) acc[p][h] *= alpha[h];
 }
 
 template <int NQ>
@@ -316,8 +311,6 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
   uint8_t *base = smem + (size_t)wave * L.bytes;
   uint8_t *kst = base + L.kst;
   uint8_t *vst = base + L.vst;
-  uint16_t *knl = reinterpret_cast<uint16_t *>(base + L.knl);
-  uint16_t *vnl = reinterpret_cast<uint16_t *>(base + L.vnl);
   uint4 *qr = reinterpret_cast<uint4 *>(base + L.qr);
   uint16_t *pl = reinterpret_cast<uint16_t *>(base + L.pl);
   uint16_t *vt = reinterpret_cast<uint16_t *>(base + L.vt);
@@ -344,63 +337,66 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
     qr[lane] = qsrc[lane];
     qr[lane + 64] = qsrc[lane + 64];
 
-    // norms of a tile: lane t holds token t's (0 past the pool)
-    auto norms = [&](int tile, uint16_t &nk, uint16_t &nv) {
+    // this lane's token norms for a tile (0 outside the pool plane)
+    auto norms = [&](int tile, uint32_t &nk, uint32_t &nv) {
       const int64_t idx = pbase + tile * kTile + lane;
       const bool ok = idx >= (int64_t)g * a.S && idx < (int64_t)(g + 1) * a.S;
-      nk = ok ? a.kn[idx] : (uint16_t)0;
-      nv = ok ? a.vn[idx] : (uint16_t)0;
+      nk = ok ? a.kn[idx] : 0u;
+      nv = ok ? a.vn[idx] : 0u;
     };
     TileRegs<NQ> rk, rv;
-    uint16_t nk, nv;
+    uint32_t nk0, nv0, nk1 = 0, nv1 = 0;
     // prologue: K of tile 0
     fetch<NQ>(rk, kplane, kTile * Ck, a.kc, kpool_end, lane);
-    norms(0, nk, nv);
+    norms(0, nk0, nv0);
     commit<NQ>(rk, kst, kTile * Ck, lane);
     const int koff0 = rk.off;
-    knl[lane] = nk;
-    vnl[lane] = nv;
     wave_sync();
     fetch<NQ>(rv, vplane, kTile * Cv, a.vc, vpool_end, lane);
     if (ntiles > 1) {
       fetch<NQ>(rk, kplane + kTile * Ck, kTile * Ck, a.kc, kpool_end, lane);
-      norms(1, nk, nv);
+      norms(1, nk1, nv1);
     }
-    float m_run = -__builtin_inff(), l_run = 0.0f;
+    float m_run[4], l_lane[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      m_run[h] = -__builtin_inff();
+      l_lane[h] = 0.0f;
+    }
     floatx4 acc[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
     floatx4 sc = {0.f, 0.f, 0.f, 0.f};
     tile_pass<true, false>(dk, dv, kst + koff0 + lane * Ck, nullptr, qr, pl, vt, sc, acc, lane);
-    softmax_tile(sc, knl, vnl, t1 - t0, a.qk_scale, m_run, l_run, pl, acc, lane);
+    softmax_tile(sc, nk0, nv0, lane < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
 
     for (int j = 0; j < ntiles; ++j) {
       const bool next = j + 1 < ntiles;
-      wave_sync();  // every read of the staging buffers and norms is done
+      wave_sync();  // every read of the staging buffers is done
       commit<NQ>(rv, vst, kTile * Cv, lane);
       const int voff = rv.off;
       int koff = 0;
       if (next) {
         commit<NQ>(rk, kst, kTile * Ck, lane);
         koff = rk.off;
-        knl[lane] = nk;
-        vnl[lane] = nv;
       }
       wave_sync();
       // prefetch the next iteration's tiles into registers
+      uint32_t nk2 = 0, nv2 = 0;
       if (next) fetch<NQ>(rv, vplane + (j + 1) * kTile * Cv, kTile * Cv, a.vc, vpool_end, lane);
       if (j + 2 < ntiles) {
         fetch<NQ>(rk, kplane + (j + 2) * kTile * Ck, kTile * Ck, a.kc, kpool_end, lane);
-        norms(j + 2, nk, nv);
+        norms(j + 2, nk2, nv2);
       }
       if (next) {
         sc = floatx4{0.f, 0.f, 0.f, 0.f};
-        tile_pass<true, true>(dk, dv, kst + koff + lane * Ck, vst + voff + lane * Cv, qr, pl, vt, sc, acc,
-                              lane);
-        softmax_tile(sc, knl, vnl, t1 - t0 - (j + 1) * kTile, a.qk_scale, m_run, l_run, pl, acc, lane);
+        tile_pass<true, true>(dk, dv, kst + koff + lane * Ck, vst + voff + lane * Cv, qr, pl, vt, sc, acc, lane);
+        softmax_tile(sc, nk1, nv1, (j + 1) * kTile + lane < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
       } else {
         tile_pass<false, true>(dk, dv, nullptr, vst + voff + lane * Cv, qr, pl, vt, sc, acc, lane);
       }
+      nk1 = nk2;
+      nv1 = nv2;
     }
 
     // partial for this item: the two token halves of every dim are summed
@@ -414,9 +410,13 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
         if (lane < 32) dst[h * kPart + p * kPass + lane] = v;
       }
     }
-    if (lane < 4) {
-      dst[lane * kPart + 128] = m_run;
-      dst[lane * kPart + 129] = l_run;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float l = wave_sum(l_lane[h]);
+      if (lane == h) {
+        dst[h * kPart + 128] = m_run[h];
+        dst[h * kPart + 129] = l;
+      }
     }
   }
 }
