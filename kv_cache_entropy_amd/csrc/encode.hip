@@ -10,13 +10,14 @@
 //   order one level inward until it does.
 //
 // MI355X mapping: one lane owns one vector end to end.  The rotation runs on
-// the 128 coordinates in VGPRs (fully unrolled butterflies); the symbols and
-// the renorm bytes then live in LDS, lane-minor ([i][lane]), so the serial
-// rANS chain of every lane reads symbol i of all lanes from one contiguous
-// 128-byte row.  Lanes of a wave take consecutive tokens of one kv head, so
-// their containers are adjacent in the pool.  The drift search is a per-lane
-// state machine around a single rANS pass, so lanes that need more passes
-// simply stay active while the others idle.
+// the 128 coordinates in VGPRs (fully unrolled butterflies); the symbols stay
+// in VGPRs as 4-bit fields, so a rANS pass is a straight unrolled chain whose
+// only memory access is the per-symbol coder constants in LDS.  Renorm bytes
+// go to a double-buffered LDS scratch, lane-minor, so the last fitting
+// stream survives a later trial pass.  The drift search moves one candidate
+// at a time around an estimate of the number of moves, so a drifted vector
+// usually costs three passes.  Lanes of a wave take consecutive tokens of one
+// kv head, so their containers are adjacent in the pool.
 //
 // Arithmetic that decides a symbol is fp32 in a fixed order (butterfly
 // widths 1..64, halving-tree sum of squares); the build uses
@@ -30,7 +31,7 @@ namespace dq {
 namespace {
 
 constexpr int kThreads = 128;
-constexpr int kScr = 128;  // renorm bytes per lane: at most one per symbol
+constexpr int kScr = 128;  // renorm bytes per lane and buffer: at most one per symbol
 
 struct EncodeArgs {
   const uint16_t *x;
@@ -85,97 +86,79 @@ __device__ __forceinline__ uint32_t nib(const uint32_t (&w)[16], int i) {
 __device__ __forceinline__ uint32_t bit(const uint32_t (&w)[4], int i) {
   return (w[i >> 5] >> (i & 31)) & 1u;
 }
-
-// Per-lane view of one vector during the drift search.
-struct Vec {
-  float ay[kD];      // |y_i|: drift order within a magnitude group
-  uint32_t mag[16];  // magnitude cell m_i, 4 bits each
-  uint32_t neg[4];   // 1: y_i < 0
-  uint32_t fl[4];    // 1: coordinate moved one level inward
-};
-
-// Writes the current symbols (base symbols with the drift flags applied) to
-// the lane's LDS column.
-__device__ __forceinline__ void materialize(const Vec &v, int h, uint8_t *sym, int lane) {
-#pragma unroll
-  for (int i = 0; i < kD; ++i) {
-    const uint32_t m = nib(v.mag, i) - bit(v.fl, i);
-    const uint32_t s = bit(v.neg, i) ? (uint32_t)(h - 1) - m : (uint32_t)h + m;
-    sym[i * kThreads + lane] = (uint8_t)s;
-  }
+__device__ __forceinline__ uint32_t magnitude(uint32_t s, int h) {
+  return s >= (uint32_t)h ? s - (uint32_t)h : (uint32_t)(h - 1) - s;
 }
 
-// Flags the not-yet-flagged member of magnitude group g with the smallest
-// (|y|, index) and updates its LDS symbol; false if the group has none left.
-__device__ __forceinline__ bool add_smallest(Vec &v, uint32_t g, int h, uint8_t *sym, int lane) {
-  float best = __builtin_inff();
+// One lane's vector during the drift search: the quantised symbols before
+// the current drift pass (4 bits each), the drift flags, and |y_i| (the
+// order key inside a magnitude group).  The current symbols (with the
+// flagged coordinates one level inward) live in the lane's LDS column.
+struct Vec {
+  float ay[kD];
+  uint32_t sym0[16];
+  uint32_t fl[4];
+};
+
+// Among the members of group mask gm: the unflagged one with the smallest
+// (|y|, index) -- the next candidate in drift order -- or, with flagged, the
+// flagged one with the largest (|y|, index) -- the last candidate taken;
+// -1 if there is none.
+__device__ __forceinline__ int extreme_in_group(const Vec &v, const uint32_t (&gm)[4], bool flagged) {
+  float best = 0.0f;
   int bi = -1;
 #pragma unroll
   for (int i = 0; i < kD; ++i) {
-    const bool take = nib(v.mag, i) == g && !bit(v.fl, i) && (bi < 0 || v.ay[i] < best);
+    const bool member = bit(gm, i) && ((bit(v.fl, i) != 0u) == flagged);
+    const bool better = flagged ? (v.ay[i] >= best) : (v.ay[i] < best);
+    const bool take = member && (bi < 0 || better);
     best = take ? v.ay[i] : best;
     bi = take ? i : bi;
   }
-  if (bi < 0) return false;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v.fl[j] |= ((bi >> 5) == j) ? (1u << (bi & 31)) : 0u;
-  // one level inward: toward the innermost pair (h - 1, h)
-  const uint32_t s = sym[bi * kThreads + lane];
-  sym[bi * kThreads + lane] = (uint8_t)(s >= (uint32_t)h ? s - 1u : s + 1u);
-  (void)h;
-  return true;
+  return bi;
 }
 
-// Flags exactly the first k candidates of the drift order (magnitude
-// descending, then |y| ascending, then index ascending) and materialises
-// the symbols.  Returns the group holding the k-th candidate.
-template <int MAXH>
-__device__ __forceinline__ uint32_t set_prefix(Vec &v, const int (&cnt)[MAXH], int k, int h, uint8_t *sym, int lane) {
-  v.fl[0] = v.fl[1] = v.fl[2] = v.fl[3] = 0u;
-  uint32_t gb = (uint32_t)(h - 1);
-  int rest = 0;
+__device__ __forceinline__ void group_mask(const Vec &v, int h, int g, uint32_t (&gm)[4]) {
+  gm[0] = gm[1] = gm[2] = gm[3] = 0u;
 #pragma unroll
-  for (int m = MAXH - 1; m >= 1; --m) {
-    if (m < h && k > 0) {
-      gb = (uint32_t)m;
-      if (k >= cnt[m]) {
+  for (int i = 0; i < kD; ++i) gm[i >> 5] |= (magnitude(nib(v.sym0, i), h) == (uint32_t)g ? 1u : 0u) << (i & 31);
+}
+
+// Moves coordinate i (dynamic) one level inward, or back out (undo), in the
+// LDS symbol column, and toggles its flag.  A moved symbol stays on its side
+// of zero, so the current value alone tells the direction.
+__device__ __forceinline__ void toggle(Vec &v, uint8_t *symL, int i, int h, bool undo, int lane) {
+  uint8_t *p = symL + i * kThreads + lane;
+  const uint32_t s = *p;
+  const bool pos = s >= (uint32_t)h;
+  *p = (uint8_t)((pos != undo) ? s - 1u : s + 1u);
 #pragma unroll
-        for (int i = 0; i < kD; ++i) v.fl[i >> 5] |= (nib(v.mag, i) == (uint32_t)m ? 1u : 0u) << (i & 31);
-        k -= cnt[m];
-      } else {
-        rest = k;
-        k = 0;
-      }
-    }
-  }
-  materialize(v, h, sym, lane);
-  for (int j = 0; j < rest; ++j) add_smallest(v, gb, h, sym, lane);
-  return gb;
+  for (int j = 0; j < 4; ++j) v.fl[j] ^= ((i >> 5) == j) ? (1u << (i & 31)) : 0u;
 }
 
 template <int MAXH>
-__device__ __forceinline__ int count_at(const int (&cnt)[MAXH], int m) {
+__device__ __forceinline__ int cnt_at(const int (&cnt)[MAXH], int m) {
   int r = 0;
 #pragma unroll
-  for (int q = 1; q < MAXH; ++q) r = q == m ? cnt[q] : r;
+  for (int q = 1; q < MAXH; ++q) r = (q == m) ? cnt[q] : r;
   return r;
 }
 
-// One rANS pass over the lane's current symbols (pushed 127 -> 0).  Renorm
-// bytes go to the lane's scratch column from the end backwards, so rows
-// kScr - B .. kScr - 1 are already in the decoder's reading order.
-__device__ __forceinline__ int rans_pass(const uint4 *etab, const uint8_t *sym, uint8_t *scr, int lane,
+// One rANS pass over the lane's LDS symbol column (pushed 127 -> 0).
+// Renorm bytes go to the lane's scratch column from the end backwards (rows
+// kScr - B .. kScr - 1 are then in the decoder's reading order); the byte
+// store is unconditional and simply overwritten when no byte is emitted.
+__device__ __forceinline__ int rans_pass(const uint8_t *symL, const uint4 *etab, uint8_t *buf, int lane,
                                          uint32_t *xfinal) {
   uint32_t x = kLow;
   int pos = kScr - 1;
+#pragma unroll 4
   for (int i = kD - 1; i >= 0; --i) {
-    const uint32_t s = sym[i * kThreads + lane];
-    const uint4 e = etab[s];  // {f << 19, magic, cum, (4096 - f) | shift << 16}
-    if (x >= e.x) {
-      scr[pos * kThreads + lane] = (uint8_t)x;
-      --pos;
-      x >>= 8;
-    }
+    const uint4 e = etab[symL[i * kThreads + lane]];  // {f << 19, magic, cum, (4096 - f) | shift << 16}
+    buf[pos * kThreads + lane] = (uint8_t)x;
+    const bool emit = x >= e.x;
+    x = emit ? x >> 8 : x;
+    pos -= emit ? 1 : 0;
     const uint32_t q = __umulhi(x, e.y) >> (e.w >> 16);
     x = x + e.z + __umul24(q, e.w & 0xFFFFu);
   }
@@ -183,14 +166,14 @@ __device__ __forceinline__ int rans_pass(const uint4 *etab, const uint8_t *sym, 
   return kScr - 1 - pos;
 }
 
-enum : int { kPhInit = 0, kPhFirst = 1, kPhDown = 2, kPhUp = 3, kPhFinal = 4, kPhDone = 5 };
-enum : int { kActNone = 0, kActPrefix = 1, kActNext = 2, kActCommit = 3 };
+enum : int { kPhInit, kPhFirst, kPhDown, kPhUp, kPhDone };
+enum : int { kActNone, kActPrefix, kActAdd, kActRemove, kActCommit };
 
 template <int MAXH>
 __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a, Tables t) {
   __shared__ uint4 etab[kMaxLevels];
-  __shared__ uint8_t sym[kD * kThreads];
-  __shared__ uint8_t scr[kScr * kThreads];
+  __shared__ uint8_t scr[2][kScr * kThreads];  // double-buffered renorm bytes
+  __shared__ uint8_t symcol[kD * kThreads];     // current symbols, lane-minor
   __shared__ uint32_t bstat[6 + kMaxC + 1];
 
   const int lane = threadIdx.x;
@@ -275,12 +258,9 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a, Tables t
 #pragma unroll
     for (int k = 0; k < MAXH; ++k) ge[k] = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v.mag[j] = 0u;
+    for (int j = 0; j < 16; ++j) v.sym0[j] = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v.neg[j] = 0u;
-      v.fl[j] = 0u;
-    }
+    for (int j = 0; j < 4; ++j) v.fl[j] = 0u;
 #pragma unroll
     for (int i = 0; i < kD; ++i) {
       const float ay = degenerate ? 0.0f : __builtin_fabsf(y[i]);
@@ -292,46 +272,72 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a, Tables t
         m += c;
         ge[k] += (int)c;
       }
-      v.mag[i >> 3] |= m << (4 * (i & 7));
-      v.neg[i >> 5] |= ((degenerate || y[i] >= 0.0f) ? 0u : 1u) << (i & 31);
+      const uint32_t sy = (degenerate || y[i] >= 0.0f) ? (uint32_t)h + m : (uint32_t)(h - 1) - m;
+      v.sym0[i >> 3] |= sy << (4 * (i & 7));
     }
-    materialize(v, h, sym, lane);
+    // current symbols into the lane's LDS column
+    uint8_t *symL = symcol;
+#pragma unroll
+    for (int i = 0; i < kD; ++i) symL[i * kThreads + lane] = (uint8_t)nib(v.sym0, i);
 
-    // drift search: a per-lane state machine around one rANS pass.  Each
-    // iteration runs the pass on the current symbols, records the result if
-    // it is the candidate answer, and picks one action for the symbols.
+    // ---- drift search: a per-lane state machine around one rANS pass.
+    // Passes alternate between the two scratch buffers, so the last fitting
+    // stream is still there after a trial pass that does not fit.
+    int buf = 1, okbuf = -1, okB = 0;
+    uint32_t okx = 0;
+    int moves = 0, passes = 0, k = 0, total = 0, gb = 0, taken = 0;
     int cnt[MAXH];
-    cnt[0] = 0;
-    int total = 0;
-    int k = 0, moves = 0, passes = 0, B = 0;
-    uint32_t gb = 0, xfin = 0;
+#pragma unroll
+    for (int m = 0; m < MAXH; ++m) cnt[m] = 0;
+    uint32_t gm[4] = {0u, 0u, 0u, 0u};
+    bool first_round = true;
     int phase = kPhInit;
-    int guard = 0;  // bounded: every lane leaves the loop (search needs < 3 * 128 passes)
-    while (phase != kPhDone && ++guard < 1024) {
+    for (int guard = 0; phase != kPhDone && guard < 4 * kD; ++guard) {
       uint32_t xf;
-      const int Bp = rans_pass(etab, sym, scr, lane, &xf);
-      const bool fits = 4 + Bp <= C;
+      buf ^= 1;
+      const int B = rans_pass(symL, etab, scr[buf], lane, &xf);
+      const bool fits = 4 + B <= C;
+      if (fits) {
+        okbuf = buf;
+        okB = B;
+        okx = xf;
+      }
       int act = kActNone;
       if (phase == kPhInit) {
         if (fits) {
-          B = Bp;
-          xfin = xf;
           phase = kPhDone;
         } else {
           // group sizes and the estimated number of moves: shed the excess
-          // bits greedily in drift order using the per-move savings
+          // bits greedily in drift order at each group's per-move saving
           float sigma_c = 0.0f;
           total = 0;
+          if (first_round) {
 #pragma unroll
-          for (int m = 0; m < MAXH; ++m) {
-            const int above = (m + 1 < MAXH) ? ge[m + 1] : 0;
-            const int c = (m == 0 ? kD : ge[m]) - above;
-            if (m < h) sigma_c += (float)c * t.cost[h + m];
-            if (m >= 1) {
-              cnt[m] = c;
-              total += c;
+            for (int m = 0; m < MAXH; ++m) {
+              const int above = (m + 1 < MAXH) ? ge[m + 1] : 0;
+              const int c = (m == 0 ? kD : ge[m]) - above;
+              if (m >= 1) cnt[m] = c;
+              if (m < h) sigma_c += (float)c * t.cost[h + m];
             }
+          } else {
+#pragma unroll
+            for (int m = 1; m < MAXH; ++m) cnt[m] = 0;
+#pragma unroll
+            for (int i = 0; i < kD; ++i) {
+              const uint32_t mg = magnitude(nib(v.sym0, i), h);
+#pragma unroll
+              for (int m = 1; m < MAXH; ++m) cnt[m] += mg == (uint32_t)m ? 1 : 0;
+            }
+            int c0 = kD;
+#pragma unroll
+            for (int m = 1; m < MAXH; ++m) {
+              c0 -= cnt[m];
+              if (m < h) sigma_c += (float)cnt[m] * t.cost[h + m];
+            }
+            sigma_c += (float)c0 * t.cost[h];
           }
+#pragma unroll
+          for (int m = 1; m < MAXH; ++m) total += cnt[m];
           float need = sigma_c - 8.0f * (float)(C - 4) - 4.0f;
           int khat = 0;
 #pragma unroll
@@ -351,84 +357,105 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a, Tables t
         }
       } else if (phase == kPhFirst || phase == kPhDown) {
         if (fits) {
-          // prefix k fits: try one shorter while possible
-          B = Bp;
-          xfin = xf;
           if (k == 1) {
             phase = kPhDone;
           } else {
-            --k;
-            act = kActPrefix;
+            act = kActRemove;  // try one candidate fewer
             phase = kPhDown;
           }
         } else if (phase == kPhDown) {
-          // prefix k + 1 was the shortest that fits: redo it (scratch)
-          ++k;
-          act = kActPrefix;
-          phase = kPhFinal;
-        } else {
-          act = kActNext;
-          phase = kPhUp;
-        }
-      } else if (phase == kPhFinal) {
-        B = Bp;
-        xfin = xf;
-        phase = kPhDone;
-      } else {  // kPhUp: prefix k did not fit before this pass added one
-        if (fits) {
-          B = Bp;
-          xfin = xf;
+          ++k;  // prefix k - 1 failed: the previous pass (prefix k) is the answer
           phase = kPhDone;
         } else {
-          act = kActNext;
+          act = kActAdd;
+          phase = kPhUp;
         }
+      } else {  // kPhUp
+        if (fits) phase = kPhDone;
+        else act = kActAdd;
       }
-      if (act == kActNext && k >= total) act = kActCommit;
+      if (act == kActAdd && k >= total) act = kActCommit;
+
       if (act == kActPrefix) {
-        gb = set_prefix<MAXH>(v, cnt, k, h, sym, lane);
-      } else if (act == kActNext) {
-        // next candidate: the boundary group's smallest unflagged member,
-        // else the next non-empty group inward
-        if (!add_smallest(v, gb, h, sym, lane)) {
-          int m = (int)gb - 1;
-          while (m > 1 && count_at<MAXH>(cnt, m) == 0) --m;
-          gb = (uint32_t)m;
-          add_smallest(v, gb, h, sym, lane);
+        // first k candidates: whole groups above the boundary, then the
+        // smallest members of the boundary group
+        int kk = k, rest = 0;
+        bool full = false;
+        gb = h - 1;
+#pragma unroll
+        for (int m = MAXH - 1; m >= 1; --m) {
+          if (m < h && kk > 0) {
+            gb = m;
+            if (kk >= cnt[m]) {
+              kk -= cnt[m];
+              full = true;
+              rest = cnt[m];
+            } else {
+              full = false;
+              rest = kk;
+              kk = 0;
+            }
+          }
         }
-        ++k;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v.fl[j] = 0u;
+#pragma unroll
+        for (int i = 0; i < kD; ++i) {
+          const uint32_t s0 = nib(v.sym0, i);
+          const uint32_t mg = magnitude(s0, h);
+          const bool f = mg > (uint32_t)gb || (full && mg == (uint32_t)gb);
+          v.fl[i >> 5] |= (f ? 1u : 0u) << (i & 31);
+          symL[i * kThreads + lane] = (uint8_t)(f ? (s0 >= (uint32_t)h ? s0 - 1u : s0 + 1u) : s0);
+        }
+        group_mask(v, h, gb, gm);
+        taken = rest;
+        if (!full)
+          for (int j = 0; j < rest; ++j) toggle(v, symL, extreme_in_group(v, gm, false), h, false, lane);
+      } else if (act == kActAdd || act == kActRemove) {
+        const bool add = act == kActAdd;
+        // move the boundary when the current boundary group has nothing left
+        if (add ? (taken == cnt_at<MAXH>(cnt, gb)) : (taken == 0)) {
+          int m = add ? gb - 1 : gb + 1;
+          while (add ? (m > 1 && cnt_at<MAXH>(cnt, m) == 0) : (m < h - 1 && cnt_at<MAXH>(cnt, m) == 0))
+            m += add ? -1 : 1;
+          gb = m;
+          taken = add ? 0 : cnt_at<MAXH>(cnt, gb);
+          group_mask(v, h, gb, gm);
+        }
+        toggle(v, symL, extreme_in_group(v, gm, !add), h, !add, lane);
+        taken += add ? 1 : -1;
+        k += add ? 1 : -1;
       } else if (act == kActCommit) {
-        // every candidate moved and the stream still does not fit: commit
-        // and search again on the new symbols (the all-innermost vector
-        // always fits)
+        // every candidate moved and the stream still does not fit: keep the
+        // moves and search again on the new symbols (the all-innermost
+        // vector always fits)
         moves += total;
         ++passes;
 #pragma unroll
-        for (int i = 0; i < kD; ++i) v.mag[i >> 3] -= bit(v.fl, i) << (4 * (i & 7));
-#pragma unroll
-        for (int q = 1; q < MAXH; ++q) ge[q] = 0;
-#pragma unroll
         for (int i = 0; i < kD; ++i) {
-          const uint32_t m = nib(v.mag, i);
-#pragma unroll
-          for (int q = 1; q < MAXH; ++q) ge[q] += m >= (uint32_t)q ? 1 : 0;
+          const uint32_t s0 = nib(v.sym0, i);
+          const uint32_t sn = bit(v.fl, i) ? (s0 >= (uint32_t)h ? s0 - 1u : s0 + 1u) : s0;
+          v.sym0[i >> 3] = (v.sym0[i >> 3] & ~(15u << (4 * (i & 7)))) | (sn << (4 * (i & 7)));
         }
-        v.fl[0] = v.fl[1] = v.fl[2] = v.fl[3] = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v.fl[j] = 0u;
         k = 0;
-        materialize(v, h, sym, lane);
+        first_round = false;
         phase = kPhInit;
       }
     }
-    moves += k;
+    if (phase == kPhDone) moves += k;
 
     // container: [final state, little endian][renorm bytes][zero pad]
-    if (in_pool) {
-    uint8_t *dst = a.cont + ((int64_t)g * a.num_slots + slot) * C;
-    dst[0] = (uint8_t)xfin;
-    dst[1] = (uint8_t)(xfin >> 8);
-    dst[2] = (uint8_t)(xfin >> 16);
-    dst[3] = (uint8_t)(xfin >> 24);
-    for (int j = 0; j < C - 4; ++j) dst[4 + j] = j < B ? scr[(kScr - B + j) * kThreads + lane] : (uint8_t)0;
-    a.norm[(int64_t)g * a.num_slots + slot] = (uint16_t)nh;
+    if (in_pool && okbuf >= 0) {
+      uint8_t *dst = a.cont + ((int64_t)g * a.num_slots + slot) * C;
+      dst[0] = (uint8_t)okx;
+      dst[1] = (uint8_t)(okx >> 8);
+      dst[2] = (uint8_t)(okx >> 16);
+      dst[3] = (uint8_t)(okx >> 24);
+      const uint8_t *sb = scr[okbuf];
+      for (int j = 0; j < C - 4; ++j) dst[4 + j] = j < okB ? sb[(kScr - okB + j) * kThreads + lane] : (uint8_t)0;
+      a.norm[(int64_t)g * a.num_slots + slot] = (uint16_t)nh;
     }
 
     if (a.stats) {
@@ -440,7 +467,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a, Tables t
       if (passes) atomicAdd(&bstat[3], (uint32_t)passes);
       if (bad) atomicAdd(&bstat[4], 1u);
       if (zero) atomicAdd(&bstat[5], 1u);
-      atomicAdd(&bstat[6 + 4 + B], 1u);
+      atomicAdd(&bstat[6 + 4 + okB], 1u);
     }
   }
   if (a.stats) {
