@@ -270,26 +270,41 @@ __device__ __forceinline__ float wave_sum(float v) {
 // heads (sc) and its own K and V norms; m_run is per head (same in every
 // lane), l_lane is this lane's share of the per-head sum (reduced once per
 // item).  Writes P = p * n_v (fp16) to LDS and rescales the V accumulators.
+// The running max only has to bound the scores, not equal their maximum:
+// while no score of the tile exceeds it (checked with one vote), the tile
+// reuses it and skips the reductions and the rescale; p stays <= 1.
 __device__ __forceinline__ void softmax_tile(const floatx4 &sc, uint32_t nk_bits, uint32_t nv_bits, bool valid,
                                              float qk_scale, float (&m_run)[4], float (&l_lane)[4],
                                              uint16_t *pl, floatx4 (&acc)[4], int lane) {
   const float nk = (float)__builtin_bit_cast(_Float16, (uint16_t)nk_bits);
   const float nv = (float)__builtin_bit_cast(_Float16, (uint16_t)nv_bits);
-  float alpha[4];
+  float s[4];
+  bool over = false;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    const float s = valid ? sc[h] * nk * qk_scale : -__builtin_inff();
-    const float m_new = fmaxf(m_run[h], wave_max(s));
-    alpha[h] = exp2f(m_run[h] - m_new);
-    const float p = valid ? exp2f(s - m_new) : 0.0f;
-    l_lane[h] = l_lane[h] * alpha[h] + p;
-    m_run[h] = m_new;
-    pl[h * kTile + lane] = __builtin_bit_cast(uint16_t, (_Float16)(valid ? p * nv : 0.0f));
+    s[h] = valid ? sc[h] * nk * qk_scale : -__builtin_inff();
+    over |= s[h] > m_run[h];  // also true while m_run is still -inf
+  }
+  if (__builtin_amdgcn_read_exec() & __ballot(over)) {
+    float alpha[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float m_new = fmaxf(m_run[h], wave_max(s[h]));
+      alpha[h] = exp2f(m_run[h] - m_new);
+      l_lane[h] *= alpha[h];
+      m_run[h] = m_new;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) acc[p][h] *= alpha[h];
   }
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
-#pragma unroll
-    for (int h = 0; h < 4; ++h) acc[p][h] *= alpha[h];
+  for (int h = 0; h < 4; ++h) {
+    const float p = valid ? exp2f(s[h] - m_run[h]) : 0.0f;
+    l_lane[h] += p;
+    pl[h * kTile + lane] = __builtin_bit_cast(uint16_t, (_Float16)(valid ? p * nv : 0.0f));
+  }
 }
 
 template <int NQ>

@@ -8,8 +8,8 @@
 // x < 2^23 (every f >= 16, so one byte always restores the interval).
 //
 // Decode tables in LDS, per codec (4352 bytes):
-//   sym8[4096]   slot -> symbol (one byte, so the slot itself is the LDS
-//                address: no index arithmetic)
+//   sym8[4096]   slot -> 8 * symbol (one byte, so the slot itself is the LDS
+//                address and the byte is already the symbol-table offset)
 //   symtab[16]   symbol -> {f, cum | fp16 level << 16}
 // The byte table is read at a random slot per lane; the symbol table has at
 // most 16 distinct entries, so its reads are mostly broadcasts.
@@ -29,7 +29,7 @@ __device__ __forceinline__ void build_tables(uint8_t *sym8, uint2 *symtab, const
   for (int u = tid; u < (int)kM; u += nthreads) {
     int s = 0;
     while (s + 1 < t.levels && (int)t.cum[s + 1] <= u) ++s;
-    sym8[u] = (uint8_t)s;
+    sym8[u] = (uint8_t)(8 * s);
   }
   if (tid < kMaxLevels)
     symtab[tid] = tid < t.levels ? make_uint2(t.freq[tid], (uint32_t)t.cum[tid] | ((uint32_t)t.recon[tid] << 16))
@@ -40,8 +40,9 @@ __device__ __forceinline__ void build_tables(uint8_t *sym8, uint2 *symtab, const
 // entry (.y >> 16 = fp16 level) and the symbol.
 __device__ __forceinline__ uint2 rans_step(uint32_t &x, const uint8_t *sym8, const uint2 *symtab, uint32_t &s) {
   const uint32_t slot = x & (kM - 1);
-  s = sym8[slot];
-  const uint2 e = symtab[s];
+  const uint32_t s8 = sym8[slot];
+  s = s8 >> 3;
+  const uint2 e = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(symtab) + s8);
   x = __umul24(e.x, x >> kMBits) + (slot - (e.y & 0xFFFFu));
   return e;
 }
