@@ -115,14 +115,13 @@ __device__ __forceinline__ uint32_t load_le32(const uint8_t *p) {
 // ---------------------------------------------------------------- split-K
 // Per-wave LDS slice (byte offsets), identical on host and device.
 struct WaveLayout {
-  int kst, vst, qr, pl, vt, bytes;
+  int kst, vst, pl, vt, bytes;
 };
 __host__ __device__ inline WaveLayout wave_layout(int Ck, int Cv) {
   WaveLayout w;
   w.kst = 0;
   w.vst = w.kst + ((kTile * Ck + 31) & ~15);
-  w.qr = w.vst + ((kTile * Cv + 31) & ~15);
-  w.pl = w.qr + 32 * 4 * 16;
+  w.pl = w.vst + ((kTile * Cv + 31) & ~15);
   w.vt = w.pl + 4 * kTile * 2;
   w.bytes = w.vt + kPass * kVtStride * 2;
   w.bytes = (w.bytes + 15) & ~15;
@@ -193,10 +192,14 @@ struct DecTab {
 //   halves); P is broadcast per half (cbsz 3), read by lanes 0..3, 32..35.
 template <bool DK, bool DV>
 __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
-                                          const uint8_t *vb, const uint4 *qr, const uint16_t *pl,
+                                          const uint8_t *vb, const uint4 *qg, const uint16_t *pl,
                                           uint16_t *vt, floatx4 &sc, floatx4 (&acc)[4], int lane) {
   const int th = lane >> 5, row = lane & 31;
   const bool qlane = lane < 4, plane = (lane & 31) < 4;
+  // rotated query (global, 2 KB per item, cache resident): lanes 0..3 load
+  // the 16 bytes of their head for the next group one group ahead
+  uint4 qnext = make_uint4(0, 0, 0, 0);
+  if (DK && qlane) qnext = qg[lane];
   uint32_t xk = 0, xv = 0;
   const uint8_t *pk = kb, *pv = vb;
   if (DK) {
@@ -211,8 +214,9 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     for (int gq = 0; gq < kPass / 4; ++gq) {
-      uint4 qv = make_uint4(0, 0, 0, 0);
-      if (DK && qlane) qv = qr[(p * (kPass / 4) + gq) * 4 + lane];
+      const uint4 qv = qnext;
+      const int gnext = p * (kPass / 4) + gq + 1;
+      if (DK && qlane && gnext < 32) qnext = qg[gnext * 4 + lane];
       uint32_t lv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -326,7 +330,6 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
   uint8_t *base = smem + (size_t)wave * L.bytes;
   uint8_t *kst = base + L.kst;
   uint8_t *vst = base + L.vst;
-  uint4 *qr = reinterpret_cast<uint4 *>(base + L.qr);
   uint16_t *pl = reinterpret_cast<uint16_t *>(base + L.pl);
   uint16_t *vt = reinterpret_cast<uint16_t *>(base + L.vt);
 
@@ -348,9 +351,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
     const uint8_t *vplane = a.vc + pbase * Cv;
 
     wave_sync();  // the previous item's LDS reads are done
-    const uint4 *qsrc = reinterpret_cast<const uint4 *>(a.qrot + bg * kQrotPerBG);
-    qr[lane] = qsrc[lane];
-    qr[lane + 64] = qsrc[lane + 64];
+    const uint4 *qr = reinterpret_cast<const uint4 *>(a.qrot + bg * kQrotPerBG);
 
     // this lane's token norms for a tile (0 outside the pool plane)
     auto norms = [&](int tile, uint32_t &nk, uint32_t &nv) {
