@@ -25,6 +25,8 @@
 // bit for bit.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "dq_internal.h"
 
 namespace dq {
@@ -478,6 +480,202 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a, Tables t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small batches (a decode step appends one token per sequence): one wave per
+// vector, so the latency is a single rANS pass instead of a serial search.
+//  - rotation and norm cooperatively: lane l holds coordinates l and l + 64;
+//    the butterflies of width 1..32 pair lanes l and l ^ w, width 64 pairs
+//    the two values in a lane (the same fp32 operations in the same order as
+//    the per-lane path); the sum of squares follows the same halving tree;
+//  - every drift candidate gets its rank in the drift order (magnitude
+//    descending, |y| ascending, index ascending) by a broadcast scan;
+//  - lane l runs the rANS pass with the first k0 + l candidates moved one
+//    level inward; the lowest lane whose stream fits is the answer (the
+//    length never increases along the order, so every lower lane failed).
+constexpr int kWaveVecs = 4;  // vectors (waves) per block
+
+__global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kernel(EncodeArgs a, Tables t) {
+  __shared__ uint4 etab[kMaxLevels];
+  __shared__ uint32_t ent[kWaveVecs][kD];          // s0 | sd << 8 | rank << 16
+  __shared__ float yabs[kWaveVecs][kD];
+  __shared__ uint8_t mag[kWaveVecs][kD];
+  __shared__ uint8_t scr[kWaveVecs][kScr * 64];   // renorm bytes, lane-minor
+  const int tid = threadIdx.x;
+  if (tid < t.levels) {
+    const uint32_t f = t.freq[tid];
+    etab[tid] = make_uint4(f << 19, t.magic[tid], t.cum[tid], (kM - f) | ((uint32_t)t.shift[tid] << 16));
+  }
+  __syncthreads();
+  const int w = tid >> 6, lane = tid & 63;
+  const int64_t nvec = a.T * (int64_t)t.hkv;
+  const int64_t vid = (int64_t)blockIdx.x * kWaveVecs + w;
+  if (vid >= nvec) return;  // whole wave exits together
+  const int h = t.half, C = t.C;
+  const int g = (int)(vid / a.T);
+  const int64_t tok = vid - (int64_t)g * a.T;
+  const int64_t slot = a.slots[tok];
+  const uint16_t *xp = a.x + tok * a.stride_t + (int64_t)g * a.stride_h;
+  const float x0 = __uint_as_float((uint32_t)xp[lane] << 16);
+  const float x1 = __uint_as_float((uint32_t)xp[lane + 64] << 16);
+
+  // ||x||^2: level 64 in-lane, then levels 32 .. 1 across lanes
+  float sq = x0 * x0 + x1 * x1;
+#pragma unroll
+  for (int wd = 32; wd >= 1; wd >>= 1) {
+    const float o = __shfl_down(sq, wd);
+    if (lane < wd) sq = sq + o;
+  }
+  const float S = __shfl(sq, 0);
+
+  // y = H * D * x
+  const uint64_t s0w = splitmix64(t.seed, 2ull * (uint64_t)g);
+  const uint64_t s1w = splitmix64(t.seed, 2ull * (uint64_t)g + 1ull);
+  float u0 = ((s0w >> lane) & 1ull) ? -x0 : x0;
+  float u1 = ((s1w >> lane) & 1ull) ? -x1 : x1;
+#pragma unroll
+  for (int wd = 1; wd < 64; wd <<= 1) {
+    const float p0 = __shfl_xor(u0, wd), p1 = __shfl_xor(u1, wd);
+    const bool hi = lane & wd;
+    u0 = hi ? p0 - u0 : u0 + p0;
+    u1 = hi ? p1 - u1 : u1 + p1;
+  }
+  {
+    const float p = u0, q = u1;
+    u0 = p + q;
+    u1 = p - q;
+  }
+
+  const uint32_t nh = norm_half(S);
+  const float nf = half_to_float(nh);
+  const bool zero = nh == 0u;
+  const bool bad = (nh & 0x7C00u) == 0x7C00u;
+  const bool degenerate = zero || bad;
+  float thr[kMaxHalf];
+#pragma unroll
+  for (int k = 1; k < kMaxHalf; ++k)
+    thr[k] = (k < h && !degenerate) ? (float)(k * t.step64) * nf * 0.015625f : __builtin_inff();
+  uint32_t sA[2], mA[2];
+  float yA[2];
+  const float ys[2] = {u0, u1};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float ay = degenerate ? 0.0f : __builtin_fabsf(ys[e]);
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxHalf; ++k) m += ay >= thr[k] ? 1u : 0u;
+    sA[e] = (degenerate || ys[e] >= 0.0f) ? (uint32_t)h + m : (uint32_t)(h - 1) - m;
+    mA[e] = m;
+    yA[e] = ay;
+  }
+  uint32_t *E = ent[w];
+  float *Y = yabs[w];
+  uint8_t *Mg = mag[w];
+  uint8_t *scol = scr[w];
+
+  int moves = 0, passes = 0, okB = 0;
+  uint32_t okx = 0;
+  int win = -1;
+  for (int outer = 0; outer < 2 * kD && win < 0; ++outer) {
+    // ranks of the candidates (magnitude >= 1) in drift order
+    Mg[lane] = (uint8_t)mA[0];
+    Mg[lane + 64] = (uint8_t)mA[1];
+    Y[lane] = yA[0];
+    Y[lane + 64] = yA[1];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int rank[2] = {0, 0};
+    for (int j = 0; j < kD; ++j) {
+      const uint32_t mj = Mg[j];
+      const float yj = Y[j];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = lane + 64 * e;
+        const bool before = mj >= 1u && (mj > mA[e] || (mj == mA[e] && (yj < yA[e] || (yj == yA[e] && j < i))));
+        rank[e] += before ? 1 : 0;
+      }
+    }
+    int total = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) total += __popcll(__ballot(mA[e] >= 1u));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t sd = mA[e] >= 1u ? (sA[e] >= (uint32_t)h ? sA[e] - 1u : sA[e] + 1u) : sA[e];
+      const uint32_t rk = mA[e] >= 1u ? (uint32_t)rank[e] : 255u;
+      E[lane + 64 * e] = sA[e] | (sd << 8) | (rk << 16);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int k0 = 0; k0 <= total && win < 0; k0 += 64) {
+      const uint32_t k = (uint32_t)(k0 + lane);
+      uint32_t x = kLow;
+      int pos = kScr - 1;
+      for (int i = kD - 1; i >= 0; --i) {
+        const uint32_t en = E[i];
+        const uint32_t s = ((en >> 16) & 0xFFu) < k ? ((en >> 8) & 0xFFu) : (en & 0xFFu);
+        const uint4 c = etab[s];
+        scol[pos * 64 + lane] = (uint8_t)x;
+        const bool emit = x >= c.x;
+        x = emit ? x >> 8 : x;
+        pos -= emit ? 1 : 0;
+        const uint32_t q = __umulhi(x, c.y) >> (c.w >> 16);
+        x = x + c.z + __umul24(q, c.w & 0xFFFFu);
+      }
+      const int B = kScr - 1 - pos;
+      const bool fits = 4 + B <= C && (int)k <= total;
+      const uint64_t vote = __ballot(fits);
+      if (vote) {
+        win = __ffsll((unsigned long long)vote) - 1;
+        okB = __shfl(B, win);
+        okx = (uint32_t)__shfl((int)x, win);
+        moves += k0 + win;
+      }
+    }
+    if (win < 0) {
+      // every candidate moved and the stream still does not fit: keep the
+      // moves and rank again on the new symbols
+      moves += total;
+      ++passes;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (mA[e] >= 1u) {
+          sA[e] = sA[e] >= (uint32_t)h ? sA[e] - 1u : sA[e] + 1u;
+          mA[e] -= 1u;
+        }
+      }
+    }
+  }
+
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (win >= 0 && slot >= 0 && slot < a.num_slots) {
+    uint8_t *dst = a.cont + ((int64_t)g * a.num_slots + slot) * C;
+    for (int j = lane; j < C; j += 64) {
+      uint8_t b;
+      if (j < 4) b = (uint8_t)(okx >> (8 * j));
+      else b = (j - 4 < okB) ? scol[(kScr - okB + (j - 4)) * 64 + win] : (uint8_t)0;
+      dst[j] = b;
+    }
+    if (lane == 0) a.norm[(int64_t)g * a.num_slots + slot] = (uint16_t)nh;
+  }
+  if (a.stats && lane == 0) {
+    unsigned long long *gs = reinterpret_cast<unsigned long long *>(a.stats);
+    atomicAdd(gs + 0, 1ull);
+    if (moves) {
+      atomicAdd(gs + 1, 1ull);
+      atomicAdd(gs + 2, (unsigned long long)moves);
+    }
+    if (passes) atomicAdd(gs + 3, (unsigned long long)passes);
+    if (bad) atomicAdd(gs + 4, 1ull);
+    if (zero) atomicAdd(gs + 5, 1ull);
+    atomicAdd(gs + 6 + 4 + okB, 1ull);
+  }
+}
+
+constexpr int64_t kWavePathMax = 16384;  // vectors: below this, latency wins
+
 template <int MAXH>
 hipError_t launch(const EncodeArgs &a, const Tables &t, hipStream_t s) {
   const int64_t nvec = a.T * (int64_t)t.hkv;
@@ -505,6 +703,18 @@ extern "C" int dq_encode(dq_codec_t codec, const void *x, int64_t T, int64_t str
   dq::EncodeArgs a{static_cast<const uint16_t *>(x), T, stride_t, stride_h, slots, num_slots,
                    cont, norm, stats};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = t.half <= 4 ? dq::launch<4>(a, t, s) : dq::launch<8>(a, t, s);
+  // DQ_ENCODE_WAVE_MAX overrides the batch size (vectors) up to which the
+  // wave-per-vector kernel runs; both kernels write identical bytes
+  int64_t wave_max = dq::kWavePathMax;
+  if (const char *ev = getenv("DQ_ENCODE_WAVE_MAX")) wave_max = atoll(ev);
+  hipError_t e;
+  if (T * (int64_t)t.hkv <= wave_max && T * (int64_t)t.hkv <= ((int64_t)1 << 30)) {
+    const int64_t nvec = T * (int64_t)t.hkv;
+    hipLaunchKernelGGL(dq::encode_wave_kernel, dim3((unsigned)((nvec + dq::kWaveVecs - 1) / dq::kWaveVecs)),
+                       dim3(64 * dq::kWaveVecs), 0, s, a, t);
+    e = hipGetLastError();
+  } else {
+    e = t.half <= 4 ? dq::launch<4>(a, t, s) : dq::launch<8>(a, t, s);
+  }
   return e == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }

@@ -35,6 +35,14 @@ def _codecs(O, levels, C, seed, hkv, step64=0):
     return g, o
 
 
+@pytest.fixture(params=["wave", "lane"])
+def encode_path(request, monkeypatch):
+    """Small batches run the wave-per-vector kernel, large ones the
+    lane-per-vector kernel; force each in turn on the same inputs."""
+    monkeypatch.setenv("DQ_ENCODE_WAVE_MAX", "1000000000" if request.param == "wave" else "0")
+    return request.param
+
+
 def _encode_both(O, gc, oc, x, slots, num_slots):
     cont, norm = dq.alloc_pool(gc, num_slots, DEV)
     st = dq.new_stats(DEV)
@@ -61,9 +69,9 @@ def O_stats(ost):
 
 @pytest.mark.parametrize("levels,C", [(8, 34), (6, 34), (8, 29), (6, 29)])
 @pytest.mark.parametrize("kind", ["iid", "outlier", "student_t5", "iid_scaled"])
-def test_encode_bit_exact(oracle_lib, levels, C, kind):
+def test_encode_bit_exact(oracle_lib, encode_path, levels, C, kind):
     O = oracle_lib
-    _say(f"encode {levels}/{C} {kind}")
+    _say(f"encode {levels}/{C} {kind} {encode_path}")
     T, hkv = 333, 3
     gc, oc = _codecs(O, levels, C, seed=101 + levels, hkv=hkv)
     x = synth.kv_tensor(kind, T, hkv, seed=7, device=DEV)
@@ -100,11 +108,11 @@ def _adversarial_batch():
 
 @pytest.mark.parametrize("levels,C,step64", [(8, 34, 0), (6, 34, 0), (8, 29, 0), (6, 29, 0),
                                              (8, 34, 64), (6, 34, 64), (4, 30, 64), (16, 60, 25), (10, 40, 34)])
-def test_encode_adversarial(oracle_lib, levels, C, step64):
+def test_encode_adversarial(oracle_lib, encode_path, levels, C, step64):
     """Degenerate norms, fp16 rounding ties, exact threshold ties (step 1.0
     and one-hot inputs put |y| exactly on a threshold), subnormals."""
     O = oracle_lib
-    _say(f"adversarial {levels}/{C}/{step64}")
+    _say(f"adversarial {levels}/{C}/{step64} {encode_path}")
     rows = _adversarial_batch()
     x = torch.from_numpy(rows).to(torch.bfloat16).reshape(-1, 1, 128).to(DEV)
     gc, oc = _codecs(O, levels, C, seed=5, hkv=1, step64=step64)
@@ -112,7 +120,7 @@ def test_encode_adversarial(oracle_lib, levels, C, step64):
     _assert_encode_equal(*_encode_both(O, gc, oc, x, slots, x.shape[0]), "adversarial")
 
 
-def test_encode_strided_input_and_pool_slots(oracle_lib):
+def test_encode_strided_input_and_pool_slots(oracle_lib, encode_path):
     O = oracle_lib
     gc, oc = _codecs(O, 8, 34, seed=9, hkv=4)
     big = synth.kv_tensor("outlier", 200, 8, seed=11, device=DEV)
