@@ -60,6 +60,135 @@ def load_traffic(bytes_per_launch_alg):
     return c.get("traffic_bytes_per_launch")
 
 
+# The profiles under profiles/ come from these commands (run from the repo
+# root on the GPU machine, one after the other), then
+# `python bench.py --summarize-profiles gpurun_out/prof` on any host.
+PROF = "gpurun_out/prof"
+PROFILE_CMDS = {
+    "trace": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -k 10 900 "
+              "rocprofv3 --kernel-trace --stats --output-format csv -d $R/" + PROF + "/trace -o run -- "
+              "python3 $R/bench.py > $R/" + PROF + "/trace_bench.json"),
+    "fetch": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
+              "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'attn_splitk|copyBuffer' --output-format csv "
+              "-d $R/" + PROF + "/fetch -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline "
+              "--copy-calibration > $R/" + PROF + "/fetch_bench.json"),
+    "write": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
+              "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'attn_splitk|copyBuffer' --output-format csv "
+              "-d $R/" + PROF + "/write -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline "
+              "--copy-calibration > $R/" + PROF + "/write_bench.json"),
+}
+
+
+def _csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for name in files:
+            if name.endswith(suffix):
+                return os.path.join(root, name)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _bench_line(path):
+    with open(path) as f:
+        lines = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+    return json.loads(lines[-1])
+
+
+def summarize_profiles(d):
+    """Writes the committed summaries from the rocprofv3 CSV output of
+    PROFILE_CMDS: the kernel-trace statistics of the default bench command,
+    and HBM bytes per split-K launch from FETCH_SIZE / WRITE_SIZE, each
+    scaled by what the same counter reads for the 1 GiB device copy that
+    --copy-calibration runs (rocprofv3 reports both in KiB per dispatch)."""
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    wl = "llama31_8b_b128_8k"
+    src = attn_source_hash()
+
+    # ---- kernel trace
+    stats = _csv(_find(os.path.join(d, "trace"), "kernel_stats.csv"))
+    live = _bench_line(os.path.join(d, "trace_bench.json"))
+    if live.get("attn_source_sha256_16") != src:
+        raise SystemExit("trace run was made on a different attention source")
+    rows = []
+    for r in stats:
+        name = r["Name"]
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
+        rows.append((float(r["TotalDurationNs"]), short, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                     float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(reverse=True)
+    split = [r for r in rows if "attn_splitk_kernel" in r[1]]
+    lines = [f"# Kernel trace: decode step, {wl}", "",
+             "Batch 128, 32 q / 8 kv heads, 8K context, K 8 levels / V 6 levels in 34-byte containers; "
+             "the default bench command (prefill encode, 3 warm-up and 16 timed decode steps, oracle timing "
+             "on the host).", "",
+             "Command (from the repository root):", "", "```", PROFILE_CMDS["trace"], "```", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for tot, short, calls, avg, mn, mx, pct in rows[:12]:
+        lines.append(f"| `{short}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.2f} |")
+    rl = live["roofline"]
+    if split:
+        sp = split[0]
+        lines += ["", f"Split-K kernel: rocprofv3 average {sp[3]:.1f} us over {sp[2]} launches (warm-up "
+                  f"included); the same run's bench line measured {rl['avg_launch_ms'] * 1e3:.1f} us with HIP "
+                  f"events around the kernel over the timed steps, {rl['achieved']:.1f} GB/s of compressed "
+                  f"bytes = {rl['frac']:.2%} of 8 TB/s.",
+                  "", "Bench line of this run:", "", "```", json.dumps(live), "```"]
+    with open(os.path.join(out_dir, f"all_kernels_{wl}_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # ---- HBM counters
+    def per_kernel(kind, counter):
+        rows = _csv(_find(os.path.join(d, kind), "counter_collection.csv"))
+        rows = [r for r in rows if r["Counter_Name"] == counter]
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        cal = max(copies, key=lambda r: float(r["Counter_Value"]))
+        att = [float(r["Counter_Value"]) for r in rows if "attn_splitk_kernel" in r["Kernel_Name"]]
+        bl = _bench_line(os.path.join(d, f"{kind}_bench.json"))
+        if bl.get("attn_source_sha256_16") != src:
+            raise SystemExit(f"{kind} run was made on a different attention source")
+        return float(cal["Counter_Value"]), att
+    f_cal, f_att = per_kernel("fetch", "FETCH_SIZE")
+    w_cal, w_att = per_kernel("write", "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    f_scale, w_scale = gib_kib / f_cal, gib_kib / w_cal
+    fetch_b = sum(f_att) / len(f_att) * 1024 * f_scale
+    write_b = sum(w_att) / len(w_att) * 1024 * w_scale
+    alg = rl["alg_bytes_per_launch"]
+    rec = {"kernel": "attn_splitk_kernel", "workload": wl, "source_sha256_16": src,
+           "fetch_kib_per_launch_raw": sum(f_att) / len(f_att), "write_kib_per_launch_raw": sum(w_att) / len(w_att),
+           "launches": [len(f_att), len(w_att)],
+           "copy_1gib_fetch_kib": f_cal, "copy_1gib_write_kib": w_cal,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+           "traffic_bytes_per_launch": fetch_b + write_b,
+           "alg_bytes_per_launch": alg, "traffic_over_alg": (fetch_b + write_b) / alg,
+           "commands": [PROFILE_CMDS["fetch"], PROFILE_CMDS["write"]]}
+    with open(os.path.join(out_dir, f"attn_splitk_{wl}_counters.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    md = [f"# HBM counters: attn_splitk_kernel, {wl}", "",
+          "Commands (from the repository root), one counter per run:", "", "```",
+          PROFILE_CMDS["fetch"], PROFILE_CMDS["write"], "```", "",
+          "| | FETCH_SIZE | WRITE_SIZE |", "|---|---:|---:|",
+          f"| 1 GiB device copy (KiB) | {f_cal:.0f} | {w_cal:.0f} |",
+          f"| scale to bytes moved | {f_scale:.3f} | {w_scale:.3f} |",
+          f"| split-K kernel, raw KiB per launch | {rec['fetch_kib_per_launch_raw']:.0f} | "
+          f"{rec['write_kib_per_launch_raw']:.0f} |",
+          f"| split-K kernel, scaled MB per launch | {fetch_b / 1e6:.1f} | {write_b / 1e6:.1f} |", "",
+          f"Algorithmic bytes per launch (containers + fp16 norms of every context token, K and V): "
+          f"{alg / 1e6:.1f} MB.  Measured traffic {(fetch_b + write_b) / 1e6:.1f} MB = "
+          f"{rec['traffic_over_alg']:.3f} x algorithmic; the writes are the split-K partial results.", ""]
+    with open(os.path.join(out_dir, f"attn_splitk_{wl}_counters.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(f"wrote profiles for source {src}: traffic {(fetch_b + write_b) / 1e6:.1f} MB per launch")
+
+
 def cpu_baseline(w, ck, cv, kc, kn, vc, vn, q, starts, ctx, seconds):
     """The oracle, as it stands, on a bounded sample: decode attention for the
     first n sequences (n grown until ~`seconds` of CPU work), on the host
@@ -110,7 +239,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter scale for rocprofv3)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ from the rocprofv3 output of PROFILE_CMDS (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -188,14 +322,17 @@ def main():
         dq.encode(cv, Vn[s], slots_s[s], vc, vn)
         if ev is not None:
             ev[1].record()
-        dq.attn_decode(ck, cv, qs[s], kc, kn, vc, vn, st_t, lens_s[s], max_len, out=out, workspace=ws)
+        dq.attn_decode(ck, cv, qs[s], kc, kn, vc, vn, st_t, lens_s[s], max_len, out=out, workspace=ws,
+                       split_events=None if ev is None else (ev[3], ev[4]))
         if ev is not None:
             ev[2].record()
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # per step: [step start, encode done, attention done, split-K start, split-K done]; all on
+    # the current stream, which is the one every library launch goes to
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -209,13 +346,15 @@ def main():
     timed_bytes = sum(bytes_s[args.warmup:])
     ms_per_step = total_s * 1e3 / args.steps
     value = timed_bytes / total_s / 1e9
+    split_ms = [evs[k][3].elapsed_time(evs[k][4]) for k in range(args.steps)]
     att_avg_ms = sum(att_ms) / len(att_ms)
+    split_avg_ms = sum(split_ms) / len(split_ms)
     alg_bytes = timed_bytes / args.steps
-    achieved = alg_bytes / (att_avg_ms / 1e3) / 1e9
+    achieved = alg_bytes / (split_avg_ms / 1e3) / 1e9
     ctx_tokens = sum(int((ctx + args.warmup + k + 1).sum()) for k in range(args.steps))
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (append encode {np.mean(enc_ms):.3f} ms, "
-        f"attention {att_avg_ms:.3f} ms), {value:.1f} GB/s step, attention {achieved:.1f} GB/s "
-        f"= {achieved / HBM_PEAK_GBPS:.1%} of HBM peak")
+        f"attention {att_avg_ms:.3f} ms of which split-K {split_avg_ms:.3f} ms), {value:.1f} GB/s step, "
+        f"split-K kernel {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of HBM peak")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -241,8 +380,11 @@ def main():
                    "levels": [ck.levels, cv.levels], "kv_distribution": w.kind},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": load_traffic(alg_bytes), "kernel": "dq_attn_decode",
-                     "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(att_avg_ms, 4)},
+                     "traffic": load_traffic(alg_bytes), "kernel": "attn_splitk_kernel",
+                     "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(split_avg_ms, 4)},
+        "attn_source_sha256_16": attn_source_hash(),
+        "attn_call_ms": round(att_avg_ms, 4),
+        "attn_call_gbps": round(alg_bytes / (att_avg_ms / 1e3) / 1e9, 2),
         "cpu_baseline": cpu,
         "attn_context_tokens_per_s": round(ctx_tokens / (sum(att_ms) / 1e3), 1),
         "append_encode_ms": round(float(np.mean(enc_ms)), 4),

@@ -171,6 +171,23 @@ int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B,
                    int32_t out_dtype, void *out, void *workspace,
                    size_t ws_bytes, dq_stream_t stream);
 
+/* dq_attn_decode plus a measurement hook: `split_begin` and `split_end`
+ * (hipEvent_t, either may be NULL) are recorded on `stream` right before
+ * and right after the split-K kernel, the one that reads the compressed
+ * cache, so that its own duration can be taken with hipEventElapsedTime
+ * without a profiler.  The events belong to the caller; results and
+ * status codes are those of dq_attn_decode (an event record that fails
+ * returns DQ_ERR_HIP). */
+int dq_attn_decode_timed(dq_codec_t ck, dq_codec_t cv, const void *q,
+                         int32_t B, int32_t Hq, const uint8_t *k_cont,
+                         const uint16_t *k_norm, const uint8_t *v_cont,
+                         const uint16_t *v_norm, int64_t num_slots,
+                         const int64_t *seq_start, const int32_t *seq_len,
+                         int64_t max_len, float sm_scale, int32_t out_dtype,
+                         void *out, void *workspace, size_t ws_bytes,
+                         dq_stream_t stream, void *split_begin,
+                         void *split_end);
+
 #ifdef __cplusplus
 }
 #endif

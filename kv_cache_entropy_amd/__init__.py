@@ -182,9 +182,13 @@ def attn_workspace_bytes(B: int, Hq: int, Hkv: int, max_len: int) -> int:
 def attn_decode(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_cont, v_norm,
                 seq_start: torch.Tensor, seq_len: torch.Tensor, max_len: int,
                 sm_scale: float | None = None, out: torch.Tensor | None = None,
-                out_dtype=torch.float32, workspace: torch.Tensor | None = None):
+                out_dtype=torch.float32, workspace: torch.Tensor | None = None,
+                split_events=None):
     """q: bf16 [B, Hq, 128]; pools from alloc_pool; seq_start int64 [B];
-    seq_len int32 [B] (1 <= len <= max_len).  Returns out [B, Hq, 128]."""
+    seq_len int32 [B] (1 <= len <= max_len).  Returns out [B, Hq, 128].
+
+    split_events: optional (begin, end) torch.cuda.Event pair, recorded on
+    the current stream around the split-K kernel alone."""
     _need_cuda("q", q, torch.bfloat16)
     for name, t, dt in (("k_cont", k_cont, torch.uint8), ("v_cont", v_cont, torch.uint8),
                         ("k_norm", k_norm, torch.float16), ("v_norm", v_norm, torch.float16),
@@ -208,9 +212,17 @@ def attn_decode(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_cont, v
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if sm_scale is None:
         sm_scale = HEAD_DIM ** -0.5
-    _check(_lib.lib().dq_attn_decode(
-        ck.handle, cv.handle, _ptr(q), B, Hq, _ptr(k_cont), _ptr(k_norm), _ptr(v_cont),
-        _ptr(v_norm), k_cont.shape[1], _ptr(seq_start), _ptr(seq_len), max_len,
-        ctypes.c_float(sm_scale), 0 if out_dtype == torch.float32 else 1, _ptr(out),
-        _ptr(workspace), workspace.numel(), _stream(q.device)), "dq_attn_decode")
+    args = (ck.handle, cv.handle, _ptr(q), B, Hq, _ptr(k_cont), _ptr(k_norm), _ptr(v_cont),
+            _ptr(v_norm), k_cont.shape[1], _ptr(seq_start), _ptr(seq_len), max_len,
+            ctypes.c_float(sm_scale), 0 if out_dtype == torch.float32 else 1, _ptr(out),
+            _ptr(workspace), workspace.numel(), _stream(q.device))
+    if split_events is None:
+        _check(_lib.lib().dq_attn_decode(*args), "dq_attn_decode")
+    else:
+        handles = []
+        for ev in split_events:
+            if ev.cuda_event == 0:  # torch creates the HIP event on first record
+                ev.record()
+            handles.append(ctypes.c_void_p(ev.cuda_event))
+        _check(_lib.lib().dq_attn_decode_timed(*args, *handles), "dq_attn_decode_timed")
     return out

@@ -558,11 +558,11 @@ extern "C" int dq_attn_decode_workspace(int32_t B, int32_t Hq, int32_t Hkv, int6
   return DQ_OK;
 }
 
-extern "C" int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,
-                              const uint8_t *k_cont, const uint16_t *k_norm, const uint8_t *v_cont,
-                              const uint16_t *v_norm, int64_t num_slots, const int64_t *seq_start,
-                              const int32_t *seq_len, int64_t max_len, float sm_scale, int32_t out_dtype,
-                              void *out, void *workspace, size_t ws_bytes, dq_stream_t stream) {
+static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq, const uint8_t *k_cont,
+                       const uint16_t *k_norm, const uint8_t *v_cont, const uint16_t *v_norm, int64_t num_slots,
+                       const int64_t *seq_start, const int32_t *seq_len, int64_t max_len, float sm_scale,
+                       int32_t out_dtype, void *out, void *workspace, size_t ws_bytes, dq_stream_t stream,
+                       hipEvent_t split_begin, hipEvent_t split_end) {
   if (!ck || !cv || !q || !k_cont || !k_norm || !v_cont || !v_norm || !seq_start || !seq_len || !out ||
       !workspace)
     return DQ_ERR_INVALID;
@@ -609,10 +609,32 @@ extern "C" int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32
   a.waves_per_block = pl.waves_per_block;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(dq::rotate_q_kernel, dim3((unsigned)(B * Hkv * 4)), dim3(64), 0, s, a, ck->t.seed);
+  if (split_begin && hipEventRecord(split_begin, s) != hipSuccess) return DQ_ERR_HIP;
   hipError_t e = pl.nq == 3   ? dq::launch_splitk<3>(pl, a, ck->t, cv->t, s)
                  : pl.nq == 5 ? dq::launch_splitk<5>(pl, a, ck->t, cv->t, s)
                               : dq::launch_splitk<9>(pl, a, ck->t, cv->t, s);
   if (e != hipSuccess) return DQ_ERR_HIP;
+  if (split_end && hipEventRecord(split_end, s) != hipSuccess) return DQ_ERR_HIP;
   hipLaunchKernelGGL(dq::combine_kernel, dim3((unsigned)(B * Hq)), dim3(128), 0, s, a, cv->t.seed);
   return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
+extern "C" int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,
+                              const uint8_t *k_cont, const uint16_t *k_norm, const uint8_t *v_cont,
+                              const uint16_t *v_norm, int64_t num_slots, const int64_t *seq_start,
+                              const int32_t *seq_len, int64_t max_len, float sm_scale, int32_t out_dtype,
+                              void *out, void *workspace, size_t ws_bytes, dq_stream_t stream) {
+  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, seq_len, max_len,
+                     sm_scale, out_dtype, out, workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" int dq_attn_decode_timed(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,
+                                    const uint8_t *k_cont, const uint16_t *k_norm, const uint8_t *v_cont,
+                                    const uint16_t *v_norm, int64_t num_slots, const int64_t *seq_start,
+                                    const int32_t *seq_len, int64_t max_len, float sm_scale, int32_t out_dtype,
+                                    void *out, void *workspace, size_t ws_bytes, dq_stream_t stream,
+                                    void *split_begin, void *split_end) {
+  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, seq_len, max_len,
+                     sm_scale, out_dtype, out, workspace, ws_bytes, stream, static_cast<hipEvent_t>(split_begin),
+                     static_cast<hipEvent_t>(split_end));
 }

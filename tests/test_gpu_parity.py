@@ -243,6 +243,18 @@ def test_attention_deterministic(oracle_lib):
     assert torch.equal(a, b)
 
 
+def test_attention_timed_entry_point(oracle_lib):
+    """dq_attn_decode_timed writes the same bytes as dq_attn_decode and the
+    two events bracket a non-empty interval."""
+    O = oracle_lib
+    c = _attn_case(O, 2, 8, 2, [3000, 1234], seed=8)
+    a = _gpu_attn(c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b = _gpu_attn(c, split_events=(e0, e1))
+    assert torch.equal(a, b)
+    assert e0.elapsed_time(e1) > 0.0
+
+
 def test_tiny_1seq_1k_config(oracle_lib):
     """1 sequence, 1 query / 1 kv head, context 1024, per-token scaled
     N(0,1) K/V, 34-byte containers: every container and the output."""
