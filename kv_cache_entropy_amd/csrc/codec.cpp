@@ -103,10 +103,14 @@ int build_tables(const dq_codec_desc &d, Tables &t) {
     const uint64_t num = 1ull << (31 + l);
     t.magic[s] = (uint32_t)((num + fs - 1) / fs);
     t.shift[s] = (uint8_t)(l - 1);
-    t.cost[s] = (float)log2(4096.0 / fs);
+    t.cost_fx[s] = (uint32_t)llround(log2(4096.0 / fs) * 1048576.0);
   }
   t.cum[L] = (uint16_t)c;
-  for (int m = 1; m < h; ++m) t.saving[m] = (float)log2((double)f[m - 1] / f[m]);
+  for (int m = 1; m < h; ++m) {
+    t.saving_fx[m] = t.cost_fx[h + m] - t.cost_fx[h + m - 1];
+    // implied by the 1.15 ratio check; the encoder's drift relies on it
+    if (t.saving_fx[m] <= kEpsHiFx + kEpsLoFx) return DQ_ERR_BUDGET;
+  }
   return DQ_OK;
 }
 

@@ -17,6 +17,22 @@ constexpr int kMaxLevels = 16;
 constexpr int kMaxHalf = kMaxLevels / 2;
 constexpr int kMaxC = DQ_MAX_CONTAINER;
 
+// Length band of the encoder's drift.  Encoding one symbol from a state
+// x >= f * 2^11 (always true after renormalisation) changes log2(x) by
+// log2(4096 / f) + d with |d| < log2(1 + 2^-11); emitting a byte from
+// x >= 2^23 takes 8 + e bits with 0 <= e < log2(1 + 255 * 2^-23), at most
+// once per symbol.  Starting from 2^23 and ending in [2^23, 2^31), a stream
+// of B renorm bytes has 8 B <= I + eps < 8 B + 8, with I the sum of
+// log2(4096 / f) over its symbols and -0.095760 < eps < 0.090147 over 128
+// symbols, so it fits C bytes iff I + eps < 8 (C - 3).  In fixed point
+// (kCostFrac fraction bits, each cost rounded: at most 64 units of total
+// rounding) the two bounds below are widened by 64 + 16 units.  The band
+// they leave, 0.186 bits, is narrower than the smallest saving of one
+// move, which the codec check keeps at or above log2(1.15) = 0.2016 bits.
+constexpr int kCostFrac = 20;
+constexpr uint32_t kEpsHiFx = 94526u + 80u;   // ceil(0.0901465 * 2^20) + margin
+constexpr uint32_t kEpsLoFx = 100412u + 80u;  // ceil(0.0957599 * 2^20) + margin
+
 // Everything a kernel needs to know about one codec; passed by value as a
 // kernel argument, so hot calls touch no device-side tables.
 struct Tables {
@@ -35,8 +51,8 @@ struct Tables {
   // (Granlund & Montgomery, PLDI 1994, with N = 31, l = ceil(log2 f))
   uint32_t magic[kMaxLevels];
   uint8_t shift[kMaxLevels];
-  float cost[kMaxLevels];              // log2(4096 / f), drift estimate only
-  float saving[kMaxHalf];              // log2(f_{m-1} / f_m) for magnitude m >= 1
+  uint32_t cost_fx[kMaxLevels];        // log2(4096 / f) * 2^20, rounded
+  uint32_t saving_fx[kMaxHalf];        // cost_fx[h + m] - cost_fx[h + m - 1], magnitude m >= 1
 };
 
 }  // namespace dq

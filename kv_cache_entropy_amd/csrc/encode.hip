@@ -9,15 +9,21 @@
 //   -> if the stream does not fit, drift the first candidates of a fixed
 //   order one level inward until it does.
 //
-// MI355X mapping: one lane owns one vector end to end.  The rotation runs on
-// the 128 coordinates in VGPRs (fully unrolled butterflies); the symbols stay
-// in VGPRs as 4-bit fields, so a rANS pass is a straight unrolled chain whose
-// only memory access is the per-symbol coder constants in LDS.  Renorm bytes
-// go to a double-buffered LDS scratch, lane-minor, so the last fitting
-// stream survives a later trial pass.  The drift search moves one candidate
-// at a time around an estimate of the number of moves, so a drifted vector
-// usually costs three passes.  Lanes of a wave take consecutive tokens of one
-// kv head, so their containers are adjacent in the pool.
+// Two kernels write the same bytes:
+//  - encode_kernel (large batches, e.g. a prompt): one lane owns one vector
+//    end to end.  The rotation runs on the 128 coordinates in VGPRs (fully
+//    unrolled butterflies); the current symbols live in the lane's column of
+//    an LDS array, so a rANS pass is a straight chain of LDS byte reads and
+//    coder-constant lookups.  Renorm bytes go to a double-buffered LDS
+//    scratch, lane-minor, so the last fitting stream survives a later trial
+//    pass.  The drift search moves one candidate at a time around an
+//    estimate of the number of moves, so a drifted vector usually costs
+//    three passes.  Lanes of a wave take consecutive tokens of one kv head,
+//    so their containers are adjacent in the pool.
+//  - encode_wave_kernel (small batches, e.g. one appended token per
+//    sequence): one wave owns one vector, so the batch fills the chip with
+//    waves instead of lanes and the serial search becomes one parallel
+//    pass: lane l tries the first k0 + l candidates.
 //
 // Arithmetic that decides a symbol is fp32 in a fixed order (butterfly
 // widths 1..64, halving-tree sum of squares); the build uses
@@ -92,90 +98,115 @@ __device__ __forceinline__ uint32_t magnitude(uint32_t s, int h) {
   return s >= (uint32_t)h ? s - (uint32_t)h : (uint32_t)(h - 1) - s;
 }
 
-// One lane's vector during the drift search: the quantised symbols before
-// the current drift pass (4 bits each), the drift flags, and |y_i| (the
-// order key inside a magnitude group).  The current symbols (with the
-// flagged coordinates one level inward) live in the lane's LDS column.
-struct Vec {
-  float ay[kD];
-  uint32_t sym0[16];
-  uint32_t fl[4];
-};
-
-// Among the members of group mask gm: the unflagged one with the smallest
-// (|y|, index) -- the next candidate in drift order -- or, with flagged, the
-// flagged one with the largest (|y|, index) -- the last candidate taken;
-// -1 if there is none.
-__device__ __forceinline__ int extreme_in_group(const Vec &v, const uint32_t (&gm)[4], bool flagged) {
+// The smallest (|y|, index) among the members of gm not yet in fl, -1 if
+// none: the next candidate of a magnitude group in drift order.
+__device__ __forceinline__ int next_in_group(const float (&ay)[kD], const uint32_t (&gm)[4],
+                                             const uint32_t (&fl)[4]) {
   float best = 0.0f;
   int bi = -1;
 #pragma unroll
   for (int i = 0; i < kD; ++i) {
-    const bool member = bit(gm, i) && ((bit(v.fl, i) != 0u) == flagged);
-    const bool better = flagged ? (v.ay[i] >= best) : (v.ay[i] < best);
-    const bool take = member && (bi < 0 || better);
-    best = take ? v.ay[i] : best;
-    bi = take ? i : bi;
+    const bool take = bit(gm, i) && !bit(fl, i) && (bi < 0 || ay[i] < best);
+    best = take ? ay[i] : best;
+    // indices above 64 are not inline constants: made at the point of use
+    // rather than hoisted into 63 registers held for the whole kernel
+    int ci = i;
+    if (i > 64) asm volatile("" : "+v"(ci));
+    bi = take ? ci : bi;
   }
   return bi;
 }
 
-__device__ __forceinline__ void group_mask(const Vec &v, int h, int g, uint32_t (&gm)[4]) {
-  gm[0] = gm[1] = gm[2] = gm[3] = 0u;
-#pragma unroll
-  for (int i = 0; i < kD; ++i) gm[i >> 5] |= (magnitude(nib(v.sym0, i), h) == (uint32_t)g ? 1u : 0u) << (i & 31);
-}
-
-// Moves coordinate i (dynamic) one level inward, or back out (undo), in the
-// LDS symbol column, and toggles its flag.  A moved symbol stays on its side
-// of zero, so the current value alone tells the direction.
-__device__ __forceinline__ void toggle(Vec &v, uint8_t *symL, int i, int h, bool undo, int lane) {
-  uint8_t *p = symL + i * kThreads + lane;
-  const uint32_t s = *p;
-  const bool pos = s >= (uint32_t)h;
-  *p = (uint8_t)((pos != undo) ? s - 1u : s + 1u);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v.fl[j] ^= ((i >> 5) == j) ? (1u << (i & 31)) : 0u;
-}
-
-template <int MAXH>
-__device__ __forceinline__ int cnt_at(const int (&cnt)[MAXH], int m) {
-  int r = 0;
-#pragma unroll
-  for (int q = 1; q < MAXH; ++q) r = (q == m) ? cnt[q] : r;
-  return r;
-}
-
-// One rANS pass over the lane's LDS symbol column (pushed 127 -> 0).
-// Renorm bytes go to the lane's scratch column from the end backwards (rows
-// kScr - B .. kScr - 1 are then in the decoder's reading order); the byte
-// store is unconditional and simply overwritten when no byte is emitted.
-__device__ __forceinline__ int rans_pass(const uint8_t *symL, const uint4 *etab, uint8_t *buf, int lane,
+// One rANS pass over the packed symbols (pushed 127 -> 0).  Renorm bytes go
+// to the lane's scratch column from the end backwards (rows kScr - B ..
+// kScr - 1 are then in the decoder's reading order); the byte store is
+// unconditional and simply overwritten when no byte is emitted.  The coder
+// constants do not depend on the state, so their loads run ahead of it.
+__device__ __forceinline__ int rans_pass(const uint32_t (&sym)[16], const uint4 *etab, uint8_t *buf, int lane,
                                          uint32_t *xfinal) {
   uint32_t x = kLow;
   int pos = kScr - 1;
-#pragma unroll 4
+#pragma unroll
   for (int i = kD - 1; i >= 0; --i) {
-    const uint4 e = etab[symL[i * kThreads + lane]];  // {f << 19, magic, cum, (4096 - f) | shift << 16}
+    const uint4 e = etab[nib(sym, i)];  // {f << 19, magic, cum, (4096 - f) | shift << 16}
     buf[pos * kThreads + lane] = (uint8_t)x;
     const bool emit = x >= e.x;
     x = emit ? x >> 8 : x;
     pos -= emit ? 1 : 0;
     const uint32_t q = __umulhi(x, e.y) >> (e.w >> 16);
     x = x + e.z + __umul24(q, e.w & 0xFFFFu);
+    if ((i & 7) == 0) __builtin_amdgcn_sched_barrier(0);  // loads run at most 8 steps ahead
   }
   *xfinal = x;
   return kScr - 1 - pos;
 }
 
-enum : int { kPhInit, kPhFirst, kPhDown, kPhUp, kPhDone };
-enum : int { kActNone, kActPrefix, kActAdd, kActRemove, kActCommit };
+
+// Makes the packed words opaque to the compiler, so nibbles extracted in one
+// region are not kept alive for reuse in the next one.
+template <int N>
+__device__ __forceinline__ void opaque(uint32_t (&w)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) asm volatile("" : "+v"(w[j]));
+}
+
+// y = H * D * x for one bf16 vector: signs from the SplitMix64 words (made
+// opaque so the 128 sign masks are not hoisted out of a loop), then fp32
+// butterflies of width 1, 2, ..., 64.  With S != nullptr also ||x||^2 by the
+// halving tree (i + 64, then i + 32, ..., i + 1).
+__device__ __forceinline__ void rotate(const uint4 *src, uint64_t s0, uint64_t s1, float (&y)[kD], float *S) {
+  uint32_t xw[64];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint4 w = src[j];
+    xw[4 * j + 0] = w.x;
+    xw[4 * j + 1] = w.y;
+    xw[4 * j + 2] = w.z;
+    xw[4 * j + 3] = w.w;
+  }
+  opaque(xw);  // a second rotation of the same vector is recomputed, not reused
+  // bf16 element i as fp32 bits
+#define DQ_ELEM(i) ((xw[(i) >> 1] << (16 * (1 - ((i) & 1)))) & 0xFFFF0000u)
+  if (S) {
+    float sq[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const float a0 = __uint_as_float(DQ_ELEM(i));
+      const float a1 = __uint_as_float(DQ_ELEM(i + 64));
+      sq[i] = a0 * a0 + a1 * a1;
+    }
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) sq[i] = sq[i] + sq[i + w];
+    *S = sq[0];
+  }
+  uint32_t sgn[4] = {(uint32_t)s0, (uint32_t)(s0 >> 32), (uint32_t)s1, (uint32_t)(s1 >> 32)};
+  opaque(sgn);
+#pragma unroll
+  for (int i = 0; i < kD; ++i) {
+    const uint32_t flip = ((sgn[i >> 5] >> (i & 31)) & 1u) << 31;
+    y[i] = __uint_as_float(DQ_ELEM(i) ^ flip);
+  }
+#undef DQ_ELEM
+#pragma unroll
+  for (int w = 1; w < kD; w <<= 1)
+#pragma unroll
+    for (int i = 0; i < kD; ++i)
+      if ((i & w) == 0) {
+        const float p = y[i], q = y[i + w];
+        y[i] = p + q;
+        y[i + w] = p - q;
+      }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ uint32_t inward(uint32_t s, int h) { return s >= (uint32_t)h ? s - 1u : s + 1u; }
 
 template <int MAXH>
-__global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a, Tables t) {
+__global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Tables t) {
   __shared__ uint4 etab[kMaxLevels];
-  __shared__ uint8_t scr[2][kScr * kThreads];  // double-buffered renorm bytes
-  __shared__ uint8_t symcol[kD * kThreads];     // current symbols, lane-minor
+  __shared__ uint8_t scr[kScr * kThreads];  // renorm bytes, lane-minor
   __shared__ uint32_t bstat[6 + kMaxC + 1];
 
   const int lane = threadIdx.x;
@@ -196,267 +227,203 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a, Tables t
     const int64_t slot = a.slots[tok];
     const bool in_pool = slot >= 0 && slot < a.num_slots;  // out-of-range slots write nothing
     const uint4 *src = reinterpret_cast<const uint4 *>(a.x + tok * a.stride_t + (int64_t)g * a.stride_h);
-    uint32_t xw[64];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint4 w = src[j];
-      xw[4 * j + 0] = w.x;
-      xw[4 * j + 1] = w.y;
-      xw[4 * j + 2] = w.z;
-      xw[4 * j + 3] = w.w;
-    }
-    // bf16 element i as fp32 bits
-#define DQ_ELEM(i) ((xw[(i) >> 1] << (16 * (1 - ((i) & 1)))) & 0xFFFF0000u)
-    // ||x||^2 by the halving tree: i + 64, then i + 32, ..., i + 1
-    float sq[64];
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const float a0 = __uint_as_float(DQ_ELEM(i));
-      const float a1 = __uint_as_float(DQ_ELEM(i + 64));
-      sq[i] = a0 * a0 + a1 * a1;
-    }
-#pragma unroll
-    for (int w = 32; w >= 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w; ++i) sq[i] = sq[i] + sq[i + w];
-    const float S = sq[0];
-
-    // y = H * D * x: signs from SplitMix64 words 2g, 2g + 1, then fp32
-    // butterflies of width 1, 2, ..., 64
     const uint64_t s0 = splitmix64(t.seed, 2ull * (uint64_t)g);
     const uint64_t s1 = splitmix64(t.seed, 2ull * (uint64_t)g + 1ull);
-    float y[kD];
-#pragma unroll
-    for (int i = 0; i < kD; ++i) {
-      const uint64_t sw = i < 64 ? s0 : s1;
-      const uint32_t flip = (uint32_t)((sw >> (i & 63)) & 1ull) << 31;
-      y[i] = __uint_as_float(DQ_ELEM(i) ^ flip);
-    }
-#undef DQ_ELEM
-#pragma unroll
-    for (int w = 1; w < kD; w <<= 1)
-#pragma unroll
-      for (int i = 0; i < kD; ++i)
-        if ((i & w) == 0) {
-          const float p = y[i], q = y[i + w];
-          y[i] = p + q;
-          y[i + w] = p - q;
-        }
 
-    const uint32_t nh = norm_half(S);
-    const float nf = half_to_float(nh);
-    const bool zero = nh == 0u;
-    const bool bad = (nh & 0x7C00u) == 0x7C00u;
-    const bool degenerate = zero || bad;
-
-    // quantise: m_i = #{k in 1..h-1 : |y_i| >= k * step * n_h}; each
-    // threshold is an integer times an fp16 value times 2^-6, exact in fp32
-    Vec v;
-    float thr[MAXH];
-#pragma unroll
-    for (int k = 1; k < MAXH; ++k)
-      thr[k] = (k < h && !degenerate) ? (float)(k * t.step64) * nf * 0.015625f : __builtin_inff();
-    int ge[MAXH];
-#pragma unroll
-    for (int k = 0; k < MAXH; ++k) ge[k] = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v.sym0[j] = 0u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v.fl[j] = 0u;
-#pragma unroll
-    for (int i = 0; i < kD; ++i) {
-      const float ay = degenerate ? 0.0f : __builtin_fabsf(y[i]);
-      v.ay[i] = ay;
-      uint32_t m = 0;
-#pragma unroll
-      for (int k = 1; k < MAXH; ++k) {
-        const uint32_t c = ay >= thr[k] ? 1u : 0u;
-        m += c;
-        ge[k] += (int)c;
-      }
-      const uint32_t sy = (degenerate || y[i] >= 0.0f) ? (uint32_t)h + m : (uint32_t)(h - 1) - m;
-      v.sym0[i >> 3] |= sy << (4 * (i & 7));
-    }
-    // current symbols into the lane's LDS column
-    uint8_t *symL = symcol;
-#pragma unroll
-    for (int i = 0; i < kD; ++i) symL[i * kThreads + lane] = (uint8_t)nib(v.sym0, i);
-
-    // ---- drift search: a per-lane state machine around one rANS pass.
-    // Passes alternate between the two scratch buffers, so the last fitting
-    // stream is still there after a trial pass that does not fit.
-    int buf = 1, okbuf = -1, okB = 0;
+    // ---- drift.  I(k), the ideal code length of the symbols after the
+    // first k moves (sum of log2(4096 / f), fixed point), decides whether
+    // prefix k fits except inside a band narrower than one move's saving
+    // (kEpsHiFx, kEpsLoFx), so at most one k per round is undecided.  The
+    // plan and the choice of the moved symbols come first; then one rANS
+    // pass, or two when the undecided prefix is tried first.  A round in
+    // which even every move is too long commits them and plans again (rare:
+    // the rotated coordinates are recomputed then, so they are not kept
+    // through the passes).
+    const uint32_t lim = (uint32_t)(8 * (C - 3)) << kCostFrac;
+    const uint32_t sure_lo = lim - kEpsHiFx;  // I(k) below: fits
+    const uint32_t sure_hi = lim + kEpsLoFx;  // I(k) at or above: does not fit
+    uint32_t sym0[16];                        // symbols at the start of the round, 4 bits each
+    int cnt[MAXH];                            // candidates per magnitude in the round
+    uint32_t I = 0u;
+    uint32_t nh = 0u;
+    bool zero = false, bad = false;
+    int moves = 0, passes = 0, okB = -1;
     uint32_t okx = 0;
-    int moves = 0, passes = 0, k = 0, total = 0, gb = 0, taken = 0;
-    int cnt[MAXH];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sym0[j] = 0u;
 #pragma unroll
     for (int m = 0; m < MAXH; ++m) cnt[m] = 0;
-    uint32_t gm[4] = {0u, 0u, 0u, 0u};
-    bool first_round = true;
-    int phase = kPhInit;
-    for (int guard = 0; phase != kPhDone && guard < 4 * kD; ++guard) {
-      uint32_t xf;
-      buf ^= 1;
-      const int B = rans_pass(symL, etab, scr[buf], lane, &xf);
-      const bool fits = 4 + B <= C;
-      if (fits) {
-        okbuf = buf;
-        okB = B;
-        okx = xf;
-      }
-      int act = kActNone;
-      if (phase == kPhInit) {
-        if (fits) {
-          phase = kPhDone;
-        } else {
-          // group sizes and the estimated number of moves: shed the excess
-          // bits greedily in drift order at each group's per-move saving
-          float sigma_c = 0.0f;
-          total = 0;
-          if (first_round) {
-#pragma unroll
-            for (int m = 0; m < MAXH; ++m) {
-              const int above = (m + 1 < MAXH) ? ge[m + 1] : 0;
-              const int c = (m == 0 ? kD : ge[m]) - above;
-              if (m >= 1) cnt[m] = c;
-              if (m < h) sigma_c += (float)c * t.cost[h + m];
-            }
-          } else {
-#pragma unroll
-            for (int m = 1; m < MAXH; ++m) cnt[m] = 0;
-#pragma unroll
-            for (int i = 0; i < kD; ++i) {
-              const uint32_t mg = magnitude(nib(v.sym0, i), h);
-#pragma unroll
-              for (int m = 1; m < MAXH; ++m) cnt[m] += mg == (uint32_t)m ? 1 : 0;
-            }
-            int c0 = kD;
-#pragma unroll
-            for (int m = 1; m < MAXH; ++m) {
-              c0 -= cnt[m];
-              if (m < h) sigma_c += (float)cnt[m] * t.cost[h + m];
-            }
-            sigma_c += (float)c0 * t.cost[h];
-          }
-#pragma unroll
-          for (int m = 1; m < MAXH; ++m) total += cnt[m];
-          float need = sigma_c - 8.0f * (float)(C - 4) - 4.0f;
-          int khat = 0;
-#pragma unroll
-          for (int m = MAXH - 1; m >= 1; --m) {
-            if (m < h && need > 0.0f) {
-              const float sv = t.saving[m];
-              int take = (int)ceilf(need / sv);
-              take = take < cnt[m] ? take : cnt[m];
-              khat += take;
-              need -= (float)take * sv;
-            }
-          }
-          khat = khat < 1 ? 1 : (khat > total ? total : khat);
-          k = khat > 1 ? khat - 1 : 1;
-          act = kActPrefix;
-          phase = kPhFirst;
-        }
-      } else if (phase == kPhFirst || phase == kPhDown) {
-        if (fits) {
-          if (k == 1) {
-            phase = kPhDone;
-          } else {
-            act = kActRemove;  // try one candidate fewer
-            phase = kPhDown;
-          }
-        } else if (phase == kPhDown) {
-          ++k;  // prefix k - 1 failed: the previous pass (prefix k) is the answer
-          phase = kPhDone;
-        } else {
-          act = kActAdd;
-          phase = kPhUp;
-        }
-      } else {  // kPhUp
-        if (fits) phase = kPhDone;
-        else act = kActAdd;
-      }
-      if (act == kActAdd && k >= total) act = kActCommit;
 
-      if (act == kActPrefix) {
-        // first k candidates: whole groups above the boundary, then the
-        // smallest members of the boundary group
-        int kk = k, rest = 0;
+    for (int round = 0; okB < 0 && round <= MAXH; ++round) {
+      if (round == 0) {
+        float y[kD], S;
+        rotate(src, s0, s1, y, &S);
+        nh = norm_half(S);
+        zero = nh == 0u;
+        bad = (nh & 0x7C00u) == 0x7C00u;
+        const bool degenerate = zero || bad;
+        // quantise: m_i = #{k in 1..h-1 : |y_i| >= k * step * n_h}; each
+        // threshold is an integer times an fp16 value times 2^-6, exact in fp32
+        const float nf = half_to_float(nh);
+        float thr[MAXH];
+#pragma unroll
+        for (int k = 1; k < MAXH; ++k)
+          thr[k] = (k < h && !degenerate) ? (float)(k * t.step64) * nf * 0.015625f : __builtin_inff();
+        // magnitude histogram: 8-bit counters, m = 0..3 in hl, 4..7 in hh
+        uint32_t hl = 0u, hh = 0u;
+#pragma unroll
+        for (int i = 0; i < kD; ++i) {
+          const float ay = degenerate ? 0.0f : __builtin_fabsf(y[i]);
+          uint32_t m = 0;
+#pragma unroll
+          for (int k = 1; k < MAXH; ++k) m += ay >= thr[k] ? 1u : 0u;
+          const uint32_t inc = 1u << (8 * (m & 3u));
+          hl += m < 4u ? inc : 0u;
+          hh += m < 4u ? 0u : inc;
+          const uint32_t sy = (degenerate || y[i] >= 0.0f) ? (uint32_t)h + m : (uint32_t)(h - 1) - m;
+          sym0[i >> 3] |= sy << (4 * (i & 7));
+          if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // one packed word at a time
+        }
+#pragma unroll
+        for (int m = 0; m < MAXH; ++m) {
+          const int c = (int)(((m < 4 ? hl : hh) >> (8 * (m & 3))) & 0xFFu);
+          if (m >= 1) cnt[m] = c;
+          if (m < h) I += (uint32_t)c * t.cost_fx[h + m];
+        }
+      }
+
+      opaque(sym0);
+      // plan: the smallest k with I(k) < sure_lo takes whole magnitude
+      // groups, outermost first, each move saving saving_fx[m]
+      int ks = 0, total = 0;
+      uint32_t Ik = I, Iprev = 0xFFFFFFFFu;  // I(ks), I(ks - 1)
+#pragma unroll
+      for (int m = MAXH - 1; m >= 1; --m) {
+        if (m < h) {
+          total += cnt[m];
+          if (Ik >= sure_lo && cnt[m] > 0) {
+            const uint32_t sv = t.saving_fx[m];
+            const uint32_t need = (Ik - sure_lo) / sv + 1u;
+            const uint32_t take = need < (uint32_t)cnt[m] ? need : (uint32_t)cnt[m];
+            Iprev = Ik - (take - 1u) * sv;
+            Ik -= take * sv;
+            ks += (int)take;
+          }
+        }
+      }
+      const bool sure = Ik < sure_lo;
+      const bool undecided = sure ? (ks >= 1 && Iprev < sure_hi) : (Ik < sure_hi);
+
+      if (sure || undecided) {
+        // the first k candidates: whole groups above the boundary group gb,
+        // then its `rest` smallest members; `nxt` is candidate k + 1 when
+        // the undecided prefix k is tried first
+        const int k = undecided ? (sure ? ks - 1 : total) : ks;
+        int kk = k, rest = 0, gb = h - 1;
         bool full = false;
-        gb = h - 1;
 #pragma unroll
         for (int m = MAXH - 1; m >= 1; --m) {
           if (m < h && kk > 0) {
             gb = m;
-            if (kk >= cnt[m]) {
-              kk -= cnt[m];
-              full = true;
-              rest = cnt[m];
-            } else {
-              full = false;
-              rest = kk;
-              kk = 0;
-            }
+            full = kk >= cnt[m];
+            rest = full ? cnt[m] : kk;
+            kk -= rest;
           }
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v.fl[j] = 0u;
+        uint32_t fl[4] = {0u, 0u, 0u, 0u}, gm[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < kD; ++i) {
-          const uint32_t s0 = nib(v.sym0, i);
-          const uint32_t mg = magnitude(s0, h);
-          const bool f = mg > (uint32_t)gb || (full && mg == (uint32_t)gb);
-          v.fl[i >> 5] |= (f ? 1u : 0u) << (i & 31);
-          symL[i * kThreads + lane] = (uint8_t)(f ? (s0 >= (uint32_t)h ? s0 - 1u : s0 + 1u) : s0);
+          const uint32_t mg = magnitude(nib(sym0, i), h);
+          fl[i >> 5] |= (mg > (uint32_t)gb || (full && mg == (uint32_t)gb) ? 1u : 0u) << (i & 31);
+          gm[i >> 5] |= (mg == (uint32_t)gb ? 1u : 0u) << (i & 31);
         }
-        group_mask(v, h, gb, gm);
-        taken = rest;
-        if (!full)
-          for (int j = 0; j < rest; ++j) toggle(v, symL, extreme_in_group(v, gm, false), h, false, lane);
-      } else if (act == kActAdd || act == kActRemove) {
-        const bool add = act == kActAdd;
-        // move the boundary when the current boundary group has nothing left
-        if (add ? (taken == cnt_at<MAXH>(cnt, gb)) : (taken == 0)) {
-          int m = add ? gb - 1 : gb + 1;
-          while (add ? (m > 1 && cnt_at<MAXH>(cnt, m) == 0) : (m < h - 1 && cnt_at<MAXH>(cnt, m) == 0))
-            m += add ? -1 : 1;
-          gb = m;
-          taken = add ? 0 : cnt_at<MAXH>(cnt, gb);
-          group_mask(v, h, gb, gm);
+        int nxt = -1;
+        const bool want_next = undecided && sure;
+        if ((!full && rest > 0) || want_next) {
+          // the order inside a group needs |y|: rotate again rather than
+          // keep 128 values alive since quantisation
+          opaque(sym0);
+          float ay[kD];
+          rotate(src, s0, s1, ay, nullptr);
+#pragma unroll
+          for (int i = 0; i < kD; ++i) ay[i] = __builtin_fabsf(ay[i]);
+          if (!full)
+            for (int j = 0; j < rest; ++j) {
+              const int i = next_in_group(ay, gm, fl);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) fl[q] |= ((i >> 5) == q) ? (1u << (i & 31)) : 0u;
+            }
+          if (want_next) {
+            if (full || rest == cnt[gb]) {
+              // the boundary group is used up: the next lower non-empty group
+              int m = k == 0 ? h - 1 : gb - 1;
+              while (m > 1 && cnt[m] == 0) --m;
+#pragma unroll
+              for (int i = 0; i < kD; ++i) {
+                const uint32_t mg = magnitude(nib(sym0, i), h);
+                gm[i >> 5] = (gm[i >> 5] & ~(1u << (i & 31))) | ((mg == (uint32_t)m ? 1u : 0u) << (i & 31));
+              }
+            }
+            nxt = next_in_group(ay, gm, fl);
+          }
         }
-        toggle(v, symL, extreme_in_group(v, gm, !add), h, !add, lane);
-        taken += add ? 1 : -1;
-        k += add ? 1 : -1;
-      } else if (act == kActCommit) {
-        // every candidate moved and the stream still does not fit: keep the
-        // moves and search again on the new symbols (the all-innermost
-        // vector always fits)
+        opaque(sym0);
+        opaque(fl);
+        // symbols of prefix k
+        uint32_t sym[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sym[j] = 0u;
+#pragma unroll
+        for (int i = 0; i < kD; ++i) {
+          const uint32_t s = nib(sym0, i);
+          sym[i >> 3] |= (bit(fl, i) ? inward(s, h) : s) << (4 * (i & 7));
+        }
+        for (int attempt = 0; attempt < 2; ++attempt) {
+          uint32_t xf;
+          const int B = rans_pass(sym, etab, scr, lane, &xf);
+          if (4 + B <= C) {
+            okB = B;
+            okx = xf;
+            moves += k + attempt;
+            break;
+          }
+          if (nxt < 0) break;
+          // prefix k did not fit: prefix k + 1 does
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int sh = 4 * (nxt & 7);
+            const uint32_t s = (sym[j] >> sh) & 15u;
+            sym[j] = ((nxt >> 3) == j) ? ((sym[j] & ~(15u << sh)) | (inward(s, h) << sh)) : sym[j];
+          }
+          nxt = -1;
+        }
+      }
+      if (okB < 0) {
+        // every candidate of the round moves one level inward; the plan is
+        // made again on the new symbols (the all-innermost vector fits)
         moves += total;
         ++passes;
+        opaque(sym0);
 #pragma unroll
         for (int i = 0; i < kD; ++i) {
-          const uint32_t s0 = nib(v.sym0, i);
-          const uint32_t sn = bit(v.fl, i) ? (s0 >= (uint32_t)h ? s0 - 1u : s0 + 1u) : s0;
-          v.sym0[i >> 3] = (v.sym0[i >> 3] & ~(15u << (4 * (i & 7)))) | (sn << (4 * (i & 7)));
+          const uint32_t s = nib(sym0, i);
+          const uint32_t sn = magnitude(s, h) >= 1u ? inward(s, h) : s;
+          sym0[i >> 3] = (sym0[i >> 3] & ~(15u << (4 * (i & 7)))) | (sn << (4 * (i & 7)));
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v.fl[j] = 0u;
-        k = 0;
-        first_round = false;
-        phase = kPhInit;
+        for (int m = 1; m < MAXH; ++m) cnt[m] = (m + 1 < MAXH) ? cnt[m + 1] : 0;
+        I = Ik;
       }
     }
-    if (phase == kPhDone) moves += k;
 
     // container: [final state, little endian][renorm bytes][zero pad]
-    if (in_pool && okbuf >= 0) {
+    if (in_pool && okB >= 0) {
       uint8_t *dst = a.cont + ((int64_t)g * a.num_slots + slot) * C;
       dst[0] = (uint8_t)okx;
       dst[1] = (uint8_t)(okx >> 8);
       dst[2] = (uint8_t)(okx >> 16);
       dst[3] = (uint8_t)(okx >> 24);
-      const uint8_t *sb = scr[okbuf];
-      for (int j = 0; j < C - 4; ++j) dst[4 + j] = j < okB ? sb[(kScr - okB + j) * kThreads + lane] : (uint8_t)0;
+      for (int j = 0; j < C - 4; ++j) dst[4 + j] = j < okB ? scr[(kScr - okB + j) * kThreads + lane] : (uint8_t)0;
       a.norm[(int64_t)g * a.num_slots + slot] = (uint16_t)nh;
     }
 
@@ -469,7 +436,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(EncodeArgs a, Tables t
       if (passes) atomicAdd(&bstat[3], (uint32_t)passes);
       if (bad) atomicAdd(&bstat[4], 1u);
       if (zero) atomicAdd(&bstat[5], 1u);
-      atomicAdd(&bstat[6 + 4 + okB], 1u);
+      atomicAdd(&bstat[6 + 4 + (okB < 0 ? 0 : okB)], 1u);
     }
   }
   if (a.stats) {
