@@ -190,6 +190,38 @@ def test_rans_roundtrip_length_bound_and_bigint(oracle_lib, levels, C):
         assert back == [int(v) for v in sym] and x0 == (1 << 23)
 
 
+@pytest.mark.parametrize("levels,C", DEFAULTS + [(16, 60), (2, 20)])
+def test_rans_length_identity_band(oracle_lib, levels, C):
+    """Per-step accounting of a byte rANS stream: each symbol changes
+    log2(x) by log2(4096/f) + d with |d| < log2(1 + 2^-11) (the state before
+    a step is at least f * 2^11), each emitted byte costs 8 + e bits with
+    0 <= e < log2(1 + 255 * 2^-23), one byte per step at most.  So over 128
+    symbols 8 B + log2(x_final) - 23 - I lies in (-0.095760, 0.090147), and
+    B = floor((I + eps) / 8) for some eps in that interval.  Extreme symbol
+    mixes (all outermost, all innermost, alternating) push the bound."""
+    O = oracle_lib
+    step = O.DEFAULT_STEP64.get((levels, C), 25 if levels == 16 else 64)
+    t = O.Codec(levels, C, seed=0, hkv=1, step64=step).tables()
+    f, cum = t["freq"], t["cum"]
+    rng = np.random.default_rng(levels * 7 + C)
+    sets = _random_symbol_sets(levels, rng)
+    h = levels // 2
+    sets += [np.full(D, s, np.uint8) for s in range(levels)]
+    sets += [np.array([0, levels - 1] * (D // 2), np.uint8), np.array([h, h - 1] * (D // 2), np.uint8)]
+    d_max = D * math.log2(1 + 2.0 ** -11)
+    e_max = D * math.log2(1 + 255 * 2.0 ** -23)
+    lo, hi = -(d_max + e_max), d_max
+    assert abs(lo + 0.095760) < 1e-6 and abs(hi - 0.090147) < 1e-6
+    for sym in sets:
+        stream = O.rans_encode(sym, f, cum)
+        B = len(stream) - 4
+        x_final = int.from_bytes(bytes(stream[:4]), "little")
+        I = float(sum(math.log2(4096.0 / f[s]) for s in sym))
+        eps = 8 * B + math.log2(x_final) - 23 - I
+        assert lo < eps < hi, (sym[:8], eps)
+        assert B == math.floor((I + eps) / 8)
+
+
 def test_rans_decode_reads_past_end_as_zero(oracle_lib):
     O = oracle_lib
     t = O.Codec(6, 34, seed=0, hkv=1).tables()
