@@ -304,3 +304,96 @@ def test_qwen3_shape_full_encode_and_sampled_attention(oracle_lib):
                       pools["V"][0].cpu().numpy(), _np_bits(pools["V"][1]),
                       ss.cpu().numpy()[rows], sl.cpu().numpy()[rows])
     _assert_close(out.cpu().numpy()[rows], ref, "qwen3 attention rows 0, 9")
+
+
+def _workload_case(O, name, cap_extra):
+    """Every context token of a workload encoded into pools with `cap_extra`
+    free slots after each sequence (as the bench lays them out); every K and
+    V container, norm and stat bit-exact against the oracle."""
+    w = synth.workloads()[name]
+    hkv = w.hkv
+    ctx = np.array(w.ctx, np.int64)
+    cap = ctx + cap_extra
+    starts = np.concatenate([[0], np.cumsum(cap)[:-1]]).astype(np.int64)
+    S = int(cap.sum())
+    ck, ock = _codecs(O, w.levels_k, w.container_k, seed=w.seed, hkv=hkv)
+    cv, ocv = _codecs(O, w.levels_v, w.container_v, seed=w.seed + 1, hkv=hkv)
+    slots = torch.from_numpy(np.concatenate([np.arange(s, s + L) for s, L in zip(starts, ctx)])).to(DEV)
+    pools = {}
+    for tag, gc, oc, seed in (("K", ck, ock, w.seed + 10), ("V", cv, ocv, w.seed + 11)):
+        _say(f"{name}: encode {tag} ({slots.numel()} tokens x {hkv} heads)")
+        x = synth.kv_tensor(w.kind, slots.numel(), hkv, seed=seed, device=DEV)
+        cont, norm, st, ocont, onorm, ost = _encode_both(O, gc, oc, x, slots, S)
+        _assert_encode_equal(cont, norm, st, ocont, onorm, ost, f"{name} {tag}")
+        s = dq.stats_dict(st)
+        _say(f"{name} {tag}: drift rate {s['drifted_symbols'] / (128 * s['vectors']):.4%}, "
+             f"multilevel {s['multilevel_events']}")
+        pools[tag] = (cont, norm)
+        del x
+    return dict(w=w, ck=ck, cv=cv, ock=ock, ocv=ocv, pools=pools, starts=starts, ctx=ctx, S=S)
+
+
+def _append_and_check(O, c, n_new, seed):
+    """Encodes n_new tokens after each sequence's context (the append of a
+    decode step or a prefill chunk) and checks the new containers."""
+    w = c["w"]
+    slots_np = np.concatenate([np.arange(s + L, s + L + n_new) for s, L in zip(c["starts"], c["ctx"])])
+    slots = torch.from_numpy(slots_np).to(DEV)
+    for tag, gc, oc, off in (("K", c["ck"], c["ock"], 0), ("V", c["cv"], c["ocv"], 1)):
+        x = synth.kv_tensor(w.kind, slots.numel(), w.hkv, seed=seed + off, device=DEV)
+        cont, norm = c["pools"][tag]
+        st = dq.new_stats(DEV)
+        dq.encode(gc, x, slots, cont, norm, st)
+        torch.cuda.synchronize()
+        ocont, onorm, ost = O.encode(oc, _np_bits(x), slots_np, num_slots=cont.shape[1])
+        got = cont[:, slots].cpu().numpy()
+        assert (got == ocont[:, slots_np]).all(), f"{w.name} appended {tag} containers differ"
+        assert (_np_bits(norm[:, slots]) == onorm[:, slots_np]).all()
+        assert dq.stats_dict(st) == O_stats(ost)
+    return torch.from_numpy(c["ctx"] + n_new)
+
+
+def _sampled_attention(O, c, lens, max_len, rows, label):
+    w = c["w"]
+    q = synth.q_tensor(w.batch, w.hq, seed=w.seed + 12, device=DEV)
+    ss = torch.from_numpy(c["starts"]).to(DEV)
+    sl = lens.to(torch.int32).to(DEV)
+    kc, kn = c["pools"]["K"]
+    vc, vn = c["pools"]["V"]
+    out = dq.attn_decode(c["ck"], c["cv"], q, kc, kn, vc, vn, ss, sl, int(max_len))
+    torch.cuda.synchronize()
+    ref = O.attention(c["ock"], c["ocv"], _np_bits(q)[rows], kc.cpu().numpy(), _np_bits(kn),
+                      vc.cpu().numpy(), _np_bits(vn), c["starts"][rows], lens.numpy().astype(np.int32)[rows])
+    _assert_close(out.cpu().numpy()[rows], ref, f"{label} attention rows {rows}")
+
+
+def test_llama31_b128_8k_bench_configuration(oracle_lib):
+    """Batch 128 x 8192, 32 q / 8 kv heads, 34-byte containers, laid out as
+    the bench does (19 free slots per sequence): the full prompt encode
+    bit-exact, one decode step's append bit-exact, and attention at the
+    bench's max_len (context + 19) on sampled sequences."""
+    O = oracle_lib
+    c = _workload_case(O, "llama31_8b_b128_8k", cap_extra=19)
+    lens = _append_and_check(O, c, 1, seed=c["w"].seed + 20)
+    _sampled_attention(O, c, lens, int(c["ctx"].max()) + 19, [0, 77, 127], "llama31 b128")
+
+
+def test_longctx_b4_64k_c29(oracle_lib):
+    """Batch 4 x 65536, 29-byte containers (1.94 bits/value), Student-t (5)
+    K/V: full encode bit-exact, attention on two sequences."""
+    O = oracle_lib
+    c = _workload_case(O, "longctx_b4_64k_c29", cap_extra=0)
+    _sampled_attention(O, c, torch.from_numpy(c["ctx"]), int(c["ctx"].max()), [1, 3], "longctx c29")
+
+
+def test_ragged_32seq_4k_128k(oracle_lib):
+    """32 sequences with log-uniform contexts in [4096, 131072]: full encode
+    bit-exact, the 8192-token chunk appended to every sequence bit-exact,
+    attention over the grown lengths on the shortest, a middle and the
+    longest sequence."""
+    O = oracle_lib
+    c = _workload_case(O, "ragged_32seq_4k_128k", cap_extra=8192)
+    lens = _append_and_check(O, c, 8192, seed=c["w"].seed + 30)
+    order = np.argsort(c["ctx"])
+    rows = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    _sampled_attention(O, c, lens, int(lens.max()), rows, "ragged")
