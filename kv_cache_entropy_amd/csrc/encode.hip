@@ -99,22 +99,31 @@ __device__ __forceinline__ uint32_t magnitude(uint32_t s, int h) {
 }
 
 // The smallest (|y|, index) among the members of gm not yet in fl, -1 if
-// none: the next candidate of a magnitude group in drift order.
+// none: the next candidate of a magnitude group in drift order.  Every |y|
+// is finite, so starting from +inf needs no "found yet" test, and the strict
+// compare keeps the lowest index among equal values.  The two halves are
+// scanned separately so every index is an inline constant (0..63); on a tie
+// the lower half wins.
 __device__ __forceinline__ int next_in_group(const float (&ay)[kD], const uint32_t (&gm)[4],
                                              const uint32_t (&fl)[4]) {
-  float best = 0.0f;
-  int bi = -1;
+  uint32_t mw[4];
 #pragma unroll
-  for (int i = 0; i < kD; ++i) {
-    const bool take = bit(gm, i) && !bit(fl, i) && (bi < 0 || ay[i] < best);
-    best = take ? ay[i] : best;
-    // indices above 64 are not inline constants: made at the point of use
-    // rather than hoisted into 63 registers held for the whole kernel
-    int ci = i;
-    if (i > 64) asm volatile("" : "+v"(ci));
-    bi = take ? ci : bi;
+  for (int q = 0; q < 4; ++q) mw[q] = gm[q] & ~fl[q];
+  float best[2];
+  int bi[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    best[half] = __builtin_inff();
+    bi[half] = -1;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const int i = 64 * half + j;
+      const bool take = ((mw[i >> 5] >> (i & 31)) & 1u) && ay[i] < best[half];
+      best[half] = take ? ay[i] : best[half];
+      bi[half] = take ? j : bi[half];
+    }
   }
-  return bi;
+  return best[1] < best[0] ? 64 + bi[1] : bi[0];
 }
 
 // One rANS pass over the packed symbols (pushed 127 -> 0).  Renorm bytes go
