@@ -94,6 +94,9 @@ def lib():
         L.dqo_attention.argtypes = [CodecArgs, CodecArgs, c_int, u16p, c_int, c_int,
                                     u8p, u16p, u8p, u16p, c_i64, i64p, i32p,
                                     ctypes.c_double, f64p, c_int]
+        L.dqo_attention_paged.argtypes = [CodecArgs, CodecArgs, c_int, u16p, c_int, c_int,
+                                          u8p, u16p, u8p, u16p, c_i64, i32p, c_int, i32p,
+                                          ctypes.c_double, f64p, c_int]
         assert L.dqo_detail_size() == ctypes.sizeof(VecDetail)
         _lib = L
     return _lib
@@ -314,6 +317,34 @@ def attention(ck: Codec, cv: Codec, q, k_cont, k_norm, v_cont, v_norm, seq_start
                              float(sm_scale), _p(out, ctypes.c_double), nthreads)
     if st != 0:
         raise ValueError(f"oracle attention failed: {st}")
+    return out
+
+
+def attention_paged(ck: Codec, cv: Codec, q, k_cont, k_norm, v_cont, v_norm, pages,
+                    seq_len, sm_scale: float | None = None, nthreads: int = 0):
+    """fp64 decode attention over a paged pool: pages int32 [B, max_pages],
+    token t of sequence b in slot pages[b, t // 64] * 64 + t % 64."""
+    qb = np.ascontiguousarray(_u16(q))
+    B, Hq, d = qb.shape
+    assert d == D
+    kc = np.ascontiguousarray(k_cont, np.uint8)
+    vc = np.ascontiguousarray(v_cont, np.uint8)
+    kn = np.ascontiguousarray(_u16(k_norm))
+    vn = np.ascontiguousarray(_u16(v_norm))
+    H, S, _ = kc.shape
+    pt = np.ascontiguousarray(pages, np.int32)
+    assert pt.ndim == 2 and pt.shape[0] == B
+    sl = np.ascontiguousarray(seq_len, np.int32)
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    out = np.zeros((B, Hq, D), np.float64)
+    st = lib().dqo_attention_paged(ck.args(), cv.args(), H, _p(qb, ctypes.c_uint16), B, Hq,
+                                   _p(kc, ctypes.c_uint8), _p(kn, ctypes.c_uint16),
+                                   _p(vc, ctypes.c_uint8), _p(vn, ctypes.c_uint16), S,
+                                   _p(pt, ctypes.c_int32), pt.shape[1], _p(sl, ctypes.c_int32),
+                                   float(sm_scale), _p(out, ctypes.c_double), nthreads)
+    if st != 0:
+        raise ValueError(f"oracle paged attention failed: {st}")
     return out
 
 

@@ -551,23 +551,47 @@ typedef struct {
   uint64_t seed;
 } dqo_codec_args;
 
-int dqo_attention(dqo_codec_args ka, dqo_codec_args va, int hkv,
-                  const uint16_t *q /* bf16 [B][Hq][128] */, int B, int Hq,
-                  const uint8_t *kc, const uint16_t *kn, const uint8_t *vc,
-                  const uint16_t *vn, int64_t num_slots,
-                  const int64_t *seq_start, const int32_t *seq_len,
-                  double sm_scale, double *out /* [B][Hq][128] */,
-                  int nthreads) {
+/* Slot of token t of sequence b: contiguous (seq_start) or paged (page
+ * table of 64-token pages, a block table; every container stays at
+ * cont + (g * S + slot) * C, the fixed stride the pages rely on). */
+typedef struct {
+  const int64_t *seq_start; /* contiguous layout, or NULL */
+  const int32_t *pages;     /* [B][max_pages] page ids, or NULL */
+  int max_pages;
+} slot_map;
+
+#define DQO_PAGE 64
+
+static int64_t slot_of(const slot_map *m, int b, int64_t t) {
+  if (m->pages)
+    return (int64_t)m->pages[(int64_t)b * m->max_pages + t / DQO_PAGE] * DQO_PAGE + t % DQO_PAGE;
+  return m->seq_start[b] + t;
+}
+
+static int attention_impl(dqo_codec_args ka, dqo_codec_args va, int hkv,
+                          const uint16_t *q, int B, int Hq, const uint8_t *kc,
+                          const uint16_t *kn, const uint8_t *vc,
+                          const uint16_t *vn, int64_t num_slots,
+                          const slot_map *map, const int32_t *seq_len,
+                          double sm_scale, double *out, int nthreads) {
   dqo_codec ck, cv;
   int st = dqo_codec_init(&ck, ka.levels, ka.step64, ka.C, hkv, ka.seed);
   if (st) return st;
   st = dqo_codec_init(&cv, va.levels, va.step64, va.C, hkv, va.seed);
   if (st) return st;
   if (B < 0 || Hq < 1 || Hq % hkv) return DQO_EINVAL;
-  for (int b = 0; b < B; b++)
-    if (seq_len[b] < 1 || seq_start[b] < 0 ||
-        seq_start[b] + seq_len[b] > num_slots)
+  for (int b = 0; b < B; b++) {
+    if (seq_len[b] < 1) return DQO_EINVAL;
+    if (map->pages) {
+      if ((int64_t)seq_len[b] > (int64_t)map->max_pages * DQO_PAGE) return DQO_EINVAL;
+      for (int64_t p = 0; p < ((int64_t)seq_len[b] + DQO_PAGE - 1) / DQO_PAGE; p++) {
+        int32_t id = map->pages[(int64_t)b * map->max_pages + p];
+        if (id < 0 || ((int64_t)id + 1) * DQO_PAGE > num_slots) return DQO_EINVAL;
+      }
+    } else if (map->seq_start[b] < 0 || map->seq_start[b] + seq_len[b] > num_slots) {
       return DQO_EINVAL;
+    }
+  }
   int group = Hq / hkv;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -580,7 +604,7 @@ int dqo_attention(dqo_codec_args ka, dqo_codec_args va, int hkv,
     double *vh = malloc(sizeof(double) * (size_t)L * DQO_D);
     double *sc = malloc(sizeof(double) * (size_t)L);
     for (int64_t t = 0; t < L; t++) {
-      int64_t idx = (int64_t)g * num_slots + seq_start[b] + t;
+      int64_t idx = (int64_t)g * num_slots + slot_of(map, b, t);
       dequant_vector(&ck, kc + idx * ck.C, kn[idx], g, kh + t * DQO_D);
       dequant_vector(&cv, vc + idx * cv.C, vn[idx], g, vh + t * DQO_D);
     }
@@ -611,6 +635,32 @@ int dqo_attention(dqo_codec_args ka, dqo_codec_args va, int hkv,
     free(sc);
   }
   return DQO_OK;
+}
+
+int dqo_attention(dqo_codec_args ka, dqo_codec_args va, int hkv,
+                  const uint16_t *q /* bf16 [B][Hq][128] */, int B, int Hq,
+                  const uint8_t *kc, const uint16_t *kn, const uint8_t *vc,
+                  const uint16_t *vn, int64_t num_slots,
+                  const int64_t *seq_start, const int32_t *seq_len,
+                  double sm_scale, double *out /* [B][Hq][128] */,
+                  int nthreads) {
+  slot_map m = {seq_start, NULL, 0};
+  return attention_impl(ka, va, hkv, q, B, Hq, kc, kn, vc, vn, num_slots, &m,
+                        seq_len, sm_scale, out, nthreads);
+}
+
+/* The same attention over a paged pool: token t of sequence b is in slot
+ * pages[b * max_pages + t / 64] * 64 + t % 64. */
+int dqo_attention_paged(dqo_codec_args ka, dqo_codec_args va, int hkv,
+                        const uint16_t *q, int B, int Hq, const uint8_t *kc,
+                        const uint16_t *kn, const uint8_t *vc,
+                        const uint16_t *vn, int64_t num_slots,
+                        const int32_t *pages, int max_pages,
+                        const int32_t *seq_len, double sm_scale, double *out,
+                        int nthreads) {
+  slot_map m = {NULL, pages, max_pages};
+  return attention_impl(ka, va, hkv, q, B, Hq, kc, kn, vc, vn, num_slots, &m,
+                        seq_len, sm_scale, out, nthreads);
 }
 
 /* table export for tests */

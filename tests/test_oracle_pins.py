@@ -481,6 +481,53 @@ def _tiny_attention_case(O, B=2, Hq=4, hkv=2, lens=(3, 5), seed=0):
     return ck, cv, q, kc, kn, vc, vn, starts, np.array(lens[:B], np.int32)
 
 
+def test_paged_attention_equals_contiguous(oracle_lib):
+    """A paged pool (64-token pages in shuffled physical order, addressed
+    through a page table) gives exactly the contiguous result; page ids
+    outside the pool are rejected."""
+    O = oracle_lib
+    hkv, Hq, P = 2, 8, 64
+    lens = np.array([100, 200, 64], np.int32)
+    ck = O.Codec(8, 34, seed=11, hkv=hkv)
+    cv = O.Codec(6, 34, seed=12, hkv=hkv)
+    npages = [(int(L) + P - 1) // P for L in lens]
+    starts = np.concatenate([[0], np.cumsum(np.array(npages) * P)[:-1]]).astype(np.int64)
+    S = int(sum(npages) * P)
+    K = synth.kv_tensor("outlier", S, hkv, seed=21)
+    V = synth.kv_tensor("student_t5", S, hkv, seed=22)
+    q = synth.q_tensor(len(lens), Hq, seed=23)
+    kc, kn, _ = O.encode(ck, K)
+    vc, vn, _ = O.encode(cv, V)
+    want = O.attention(ck, cv, q, kc, kn, vc, vn, starts, lens)
+    # shuffle the pages into a larger pool with gaps
+    rng = np.random.default_rng(5)
+    total = sum(npages)
+    phys = rng.permutation(total + 3)[:total]
+    S2 = (total + 3) * P
+    kc2 = np.zeros((hkv, S2, ck.C), np.uint8)
+    vc2 = np.zeros((hkv, S2, cv.C), np.uint8)
+    kn2 = np.zeros((hkv, S2), np.uint16)
+    vn2 = np.zeros((hkv, S2), np.uint16)
+    kn_b, vn_b = np.asarray(kn).view(np.uint16), np.asarray(vn).view(np.uint16)
+    maxp = max(npages) + 1
+    pages = np.full((len(lens), maxp), -1, np.int32)
+    logical = 0
+    for b, n in enumerate(npages):
+        for j in range(n):
+            src = slice(int(starts[b]) + j * P, int(starts[b]) + (j + 1) * P)
+            dst = slice(int(phys[logical]) * P, (int(phys[logical]) + 1) * P)
+            kc2[:, dst], vc2[:, dst] = kc[:, src], vc[:, src]
+            kn2[:, dst], vn2[:, dst] = kn_b[:, src], vn_b[:, src]
+            pages[b, j] = phys[logical]
+            logical += 1
+    got = O.attention_paged(ck, cv, q, kc2, kn2, vc2, vn2, pages, lens)
+    assert np.array_equal(got, want)
+    bad = pages.copy()
+    bad[1, 0] = total + 3  # one page past the pool
+    with pytest.raises(ValueError):
+        O.attention_paged(ck, cv, q, kc2, kn2, vc2, vn2, bad, lens)
+
+
 def test_attention_brute_force_loops(oracle_lib):
     O = oracle_lib
     ck, cv, q, kc, kn, vc, vn, starts, lens = _tiny_attention_case(O)
