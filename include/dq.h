@@ -171,6 +171,31 @@ int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B,
                    int32_t out_dtype, void *out, void *workspace,
                    size_t ws_bytes, dq_stream_t stream);
 
+/* Paged pool: the same attention, with each sequence's cache split into
+ * pages of DQ_PAGE_TOKENS consecutive slots anywhere in the pool (a block
+ * table, so sequences can grow without contiguous reservations).  Token t
+ * of sequence b is in slot pages[b * max_pages + t / 64] * 64 + t % 64 of
+ * every kv head's plane; the fixed-stride container address the pages rely
+ * on ("D-Quant: Driftable Entropy Coding for KV Cache Quantization",
+ * abstract) is unchanged.
+ *   pages      device int32 [B][max_pages]; entries past a sequence's last
+ *              page are not read.  A page id outside [0, num_slots / 64)
+ *              reads zero containers (a caller error, never a fault).
+ *   max_pages  >= 1, and max_len <= max_pages * 64 (else DQ_ERR_INVALID);
+ *              longer seq_len values are cut at max_pages * 64.
+ * Every other argument, the workspace and the result are as for
+ * dq_attn_decode; dq_encode writes a page by passing its slots. */
+#define DQ_PAGE_TOKENS 64
+int dq_attn_decode_paged(dq_codec_t ck, dq_codec_t cv, const void *q,
+                         int32_t B, int32_t Hq, const uint8_t *k_cont,
+                         const uint16_t *k_norm, const uint8_t *v_cont,
+                         const uint16_t *v_norm, int64_t num_slots,
+                         const int32_t *pages, int32_t max_pages,
+                         const int32_t *seq_len, int64_t max_len,
+                         float sm_scale, int32_t out_dtype, void *out,
+                         void *workspace, size_t ws_bytes,
+                         dq_stream_t stream);
+
 /* dq_attn_decode plus a measurement hook: `split_begin` and `split_end`
  * (hipEvent_t, either may be NULL) are recorded on `stream` right before
  * and right after the split-K kernel, the one that reads the compressed

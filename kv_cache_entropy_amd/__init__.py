@@ -23,9 +23,10 @@ from . import _lib
 
 HEAD_DIM = 128
 MAX_CONTAINER = 132
+PAGE_TOKENS = 64
 NSTATS = 6 + MAX_CONTAINER + 1
 
-__all__ = ["Codec", "alloc_pool", "encode", "decode_symbols", "attn_decode",
+__all__ = ["Codec", "alloc_pool", "encode", "decode_symbols", "attn_decode", "attn_decode_paged",
            "attn_workspace_bytes", "new_stats", "stats_dict", "DQError", "library_path"]
 
 
@@ -225,4 +226,43 @@ def attn_decode(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_cont, v
                 ev.record()
             handles.append(ctypes.c_void_p(ev.cuda_event))
         _check(_lib.lib().dq_attn_decode_timed(*args, *handles), "dq_attn_decode_timed")
+    return out
+
+
+def attn_decode_paged(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_cont, v_norm,
+                      pages: torch.Tensor, seq_len: torch.Tensor, max_len: int,
+                      sm_scale: float | None = None, out: torch.Tensor | None = None,
+                      out_dtype=torch.float32, workspace: torch.Tensor | None = None):
+    """attn_decode over a paged pool: pages int32 [B, max_pages], token t of
+    sequence b in slot pages[b, t // 64] * 64 + t % 64."""
+    _need_cuda("q", q, torch.bfloat16)
+    for name, t, dt in (("k_cont", k_cont, torch.uint8), ("v_cont", v_cont, torch.uint8),
+                        ("k_norm", k_norm, torch.float16), ("v_norm", v_norm, torch.float16),
+                        ("pages", pages, torch.int32), ("seq_len", seq_len, torch.int32)):
+        _need_cuda(name, t, dt)
+        if not t.is_contiguous():
+            raise DQError(f"{name} must be contiguous")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise DQError("q must be a contiguous bf16 [B, Hq, 128]")
+    B, Hq, _ = q.shape
+    if pages.dim() != 2 or pages.shape[0] != B:
+        raise DQError("pages must be int32 [B, max_pages]")
+    if k_cont.shape[1] != v_cont.shape[1]:
+        raise DQError("K and V pools must have the same slot count")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise DQError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, Hq, HEAD_DIM) or not out.is_contiguous():
+        raise DQError("out has the wrong shape or dtype")
+    need = attn_workspace_bytes(B, Hq, ck.kv_heads, max_len)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if sm_scale is None:
+        sm_scale = HEAD_DIM ** -0.5
+    _check(_lib.lib().dq_attn_decode_paged(
+        ck.handle, cv.handle, _ptr(q), B, Hq, _ptr(k_cont), _ptr(k_norm), _ptr(v_cont),
+        _ptr(v_norm), k_cont.shape[1], _ptr(pages), pages.shape[1], _ptr(seq_len), max_len,
+        ctypes.c_float(sm_scale), 0 if out_dtype == torch.float32 else 1, _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(q.device)), "dq_attn_decode_paged")
     return out

@@ -20,8 +20,9 @@
 //     (16 blocks = the wave's 64 tokens) against q~ (4 heads), so the decoded
 //     keys never leave registers.  Online softmax in fp32 (exp2 domain).
 //     V: decoded levels are written transposed into an LDS tile [dim][token]
-//     and contracted with p * n_v by 4x4x4 MFMAs whose 16 blocks cover 64
-//     dims.  Each item leaves (m, l, acc[4][128]) in the workspace.
+//     and contracted with p * n_v (an fp16 hi/lo pair, so ~22 bits) by
+//     4x4x4 MFMAs whose 16 blocks cover 64 dims.  Each item leaves
+//     (m, l, acc[4][128]) in the workspace.
 //  3. combine: log-sum-exp merge of an item's chunks, then the inverse
 //     rotation D_V * H / 128 and the store.
 #include "decode_common.h"
@@ -36,6 +37,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;
+static_assert(kTile == DQ_PAGE_TOKENS, "a page is one attention tile");
 constexpr int kVtStride = 66;    // halves per V-tile row: 33 dwords, spreads LDS banks
 constexpr int kPass = 32;        // dims per V-tile pass
 constexpr int kPart = 132;       // floats per (item, head): acc[128], m, l, pad
@@ -50,7 +52,9 @@ struct AttnArgs {
   const uint8_t *vc;
   const uint16_t *vn;
   int64_t S;
-  const int64_t *seq_start;
+  const int64_t *seq_start;  // contiguous layout, or
+  const int32_t *pages;      // [B][max_pages] 64-token page ids (paged layout)
+  int max_pages;
   const int32_t *seq_len;
   float qk_scale;  // sm_scale * log2(e) / 128
   int chunk, nc;
@@ -122,7 +126,7 @@ __host__ __device__ inline WaveLayout wave_layout(int Ck, int Cv) {
   w.kst = 0;
   w.vst = w.kst + ((kTile * Ck + 31) & ~15);
   w.pl = w.vst + ((kTile * Cv + 31) & ~15);
-  w.vt = w.pl + 4 * kTile * 2;
+  w.vt = w.pl + 2 * 4 * kTile * 2;  // P: [head][token quad][hi x4, lo x4] fp16
   w.bytes = w.vt + kPass * kVtStride * 2;
   w.bytes = (w.bytes + 15) & ~15;
   return w;
@@ -188,12 +192,13 @@ struct DecTab {
 //   own 4 levels are the B column, and the lane ends with its token's
 //   scores for the 4 heads.
 // V: levels go to the transposed LDS tile, 32 dims per pass; each pass is
-//   contracted with P by 8 MFMAs whose blocks are (8 dim quads) x (2 token
-//   halves); P is broadcast per half (cbsz 3), read by lanes 0..3, 32..35.
+//   contracted with P (hi, then lo) by 16 MFMAs whose blocks are (8 dim
+//   quads) x (2 token halves); P is broadcast per half (cbsz 3), read by
+//   lanes 0..3, 32..35.
 template <bool DK, bool DV>
 __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
                                           const uint8_t *vb, const uint4 *qg, const uint16_t *pl,
-                                          uint16_t *vt, floatx4 &sc, floatx4 (&acc)[4], int lane) {
+                                          uint16_t *vt, floatx4 &sc, floatx4 (&acc)[8], int lane) {
   const int th = lane >> 5, row = lane & 31;
   const bool qlane = lane < 4, plane = (lane & 31) < 4;
   // rotated query (global, 2 KB per item, cache resident): lanes 0..3 load
@@ -248,11 +253,17 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
       wave_sync();
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        uint2 pa = make_uint2(0, 0);
-        if (plane) pa = *reinterpret_cast<const uint2 *>(pl + (lane & 3) * kTile + th * 32 + 4 * c);
+        uint2 pa = make_uint2(0, 0), pb = make_uint2(0, 0);
+        if (plane) {
+          const uint4 pp = *reinterpret_cast<const uint4 *>(pl + ((lane & 3) * 16 + th * 8 + c) * 8);
+          pa = make_uint2(pp.x, pp.y);
+          pb = make_uint2(pp.z, pp.w);
+        }
         const uint32_t *r = reinterpret_cast<const uint32_t *>(vt) + row * (kVtStride / 2) + th * 16 + 2 * c;
         const half4 V = __builtin_bit_cast(half4, make_uint2(r[0], r[1]));
+        // hi and lo accumulate separately: two independent MFMA chains
         acc[p] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, pa), V, acc[p], 3, 0, 0);
+        acc[4 + p] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, pb), V, acc[4 + p], 3, 0, 0);
       }
       wave_sync();
     }
@@ -279,7 +290,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // reuses it and skips the reductions and the rescale; p stays <= 1.
 __device__ __forceinline__ void softmax_tile(const floatx4 &sc, uint32_t nk_bits, uint32_t nv_bits, bool valid,
                                              float qk_scale, float (&m_run)[4], float (&l_lane)[4],
-                                             uint16_t *pl, floatx4 (&acc)[4], int lane) {
+                                             uint16_t *pl, floatx4 (&acc)[8], int lane) {
   const float nk = (float)__builtin_bit_cast(_Float16, (uint16_t)nk_bits);
   const float nv = (float)__builtin_bit_cast(_Float16, (uint16_t)nv_bits);
   float s[4];
@@ -299,7 +310,7 @@ __device__ __forceinline__ void softmax_tile(const floatx4 &sc, uint32_t nk_bits
       m_run[h] = m_new;
     }
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+    for (int p = 0; p < 8; ++p)
 #pragma unroll
       for (int h = 0; h < 4; ++h) acc[p][h] *= alpha[h];
   }
@@ -307,7 +318,13 @@ __device__ __forceinline__ void softmax_tile(const floatx4 &sc, uint32_t nk_bits
   for (int h = 0; h < 4; ++h) {
     const float p = valid ? exp2f(s[h] - m_run[h]) : 0.0f;
     l_lane[h] += p;
-    pl[h * kTile + lane] = __builtin_bit_cast(uint16_t, (_Float16)(valid ? p * nv : 0.0f));
+    // P = p * n_v as an fp16 pair (hi + lo carries ~22 bits): one fp16
+    // rounding alone would cost up to 2^-11 of an output of norm size
+    const float pv = valid ? p * nv : 0.0f;
+    const _Float16 hi = (_Float16)pv;
+    uint16_t *q8 = pl + (h * 16 + (lane >> 2)) * 8 + (lane & 3);
+    q8[0] = __builtin_bit_cast(uint16_t, hi);
+    q8[4] = __builtin_bit_cast(uint16_t, (_Float16)(pv - (float)hi));
   }
 }
 
@@ -341,21 +358,27 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
     const int c = (int)(item % a.nc);
     const int64_t bg = item / a.nc;
     const int b = (int)(bg / a.Hkv), g = (int)(bg - (int64_t)b * a.Hkv);
-    const int len = a.seq_len[b];
+    // a paged sequence never reads past its row of the page table
+    const int len = a.pages ? min(a.seq_len[b], a.max_pages * kTile) : a.seq_len[b];
     const int t0 = c * a.chunk;
     if (t0 >= len) continue;
     const int t1 = min(t0 + a.chunk, len);
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-    const int64_t pbase = (int64_t)g * a.S + a.seq_start[b] + t0;  // pool index of token t0
-    const uint8_t *kplane = a.kc + pbase * Ck;
-    const uint8_t *vplane = a.vc + pbase * Cv;
+    const int64_t plane0 = (int64_t)g * a.S;
+    // pool index of the first token of tile `tile` of this item: a page is
+    // one tile, so a tile's containers are contiguous in either layout
+    auto tile_base = [&](int tile) -> int64_t {
+      const int t = t0 + tile * kTile;
+      return a.pages ? plane0 + (int64_t)a.pages[(int64_t)b * a.max_pages + t / kTile] * kTile
+                     : plane0 + a.seq_start[b] + t;
+    };
 
     wave_sync();  // the previous item's LDS reads are done
     const uint4 *qr = reinterpret_cast<const uint4 *>(a.qrot + bg * kQrotPerBG);
 
     // this lane's token norms for a tile (0 outside the pool plane)
-    auto norms = [&](int tile, uint32_t &nk, uint32_t &nv) {
-      const int64_t idx = pbase + tile * kTile + lane;
+    auto norms = [&](int64_t tbase, uint32_t &nk, uint32_t &nv) {
+      const int64_t idx = tbase + lane;
       const bool ok = idx >= (int64_t)g * a.S && idx < (int64_t)(g + 1) * a.S;
       nk = ok ? a.kn[idx] : 0u;
       nv = ok ? a.vn[idx] : 0u;
@@ -363,15 +386,19 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
     TileRegs<NQ> rk, rv;
     uint32_t nk0, nv0, nk1 = 0, nv1 = 0;
     // prologue: K of tile 0
-    fetch<NQ>(rk, kplane, kTile * Ck, a.kc, kpool_end, lane);
-    norms(0, nk0, nv0);
+    const int64_t base0 = tile_base(0);
+    int64_t vbase = base0;  // V tile to fetch next
+    fetch<NQ>(rk, a.kc + base0 * Ck, kTile * Ck, a.kc, kpool_end, lane);
+    norms(base0, nk0, nv0);
     commit<NQ>(rk, kst, kTile * Ck, lane);
     const int koff0 = rk.off;
     wave_sync();
-    fetch<NQ>(rv, vplane, kTile * Cv, a.vc, vpool_end, lane);
+    fetch<NQ>(rv, a.vc + vbase * Cv, kTile * Cv, a.vc, vpool_end, lane);
     if (ntiles > 1) {
-      fetch<NQ>(rk, kplane + kTile * Ck, kTile * Ck, a.kc, kpool_end, lane);
-      norms(1, nk1, nv1);
+      const int64_t base1 = tile_base(1);
+      fetch<NQ>(rk, a.kc + base1 * Ck, kTile * Ck, a.kc, kpool_end, lane);
+      norms(base1, nk1, nv1);
+      vbase = base1;
     }
     float m_run[4], l_lane[4];
 #pragma unroll
@@ -379,9 +406,9 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
       m_run[h] = -__builtin_inff();
       l_lane[h] = 0.0f;
     }
-    floatx4 acc[4];
+    floatx4 acc[8];  // [0..3]: P hi contributions, [4..7]: P lo
 #pragma unroll
-    for (int p = 0; p < 4; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < 8; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
     floatx4 sc = {0.f, 0.f, 0.f, 0.f};
     tile_pass<true, false>(dk, dv, kst + koff0 + lane * Ck, nullptr, qr, pl, vt, sc, acc, lane);
     softmax_tile(sc, nk0, nv0, lane < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
@@ -399,10 +426,12 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
       wave_sync();
       // prefetch the next iteration's tiles into registers
       uint32_t nk2 = 0, nv2 = 0;
-      if (next) fetch<NQ>(rv, vplane + (j + 1) * kTile * Cv, kTile * Cv, a.vc, vpool_end, lane);
+      if (next) fetch<NQ>(rv, a.vc + vbase * Cv, kTile * Cv, a.vc, vpool_end, lane);
       if (j + 2 < ntiles) {
-        fetch<NQ>(rk, kplane + (j + 2) * kTile * Ck, kTile * Ck, a.kc, kpool_end, lane);
-        norms(j + 2, nk2, nv2);
+        const int64_t base2 = tile_base(j + 2);
+        fetch<NQ>(rk, a.kc + base2 * Ck, kTile * Ck, a.kc, kpool_end, lane);
+        norms(base2, nk2, nv2);
+        vbase = base2;
       }
       if (next) {
         sc = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -422,7 +451,8 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
     for (int p = 0; p < 4; ++p) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const float v = acc[p][h] + __shfl_xor(acc[p][h], 32);
+        const float a2 = acc[p][h] + acc[4 + p][h];
+        const float v = a2 + __shfl_xor(a2, 32);
         if (lane < 32) dst[h * kPart + p * kPass + lane] = v;
       }
     }
@@ -560,12 +590,14 @@ extern "C" int dq_attn_decode_workspace(int32_t B, int32_t Hq, int32_t Hkv, int6
 
 static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq, const uint8_t *k_cont,
                        const uint16_t *k_norm, const uint8_t *v_cont, const uint16_t *v_norm, int64_t num_slots,
-                       const int64_t *seq_start, const int32_t *seq_len, int64_t max_len, float sm_scale,
-                       int32_t out_dtype, void *out, void *workspace, size_t ws_bytes, dq_stream_t stream,
-                       hipEvent_t split_begin, hipEvent_t split_end) {
-  if (!ck || !cv || !q || !k_cont || !k_norm || !v_cont || !v_norm || !seq_start || !seq_len || !out ||
-      !workspace)
+                       const int64_t *seq_start, const int32_t *pages, int32_t max_pages,
+                       const int32_t *seq_len, int64_t max_len, float sm_scale, int32_t out_dtype, void *out,
+                       void *workspace, size_t ws_bytes, dq_stream_t stream, hipEvent_t split_begin,
+                       hipEvent_t split_end) {
+  if (!ck || !cv || !q || !k_cont || !k_norm || !v_cont || !v_norm || (!seq_start && !pages) || !seq_len ||
+      !out || !workspace)
     return DQ_ERR_INVALID;
+  if (pages && (max_pages < 1 || max_len > (int64_t)max_pages * dq::kTile)) return DQ_ERR_INVALID;
   const int Hkv = ck->t.hkv;
   if (cv->t.hkv != Hkv || B < 1 || Hq < 1 || Hq % Hkv || num_slots < 1 || max_len < 1) return DQ_ERR_INVALID;
   const int group = Hq / Hkv;
@@ -597,6 +629,8 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
   a.vn = v_norm;
   a.S = num_slots;
   a.seq_start = seq_start;
+  a.pages = pages;
+  a.max_pages = pages ? max_pages : 0;
   a.seq_len = seq_len;
   a.qk_scale = sm_scale * 1.4426950408889634f / 128.0f;
   a.chunk = pl.chunk;
@@ -624,8 +658,19 @@ extern "C" int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32
                               const uint16_t *v_norm, int64_t num_slots, const int64_t *seq_start,
                               const int32_t *seq_len, int64_t max_len, float sm_scale, int32_t out_dtype,
                               void *out, void *workspace, size_t ws_bytes, dq_stream_t stream) {
-  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, seq_len, max_len,
-                     sm_scale, out_dtype, out, workspace, ws_bytes, stream, nullptr, nullptr);
+  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, nullptr, 0, seq_len,
+                     max_len, sm_scale, out_dtype, out, workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" int dq_attn_decode_paged(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,
+                                    const uint8_t *k_cont, const uint16_t *k_norm, const uint8_t *v_cont,
+                                    const uint16_t *v_norm, int64_t num_slots, const int32_t *pages,
+                                    int32_t max_pages, const int32_t *seq_len, int64_t max_len, float sm_scale,
+                                    int32_t out_dtype, void *out, void *workspace, size_t ws_bytes,
+                                    dq_stream_t stream) {
+  if (!pages) return DQ_ERR_INVALID;
+  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, nullptr, pages, max_pages,
+                     seq_len, max_len, sm_scale, out_dtype, out, workspace, ws_bytes, stream, nullptr, nullptr);
 }
 
 extern "C" int dq_attn_decode_timed(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,
@@ -634,7 +679,7 @@ extern "C" int dq_attn_decode_timed(dq_codec_t ck, dq_codec_t cv, const void *q,
                                     const int32_t *seq_len, int64_t max_len, float sm_scale, int32_t out_dtype,
                                     void *out, void *workspace, size_t ws_bytes, dq_stream_t stream,
                                     void *split_begin, void *split_end) {
-  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, seq_len, max_len,
-                     sm_scale, out_dtype, out, workspace, ws_bytes, stream, static_cast<hipEvent_t>(split_begin),
-                     static_cast<hipEvent_t>(split_end));
+  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, nullptr, 0, seq_len,
+                     max_len, sm_scale, out_dtype, out, workspace, ws_bytes, stream,
+                     static_cast<hipEvent_t>(split_begin), static_cast<hipEvent_t>(split_end));
 }

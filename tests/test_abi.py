@@ -142,3 +142,22 @@ def test_host_argument_checks_launch_nothing():
     bad_pool = list(args)
     bad_pool[7] = 15  # 15 * 34 not a multiple of 16
     assert L.dq_attn_decode(c.handle, v2.handle, *bad_pool) == -1
+
+
+def test_paged_attention_argument_checks():
+    L = _lib.lib()
+    c = dq.Codec(8, 34, seed=1, kv_heads=2)
+    v = dq.Codec(6, 34, seed=2, kv_heads=2)
+    vp = ctypes.c_void_p
+    fake = vp(256)
+    base = [c.handle, v.handle, fake, 1, 4, fake, fake, fake, fake, 64, fake, 2, fake, 128,
+            ctypes.c_float(0.1), 0, fake, fake, 1 << 20, None]
+    nopages = list(base)
+    nopages[10] = None
+    assert L.dq_attn_decode_paged(*nopages) == -1
+    zero = list(base)
+    zero[11] = 0  # max_pages
+    assert L.dq_attn_decode_paged(*zero) == -1
+    short = list(base)
+    short[13] = 129  # max_len > max_pages * 64
+    assert L.dq_attn_decode_paged(*short) == -1

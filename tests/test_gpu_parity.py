@@ -255,6 +255,77 @@ def test_attention_timed_entry_point(oracle_lib):
     assert e0.elapsed_time(e1) > 0.0
 
 
+def _paged_copy(c, rng, extra_pages=5):
+    """The contiguous pools of an attention case re-laid as shuffled 64-token
+    pages in a larger pool, with the page table that addresses them."""
+    P = dq.PAGE_TOKENS
+    lens, starts = c["lens"], c["starts"]
+    npages = [(int(L) + P - 1) // P for L in lens]
+    total = sum(npages)
+    phys = rng.permutation(total + extra_pages)[:total]
+    pools = {}
+    for tag, cont, norm in (("K", c["kc"], c["kn"]), ("V", c["vc"], c["vn"])):
+        S2 = (total + extra_pages) * P
+        cont2 = torch.zeros((cont.shape[0], dq.pool_slots(S2), cont.shape[2]), dtype=torch.uint8, device=DEV)
+        norm2 = torch.zeros((cont.shape[0], cont2.shape[1]), dtype=torch.float16, device=DEV)
+        pools[tag] = (cont2, norm2)
+    pages = np.full((len(lens), max(npages) + 2), -7, np.int32)  # unused entries: never read
+    logical = 0
+    for b, n in enumerate(npages):
+        for j in range(n):
+            s0 = int(starts[b]) + j * P
+            d0 = int(phys[logical]) * P
+            for tag, cont, norm in (("K", c["kc"], c["kn"]), ("V", c["vc"], c["vn"])):
+                hi = min(s0 + P, cont.shape[1])
+                pools[tag][0][:, d0:d0 + hi - s0] = cont[:, s0:hi]
+                pools[tag][1][:, d0:d0 + hi - s0] = norm[:, s0:hi]
+            pages[b, j] = phys[logical]
+            logical += 1
+    return pools, pages
+
+
+def test_attention_paged_pool(oracle_lib):
+    """Shuffled 64-token pages addressed through a page table: the same
+    result as the contiguous call bit for bit, and within tolerance of the
+    oracle's paged attention, for ragged lengths and two group sizes."""
+    O = oracle_lib
+    rng = np.random.default_rng(17)
+    for Hq, hkv in ((8, 2), (4, 4)):
+        lens = [1, 63, 64, 65, 300, 129]
+        c = _attn_case(O, len(lens), Hq, hkv, lens, seed=40 + Hq, gap=64)
+        ref_contig = _gpu_attn(c)
+        pools, pages = _paged_copy(c, rng)
+        pg = torch.from_numpy(pages).to(DEV)
+        out = dq.attn_decode_paged(c["ck"], c["cv"], c["q"], *pools["K"], *pools["V"], pg, c["sl"],
+                                   int(c["lens"].max()))
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_contig), "paged and contiguous results differ"
+        ref = O.attention_paged(c["ock"], c["ocv"], _np_bits(c["q"]), pools["K"][0].cpu().numpy(),
+                                _np_bits(pools["K"][1]), pools["V"][0].cpu().numpy(),
+                                _np_bits(pools["V"][1]), pages, c["lens"])
+        _assert_close(out.cpu().numpy(), ref, f"paged Hq={Hq} hkv={hkv}")
+
+
+def test_attention_paged_ids_outside_pool_read_zeros(oracle_lib):
+    """A page id past the pool or negative is a caller error: the kernel's
+    pool bounds checks turn it into zero containers; the other sequences
+    are unaffected."""
+    O = oracle_lib
+    lens = [130, 70]
+    c = _attn_case(O, 2, 8, 2, lens, seed=3, gap=64)
+    pools, pages = _paged_copy(c, np.random.default_rng(2), extra_pages=0)
+    n_pool_pages = pools["K"][0].shape[1] // dq.PAGE_TOKENS
+    bad = pages.copy()
+    bad[0, 1] = n_pool_pages + 1
+    bad[0, 2] = -1
+    pg = torch.from_numpy(bad).to(DEV)
+    out = dq.attn_decode_paged(c["ck"], c["cv"], c["q"], *pools["K"], *pools["V"], pg, c["sl"], 130)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    good = _gpu_attn(c)
+    assert torch.equal(out[1], good[1])
+
+
 def test_tiny_1seq_1k_config(oracle_lib):
     """1 sequence, 1 query / 1 kv head, context 1024, per-token scaled
     N(0,1) K/V, 34-byte containers: every container and the output."""
@@ -365,6 +436,7 @@ def _sampled_attention(O, c, lens, max_len, rows, label):
     ref = O.attention(c["ock"], c["ocv"], _np_bits(q)[rows], kc.cpu().numpy(), _np_bits(kn),
                       vc.cpu().numpy(), _np_bits(vn), c["starts"][rows], lens.numpy().astype(np.int32)[rows])
     _assert_close(out.cpu().numpy()[rows], ref, f"{label} attention rows {rows}")
+    return out
 
 
 def test_llama31_b128_8k_bench_configuration(oracle_lib):
@@ -375,7 +447,32 @@ def test_llama31_b128_8k_bench_configuration(oracle_lib):
     O = oracle_lib
     c = _workload_case(O, "llama31_8b_b128_8k", cap_extra=19)
     lens = _append_and_check(O, c, 1, seed=c["w"].seed + 20)
-    _sampled_attention(O, c, lens, int(c["ctx"].max()) + 19, [0, 77, 127], "llama31 b128")
+    out = _sampled_attention(O, c, lens, int(c["ctx"].max()) + 19, [0, 77, 127], "llama31 b128")
+    # the same pools re-laid as shuffled 64-token pages: identical output
+    P = dq.PAGE_TOKENS
+    cap = int(c["ctx"][0]) + 19
+    npg = (cap + P - 1) // P
+    B = c["w"].batch
+    rng = np.random.default_rng(8)
+    phys = torch.from_numpy(rng.permutation(B * npg).astype(np.int64)).to(DEV)
+    pages = phys.view(B, npg).to(torch.int32).contiguous()
+    src = (torch.from_numpy(c["starts"]).to(DEV)[:, None] + torch.arange(npg, device=DEV)[None, :] * P)
+    paged = {}
+    for tag in ("K", "V"):
+        cont, norm = c["pools"][tag]
+        cont2 = torch.zeros((cont.shape[0], B * npg * P, cont.shape[2]), dtype=torch.uint8, device=DEV)
+        norm2 = torch.zeros((cont.shape[0], B * npg * P), dtype=torch.float16, device=DEV)
+        for j in range(P):
+            s_idx = (src + j).clamp(max=cont.shape[1] - 1).flatten()
+            d_idx = (phys.view(B, npg) * P + j).flatten()
+            cont2[:, d_idx] = cont[:, s_idx]
+            norm2[:, d_idx] = norm[:, s_idx]
+        paged[tag] = (cont2, norm2)
+    q = synth.q_tensor(B, c["w"].hq, seed=c["w"].seed + 12, device=DEV)
+    outp = dq.attn_decode_paged(c["ck"], c["cv"], q, *paged["K"], *paged["V"], pages,
+                                lens.to(torch.int32).to(DEV), int(c["ctx"].max()) + 19)
+    torch.cuda.synchronize()
+    assert torch.equal(outp, out), "paged pool differs from the contiguous pool at full size"
 
 
 def test_longctx_b4_64k_c29(oracle_lib):
