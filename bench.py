@@ -134,8 +134,9 @@ def summarize_profiles(d):
     rl = live["roofline"]
     if split:
         sp = split[0]
-        lines += ["", f"Split-K kernel: rocprofv3 average {sp[3]:.1f} us over {sp[2]} launches (warm-up "
-                  f"included); the same run's bench line measured {rl['avg_launch_ms'] * 1e3:.1f} us with HIP "
+        lines += ["", f"Split-K kernel: rocprofv3 average {sp[3]:.1f} us over {sp[2]} launches (warm-up and the "
+                  f"paged-pool timing included); the same run's bench line measured "
+                  f"{rl['avg_launch_ms'] * 1e3:.1f} us with HIP "
                   f"events around the kernel over the timed steps, {rl['achieved']:.1f} GB/s of compressed "
                   f"bytes = {rl['frac']:.2%} of 8 TB/s.",
                   "", "Bench line of this run:", "", "```", json.dumps(live), "```"]
@@ -237,6 +238,7 @@ def main():
     ap.add_argument("--workload", default="llama31_8b_b128_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-pool attention timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter scale for rocprofv3)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -356,6 +358,43 @@ def main():
         f"attention {att_avg_ms:.3f} ms of which split-K {split_avg_ms:.3f} ms), {value:.1f} GB/s step, "
         f"split-K kernel {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of HBM peak")
 
+    # the same caches re-laid as shuffled 64-token pages (page-table pool)
+    paged = None
+    if not args.no_paged:
+        P = dq.PAGE_TOKENS
+        npg = int((cap.max() + P - 1) // P)
+        gen = torch.Generator(device="cpu").manual_seed(w.seed + 50)
+        phys = torch.randperm(B * npg, generator=gen).to(dev).view(B, npg)
+        src = torch.from_numpy(starts).to(dev)[:, None] + torch.arange(npg, device=dev)[None, :] * P
+        pools = []
+        for cont, norm in ((kc, kn), (vc, vn)):
+            cont2 = torch.zeros((Hkv, dq.pool_slots(B * npg * P), cont.shape[2]), dtype=torch.uint8, device=dev)
+            norm2 = torch.zeros((Hkv, cont2.shape[1]), dtype=torch.float16, device=dev)
+            for j in range(P):
+                s_idx = (src + j).clamp(max=cont.shape[1] - 1).flatten()
+                d_idx = (phys * P + j).flatten()
+                cont2[:, d_idx] = cont[:, s_idx]
+                norm2[:, d_idx] = norm[:, s_idx]
+            pools += [cont2, norm2]
+        pages = phys.to(torch.int32).contiguous()
+        outp = torch.empty_like(out)
+        for s in range(args.warmup):
+            dq.attn_decode_paged(ck, cv, qs[s], *pools, pages, lens_s[s], max_len, out=outp, workspace=ws)
+        torch.cuda.synchronize()
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for k in range(args.steps):
+            s = args.warmup + k
+            pev[k][0].record()
+            dq.attn_decode_paged(ck, cv, qs[s], *pools, pages, lens_s[s], max_len, out=outp, workspace=ws)
+            pev[k][1].record()
+        torch.cuda.synchronize()
+        paged_ms = sum(e[0].elapsed_time(e[1]) for e in pev) / args.steps
+        paged = {"attn_call_ms": round(paged_ms, 4), "gbps": round(alg_bytes / (paged_ms / 1e3) / 1e9, 2),
+                 "page_tokens": P, "layout": "pages shuffled over the pool"}
+        log(f"[bench] paged pool: attention call {paged_ms:.3f} ms ({paged['gbps']:.1f} GB/s) "
+            f"vs contiguous {att_avg_ms:.3f} ms")
+        del pools
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")
@@ -385,6 +424,7 @@ def main():
         "attn_source_sha256_16": attn_source_hash(),
         "attn_call_ms": round(att_avg_ms, 4),
         "attn_call_gbps": round(alg_bytes / (att_avg_ms / 1e3) / 1e9, 2),
+        "paged_attn": paged,
         "cpu_baseline": cpu,
         "attn_context_tokens_per_s": round(ctx_tokens / (sum(att_ms) / 1e3), 1),
         "append_encode_ms": round(float(np.mean(enc_ms)), 4),
