@@ -83,9 +83,9 @@ def lib():
         L.dqo_rans_encode.argtypes = [u8p, u32p, u32p, u8p, c_int]
         L.dqo_rans_decode.restype = None
         L.dqo_rans_decode.argtypes = [u8p, c_int, c_int, u32p, u32p, u8p, u32p, i32p]
-        L.dqo_encode.argtypes = [c_int, c_int, c_int, c_int, c_u64, u16p, c_i64,
+        L.dqo_encode.argtypes = [c_int, c_int, c_int, c_int, c_u64, c_int, u16p, c_i64,
                                  c_i64, c_i64, i64p, c_i64, u8p, u16p, u64p, c_int]
-        L.dqo_encode_detail.argtypes = [c_int, c_int, c_int, c_int, c_u64, c_int,
+        L.dqo_encode_detail.argtypes = [c_int, c_int, c_int, c_int, c_u64, c_int, c_int,
                                         u16p, u8p, ctypes.c_void_p]
         L.dqo_decode_symbols.argtypes = [c_int, c_int, c_int, u8p, c_i64, c_int,
                                          c_int, i64p, c_i64, u8p, u32p, i32p]
@@ -129,10 +129,12 @@ def _u16(x):
 
 class Codec:
     """Parameters of one K or V stream: levels, step (1/64 sigma units),
-    container bytes C, rotation seed and number of kv heads."""
+    container bytes C, rotation seed, number of kv heads and drift order
+    (0: magnitude order, 1: rate-distortion order)."""
 
-    def __init__(self, levels: int, C: int, seed: int, hkv: int, step64: int = 0):
-        self.levels, self.C, self.seed, self.hkv = levels, C, seed, hkv
+    def __init__(self, levels: int, C: int, seed: int, hkv: int, step64: int = 0,
+                 order: int = 0):
+        self.levels, self.C, self.seed, self.hkv, self.order = levels, C, seed, hkv, order
         self.step64 = step64 or DEFAULT_STEP64[(levels, C)]
         st = lib().dqo_codec_check(levels, self.step64, C)
         if st != 0:
@@ -230,7 +232,7 @@ def encode(codec: Codec, x, slots=None, num_slots=None, nthreads: int = 0):
     cont = np.zeros((H, num_slots, codec.C), np.uint8)
     norm = np.zeros((H, num_slots), np.uint16)
     stats = np.zeros(NSTATS, np.uint64)
-    st = lib().dqo_encode(codec.levels, codec.step64, codec.C, H, codec.seed,
+    st = lib().dqo_encode(codec.levels, codec.step64, codec.C, H, codec.seed, codec.order,
                           _p(xb, ctypes.c_uint16), T, H * D, D,
                           _p(slots, ctypes.c_int64), num_slots,
                           _p(cont, ctypes.c_uint8), _p(norm, ctypes.c_uint16),
@@ -246,7 +248,7 @@ def encode_detail(codec: Codec, xvec, g: int = 0):
     cont = np.zeros(codec.C, np.uint8)
     d = VecDetail()
     st = lib().dqo_encode_detail(codec.levels, codec.step64, codec.C, codec.hkv,
-                                 codec.seed, g, _p(xb, ctypes.c_uint16),
+                                 codec.seed, codec.order, g, _p(xb, ctypes.c_uint16),
                                  _p(cont, ctypes.c_uint8), ctypes.byref(d))
     if st != 0:
         raise ValueError(f"oracle encode_detail failed: {st}")

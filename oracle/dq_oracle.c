@@ -132,6 +132,8 @@ typedef struct {
   uint32_t cum[DQO_MAX_LEVELS + 1];
   uint16_t recon[DQO_MAX_LEVELS]; /* fp16 bits */
   double mass[DQO_MAX_LEVELS];    /* true cell probability of each symbol */
+  int order;                      /* drift order: 0 magnitude, 1 rate-distortion */
+  float rd_w[DQO_MAX_LEVELS / 2]; /* rate-distortion weights, magnitude m >= 1 */
 } dqo_codec;
 
 static double normal_upper_tail(double t) { /* P(Z >= t), t >= 0 or inf */
@@ -200,6 +202,15 @@ int dqo_codec_init(dqo_codec *c, int levels, int step64, int C, int hkv,
   double bits = DQO_D * log2((double)DQO_M / c->freq[c->half]) + 0.0903;
   int bmax = (int)floor(bits / 8.0);
   if (4 + bmax > C) return DQO_EBUDGET;
+  /* rate-distortion weight of a move from magnitude m to m - 1: the level
+   * gap over the bits it saves, (l_m - l_{m-1}) / log2(f_{m-1} / f_m),
+   * evaluated in double and rounded once to fp32 */
+  for (int m = 1; m < c->half; m++) {
+    double lm = dqo_f64_from_f16(c->recon[c->half + m]);
+    double lm1 = dqo_f64_from_f16(c->recon[c->half + m - 1]);
+    double bits_saved = log2((double)c->freq[c->half + m - 1] / (double)c->freq[c->half + m]);
+    c->rd_w[m] = (float)((lm - lm1) / bits_saved);
+  }
   return DQO_OK;
 }
 
@@ -334,6 +345,34 @@ typedef struct {
  * first k candidates one level inward fits.  If even all of them do not fit,
  * all are moved and the search repeats on the new symbols (a multilevel
  * event; the codec check guarantees the all-innermost vector fits). */
+/* Rate-distortion drift order (the pages point to the
+ * rate-distortion toolbox of video coding [P1, So What]).  Moving |y| = a
+ * from magnitude m to m - 1 adds n (l_m - l_{m-1}) (2a - n (l_m + l_{m-1}))
+ * to the squared error (l = fp16 levels, n = stored norm); dropping the
+ * common factor n and dividing by the bits saved gives the key
+ *   key = (2a - n (l_m + l_{m-1})) * w_m,
+ * computed in fp32: n (l_m + l_{m-1}) is exact (11 x 12 significant bits),
+ * then one rounding for the difference and one for the product.
+ * Candidates are taken in ascending key, then ascending index. */
+static float rd_key(const dqo_codec *c, int m, float a, float nf) {
+  float lm = (float)dqo_f64_from_f16(c->recon[c->half + m]);
+  float lm1 = (float)dqo_f64_from_f16(c->recon[c->half + m - 1]);
+  float t = nf * (lm + lm1);
+  float u = 2.0f * a - t;
+  return u * c->rd_w[m];
+}
+
+/* Does candidate i come before candidate j in the codec's drift order? */
+static int drift_before(const dqo_codec *c, const uint8_t *mlev, const float *y,
+                        float nf, int i, int j) {
+  float ai = fabsf(y[i]), aj = fabsf(y[j]);
+  if (c->order == 1) {
+    float ki = rd_key(c, mlev[i], ai, nf), kj = rd_key(c, mlev[j], aj, nf);
+    return ki < kj || (ki == kj && i < j);
+  }
+  return mlev[i] > mlev[j] || (mlev[i] == mlev[j] && (ai < aj || (ai == aj && i < j)));
+}
+
 static void encode_vector(const dqo_codec *c, const uint16_t *xb, int g,
                           uint8_t *cont, dqo_vec_detail *d) {
   float x[DQO_D], y[DQO_D];
@@ -374,13 +413,8 @@ static void encode_vector(const dqo_codec *c, const uint16_t *xb, int g,
       if (mlev[i] >= 1) cand[n++] = i;
     for (int a = 0; a < n; a++) {
       int best = a;
-      for (int b = a + 1; b < n; b++) {
-        int i = cand[b], j = cand[best];
-        float ai = fabsf(y[i]), aj = fabsf(y[j]);
-        int before = mlev[i] > mlev[j] ||
-                     (mlev[i] == mlev[j] && (ai < aj || (ai == aj && i < j)));
-        if (before) best = b;
-      }
+      for (int b = a + 1; b < n; b++)
+        if (drift_before(c, mlev, y, (float)nf, cand[b], cand[best])) best = b;
       int t = cand[a]; cand[a] = cand[best]; cand[best] = t;
     }
     uint8_t trial[DQO_D];
@@ -428,13 +462,15 @@ static void encode_vector(const dqo_codec *c, const uint16_t *xb, int g,
 /* Batch encode of x[T][Hkv][128] (bf16 bits, element strides stride_t and
  * stride_h) into cont[Hkv][num_slots][C] and norm[Hkv][num_slots] at the
  * given slots.  Returns DQO_OK or a negative code. */
-int dqo_encode(int levels, int step64, int C, int hkv, uint64_t seed,
+int dqo_encode(int levels, int step64, int C, int hkv, uint64_t seed, int order,
                const uint16_t *x, int64_t T, int64_t stride_t, int64_t stride_h,
                const int64_t *slots, int64_t num_slots, uint8_t *cont,
                uint16_t *norm, uint64_t *stats, int nthreads) {
   dqo_codec c;
   int st = dqo_codec_init(&c, levels, step64, C, hkv, seed);
   if (st) return st;
+  if (order != 0 && order != 1) return DQO_EINVAL;
+  c.order = order;
   for (int64_t t = 0; t < T; t++)
     if (slots[t] < 0 || slots[t] >= num_slots) return DQO_EINVAL;
   uint64_t acc[DQO_NSTATS];
@@ -475,11 +511,13 @@ int dqo_encode(int levels, int step64, int C, int hkv, uint64_t seed,
 
 /* Single-vector encode with full detail (tests). */
 int dqo_encode_detail(int levels, int step64, int C, int hkv, uint64_t seed,
-                      int g, const uint16_t *xb, uint8_t *cont,
+                      int order, int g, const uint16_t *xb, uint8_t *cont,
                       dqo_vec_detail *d) {
   dqo_codec c;
   int st = dqo_codec_init(&c, levels, step64, C, hkv, seed);
   if (st) return st;
+  if (order != 0 && order != 1) return DQO_EINVAL;
+  c.order = order;
   if (g < 0 || g >= hkv) return DQO_EINVAL;
   encode_vector(&c, xb, g, cont, d);
   return DQO_OK;

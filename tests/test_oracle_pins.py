@@ -371,6 +371,78 @@ def test_drift_invariants(oracle_lib, levels, C):
     assert drifted > 0
 
 
+def _rd_cost_f64(t, h, nh, y, m):
+    """Added squared error per bit saved when |y| moves from magnitude m to
+    m - 1, from the definitions in float64: the two reconstructions n*l and
+    their squared errors, over log2 of the frequency ratio."""
+    lv = np.uint16(t["recon_f16"][h + m]).view(np.float16).astype(np.float64)
+    lv1 = np.uint16(t["recon_f16"][h + m - 1]).view(np.float16).astype(np.float64)
+    a = abs(float(y))
+    added = (a - nh * lv1) ** 2 - (a - nh * lv) ** 2
+    return added / math.log2(float(t["freq"][h + m - 1]) / float(t["freq"][h + m]))
+
+
+@pytest.mark.parametrize("levels,C", [(8, 34), (6, 34), (6, 29)])
+def test_rd_drift_order(oracle_lib, levels, C):
+    """Rate-distortion drift order: still one level inward, minimal k and a
+    fitting stream; the moved candidates are those with the least added
+    squared error per bit saved (ranked here from the definition in float64;
+    the fp32 key may order near-ties differently by rounding only)."""
+    O = oracle_lib
+    codec = O.Codec(levels, C, seed=3, hkv=1, order=1)
+    t = codec.tables()
+    h = levels // 2
+    rng = np.random.default_rng(levels * 3 + C)
+    drifted = 0
+    for xb in _vectors(rng, 96):
+        cont, d = O.encode_detail(codec, xb, 0)
+        s0 = np.array(d.sym0, np.int32)
+        s1 = np.array(d.sym, np.int32)
+        assert d.len <= C and (cont[d.len:] == 0).all()
+        dec, fs, _ = O.rans_decode(cont, C, t["freq"], t["cum"])
+        assert (dec == s1).all() and fs == 1 << 23
+        if d.len0 <= C or d.passes:
+            continue
+        drifted += 1
+        changed = set(np.nonzero(s0 != s1)[0].tolist())
+        for i in changed:
+            assert (s1[i] == s0[i] - 1) if s0[i] >= h else (s1[i] == s0[i] + 1)
+        nh = float(np.uint16(d.norm).view(np.float16))
+        mag = np.where(s0 >= h, s0 - h, h - 1 - s0)
+        cand = [i for i in range(D) if mag[i] >= 1]
+        cost = {i: _rd_cost_f64(t, h, nh, d.y[i], mag[i]) for i in cand}
+        worst_taken = max(cost[i] for i in changed)
+        best_left = min((cost[i] for i in cand if i not in changed), default=math.inf)
+        assert worst_taken <= best_left + 1e-6 * max(1.0, abs(best_left)), (worst_taken, best_left)
+        # minimal: without the most costly moved candidate the stream is too long
+        j = max(changed, key=lambda i: (cost[i], i))
+        prev = s1.copy()
+        prev[j] = s0[j]
+        assert len(O.rans_encode(prev.astype(np.uint8), t["freq"], t["cum"])) > C
+    assert drifted > 0
+
+
+def test_rd_drift_lowers_distortion(oracle_lib):
+    """At the same codec, taking the moves in rate-distortion order gives a
+    lower mean squared reconstruction error than magnitude order (N(0,1) and
+    outlier-channel data)."""
+    O = oracle_lib
+    for kind in ("iid", "outlier"):
+        x = synth.kv_tensor(kind, 1024, 2, seed=9)
+        xf = x.float().numpy().astype(np.float64)
+        for levels in (6, 8):
+            err = {}
+            for order in (0, 1):
+                codec = O.Codec(levels, 34, seed=4, hkv=2, order=order)
+                cont, norm, _ = O.encode(codec, x)
+                e = 0.0
+                for g in range(2):
+                    xh = O.dequant(codec, cont, norm, g, np.arange(1024))
+                    e += float(((xh - xf[:, g]) ** 2).sum())
+                err[order] = e
+            assert err[1] < err[0], (kind, levels, err)
+
+
 def test_degenerate_vectors(oracle_lib):
     O = oracle_lib
     codec = O.Codec(6, 34, seed=5, hkv=1)
