@@ -239,6 +239,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-pool attention timing")
+    ap.add_argument("--no-rd", action="store_true", help="skip the rate-distortion drift-order encode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter scale for rocprofv3)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -295,6 +296,31 @@ def main():
     drift_v = sv["drifted_symbols"] / (128.0 * sv["vectors"])
     log(f"[bench] prefill encode {2 * T_pre * Hkv} vectors in {prefill_ms:.2f} ms "
         f"({prefill_vps / 1e9:.2f} G vectors/s); drift K {drift_k:.3%} V {drift_v:.3%}")
+
+    # the same prompt with the rate-distortion drift order (separate pools)
+    rd = None
+    if not args.no_rd:
+        ck_rd = dq.Codec(w.levels_k, w.container_k, seed=w.seed, kv_heads=Hkv, drift_order=1)
+        cv_rd = dq.Codec(w.levels_v, w.container_v, seed=w.seed + 1, kv_heads=Hkv, drift_order=1)
+        rk_c, rk_n = dq.alloc_pool(ck_rd, S_total, dev)
+        rv_c, rv_n = dq.alloc_pool(cv_rd, S_total, dev)
+        srk, srv = dq.new_stats(dev), dq.new_stats(dev)
+        torch.cuda.synchronize()
+        e_a.record()
+        dq.encode(ck_rd, K, slots_pre, rk_c, rk_n, srk)
+        dq.encode(cv_rd, V, slots_pre, rv_c, rv_n, srv)
+        e_b.record()
+        torch.cuda.synchronize()
+        rd_ms = e_a.elapsed_time(e_b)
+        a_k, a_v = dq.stats_dict(srk), dq.stats_dict(srv)
+        rd = {"encode_vectors_per_s": round(2 * T_pre * Hkv / (rd_ms / 1e3), 1),
+              "drift_rate": {"k": round(a_k["drifted_symbols"] / (128.0 * a_k["vectors"]), 5),
+                             "v": round(a_v["drifted_symbols"] / (128.0 * a_v["vectors"]), 5)},
+              "kernel": "encode_wave_kernel"}
+        log(f"[bench] rate-distortion drift order: prefill encode {rd_ms:.1f} ms "
+            f"({rd['encode_vectors_per_s'] / 1e9:.3f} G vectors/s); drift K {rd['drift_rate']['k']:.3%} "
+            f"V {rd['drift_rate']['v']:.3%}")
+        del rk_c, rk_n, rv_c, rv_n
     del K, V
 
     if args.copy_calibration:
@@ -425,6 +451,7 @@ def main():
         "attn_call_ms": round(att_avg_ms, 4),
         "attn_call_gbps": round(alg_bytes / (att_avg_ms / 1e3) / 1e9, 2),
         "paged_attn": paged,
+        "rd_drift_order": rd,
         "cpu_baseline": cpu,
         "attn_context_tokens_per_s": round(ctx_tokens / (sum(att_ms) / 1e3), 1),
         "append_encode_ms": round(float(np.mean(enc_ms)), 4),

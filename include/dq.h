@@ -49,7 +49,7 @@ typedef void *dq_stream_t; /* hipStream_t */
 /* Human-readable text for a status code (static storage). */
 const char *dq_status_string(int status);
 
-/* ABI version: 100 * major + minor. */
+/* ABI version: 100 * major + minor (101: dq_codec_desc.drift_order). */
 int dq_version(void);
 
 /* ------------------------------------------------------------------------ */
@@ -74,8 +74,23 @@ typedef struct {
   uint64_t seed;           /* rotation seed                                  */
   int32_t step64;          /* cell width * 64, 1..1023; 0 = default for
                               (levels, C) where one exists, else DQ_ERR_INVALID */
-  int32_t reserved;        /* must be 0                                      */
+  int32_t drift_order;     /* 0: magnitude order (default); 1: rate-distortion
+                              order (below); else DQ_ERR_INVALID            */
 } dq_codec_desc;
+
+/* Drift order.  When a stream does not fit, candidates (symbols off the
+ * innermost pair) move one level inward, the first k of a fixed order with
+ * k minimal ("D-Quant: Entropy Coding Meets KV Cache at 2.26 Bits", Drift:
+ * Bending Variable Back to Fixed).
+ *   0  magnitude descending, then |y| ascending, then index ascending.
+ *   1  rate-distortion (the page's So What points to that toolbox): the key
+ *      (2|y| - n (l_m + l_{m-1})) * w_m ascending, then index ascending,
+ *      where l are the fp16 levels of magnitudes m and m - 1, n the stored
+ *      norm and w_m = (l_m - l_{m-1}) / log2(f_{m-1} / f_m) (double, rounded
+ *      once to fp32); the key is the added squared error per bit saved up to
+ *      the vector's common factor n, evaluated in fp32 with one rounding for
+ *      the difference and one for the product.  Lower distortion at the same
+ *      budget; every batch size runs the small-batch encode kernel. */
 
 /* Validates `desc`, builds the tables (host memory only) and returns a new
  * codec in *out.  DQ_ERR_BUDGET when a frequency would fall below 16, when

@@ -61,13 +61,14 @@ def _need_cuda(name, t, dtype=None):
 
 class Codec:
     """One coded stream (K or V): level count, container bytes, rotation
-    seed, kv heads and cell width (step64 / 64 sigma; 0 = default)."""
+    seed, kv heads, cell width (step64 / 64 sigma; 0 = default) and drift
+    order (0 magnitude, 1 rate-distortion)."""
 
     def __init__(self, levels: int, container_bytes: int, seed: int, kv_heads: int,
-                 step64: int = 0):
+                 step64: int = 0, drift_order: int = 0):
         L = _lib.lib()
         desc = _lib.CodecDesc(HEAD_DIM, levels, container_bytes, kv_heads,
-                              seed & (2**64 - 1), step64, 0)
+                              seed & (2**64 - 1), step64, drift_order)
         h = ctypes.c_void_p()
         _check(L.dq_codec_create(ctypes.byref(desc), ctypes.byref(h)), "dq_codec_create")
         self._h = h
@@ -78,6 +79,7 @@ class Codec:
         self.seed = info.seed
         self.kv_heads = info.num_kv_heads
         self.step64 = info.step64
+        self.drift_order = info.drift_order
 
     @property
     def handle(self):

@@ -12,7 +12,7 @@ class CodecDesc(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("levels", ctypes.c_int32),
                 ("container_bytes", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("seed", ctypes.c_uint64), ("step64", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("drift_order", ctypes.c_int32)]
 
 
 _handle = None

@@ -38,6 +38,13 @@ int default_step64(int levels, int C) {
 }
 
 // IEEE binary16 nearest to v (ties to even), from its binary64 value.
+// value of fp16 bits (finite levels only)
+double half_value(uint16_t b) {
+  const int e = (b >> 10) & 31, f = b & 1023;
+  const double v = e ? ldexp(1024.0 + f, e - 25) : ldexp((double)f, -24);
+  return (b & 0x8000) ? -v : v;
+}
+
 uint16_t half_bits(double v) {
   if (v != v) return 0x7E00;
   uint16_t sgn = v < 0 ? 0x8000 : 0;
@@ -110,7 +117,12 @@ int build_tables(const dq_codec_desc &d, Tables &t) {
     t.saving_fx[m] = t.cost_fx[h + m] - t.cost_fx[h + m - 1];
     // implied by the 1.15 ratio check; the encoder's drift relies on it
     if (t.saving_fx[m] <= kEpsHiFx + kEpsLoFx) return DQ_ERR_BUDGET;
+    // rate-distortion weight: level gap over the bits one move saves
+    const double lm = half_value(t.recon[h + m]), lm1 = half_value(t.recon[h + m - 1]);
+    const double bits = log2((double)t.freq[h + m - 1] / (double)t.freq[h + m]);
+    t.rd_w[m] = (float)((lm - lm1) / bits);
   }
+  t.order = d.drift_order;
   return DQ_OK;
 }
 
@@ -131,7 +143,7 @@ const char *dq_status_string(int status) {
   }
 }
 
-int dq_version(void) { return 100; }
+int dq_version(void) { return 101; }
 
 int dq_codec_create(const dq_codec_desc *desc, dq_codec_t *out) {
   if (!desc || !out) return DQ_ERR_INVALID;
@@ -141,7 +153,7 @@ int dq_codec_create(const dq_codec_desc *desc, dq_codec_t *out) {
   if (d.levels < 2 || d.levels > dq::kMaxLevels || (d.levels & 1)) return DQ_ERR_INVALID;
   if (d.container_bytes < 5 || d.container_bytes > dq::kMaxC) return DQ_ERR_INVALID;
   if (d.num_kv_heads < 1 || d.num_kv_heads > 1024) return DQ_ERR_INVALID;
-  if (d.reserved != 0) return DQ_ERR_INVALID;
+  if (d.drift_order != 0 && d.drift_order != 1) return DQ_ERR_INVALID;
   if (d.step64 == 0) d.step64 = dq::default_step64(d.levels, d.container_bytes);
   if (d.step64 < 1 || d.step64 > 1023) return DQ_ERR_INVALID;
   dq_codec *c = new (std::nothrow) dq_codec;

@@ -41,7 +41,7 @@ struct Tables {
   int32_t C;        // container bytes
   int32_t step64;   // cell width * 64
   int32_t hkv;      // kv heads
-  int32_t pad0;
+  int32_t order;    // drift order: 0 magnitude, 1 rate-distortion
   uint64_t seed;    // rotation seed
   uint16_t freq[kMaxLevels];
   uint16_t cum[kMaxLevels + 1];
@@ -53,6 +53,7 @@ struct Tables {
   uint8_t shift[kMaxLevels];
   uint32_t cost_fx[kMaxLevels];        // log2(4096 / f) * 2^20, rounded
   uint32_t saving_fx[kMaxHalf];        // cost_fx[h + m] - cost_fx[h + m - 1], magnitude m >= 1
+  float rd_w[kMaxHalf];                // rate-distortion weight of a move from magnitude m
 };
 
 }  // namespace dq

@@ -470,22 +470,29 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
 //    length never increases along the order, so every lower lane failed).
 constexpr int kWaveVecs = 4;  // vectors (waves) per block
 
+template <bool RD>  // drift order: rate-distortion (true) or magnitude (false)
 __global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kernel(EncodeArgs a, Tables t) {
   __shared__ uint4 etab[kMaxLevels];
   __shared__ uint32_t ent[kWaveVecs][kD];          // s0 | sd << 8 | rank << 16
   __shared__ float yabs[kWaveVecs][kD];
   __shared__ uint8_t mag[kWaveVecs][kD];
   __shared__ uint8_t scr[kWaveVecs][kScr * 64];   // renorm bytes, lane-minor
+  __shared__ float2 rdtab[kMaxHalf];              // {l_m + l_{m-1}, w_m} for the rate-distortion key
+  __shared__ uint32_t bstat[6 + kMaxC + 1];       // per-block stats, flushed once
   const int tid = threadIdx.x;
+  for (int k = tid; k < 6 + kMaxC + 1; k += 64 * kWaveVecs) bstat[k] = 0u;
   if (tid < t.levels) {
     const uint32_t f = t.freq[tid];
     etab[tid] = make_uint4(f << 19, t.magic[tid], t.cum[tid], (kM - f) | ((uint32_t)t.shift[tid] << 16));
   }
+  if (tid >= 1 && tid < t.half)
+    rdtab[tid] = make_float2(half_to_float(t.recon[t.half + tid]) + half_to_float(t.recon[t.half + tid - 1]),
+                             t.rd_w[tid]);
   __syncthreads();
   const int w = tid >> 6, lane = tid & 63;
   const int64_t nvec = a.T * (int64_t)t.hkv;
   const int64_t vid = (int64_t)blockIdx.x * kWaveVecs + w;
-  if (vid >= nvec) return;  // whole wave exits together
+  if (vid < nvec) {  // whole waves; every wave reaches the block barrier below
   const int h = t.half, C = t.C;
   const int g = (int)(vid / a.T);
   const int64_t tok = vid - (int64_t)g * a.T;
@@ -552,11 +559,26 @@ __global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kernel(EncodeArgs 
   uint32_t okx = 0;
   int win = -1;
   for (int outer = 0; outer < 2 * kD && win < 0; ++outer) {
-    // ranks of the candidates (magnitude >= 1) in drift order
+    // ranks of the candidates (magnitude >= 1) in drift order.  Magnitude
+    // order compares (m desc, |y| asc); rate-distortion order compares its
+    // key (2|y| - n (l_m + l_{m-1})) * w_m ascending, n (l_m + l_{m-1})
+    // being exact in fp32.  Both then break ties by index.
+    constexpr bool rd = RD;
+    float kA[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float key = yA[e];
+      if (rd && mA[e] >= 1u) {
+        const float2 r = rdtab[mA[e]];
+        const float tt = nf * r.x;
+        key = (2.0f * yA[e] - tt) * r.y;
+      }
+      kA[e] = key;
+    }
     Mg[lane] = (uint8_t)mA[0];
     Mg[lane + 64] = (uint8_t)mA[1];
-    Y[lane] = yA[0];
-    Y[lane + 64] = yA[1];
+    Y[lane] = kA[0];
+    Y[lane + 64] = kA[1];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -567,7 +589,8 @@ __global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kernel(EncodeArgs 
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int i = lane + 64 * e;
-        const bool before = mj >= 1u && (mj > mA[e] || (mj == mA[e] && (yj < yA[e] || (yj == yA[e] && j < i))));
+        const bool tie_first = yj < kA[e] || (yj == kA[e] && j < i);
+        const bool before = mj >= 1u && (rd ? tie_first : (mj > mA[e] || (mj == mA[e] && tie_first)));
         rank[e] += before ? 1 : 0;
       }
     }
@@ -637,16 +660,22 @@ __global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kernel(EncodeArgs 
     if (lane == 0) a.norm[(int64_t)g * a.num_slots + slot] = (uint16_t)nh;
   }
   if (a.stats && lane == 0) {
-    unsigned long long *gs = reinterpret_cast<unsigned long long *>(a.stats);
-    atomicAdd(gs + 0, 1ull);
+    atomicAdd(&bstat[0], 1u);
     if (moves) {
-      atomicAdd(gs + 1, 1ull);
-      atomicAdd(gs + 2, (unsigned long long)moves);
+      atomicAdd(&bstat[1], 1u);
+      atomicAdd(&bstat[2], (uint32_t)moves);
     }
-    if (passes) atomicAdd(gs + 3, (unsigned long long)passes);
-    if (bad) atomicAdd(gs + 4, 1ull);
-    if (zero) atomicAdd(gs + 5, 1ull);
-    atomicAdd(gs + 6 + 4 + okB, 1ull);
+    if (passes) atomicAdd(&bstat[3], (uint32_t)passes);
+    if (bad) atomicAdd(&bstat[4], 1u);
+    if (zero) atomicAdd(&bstat[5], 1u);
+    atomicAdd(&bstat[6 + 4 + okB], 1u);
+  }
+  }
+  if (a.stats) {
+    __syncthreads();
+    unsigned long long *gs = reinterpret_cast<unsigned long long *>(a.stats);
+    for (int q = tid; q < 6 + kMaxC + 1; q += 64 * kWaveVecs)
+      if (bstat[q]) atomicAdd(gs + q, (unsigned long long)bstat[q]);
   }
 }
 
@@ -684,10 +713,15 @@ extern "C" int dq_encode(dq_codec_t codec, const void *x, int64_t T, int64_t str
   int64_t wave_max = dq::kWavePathMax;
   if (const char *ev = getenv("DQ_ENCODE_WAVE_MAX")) wave_max = atoll(ev);
   hipError_t e;
-  if (T * (int64_t)t.hkv <= wave_max && T * (int64_t)t.hkv <= ((int64_t)1 << 30)) {
+  // the rate-distortion order interleaves magnitude groups, which the
+  // large-batch kernel's drift plan assumes it does not: it always takes
+  // the wave-per-vector kernel
+  if (t.order == 1 && T * (int64_t)t.hkv > ((int64_t)1 << 30)) return DQ_ERR_UNSUPPORTED;
+  if ((t.order == 1 || T * (int64_t)t.hkv <= wave_max) && T * (int64_t)t.hkv <= ((int64_t)1 << 30)) {
     const int64_t nvec = T * (int64_t)t.hkv;
-    hipLaunchKernelGGL(dq::encode_wave_kernel, dim3((unsigned)((nvec + dq::kWaveVecs - 1) / dq::kWaveVecs)),
-                       dim3(64 * dq::kWaveVecs), 0, s, a, t);
+    const dim3 grid((unsigned)((nvec + dq::kWaveVecs - 1) / dq::kWaveVecs)), block(64 * dq::kWaveVecs);
+    if (t.order == 1) hipLaunchKernelGGL(dq::encode_wave_kernel<true>, grid, block, 0, s, a, t);
+    else hipLaunchKernelGGL(dq::encode_wave_kernel<false>, grid, block, 0, s, a, t);
     e = hipGetLastError();
   } else {
     e = t.half <= 4 ? dq::launch<4>(a, t, s) : dq::launch<8>(a, t, s);

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     L = _lib.lib()
-    assert L.dq_version() == 100
+    assert L.dq_version() == 101
     assert L.dq_status_string(0) == b"ok"
     for code in (-1, -2, -3, -4, -5):
         assert L.dq_status_string(code) not in (b"ok", b"unknown status")
@@ -99,7 +99,7 @@ def test_invalid_descriptors():
         (_lib.CodecDesc(128, 8, 4, 1, 0, 73, 0), -1),    # container too small
         (_lib.CodecDesc(128, 8, 133, 1, 0, 73, 0), -1),  # container too large
         (_lib.CodecDesc(128, 8, 34, 0, 0, 0, 0), -1),    # no kv heads
-        (_lib.CodecDesc(128, 8, 34, 1, 0, 0, 7), -1),    # reserved != 0
+        (_lib.CodecDesc(128, 8, 34, 1, 0, 0, 7), -1),    # drift order not 0 or 1
         (_lib.CodecDesc(128, 8, 40, 1, 0, 0, 0), -1),    # no default width
         (_lib.CodecDesc(128, 8, 34, 1, 0, 2000, 0), -1),  # width out of range
         (_lib.CodecDesc(128, 8, 29, 1, 0, 84, 0), -3),   # outer cells too close
@@ -161,3 +161,11 @@ def test_paged_attention_argument_checks():
     short = list(base)
     short[13] = 129  # max_len > max_pages * 64
     assert L.dq_attn_decode_paged(*short) == -1
+
+
+def test_drift_order_codec():
+    c = dq.Codec(6, 34, seed=1, kv_heads=2, drift_order=1)
+    assert c.drift_order == 1
+    assert dq.Codec(6, 34, seed=1, kv_heads=2).drift_order == 0
+    with pytest.raises(dq.DQError):
+        dq.Codec(6, 34, seed=1, kv_heads=2, drift_order=2)

@@ -29,9 +29,9 @@ def _np_bits(t):
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def _codecs(O, levels, C, seed, hkv, step64=0):
-    g = dq.Codec(levels, C, seed=seed, kv_heads=hkv, step64=step64)
-    o = O.Codec(levels, C, seed=seed, hkv=hkv, step64=g.step64)
+def _codecs(O, levels, C, seed, hkv, step64=0, order=0):
+    g = dq.Codec(levels, C, seed=seed, kv_heads=hkv, step64=step64, drift_order=order)
+    o = O.Codec(levels, C, seed=seed, hkv=hkv, step64=g.step64, order=order)
     return g, o
 
 
@@ -118,6 +118,26 @@ def test_encode_adversarial(oracle_lib, encode_path, levels, C, step64):
     gc, oc = _codecs(O, levels, C, seed=5, hkv=1, step64=step64)
     slots = torch.arange(x.shape[0], dtype=torch.int64, device=DEV)
     _assert_encode_equal(*_encode_both(O, gc, oc, x, slots, x.shape[0]), "adversarial")
+
+
+@pytest.mark.parametrize("levels,C,step64", [(8, 34, 0), (6, 34, 0), (8, 29, 0), (6, 29, 0),
+                                             (4, 30, 64), (10, 40, 34)])
+def test_encode_rate_distortion_order(oracle_lib, levels, C, step64):
+    """Rate-distortion drift order: containers, norms and stats bit-exact on
+    the four distributions and on the adversarial rows (ties, degenerate
+    norms, one-hot vectors)."""
+    O = oracle_lib
+    _say(f"rd order {levels}/{C}/{step64}")
+    gc, oc = _codecs(O, levels, C, seed=33 + levels, hkv=3, step64=step64, order=1)
+    for kind in ("iid", "outlier", "student_t5", "iid_scaled"):
+        x = synth.kv_tensor(kind, 200, 3, seed=71, device=DEV)
+        slots = torch.arange(200, dtype=torch.int64, device=DEV)
+        _assert_encode_equal(*_encode_both(O, gc, oc, x, slots, 200), f"rd {levels}/{C} {kind}")
+    rows = _adversarial_batch()
+    x = torch.from_numpy(rows).to(torch.bfloat16).reshape(-1, 1, 128).to(DEV)
+    gc1, oc1 = _codecs(O, levels, C, seed=5, hkv=1, step64=step64, order=1)
+    slots = torch.arange(x.shape[0], dtype=torch.int64, device=DEV)
+    _assert_encode_equal(*_encode_both(O, gc1, oc1, x, slots, x.shape[0]), f"rd adversarial {levels}/{C}")
 
 
 def test_encode_strided_input_and_pool_slots(oracle_lib, encode_path):
