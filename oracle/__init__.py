@@ -94,6 +94,9 @@ def lib():
         L.dqo_attention.argtypes = [CodecArgs, CodecArgs, c_int, u16p, c_int, c_int,
                                     u8p, u16p, u8p, u16p, c_i64, i64p, i32p,
                                     ctypes.c_double, f64p, c_int]
+        L.dqo_attention_prefill.argtypes = [CodecArgs, CodecArgs, c_int, u16p, c_int, c_int, c_int,
+                                            u8p, u16p, u8p, u16p, c_i64, i64p, i32p,
+                                            ctypes.c_double, f64p, c_int]
         L.dqo_attention_paged.argtypes = [CodecArgs, CodecArgs, c_int, u16p, c_int, c_int,
                                           u8p, u16p, u8p, u16p, c_i64, i32p, c_int, i32p,
                                           ctypes.c_double, f64p, c_int]
@@ -352,3 +355,32 @@ def attention_paged(ck: Codec, cv: Codec, q, k_cont, k_norm, v_cont, v_norm, pag
 
 def max_threads() -> int:
     return int(lib().dqo_max_threads())
+
+
+def attention_prefill(ck: Codec, cv: Codec, q, k_cont, k_norm, v_cont, v_norm, seq_start,
+                      seq_len, sm_scale: float | None = None, nthreads: int = 0):
+    """fp64 causal chunked-prefill attention: q bf16 [B, Tq, Hq, 128]; the
+    last Tq cached tokens of each sequence are the queries (query j at
+    position seq_len - Tq + j attends to tokens 0..that position).
+    Returns float64 [B, Tq, Hq, 128]."""
+    qb = np.ascontiguousarray(_u16(q))
+    B, Tq, Hq, d = qb.shape
+    assert d == D
+    kc = np.ascontiguousarray(k_cont, np.uint8)
+    vc = np.ascontiguousarray(v_cont, np.uint8)
+    kn = np.ascontiguousarray(_u16(k_norm))
+    vn = np.ascontiguousarray(_u16(v_norm))
+    H, S, _ = kc.shape
+    ss = np.ascontiguousarray(seq_start, np.int64)
+    sl = np.ascontiguousarray(seq_len, np.int32)
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    out = np.zeros((B, Tq, Hq, D), np.float64)
+    st = lib().dqo_attention_prefill(ck.args(), cv.args(), H, _p(qb, ctypes.c_uint16), B, Tq, Hq,
+                                     _p(kc, ctypes.c_uint8), _p(kn, ctypes.c_uint16),
+                                     _p(vc, ctypes.c_uint8), _p(vn, ctypes.c_uint16), S,
+                                     _p(ss, ctypes.c_int64), _p(sl, ctypes.c_int32),
+                                     float(sm_scale), _p(out, ctypes.c_double), nthreads)
+    if st != 0:
+        raise ValueError(f"oracle prefill attention failed: {st}")
+    return out

@@ -687,6 +687,78 @@ int dqo_attention(dqo_codec_args ka, dqo_codec_args va, int hkv,
                         seq_len, sm_scale, out, nthreads);
 }
 
+/* Chunked-prefill attention over the compressed cache (the
+ * pages' serving figures include an 8K prompt [P1, The Numbers]).
+ * Reading: a chunk of Tq new tokens has already been encoded at the end of
+ * each sequence, so the sequence holds seq_len[b] tokens of which the last
+ * Tq are the chunk; query j of sequence b sits at position
+ * p = seq_len[b] - Tq + j and attends causally to tokens 0..p, all of
+ * them read from their containers.
+ * q: bf16 [B][Tq][Hq][128]; out: [B][Tq][Hq][128]. */
+int dqo_attention_prefill(dqo_codec_args ka, dqo_codec_args va, int hkv,
+                          const uint16_t *q, int B, int Tq, int Hq,
+                          const uint8_t *kc, const uint16_t *kn,
+                          const uint8_t *vc, const uint16_t *vn,
+                          int64_t num_slots, const int64_t *seq_start,
+                          const int32_t *seq_len, double sm_scale, double *out,
+                          int nthreads) {
+  dqo_codec ck, cv;
+  int st = dqo_codec_init(&ck, ka.levels, ka.step64, ka.C, hkv, ka.seed);
+  if (st) return st;
+  st = dqo_codec_init(&cv, va.levels, va.step64, va.C, hkv, va.seed);
+  if (st) return st;
+  if (B < 0 || Tq < 1 || Hq < 1 || Hq % hkv) return DQO_EINVAL;
+  for (int b = 0; b < B; b++)
+    if (seq_len[b] < Tq || seq_start[b] < 0 || seq_start[b] + seq_len[b] > num_slots)
+      return DQO_EINVAL;
+  int group = Hq / hkv;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bg = 0; bg < (int64_t)B * hkv; bg++) {
+    int b = (int)(bg / hkv), g = (int)(bg % hkv);
+    int64_t L = seq_len[b];
+    double *kh = malloc(sizeof(double) * (size_t)L * DQO_D);
+    double *vh = malloc(sizeof(double) * (size_t)L * DQO_D);
+    double *sc = malloc(sizeof(double) * (size_t)L);
+    for (int64_t t = 0; t < L; t++) {
+      int64_t idx = (int64_t)g * num_slots + seq_start[b] + t;
+      dequant_vector(&ck, kc + idx * ck.C, kn[idx], g, kh + t * DQO_D);
+      dequant_vector(&cv, vc + idx * cv.C, vn[idx], g, vh + t * DQO_D);
+    }
+    for (int j = 0; j < Tq; j++) {
+      int64_t pos = L - Tq + j; /* keys 0..pos */
+      for (int hh = 0; hh < group; hh++) {
+        int h = g * group + hh;
+        const uint16_t *qp = q + (((int64_t)b * Tq + j) * Hq + h) * DQO_D;
+        double qv[DQO_D];
+        for (int i = 0; i < DQO_D; i++) qv[i] = (double)f32_from_bf16(qp[i]);
+        double mx = -INFINITY;
+        for (int64_t t = 0; t <= pos; t++) {
+          double a = 0.0;
+          for (int i = 0; i < DQO_D; i++) a += qv[i] * kh[t * DQO_D + i];
+          sc[t] = sm_scale * a;
+          if (sc[t] > mx) mx = sc[t];
+        }
+        double den = 0.0, o[DQO_D];
+        for (int i = 0; i < DQO_D; i++) o[i] = 0.0;
+        for (int64_t t = 0; t <= pos; t++) {
+          double p = exp(sc[t] - mx);
+          den += p;
+          for (int i = 0; i < DQO_D; i++) o[i] += p * vh[t * DQO_D + i];
+        }
+        double *op = out + (((int64_t)b * Tq + j) * Hq + h) * DQO_D;
+        for (int i = 0; i < DQO_D; i++) op[i] = o[i] / den;
+      }
+    }
+    free(kh);
+    free(vh);
+    free(sc);
+  }
+  return DQO_OK;
+}
+
 /* The same attention over a paged pool: token t of sequence b is in slot
  * pages[b * max_pages + t / 64] * 64 + t % 64. */
 int dqo_attention_paged(dqo_codec_args ka, dqo_codec_args va, int hkv,

@@ -600,6 +600,48 @@ def test_paged_attention_equals_contiguous(oracle_lib):
         O.attention_paged(ck, cv, q, kc2, kn2, vc2, vn2, bad, lens)
 
 
+def test_prefill_attention_pins(oracle_lib):
+    """Chunked-prefill attention: query j of a Tq-token chunk equals decode
+    attention over the first L - Tq + j + 1 tokens (causality and the
+    decode case in one), matches brute-force loops on a tiny case, and is
+    unchanged by the containers after its position."""
+    O = oracle_lib
+    hkv, Hq, Tq = 2, 8, 5
+    lens = np.array([9, 70, 5], np.int32)
+    ck = O.Codec(8, 34, seed=31, hkv=hkv)
+    cv = O.Codec(6, 34, seed=32, hkv=hkv)
+    starts = np.array([0, 20, 100], np.int64)
+    S = 110
+    K = synth.kv_tensor("outlier", S, hkv, seed=33)
+    V = synth.kv_tensor("iid_scaled", S, hkv, seed=34)
+    kc, kn, _ = O.encode(ck, K)
+    vc, vn, _ = O.encode(cv, V)
+    q = synth.q_tensor(len(lens) * Tq, Hq, seed=35).reshape(len(lens), Tq, Hq, D)
+    out = O.attention_prefill(ck, cv, q, kc, kn, vc, vn, starts, lens)
+    for j in range(Tq):
+        dec = O.attention(ck, cv, q[:, j].contiguous(), kc, kn, vc, vn, starts, lens - Tq + j + 1)
+        assert np.array_equal(out[:, j], dec)
+    # brute force for sequence 0, query 2, head 3
+    b, j, h = 0, 2, 3
+    pos = int(lens[b]) - Tq + j
+    g = h // (Hq // hkv)
+    slots = np.arange(starts[b], starts[b] + pos + 1)
+    kh = O.dequant(ck, kc, kn, g, slots)
+    vh = O.dequant(cv, vc, vn, g, slots)
+    qv = q[b, j, h].float().numpy().astype(np.float64)
+    sc = kh @ qv / math.sqrt(D)
+    w = np.exp(sc - sc.max())
+    assert np.allclose(out[b, j, h], (w[:, None] * vh).sum(0) / w.sum(), rtol=0, atol=1e-12)
+    # causality: scrambling every container after the first query's position
+    kc2, vc2 = kc.copy(), vc.copy()
+    p0 = int(starts[1]) + int(lens[1]) - Tq
+    kc2[:, p0 + 1:int(starts[1]) + int(lens[1])] ^= 0x5A
+    vc2[:, p0 + 1:int(starts[1]) + int(lens[1])] ^= 0xA5
+    out2 = O.attention_prefill(ck, cv, q, kc2, kn, vc2, vn, starts, lens)
+    assert np.array_equal(out2[1, 0], out[1, 0])
+    assert not np.array_equal(out2[1, Tq - 1], out[1, Tq - 1])
+
+
 def test_attention_brute_force_loops(oracle_lib):
     O = oracle_lib
     ck, cv, q, kc, kn, vc, vn, starts, lens = _tiny_attention_case(O)
