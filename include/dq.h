@@ -186,6 +186,31 @@ int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B,
                    int32_t out_dtype, void *out, void *workspace,
                    size_t ws_bytes, dq_stream_t stream);
 
+/* Chunked-prefill attention over the compressed cache.  A chunk of Tq new
+ * tokens per sequence has been encoded with dq_encode at the end of the
+ * sequence's slots, so seq_len[b] counts it; query j of sequence b sits at
+ * position seq_len[b] - Tq + j and attends causally to tokens 0..that
+ * position, all read from their containers ("D-Quant: Entropy Coding Meets
+ * KV Cache at 2.26 Bits", The Numbers: served with an 8K prompt).
+ *   q          bf16 [B][Tq][Hq][128], contiguous
+ *   out        [B][Tq][Hq][128], fp32 (out_dtype 0) or bf16 (1)
+ *   seq_len    device int32 [B], each >= Tq (a query with a negative
+ *              position gets a zero output row) and <= max_len
+ *   max_len    host value >= Tq; plans the context split
+ *   workspace  >= dq_attn_prefill_workspace(B, Tq, Hq, Hkv, max_len) bytes,
+ *              256-byte aligned
+ * Pools, codecs, sm_scale and error codes as for dq_attn_decode. */
+int dq_attn_prefill_workspace(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
+                              int64_t max_len, size_t *bytes);
+int dq_attn_prefill(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B,
+                    int32_t Tq, int32_t Hq, const uint8_t *k_cont,
+                    const uint16_t *k_norm, const uint8_t *v_cont,
+                    const uint16_t *v_norm, int64_t num_slots,
+                    const int64_t *seq_start, const int32_t *seq_len,
+                    int64_t max_len, float sm_scale, int32_t out_dtype,
+                    void *out, void *workspace, size_t ws_bytes,
+                    dq_stream_t stream);
+
 /* Paged pool: the same attention, with each sequence's cache split into
  * pages of DQ_PAGE_TOKENS consecutive slots anywhere in the pool (a block
  * table, so sequences can grow without contiguous reservations).  Token t

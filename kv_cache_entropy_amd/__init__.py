@@ -27,6 +27,7 @@ PAGE_TOKENS = 64
 NSTATS = 6 + MAX_CONTAINER + 1
 
 __all__ = ["Codec", "alloc_pool", "encode", "decode_symbols", "attn_decode", "attn_decode_paged",
+           "attn_prefill", "attn_prefill_workspace_bytes",
            "attn_workspace_bytes", "new_stats", "stats_dict", "DQError", "library_path"]
 
 
@@ -267,4 +268,48 @@ def attn_decode_paged(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_c
         _ptr(v_norm), k_cont.shape[1], _ptr(pages), pages.shape[1], _ptr(seq_len), max_len,
         ctypes.c_float(sm_scale), 0 if out_dtype == torch.float32 else 1, _ptr(out),
         _ptr(workspace), workspace.numel(), _stream(q.device)), "dq_attn_decode_paged")
+    return out
+
+
+def attn_prefill_workspace_bytes(B: int, Tq: int, Hq: int, Hkv: int, max_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.lib().dq_attn_prefill_workspace(B, Tq, Hq, Hkv, max_len, ctypes.byref(n)),
+           "dq_attn_prefill_workspace")
+    return n.value
+
+
+def attn_prefill(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_cont, v_norm,
+                 seq_start: torch.Tensor, seq_len: torch.Tensor, max_len: int,
+                 sm_scale: float | None = None, out: torch.Tensor | None = None,
+                 out_dtype=torch.float32, workspace: torch.Tensor | None = None):
+    """Causal chunked-prefill attention: q bf16 [B, Tq, Hq, 128]; the last Tq
+    cached tokens of each sequence are the queries.  Returns [B, Tq, Hq, 128]."""
+    _need_cuda("q", q, torch.bfloat16)
+    for name, t, dt in (("k_cont", k_cont, torch.uint8), ("v_cont", v_cont, torch.uint8),
+                        ("k_norm", k_norm, torch.float16), ("v_norm", v_norm, torch.float16),
+                        ("seq_start", seq_start, torch.int64), ("seq_len", seq_len, torch.int32)):
+        _need_cuda(name, t, dt)
+        if not t.is_contiguous():
+            raise DQError(f"{name} must be contiguous")
+    if q.dim() != 4 or q.shape[3] != HEAD_DIM or not q.is_contiguous():
+        raise DQError("q must be a contiguous bf16 [B, Tq, Hq, 128]")
+    B, Tq, Hq, _ = q.shape
+    if k_cont.shape[1] != v_cont.shape[1]:
+        raise DQError("K and V pools must have the same slot count")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise DQError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((B, Tq, Hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, Tq, Hq, HEAD_DIM) or not out.is_contiguous():
+        raise DQError("out has the wrong shape or dtype")
+    need = attn_prefill_workspace_bytes(B, Tq, Hq, ck.kv_heads, max_len)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if sm_scale is None:
+        sm_scale = HEAD_DIM ** -0.5
+    _check(_lib.lib().dq_attn_prefill(
+        ck.handle, cv.handle, _ptr(q), B, Tq, Hq, _ptr(k_cont), _ptr(k_norm), _ptr(v_cont),
+        _ptr(v_norm), k_cont.shape[1], _ptr(seq_start), _ptr(seq_len), max_len,
+        ctypes.c_float(sm_scale), 0 if out_dtype == torch.float32 else 1, _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(q.device)), "dq_attn_prefill")
     return out

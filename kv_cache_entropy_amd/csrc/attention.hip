@@ -64,6 +64,7 @@ struct AttnArgs {
   void *out;
   int out_bf16;
   int waves_per_block;
+  int Tq, tb, nqb;  // prefill: query tokens, tokens per 16-row block, blocks per sequence
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -508,6 +509,390 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
   }
 }
 
+// ---------------------------------------------------------------- prefill
+// Chunked prefill: the last Tq cached tokens of each sequence are queries;
+// query j (position L - Tq + j) attends causally to tokens 0..its position.
+// An item is (sequence, kv head, block of tb = 16 / group query tokens,
+// context chunk): every decoded tile serves 16 query rows (row r = token
+// r / group of the block, head r % group of the kv group).
+//  - QK: as in decode, each lane decodes one token and its 4 levels per
+//    step are the B column of 4x4x4 MFMAs; the four row groups' query
+//    operands (fp16 hi/lo) sit in lanes 0..3 and are broadcast (cbsz 4).
+//  - softmax per row with the causal mask; P (hi/lo) to LDS as
+//    [row][token quad][hi x4, lo x4].
+//  - PV: 16x16x16 MFMAs of P (16 rows x 16 tokens) with the transposed V
+//    tile (16 tokens x 16 dims); lane l ends with rows 4 (l / 16) + i of
+//    dim 16 db + l % 16.
+constexpr int kRows = 16;
+constexpr int kQrotPrefill = 32 * 4 * 4 * 8;  // halves per (b, g, block): [dim quad][lane][row group][hi4 lo4]
+
+typedef float floatx4v __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(64) rotate_qp_kernel(AttnArgs a, uint64_t kseed) {
+  const int lane = threadIdx.x;
+  // block = ((b * nqb + qb) * tb + tl) * Hq + h
+  int64_t blk = blockIdx.x;
+  const int h = (int)(blk % a.Hq);
+  blk /= a.Hq;
+  const int tl = (int)(blk % a.tb);
+  blk /= a.tb;
+  const int qb = (int)(blk % a.nqb);
+  const int b = (int)(blk / a.nqb);
+  const int g = h / a.group, hh = h - g * a.group;
+  const int tq = qb * a.tb + tl;
+  const int r = tl * a.group + hh, i = r & 3, rg = r >> 2;
+  uint16_t *dst = a.qrot + (((int64_t)b * a.Hkv + g) * a.nqb + qb) * kQrotPrefill;
+  const int d0 = lane, d1 = lane + 64;
+  auto at = [&](int d) { return ((((d >> 2) * 4 + i) * 4 + rg) * 8) + (d & 3); };
+  if (tq >= a.Tq) {
+    dst[at(d0)] = 0; dst[at(d0) + 4] = 0; dst[at(d1)] = 0; dst[at(d1) + 4] = 0;
+    return;
+  }
+  const uint16_t *qp = a.q + (((int64_t)b * a.Tq + tq) * a.Hq + h) * kD;
+  const uint64_t w0 = dev_splitmix64(kseed, 2ull * (uint64_t)g);
+  const uint64_t w1 = dev_splitmix64(kseed, 2ull * (uint64_t)g + 1ull);
+  float v0 = __uint_as_float((uint32_t)qp[d0] << 16);
+  float v1 = __uint_as_float((uint32_t)qp[d1] << 16);
+  if ((w0 >> lane) & 1ull) v0 = -v0;
+  if ((w1 >> lane) & 1ull) v1 = -v1;
+  float t0 = v0 + v1, t1 = v0 - v1;
+  v0 = t0;
+  v1 = t1;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const float p0 = __shfl_xor(v0, w), p1 = __shfl_xor(v1, w);
+    const bool hi = lane & w;
+    v0 = hi ? p0 - v0 : v0 + p0;
+    v1 = hi ? p1 - v1 : v1 + p1;
+  }
+  const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+  const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
+  dst[at(d0)] = __builtin_bit_cast(uint16_t, h0);
+  dst[at(d0) + 4] = __builtin_bit_cast(uint16_t, l0);
+  dst[at(d1)] = __builtin_bit_cast(uint16_t, h1);
+  dst[at(d1) + 4] = __builtin_bit_cast(uint16_t, l1);
+}
+
+__host__ __device__ inline WaveLayout prefill_layout(int Ck, int Cv) {
+  WaveLayout w;
+  w.kst = 0;
+  w.vst = w.kst + ((kTile * Ck + 31) & ~15);
+  w.pl = w.vst + ((kTile * Cv + 31) & ~15);
+  w.vt = w.pl + kRows * kTile * 2 * 2;  // P: [16 rows][16 quads][hi4 lo4]
+  w.bytes = w.vt + kPass * kVtStride * 2;
+  w.bytes = (w.bytes + 15) & ~15;
+  return w;
+}
+
+template <bool DK, bool DV>
+__device__ __forceinline__ void prefill_tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
+                                                  const uint8_t *vb, const uint4 *qg, const uint16_t *pl,
+                                                  uint16_t *vt, floatx4 (&sc)[4], floatx4 (&acc)[8], int lane) {
+  const bool qlane = lane < 4;
+  uint4 qn[4] = {};
+  if (DK && qlane) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) qn[rg] = qg[lane * 4 + rg];
+  }
+  uint32_t xk = 0, xv = 0;
+  const uint8_t *pk = kb, *pv = vb;
+  if (DK) {
+    xk = load_le32(kb);
+    pk = kb + 4;
+  }
+  if (DV) {
+    xv = load_le32(vb);
+    pv = vb + 4;
+  }
+  uint16_t *col = vt + lane;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    for (int gq = 0; gq < kPass / 4; ++gq) {
+      const int gnext = p * (kPass / 4) + gq + 1;
+      uint32_t lv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t bk = 0, bv = 0;
+        if (DK) bk = next_byte(pk);
+        if (DV) bv = next_byte(pv);
+        if (DK) {
+          uint32_t sy;
+          const uint2 e = rans_step(xk, tk.sym8, tk.symtab, sy);
+          renorm(xk, pk, bk);
+          lv[j] = e.y;
+        }
+        if (DV) {
+          uint32_t sy;
+          const uint2 e = rans_step(xv, tv.sym8, tv.symtab, sy);
+          renorm(xv, pv, bv);
+          col[(gq * 4 + j) * kVtStride] = (uint16_t)(e.y >> 16);
+        }
+      }
+      if (DK) {
+        const uint32_t b01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
+        const uint32_t b23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
+        const half4 Bk = __builtin_bit_cast(half4, make_uint2(b01, b23));
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          sc[rg] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(qn[rg].x, qn[rg].y)), Bk,
+                                                      sc[rg], 4, 0, 0);
+          sc[rg] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(qn[rg].z, qn[rg].w)), Bk,
+                                                      sc[rg], 4, 0, 0);
+        }
+        // next dim group's query operands, in flight during its decode
+        if (qlane && gnext < 32) {
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) qn[rg] = qg[(gnext * 4 + lane) * 4 + rg];
+        }
+      }
+    }
+    if (DV) {
+      wave_sync();
+      const int m = lane & 15, kq = lane >> 4;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        // P rows x tokens 16 kc .. 16 kc + 15: this lane's row m, tokens 4 kq .. 4 kq + 3
+        const uint4 pp = *reinterpret_cast<const uint4 *>(pl + (m * 16 + kc * 4 + kq) * 8);
+        const half4 Ph = __builtin_bit_cast(half4, make_uint2(pp.x, pp.y));
+        const half4 Pl = __builtin_bit_cast(half4, make_uint2(pp.z, pp.w));
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          // V tokens 16 kc + 4 kq .. + 3 of dim 16 db + m (of this pass)
+          const uint32_t *r = reinterpret_cast<const uint32_t *>(vt + (16 * db + m) * kVtStride + 16 * kc + 4 * kq);
+          const half4 V = __builtin_bit_cast(half4, make_uint2(r[0], r[1]));
+          acc[2 * p + db] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ph, V, acc[2 * p + db], 0, 0, 0);
+          acc[2 * p + db] = __builtin_amdgcn_mfma_f32_16x16x16f16(Pl, V, acc[2 * p + db], 0, 0, 0);
+        }
+      }
+      wave_sync();
+    }
+  }
+}
+
+// Online softmax for one tile and 16 rows.  Lane = token (absolute position
+// tpos); row r is valid for it when tpos <= pos0 + r / group (causal) and
+// the token is inside the item's range.
+__device__ __forceinline__ void prefill_softmax(const floatx4 (&sc)[4], uint32_t nk_bits, uint32_t nv_bits,
+                                                bool in_range, int tpos, int pos0, int group, float qk_scale,
+                                                float (&m_run)[kRows], float (&l_lane)[kRows], uint16_t *pl,
+                                                floatx4 (&acc)[8], int lane) {
+  const float nk = (float)__builtin_bit_cast(_Float16, (uint16_t)nk_bits);
+  const float nv = (float)__builtin_bit_cast(_Float16, (uint16_t)nv_bits);
+  float s[kRows];
+  bool ok[kRows];
+  bool over = false;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    ok[r] = in_range && tpos <= pos0 + r / group;
+    s[r] = ok[r] ? sc[r >> 2][r & 3] * nk * qk_scale : -__builtin_inff();
+    over |= s[r] > m_run[r];
+  }
+  if (__builtin_amdgcn_read_exec() & __ballot(over)) {
+    float alpha[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const float m_new = fmaxf(m_run[r], wave_max(s[r]));
+      alpha[r] = m_new == -__builtin_inff() ? 1.0f : exp2f(m_run[r] - m_new);
+      l_lane[r] *= alpha[r];
+      m_run[r] = m_new;
+    }
+    // acc[db][i] holds row 4 (lane / 16) + i
+    const int q4 = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = q4 == 0 ? alpha[i] : q4 == 1 ? alpha[4 + i] : q4 == 2 ? alpha[8 + i] : alpha[12 + i];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[db][i] *= ai;
+    }
+  }
+  uint16_t *q8 = pl + (lane >> 2) * 8 + (lane & 3);
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const float p = ok[r] ? exp2f(s[r] - m_run[r]) : 0.0f;
+    l_lane[r] += p;
+    const float pv = p * nv;
+    const _Float16 hi = (_Float16)pv;
+    q8[r * 16 * 8] = __builtin_bit_cast(uint16_t, hi);
+    q8[r * 16 * 8 + 4] = __builtin_bit_cast(uint16_t, (_Float16)(pv - (float)hi));
+  }
+}
+
+template <int NQ>
+__global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk, Tables tv) {
+  __shared__ uint8_t sym8[2][kM];
+  __shared__ uint2 symtab[2][kMaxLevels];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const DecTab dk{sym8[0], symtab[0]};
+  const DecTab dv{sym8[1], symtab[1]};
+  build_tables(sym8[0], symtab[0], tk, threadIdx.x, blockDim.x);
+  build_tables(sym8[1], symtab[1], tv, threadIdx.x, blockDim.x);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int Ck = tk.C, Cv = tv.C;
+  const WaveLayout L = prefill_layout(Ck, Cv);
+  uint8_t *base = smem + (size_t)wave * L.bytes;
+  uint8_t *kst = base + L.kst;
+  uint8_t *vst = base + L.vst;
+  uint16_t *pl = reinterpret_cast<uint16_t *>(base + L.pl);
+  uint16_t *vt = reinterpret_cast<uint16_t *>(base + L.vt);
+  const uint8_t *kpool_end = a.kc + (size_t)a.Hkv * a.S * Ck;
+  const uint8_t *vpool_end = a.vc + (size_t)a.Hkv * a.S * Cv;
+  const int64_t W = (int64_t)gridDim.x * a.waves_per_block;
+
+  for (int64_t item = (int64_t)blockIdx.x * a.waves_per_block + wave; item < a.n_items; item += W) {
+    const int c = (int)(item % a.nc);
+    int64_t rest = item / a.nc;
+    const int qb = (int)(rest % a.nqb);
+    const int64_t bg = rest / a.nqb;
+    const int b = (int)(bg / a.Hkv), g = (int)(bg - (int64_t)b * a.Hkv);
+    const int len = a.seq_len[b];
+    const int pos0 = len - a.Tq + qb * a.tb;                  // position of the block's first query
+    const int pmax = pos0 + min(a.tb, a.Tq - qb * a.tb) - 1;  // of its last
+    const int t0 = c * a.chunk;
+    if (t0 > pmax || pmax < 0) continue;
+    const int t1 = min(t0 + a.chunk, pmax + 1);
+    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+    const int64_t plane0 = (int64_t)g * a.S;
+    auto tile_base = [&](int tile) -> int64_t { return plane0 + a.seq_start[b] + t0 + tile * kTile; };
+
+    wave_sync();
+    const uint4 *qr = reinterpret_cast<const uint4 *>(a.qrot + ((bg * a.nqb) + qb) * kQrotPrefill);
+    auto norms = [&](int64_t tbase, uint32_t &nk, uint32_t &nv) {
+      const int64_t idx = tbase + lane;
+      const bool ok = idx >= plane0 && idx < plane0 + a.S;
+      nk = ok ? a.kn[idx] : 0u;
+      nv = ok ? a.vn[idx] : 0u;
+    };
+    TileRegs<NQ> rk, rv;
+    uint32_t nk0, nv0, nk1 = 0, nv1 = 0;
+    const int64_t base0 = tile_base(0);
+    int64_t vbase = base0;
+    fetch<NQ>(rk, a.kc + base0 * Ck, kTile * Ck, a.kc, kpool_end, lane);
+    norms(base0, nk0, nv0);
+    commit<NQ>(rk, kst, kTile * Ck, lane);
+    const int koff0 = rk.off;
+    wave_sync();
+    fetch<NQ>(rv, a.vc + vbase * Cv, kTile * Cv, a.vc, vpool_end, lane);
+    if (ntiles > 1) {
+      const int64_t base1 = tile_base(1);
+      fetch<NQ>(rk, a.kc + base1 * Ck, kTile * Ck, a.kc, kpool_end, lane);
+      norms(base1, nk1, nv1);
+      vbase = base1;
+    }
+    float m_run[kRows], l_lane[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      m_run[r] = -__builtin_inff();
+      l_lane[r] = 0.0f;
+    }
+    floatx4 acc[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 sc[4];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) sc[rg] = floatx4{0.f, 0.f, 0.f, 0.f};
+    prefill_tile_pass<true, false>(dk, dv, kst + koff0 + lane * Ck, nullptr, qr, pl, vt, sc, acc, lane);
+    prefill_softmax(sc, nk0, nv0, t0 + lane < t1, t0 + lane, pos0, a.group, a.qk_scale, m_run, l_lane, pl, acc,
+                    lane);
+
+    for (int j = 0; j < ntiles; ++j) {
+      const bool next = j + 1 < ntiles;
+      wave_sync();
+      commit<NQ>(rv, vst, kTile * Cv, lane);
+      const int voff = rv.off;
+      int koff = 0;
+      if (next) {
+        commit<NQ>(rk, kst, kTile * Ck, lane);
+        koff = rk.off;
+      }
+      wave_sync();
+      uint32_t nk2 = 0, nv2 = 0;
+      if (next) fetch<NQ>(rv, a.vc + vbase * Cv, kTile * Cv, a.vc, vpool_end, lane);
+      if (j + 2 < ntiles) {
+        const int64_t base2 = tile_base(j + 2);
+        fetch<NQ>(rk, a.kc + base2 * Ck, kTile * Ck, a.kc, kpool_end, lane);
+        norms(base2, nk2, nv2);
+        vbase = base2;
+      }
+      if (next) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) sc[rg] = floatx4{0.f, 0.f, 0.f, 0.f};
+        prefill_tile_pass<true, true>(dk, dv, kst + koff + lane * Ck, vst + voff + lane * Cv, qr, pl, vt, sc, acc,
+                                      lane);
+        const int tp = t0 + (j + 1) * kTile + lane;
+        prefill_softmax(sc, nk1, nv1, tp < t1, tp, pos0, a.group, a.qk_scale, m_run, l_lane, pl, acc, lane);
+      } else {
+        prefill_tile_pass<false, true>(dk, dv, nullptr, vst + voff + lane * Cv, qr, pl, vt, sc, acc, lane);
+      }
+      nk1 = nk2;
+      nv1 = nv2;
+    }
+
+    // partial: lane l holds rows 4 (l / 16) + i of dims 16 db + l % 16
+    float *dst = a.part + item * kRows * kPart;
+    const int q4 = lane >> 4, dn = lane & 15;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(4 * q4 + i) * kPart + 16 * db + dn] = acc[db][i];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const float l = wave_sum(l_lane[r]);
+      if (lane == r) {
+        dst[r * kPart + 128] = m_run[r];
+        dst[r * kPart + 129] = l;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(128) prefill_combine_kernel(AttnArgs a, uint64_t vseed) {
+  __shared__ float buf[kD];
+  const int d = threadIdx.x;
+  int64_t blk = blockIdx.x;  // (b * Tq + tq) * Hq + h
+  const int h = (int)(blk % a.Hq);
+  blk /= a.Hq;
+  const int tq = (int)(blk % a.Tq);
+  const int b = (int)(blk / a.Tq);
+  const int g = h / a.group, hh = h - g * a.group;
+  const int qb = tq / a.tb, r = (tq - qb * a.tb) * a.group + hh;
+  const int pos = a.seq_len[b] - a.Tq + tq;
+  const int n = pos < 0 ? 0 : min(pos / a.chunk + 1, a.nc);
+  const float *src = a.part + ((((int64_t)b * a.Hkv + g) * a.nqb + qb) * a.nc) * kRows * kPart + r * kPart;
+  float M = -__builtin_inff();
+  for (int c = 0; c < n; ++c) M = fmaxf(M, src[(int64_t)c * kRows * kPart + 128]);
+  float Ls = 0.0f, o = 0.0f;
+  for (int c = 0; c < n; ++c) {
+    const float *p = src + (int64_t)c * kRows * kPart;
+    if (p[128] == -__builtin_inff()) continue;  // no token of this chunk is visible to the row
+    const float w = exp2f(p[128] - M);
+    Ls += w * p[129];
+    o += w * p[d];
+  }
+  buf[d] = Ls > 0.0f ? o / Ls : 0.0f;
+#pragma unroll
+  for (int w = 1; w < kD; w <<= 1) {
+    __syncthreads();
+    const float v = buf[d], pv = buf[d ^ w];
+    __syncthreads();
+    buf[d] = (d & w) ? pv - v : v + pv;
+  }
+  __syncthreads();
+  const uint64_t sw = dev_splitmix64(vseed, 2ull * (uint64_t)g + (uint64_t)(d >> 6));
+  float rv = buf[d] * 0.0078125f;
+  if ((sw >> (d & 63)) & 1ull) rv = -rv;
+  const int64_t oi = (((int64_t)b * a.Tq + tq) * a.Hq + h) * kD + d;
+  if (a.out_bf16) {
+    const uint32_t u = __float_as_uint(rv);
+    const uint32_t rb = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    reinterpret_cast<uint16_t *>(a.out)[oi] = (rv != rv) ? (uint16_t)0x7FC0u : (uint16_t)rb;
+  } else {
+    reinterpret_cast<float *>(a.out)[oi] = rv;
+  }
+}
+
 // ---------------------------------------------------------------- planning
 struct Plan {
   int chunk, nc, waves_per_block, blocks, nq;
@@ -575,8 +960,140 @@ hipError_t launch_splitk(const Plan &pl, const AttnArgs &a, const Tables &tk, co
   return hipGetLastError();
 }
 
+struct PrefillPlan {
+  int chunk, nc, waves_per_block, blocks, nq, tb, nqb;
+  int64_t n_items;
+  size_t lds, qrot_bytes, part_bytes, total;
+};
+
+int make_prefill_plan(int B, int Tq, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, PrefillPlan *pl) {
+  const int cus = device_cus();
+  if (cus <= 0) return DQ_ERR_HIP;
+  const int group = Hq / Hkv;
+  pl->tb = kRows / group;
+  pl->nqb = (Tq + pl->tb - 1) / pl->tb;
+  const int cmax = Ck > Cv ? Ck : Cv;
+  pl->nq = cmax <= 47 ? 3 : (cmax <= 79 ? 5 : 9);
+  const int wb = prefill_layout(Ck, Cv).bytes;
+  int wpb = 8;
+  while (wpb > 1 && kLutBytes + wpb * wb > 160 * 1024) wpb -= 1;
+  if (kLutBytes + wpb * wb > 160 * 1024) return DQ_ERR_UNSUPPORTED;
+  const int64_t waves = (int64_t)cus * 8;
+  const int64_t units = (int64_t)B * Hkv * pl->nqb;
+  int64_t chunk = (max_len * units + 8 * waves - 1) / (8 * waves);
+  chunk = ((chunk + kTile - 1) / kTile) * kTile;
+  if (chunk < 256) chunk = 256;
+  if (chunk > 1024) chunk = 1024;
+  if (const char *e = getenv("DQ_SPLIT_TOKENS")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= kTile && v % kTile == 0) chunk = v;
+  }
+  pl->chunk = (int)chunk;
+  pl->nc = (int)((max_len + chunk - 1) / chunk);
+  pl->waves_per_block = wpb;
+  pl->n_items = units * pl->nc;
+  pl->lds = (size_t)wpb * wb;
+  const int64_t want_blocks = (pl->n_items + wpb - 1) / wpb;
+  pl->blocks = (int)(want_blocks < cus ? want_blocks : cus);
+  pl->qrot_bytes = ((size_t)units * kQrotPrefill * 2 + 255) & ~(size_t)255;
+  pl->part_bytes = (size_t)pl->n_items * kRows * kPart * sizeof(float);
+  pl->total = pl->qrot_bytes + pl->part_bytes;
+  return DQ_OK;
+}
+
+template <int NQ>
+hipError_t launch_prefill(const PrefillPlan &pl, const AttnArgs &a, const Tables &tk, const Tables &tv,
+                          hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_prefill_kernel<NQ>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kLutBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(attn_prefill_kernel<NQ>, dim3((unsigned)pl.blocks), dim3(64 * pl.waves_per_block), pl.lds, s,
+                     a, tk, tv);
+  return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace dq
+
+extern "C" int dq_attn_prefill_workspace(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int64_t max_len,
+                                         size_t *bytes) {
+  if (!bytes || B < 1 || Tq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_len < Tq) return DQ_ERR_INVALID;
+  const int group = Hq / Hkv;
+  if (group != 1 && group != 2 && group != 4) return DQ_ERR_UNSUPPORTED;
+  dq::PrefillPlan pl;
+  const int st = dq::make_prefill_plan(B, Tq, Hq, Hkv, max_len, 34, 34, &pl);
+  if (st) return st;
+  *bytes = pl.total;
+  return DQ_OK;
+}
+
+extern "C" int dq_attn_prefill(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Tq, int32_t Hq,
+                               const uint8_t *k_cont, const uint16_t *k_norm, const uint8_t *v_cont,
+                               const uint16_t *v_norm, int64_t num_slots, const int64_t *seq_start,
+                               const int32_t *seq_len, int64_t max_len, float sm_scale, int32_t out_dtype,
+                               void *out, void *workspace, size_t ws_bytes, dq_stream_t stream) {
+  if (!ck || !cv || !q || !k_cont || !k_norm || !v_cont || !v_norm || !seq_start || !seq_len || !out ||
+      !workspace)
+    return DQ_ERR_INVALID;
+  const int Hkv = ck->t.hkv;
+  if (cv->t.hkv != Hkv || B < 1 || Tq < 1 || Hq < 1 || Hq % Hkv || num_slots < 1 || max_len < Tq)
+    return DQ_ERR_INVALID;
+  const int group = Hq / Hkv;
+  if (group != 1 && group != 2 && group != 4) return DQ_ERR_UNSUPPORTED;
+  if (out_dtype != 0 && out_dtype != 1) return DQ_ERR_INVALID;
+  if (max_len > (int64_t)1 << 31) return DQ_ERR_INVALID;
+  const uintptr_t kca = reinterpret_cast<uintptr_t>(k_cont), vca = reinterpret_cast<uintptr_t>(v_cont);
+  if ((kca & 15u) || (vca & 15u) || ((num_slots * ck->t.C) & 15) || ((num_slots * cv->t.C) & 15))
+    return DQ_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return DQ_ERR_INVALID;
+  dq::PrefillPlan pl;
+  int st = dq::make_prefill_plan(B, Tq, Hq, Hkv, max_len, ck->t.C, cv->t.C, &pl);
+  if (st) return st;
+  size_t need = 0;
+  st = dq_attn_prefill_workspace(B, Tq, Hq, Hkv, max_len, &need);
+  if (st) return st;
+  if (ws_bytes < need || pl.total > need) return DQ_ERR_WORKSPACE;
+
+  dq::AttnArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = group;
+  a.kc = k_cont;
+  a.kn = k_norm;
+  a.vc = v_cont;
+  a.vn = v_norm;
+  a.S = num_slots;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.qk_scale = sm_scale * 1.4426950408889634f / 128.0f;
+  a.chunk = pl.chunk;
+  a.nc = pl.nc;
+  a.n_items = pl.n_items;
+  a.qrot = static_cast<uint16_t *>(workspace);
+  a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.qrot_bytes);
+  a.out = out;
+  a.out_bf16 = out_dtype;
+  a.waves_per_block = pl.waves_per_block;
+  a.Tq = Tq;
+  a.tb = pl.tb;
+  a.nqb = pl.nqb;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t rot_blocks = (int64_t)B * pl.nqb * pl.tb * Hq;
+  hipLaunchKernelGGL(dq::rotate_qp_kernel, dim3((unsigned)rot_blocks), dim3(64), 0, s, a, ck->t.seed);
+  hipError_t e = pl.nq == 3   ? dq::launch_prefill<3>(pl, a, ck->t, cv->t, s)
+                 : pl.nq == 5 ? dq::launch_prefill<5>(pl, a, ck->t, cv->t, s)
+                              : dq::launch_prefill<9>(pl, a, ck->t, cv->t, s);
+  if (e != hipSuccess) return DQ_ERR_HIP;
+  hipLaunchKernelGGL(dq::prefill_combine_kernel, dim3((unsigned)((int64_t)B * Tq * Hq)), dim3(128), 0, s, a,
+                     cv->t.seed);
+  return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
 
 extern "C" int dq_attn_decode_workspace(int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, size_t *bytes) {
   if (!bytes || B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_len < 1) return DQ_ERR_INVALID;

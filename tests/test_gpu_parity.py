@@ -514,3 +514,66 @@ def test_ragged_32seq_4k_128k(oracle_lib):
     order = np.argsort(c["ctx"])
     rows = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
     _sampled_attention(O, c, lens, int(lens.max()), rows, "ragged")
+
+
+def _prefill_case(O, lens, Tq, Hq, hkv, seed, kinds=("outlier", "iid_scaled"), C=(34, 34)):
+    c = _attn_case(O, len(lens), Hq, hkv, lens, kinds=kinds, C=C, seed=seed)
+    q = synth.q_tensor(len(lens) * Tq, Hq, seed=seed + 9, device=DEV).view(len(lens), Tq, Hq, 128).contiguous()
+    return c, q
+
+
+def _gpu_prefill(c, q, max_len=None, **kw):
+    out = dq.attn_prefill(c["ck"], c["cv"], q, c["kc"], c["kn"], c["vc"], c["vn"], c["ss"], c["sl"],
+                          int(max_len or c["lens"].max()), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_prefill(O, c, q, sm_scale=None):
+    return O.attention_prefill(c["ock"], c["ocv"], _np_bits(q), c["kc"].cpu().numpy(), _np_bits(c["kn"]),
+                               c["vc"].cpu().numpy(), _np_bits(c["vn"]), c["starts"], c["lens"],
+                               sm_scale=sm_scale)
+
+
+@pytest.mark.parametrize("Hq,hkv,Tq", [(8, 2, 5), (4, 4, 16), (4, 2, 1), (8, 2, 16), (2, 2, 3)])
+def test_prefill_attention_small(oracle_lib, Hq, hkv, Tq):
+    """Causal chunked prefill on ragged contexts (including a context equal
+    to the chunk), every query row against the oracle."""
+    O = oracle_lib
+    lens = [max(Tq, 1), 63 + Tq, 300, 129, 64 + Tq]
+    c, q = _prefill_case(O, lens, Tq, Hq, hkv, seed=Hq * 7 + hkv + Tq)
+    _assert_close(_gpu_prefill(c, q).cpu().numpy(), _oracle_prefill(O, c, q), f"prefill Hq={Hq} hkv={hkv} Tq={Tq}")
+
+
+def test_prefill_one_query_equals_decode(oracle_lib):
+    O = oracle_lib
+    lens = [1, 100, 777]
+    c, q = _prefill_case(O, lens, 1, 8, 2, seed=5)
+    pre = _gpu_prefill(c, q)[:, 0]
+    c["q"] = q[:, 0].contiguous()
+    dec = _gpu_attn(c)
+    err = float((pre - dec).abs().max())
+    assert err <= MAX_ABS / 4, err
+
+
+def test_prefill_split_invariance(oracle_lib):
+    O = oracle_lib
+    lens = [2000, 900]
+    c, q = _prefill_case(O, lens, 12, 8, 2, seed=11, kinds=("iid_scaled", "student_t5"), C=(34, 29))
+    ref = _oracle_prefill(O, c, q, sm_scale=0.1)
+    try:
+        for split in ("64", "256", "1024"):
+            os.environ["DQ_SPLIT_TOKENS"] = split
+            _assert_close(_gpu_prefill(c, q, sm_scale=0.1).cpu().numpy(), ref, f"prefill split={split}")
+    finally:
+        os.environ.pop("DQ_SPLIT_TOKENS", None)
+    _assert_close(_gpu_prefill(c, q, sm_scale=0.1).cpu().numpy(), ref, "prefill split=default")
+
+
+def test_prefill_8k_context_64_token_chunk(oracle_lib):
+    """Two sequences of 8192 tokens (Qwen3-8B-shaped heads, outlier
+    channels) whose last 64 tokens are the chunk: every row."""
+    O = oracle_lib
+    lens = [8192, 8192]
+    c, q = _prefill_case(O, lens, 64, 32, 8, seed=23)
+    _assert_close(_gpu_prefill(c, q).cpu().numpy(), _oracle_prefill(O, c, q), "prefill 8k/64")
