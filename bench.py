@@ -240,6 +240,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-pool attention timing")
     ap.add_argument("--no-rd", action="store_true", help="skip the rate-distortion drift-order encode")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill attention timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter scale for rocprofv3)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -421,6 +422,42 @@ def main():
             f"vs contiguous {att_avg_ms:.3f} ms")
         del pools
 
+    # chunked prefill over the same caches: the first 16 sequences, their
+    # last 512 cached tokens taken as the chunk (8K-token prompts)
+    prefill = None
+    if not args.no_prefill:
+        nb, tq = min(16, B), 512
+        lens_p = lens_s[-1][:nb].contiguous()
+        qp = synth.kv_tensor("iid", nb * tq, Hq, seed=w.seed + 60, device=dev).view(nb, tq, Hq, 128).contiguous()
+        max_p = int(lens_p.max())
+        wsp = torch.empty(dq.attn_prefill_workspace_bytes(nb, tq, Hq, Hkv, max_p), dtype=torch.uint8, device=dev)
+        outp = torch.empty((nb, tq, Hq, 128), dtype=torch.float32, device=dev)
+        ss_p = st_t[:nb].contiguous()
+        dq.attn_prefill(ck, cv, qp, kc, kn, vc, vn, ss_p, lens_p, max_p, out=outp, workspace=wsp)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        reps = 3
+        for _ in range(reps):
+            dq.attn_prefill(ck, cv, qp, kc, kn, vc, vn, ss_p, lens_p, max_p, out=outp, workspace=wsp)
+        e1.record()
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / reps
+        group = Hq // Hkv
+        tb = 16 // group
+        # compressed bytes the kernel reads: each block of tb queries reads its causal prefix
+        lens_np = lens_p.cpu().numpy().astype(np.int64)
+        read = 0
+        for L in lens_np:
+            for qb in range((tq + tb - 1) // tb):
+                read += (L - tq + min(tq, (qb + 1) * tb)) * Hkv * (ck.C + 2 + cv.C + 2)
+        prefill = {"batch": nb, "chunk_tokens": tq, "context": int(lens_np.max()), "call_ms": round(pms, 3),
+                   "query_tokens_per_s": round(nb * tq / (pms / 1e3), 1),
+                   "kv_bytes_read_gbps": round(read / (pms / 1e3) / 1e9, 1), "rows_per_item": 16}
+        log(f"[bench] chunked prefill: {nb} x {tq} queries over {prefill['context']} tokens in {pms:.2f} ms "
+            f"({prefill['query_tokens_per_s'] / 1e3:.1f} K query tokens/s, {prefill['kv_bytes_read_gbps']} GB/s read)")
+        del qp, wsp, outp
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on host cores")
@@ -452,6 +489,7 @@ def main():
         "attn_call_gbps": round(alg_bytes / (att_avg_ms / 1e3) / 1e9, 2),
         "paged_attn": paged,
         "rd_drift_order": rd,
+        "prefill_attn": prefill,
         "cpu_baseline": cpu,
         "attn_context_tokens_per_s": round(ctx_tokens / (sum(att_ms) / 1e3), 1),
         "append_encode_ms": round(float(np.mean(enc_ms)), 4),
