@@ -900,13 +900,15 @@ struct Plan {
   size_t lds, qrot_bytes, part_bytes, total;
 };
 
+// CU count of the current device, read once per process (thread-safe static
+// initialisation; the library plans for the one device it runs on)
 int device_cus() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
+  static const int cus = [] {
+    int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  }
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+  }();
   return cus;
 }
 
@@ -948,13 +950,11 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
 
 template <int NQ>
 hipError_t launch_splitk(const Plan &pl, const AttnArgs &a, const Tables &tk, const Tables &tv, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kLutBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // dynamic LDS beyond the default limit, requested once (thread-safe static)
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     160 * 1024 - kLutBytes);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(attn_splitk_kernel<NQ>, dim3((unsigned)pl.blocks), dim3(64 * pl.waves_per_block), pl.lds, s,
                      a, tk, tv);
   return hipGetLastError();
@@ -1004,13 +1004,10 @@ int make_prefill_plan(int B, int Tq, int Hq, int Hkv, int64_t max_len, int Ck, i
 template <int NQ>
 hipError_t launch_prefill(const PrefillPlan &pl, const AttnArgs &a, const Tables &tk, const Tables &tv,
                           hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_prefill_kernel<NQ>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kLutBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_prefill_kernel<NQ>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     160 * 1024 - kLutBytes);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(attn_prefill_kernel<NQ>, dim3((unsigned)pl.blocks), dim3(64 * pl.waves_per_block), pl.lds, s,
                      a, tk, tv);
   return hipGetLastError();
