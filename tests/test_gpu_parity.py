@@ -178,9 +178,10 @@ def test_decode_symbols_bit_exact(oracle_lib, levels, C):
         assert (ofs[valid] == 1 << 23).all()
 
 
-def _attn_case(O, B, Hq, hkv, lens, kinds=("outlier", "outlier"), C=(34, 34), seed=0, gap=5):
-    ck, ock = _codecs(O, 8, C[0], seed=seed + 1, hkv=hkv)
-    cv, ocv = _codecs(O, 6, C[1], seed=seed + 2, hkv=hkv)
+def _attn_case(O, B, Hq, hkv, lens, kinds=("outlier", "outlier"), C=(34, 34), seed=0, gap=5,
+               levels=(8, 6), step64=(0, 0)):
+    ck, ock = _codecs(O, levels[0], C[0], seed=seed + 1, hkv=hkv, step64=step64[0])
+    cv, ocv = _codecs(O, levels[1], C[1], seed=seed + 2, hkv=hkv, step64=step64[1])
     starts, s = [], 0
     for L in lens:
         starts.append(s)
@@ -516,8 +517,9 @@ def test_ragged_32seq_4k_128k(oracle_lib):
     _sampled_attention(O, c, lens, int(lens.max()), rows, "ragged")
 
 
-def _prefill_case(O, lens, Tq, Hq, hkv, seed, kinds=("outlier", "iid_scaled"), C=(34, 34)):
-    c = _attn_case(O, len(lens), Hq, hkv, lens, kinds=kinds, C=C, seed=seed)
+def _prefill_case(O, lens, Tq, Hq, hkv, seed, kinds=("outlier", "iid_scaled"), C=(34, 34), levels=(8, 6),
+                  step64=(0, 0)):
+    c = _attn_case(O, len(lens), Hq, hkv, lens, kinds=kinds, C=C, seed=seed, levels=levels, step64=step64)
     q = synth.q_tensor(len(lens) * Tq, Hq, seed=seed + 9, device=DEV).view(len(lens), Tq, Hq, 128).contiguous()
     return c, q
 
@@ -577,3 +579,30 @@ def test_prefill_8k_context_64_token_chunk(oracle_lib):
     lens = [8192, 8192]
     c, q = _prefill_case(O, lens, 64, 32, 8, seed=23)
     _assert_close(_gpu_prefill(c, q).cpu().numpy(), _oracle_prefill(O, c, q), "prefill 8k/64")
+
+
+
+@pytest.mark.parametrize("C,levels,step64", [((60, 48), (8, 6), (30, 40)), ((132, 100), (16, 12), (25, 25)),
+                                             ((80, 48), (2, 8), (20, 64))])
+def test_attention_large_containers(oracle_lib, C, levels, step64):
+    """Containers above 47 and 79 bytes take the 5- and 9-piece tile fetch
+    and fewer waves per block; 2, 12 and 16 levels."""
+    O = oracle_lib
+    lens = [1, 64, 65, 300, 1000]
+    for Hq, hkv in ((8, 2), (4, 4)):
+        c = _attn_case(O, len(lens), Hq, hkv, lens, kinds=("student_t5", "outlier"), C=C, seed=C[0] + Hq,
+                       levels=levels, step64=step64)
+        _assert_close(_gpu_attn(c).cpu().numpy(), _oracle_attn(O, c), f"decode C={C} L={levels} Hq={Hq}")
+    c, q = _prefill_case(O, [70, 300], 9, 8, 2, seed=C[1], C=C, levels=levels, step64=step64)
+    _assert_close(_gpu_prefill(c, q).cpu().numpy(), _oracle_prefill(O, c, q), f"prefill C={C} L={levels}")
+
+
+@pytest.mark.parametrize("levels,C,step64", [(16, 132, 25), (2, 20, 64), (12, 48, 30), (8, 132, 30)])
+def test_encode_extreme_codecs(oracle_lib, encode_path, levels, C, step64):
+    """Largest container, most and fewest levels: bit-exact containers."""
+    O = oracle_lib
+    gc, oc = _codecs(O, levels, C, seed=77, hkv=2, step64=step64)
+    for kind in ("iid", "outlier"):
+        x = synth.kv_tensor(kind, 150, 2, seed=78, device=DEV)
+        slots = torch.arange(150, dtype=torch.int64, device=DEV)
+        _assert_encode_equal(*_encode_both(O, gc, oc, x, slots, 150), f"extreme {levels}/{C}/{kind}")
