@@ -28,6 +28,7 @@
 #include "decode_common.h"
 
 #include <math.h>
+#include <stdint.h>
 #include <stdlib.h>
 
 namespace dq {
@@ -912,6 +913,36 @@ int device_cus() {
   return cus;
 }
 
+// Context split.  A launch deals its items (units x nc, each covering up to
+// `chunk` tokens) round-robin to W resident waves, so it takes about
+// ceil(units * nc / W) rounds of (chunk + c0) token-times, c0 being an
+// item's fixed cost (a K-only and a V-only tile pass and the partial; about
+// 32 tokens on MI355X).  The chunk (a multiple of the 64-token tile, 128 to
+// 2048: only max_len is known here, and ragged batches need the finer
+// items to balance) minimising that is chosen; W is a fixed function of the
+// CU count, so the workspace size depends only on the call's shape.
+// DQ_SPLIT_TOKENS forces a chunk (tests use it).
+int64_t choose_chunk(int64_t units, int64_t max_len, int64_t W) {
+  const int64_t c0 = 32;
+  int64_t best = 1024, best_cost = INT64_MAX;
+  for (int64_t chunk = 128; chunk <= 2048; chunk += kTile) {
+    const int64_t nc = (max_len + chunk - 1) / chunk;
+    const int64_t span = nc == 1 ? ((max_len + kTile - 1) / kTile) * kTile : chunk;
+    const int64_t rounds = (units * nc + W - 1) / W;
+    const int64_t cost = rounds * (span + c0);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = chunk;
+    }
+    if (nc == 1) break;  // larger chunks change nothing
+  }
+  if (const char *e = getenv("DQ_SPLIT_TOKENS")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= kTile && v % kTile == 0) best = v;
+  }
+  return best;
+}
+
 int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl) {
   (void)Hq;
   const int cus = device_cus();
@@ -925,15 +956,7 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   if (kLutBytes + wpb * wb > lds_cap) return DQ_ERR_UNSUPPORTED;
   // chunk: aim for ~8 items per resident wave (8 waves per CU) if every
   // sequence were max_len; independent of C so the workspace size is too
-  const int64_t waves = (int64_t)cus * 8;
-  int64_t chunk = (max_len * (int64_t)B * Hkv + 8 * waves - 1) / (8 * waves);
-  chunk = ((chunk + kTile - 1) / kTile) * kTile;
-  if (chunk < 256) chunk = 256;
-  if (chunk > 1024) chunk = 1024;
-  if (const char *e = getenv("DQ_SPLIT_TOKENS")) {
-    const long v = strtol(e, nullptr, 10);
-    if (v >= kTile && v % kTile == 0) chunk = v;
-  }
+  const int64_t chunk = choose_chunk((int64_t)B * Hkv, max_len, (int64_t)cus * 12);
   const int64_t nc = (max_len + chunk - 1) / chunk;
   pl->chunk = (int)chunk;
   pl->nc = (int)nc;
@@ -978,16 +1001,8 @@ int make_prefill_plan(int B, int Tq, int Hq, int Hkv, int64_t max_len, int Ck, i
   int wpb = 8;
   while (wpb > 1 && kLutBytes + wpb * wb > 160 * 1024) wpb -= 1;
   if (kLutBytes + wpb * wb > 160 * 1024) return DQ_ERR_UNSUPPORTED;
-  const int64_t waves = (int64_t)cus * 8;
   const int64_t units = (int64_t)B * Hkv * pl->nqb;
-  int64_t chunk = (max_len * units + 8 * waves - 1) / (8 * waves);
-  chunk = ((chunk + kTile - 1) / kTile) * kTile;
-  if (chunk < 256) chunk = 256;
-  if (chunk > 1024) chunk = 1024;
-  if (const char *e = getenv("DQ_SPLIT_TOKENS")) {
-    const long v = strtol(e, nullptr, 10);
-    if (v >= kTile && v % kTile == 0) chunk = v;
-  }
+  const int64_t chunk = choose_chunk(units, max_len, (int64_t)cus * 8);
   pl->chunk = (int)chunk;
   pl->nc = (int)((max_len + chunk - 1) / chunk);
   pl->waves_per_block = wpb;
