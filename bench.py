@@ -8,8 +8,8 @@ outlier channels per head.  Synthetic data (synth/), no model weights.
 
 Untimed setup: draw K/V, encode the whole prompt into the compressed pools
 (timed separately for encode vectors/s).  One timed step = one decode step:
-  dq_encode of the new token's K and V for every sequence (append), then
-  dq_attn_decode for every sequence over its grown context.
+  dq_encode_kv of the new token's K and V for every sequence (append, one
+  launch), then dq_attn_decode for every sequence over its grown context.
 `value` = compressed KV bytes (containers + fp16 norms) read by attention per
 step / wall time per step.  The roofline entry measures the attention call
 alone with HIP events on its stream inside the timed region.
@@ -347,8 +347,7 @@ def main():
     def step(s, ev=None):
         if ev is not None:
             ev[0].record()
-        dq.encode(ck, Kn[s], slots_s[s], kc, kn)
-        dq.encode(cv, Vn[s], slots_s[s], vc, vn)
+        dq.encode_kv(ck, cv, Kn[s], Vn[s], slots_s[s], kc, kn, vc, vn)
         if ev is not None:
             ev[1].record()
         dq.attn_decode(ck, cv, qs[s], kc, kn, vc, vn, st_t, lens_s[s], max_len, out=out, workspace=ws,

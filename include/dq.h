@@ -141,6 +141,19 @@ int dq_encode(dq_codec_t codec, const void *x, int64_t T, int64_t stride_t,
               uint8_t *cont, uint16_t *norm, dq_stats *stats,
               dq_stream_t stream);
 
+/* K and V of the same tokens in one call: the same bytes as dq_encode(ck,
+ * k, ...) followed by dq_encode(cv, v, ...) with the shared slots, strides
+ * and pools' slot count.  When both batches take the small-batch kernel
+ * (a decode step's append) and the codecs share a drift order, it is one
+ * launch instead of two.  k and v have the same shape and strides; the
+ * codecs the same num_kv_heads (else DQ_ERR_INVALID); either stats may be
+ * NULL. */
+int dq_encode_kv(dq_codec_t ck, dq_codec_t cv, const void *k, const void *v,
+                 int64_t T, int64_t stride_t, int64_t stride_h,
+                 const int64_t *slots, int64_t num_slots, uint8_t *k_cont,
+                 uint16_t *k_norm, uint8_t *v_cont, uint16_t *v_norm,
+                 dq_stats *k_stats, dq_stats *v_stats, dq_stream_t stream);
+
 /* dq_decode_symbols: container -> the 128 symbols, for kv head `head` at n
  * slots (inspection and checking; attention decodes inside its own kernel).
  *   sym_out      device uint8[n][128]

@@ -26,7 +26,7 @@ MAX_CONTAINER = 132
 PAGE_TOKENS = 64
 NSTATS = 6 + MAX_CONTAINER + 1
 
-__all__ = ["Codec", "alloc_pool", "encode", "decode_symbols", "attn_decode", "attn_decode_paged",
+__all__ = ["Codec", "alloc_pool", "encode", "encode_kv", "decode_symbols", "attn_decode", "attn_decode_paged",
            "attn_prefill", "attn_prefill_workspace_bytes",
            "attn_workspace_bytes", "new_stats", "stats_dict", "DQError", "library_path"]
 
@@ -160,6 +160,40 @@ def encode(codec: Codec, x: torch.Tensor, slots: torch.Tensor, cont: torch.Tenso
     _check(_lib.lib().dq_encode(codec.handle, _ptr(x), x.shape[0], x.stride(0), x.stride(1),
                                 _ptr(slots), cont.shape[1], _ptr(cont), _ptr(norm),
                                 _ptr(stats), _stream(x.device)), "dq_encode")
+
+
+def encode_kv(ck: Codec, cv: Codec, k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor,
+              k_cont: torch.Tensor, k_norm: torch.Tensor, v_cont: torch.Tensor, v_norm: torch.Tensor,
+              k_stats: torch.Tensor | None = None, v_stats: torch.Tensor | None = None):
+    """encode(ck, k, ...) and encode(cv, v, ...) with shared slots, in one
+    launch when both are small batches.  k, v: bf16 [T, Hkv, 128] with the
+    same strides."""
+    for name, x in (("k", k), ("v", v)):
+        _need_cuda(name, x, torch.bfloat16)
+        if x.dim() != 3 or x.shape[1] != ck.kv_heads or x.shape[2] != HEAD_DIM or x.stride(2) != 1:
+            raise DQError(f"{name} must be [T, {ck.kv_heads}, 128] with unit inner stride")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise DQError("k and v must have the same shape and strides")
+    _need_cuda("slots", slots, torch.int64)
+    if slots.dim() != 1 or slots.shape[0] != k.shape[0] or not slots.is_contiguous():
+        raise DQError("slots must be a contiguous int64 [T]")
+    for name, codec, cont, norm in (("k", ck, k_cont, k_norm), ("v", cv, v_cont, v_norm)):
+        _need_cuda(f"{name}_cont", cont, torch.uint8)
+        _need_cuda(f"{name}_norm", norm, torch.float16)
+        if (cont.dim() != 3 or cont.shape[0] != codec.kv_heads or cont.shape[2] != codec.C
+                or not cont.is_contiguous() or norm.shape != cont.shape[:2] or not norm.is_contiguous()):
+            raise DQError(f"{name} pool must be contiguous [Hkv, S, C] / [Hkv, S]")
+    if k_cont.shape[1] != v_cont.shape[1]:
+        raise DQError("K and V pools must have the same slot count")
+    for st in (k_stats, v_stats):
+        if st is not None:
+            _need_cuda("stats", st, torch.int64)
+            if st.numel() != NSTATS or not st.is_contiguous():
+                raise DQError(f"stats must be a contiguous int64 [{NSTATS}]")
+    _check(_lib.lib().dq_encode_kv(ck.handle, cv.handle, _ptr(k), _ptr(v), k.shape[0], k.stride(0),
+                                   k.stride(1), _ptr(slots), k_cont.shape[1], _ptr(k_cont), _ptr(k_norm),
+                                   _ptr(v_cont), _ptr(v_norm), _ptr(k_stats), _ptr(v_stats),
+                                   _stream(k.device)), "dq_encode_kv")
 
 
 def decode_symbols(codec: Codec, cont: torch.Tensor, head: int, slots: torch.Tensor):

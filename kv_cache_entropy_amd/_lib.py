@@ -35,6 +35,7 @@ def lib():
         L.dq_codec_info.argtypes = [vp, ctypes.POINTER(CodecDesc)]
         L.dq_codec_tables.argtypes = [vp, vp, vp, vp, vp]
         L.dq_encode.argtypes = [vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
+        L.dq_encode_kv.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp]
         L.dq_decode_symbols.argtypes = [vp, vp, i64, i32, vp, i64, vp, vp, vp, vp]
         L.dq_attn_decode_workspace.argtypes = [i32, i32, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
         L.dq_attn_decode.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, vp, i64,
@@ -46,7 +47,7 @@ def lib():
         L.dq_attn_decode_paged.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, i32, vp,
                                            i64, ctypes.c_float, i32, vp, vp, ctypes.c_size_t, vp]
         for f in ("dq_codec_create", "dq_codec_destroy", "dq_codec_info", "dq_codec_tables",
-                  "dq_encode", "dq_decode_symbols", "dq_attn_decode_workspace",
+                  "dq_encode", "dq_encode_kv", "dq_decode_symbols", "dq_attn_decode_workspace",
                   "dq_attn_decode", "dq_attn_decode_timed", "dq_attn_decode_paged",
                   "dq_attn_prefill_workspace", "dq_attn_prefill"):
             getattr(L, f).restype = ctypes.c_int

@@ -470,8 +470,10 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
 //    length never increases along the order, so every lower lane failed).
 constexpr int kWaveVecs = 4;  // vectors (waves) per block
 
+// One block's vectors (kWaveVecs of them) of a wave-per-vector encode; the
+// block index is passed in so one launch can serve two streams (K and V).
 template <bool RD>  // drift order: rate-distortion (true) or magnitude (false)
-__global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kernel(EncodeArgs a, Tables t) {
+__device__ __forceinline__ void wave_encode_block(const EncodeArgs &a, const Tables &t, int64_t block) {
   __shared__ uint4 etab[kMaxLevels];
   __shared__ uint32_t ent[kWaveVecs][kD];          // s0 | sd << 8 | rank << 16
   __shared__ float yabs[kWaveVecs][kD];
@@ -491,7 +493,7 @@ __global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kernel(EncodeArgs 
   __syncthreads();
   const int w = tid >> 6, lane = tid & 63;
   const int64_t nvec = a.T * (int64_t)t.hkv;
-  const int64_t vid = (int64_t)blockIdx.x * kWaveVecs + w;
+  const int64_t vid = block * kWaveVecs + w;
   if (vid < nvec) {  // whole waves; every wave reaches the block barrier below
     const int h = t.half, C = t.C;
     const int g = (int)(vid / a.T);
@@ -679,6 +681,20 @@ __global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kernel(EncodeArgs 
   }
 }
 
+template <bool RD>
+__global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kernel(EncodeArgs a, Tables t) {
+  wave_encode_block<RD>(a, t, blockIdx.x);
+}
+
+// K and V of the same tokens in one launch: blocks [0, nbk) take K, the
+// rest V (a decode step's append is then one launch, not two).
+template <bool RD>
+__global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kv_kernel(EncodeArgs ak, Tables tk, EncodeArgs av,
+                                                                        Tables tv, int64_t nbk) {
+  if ((int64_t)blockIdx.x < nbk) wave_encode_block<RD>(ak, tk, blockIdx.x);
+  else wave_encode_block<RD>(av, tv, blockIdx.x - nbk);
+}
+
 constexpr int64_t kWavePathMax = 16384;  // vectors: below this, latency wins
 
 template <int MAXH>
@@ -692,10 +708,10 @@ hipError_t launch(const EncodeArgs &a, const Tables &t, hipStream_t s) {
 }  // namespace
 }  // namespace dq
 
-extern "C" int dq_encode(dq_codec_t codec, const void *x, int64_t T, int64_t stride_t,
-                         int64_t stride_h, const int64_t *slots, int64_t num_slots,
-                         uint8_t *cont, uint16_t *norm, dq_stats *stats,
-                         dq_stream_t stream) {
+// Validates a dq_encode call and fills its kernel arguments.
+static int encode_args(dq_codec_t codec, const void *x, int64_t T, int64_t stride_t, int64_t stride_h,
+                       const int64_t *slots, int64_t num_slots, uint8_t *cont, uint16_t *norm, dq_stats *stats,
+                       dq::EncodeArgs *a) {
   if (!codec || T < 0) return DQ_ERR_INVALID;
   if (T == 0) return DQ_OK;
   if (!x || !slots || !cont || !norm || num_slots < 1) return DQ_ERR_INVALID;
@@ -705,26 +721,64 @@ extern "C" int dq_encode(dq_codec_t codec, const void *x, int64_t T, int64_t str
       stride_h < 0)
     return DQ_ERR_INVALID;
   if (T > ((int64_t)1 << 40) / t.hkv || num_slots > ((int64_t)1 << 40) / t.C) return DQ_ERR_INVALID;
-  dq::EncodeArgs a{static_cast<const uint16_t *>(x), T, stride_t, stride_h, slots, num_slots,
-                   cont, norm, stats};
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // DQ_ENCODE_WAVE_MAX overrides the batch size (vectors) up to which the
-  // wave-per-vector kernel runs; both kernels write identical bytes
-  int64_t wave_max = dq::kWavePathMax;
-  if (const char *ev = getenv("DQ_ENCODE_WAVE_MAX")) wave_max = atoll(ev);
-  hipError_t e;
   // the rate-distortion order interleaves magnitude groups, which the
   // large-batch kernel's drift plan assumes it does not: it always takes
-  // the wave-per-vector kernel
+  // the wave-per-vector kernel, whose grid bounds the batch
   if (t.order == 1 && T * (int64_t)t.hkv > ((int64_t)1 << 30)) return DQ_ERR_UNSUPPORTED;
-  if ((t.order == 1 || T * (int64_t)t.hkv <= wave_max) && T * (int64_t)t.hkv <= ((int64_t)1 << 30)) {
-    const int64_t nvec = T * (int64_t)t.hkv;
+  *a = dq::EncodeArgs{static_cast<const uint16_t *>(x), T, stride_t, stride_h, slots, num_slots, cont, norm, stats};
+  return DQ_OK;
+}
+
+// Does a batch of this codec take the wave-per-vector kernel?
+// DQ_ENCODE_WAVE_MAX overrides the batch size (vectors) up to which it
+// does; both kernels write identical bytes.
+static bool wave_path(const dq::Tables &t, int64_t T) {
+  int64_t wave_max = dq::kWavePathMax;
+  if (const char *ev = getenv("DQ_ENCODE_WAVE_MAX")) wave_max = atoll(ev);
+  const int64_t nvec = T * (int64_t)t.hkv;
+  return (t.order == 1 || nvec <= wave_max) && nvec <= ((int64_t)1 << 30);
+}
+
+static hipError_t launch_encode(const dq::EncodeArgs &a, const dq::Tables &t, hipStream_t s) {
+  if (wave_path(t, a.T)) {
+    const int64_t nvec = a.T * (int64_t)t.hkv;
     const dim3 grid((unsigned)((nvec + dq::kWaveVecs - 1) / dq::kWaveVecs)), block(64 * dq::kWaveVecs);
     if (t.order == 1) hipLaunchKernelGGL(dq::encode_wave_kernel<true>, grid, block, 0, s, a, t);
     else hipLaunchKernelGGL(dq::encode_wave_kernel<false>, grid, block, 0, s, a, t);
-    e = hipGetLastError();
-  } else {
-    e = t.half <= 4 ? dq::launch<4>(a, t, s) : dq::launch<8>(a, t, s);
+    return hipGetLastError();
   }
-  return e == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+  return t.half <= 4 ? dq::launch<4>(a, t, s) : dq::launch<8>(a, t, s);
+}
+
+extern "C" int dq_encode(dq_codec_t codec, const void *x, int64_t T, int64_t stride_t,
+                         int64_t stride_h, const int64_t *slots, int64_t num_slots,
+                         uint8_t *cont, uint16_t *norm, dq_stats *stats,
+                         dq_stream_t stream) {
+  dq::EncodeArgs a{};
+  const int st = encode_args(codec, x, T, stride_t, stride_h, slots, num_slots, cont, norm, stats, &a);
+  if (st || T == 0) return st;
+  return launch_encode(a, codec->t, static_cast<hipStream_t>(stream)) == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+}
+
+extern "C" int dq_encode_kv(dq_codec_t ck, dq_codec_t cv, const void *k, const void *v, int64_t T,
+                            int64_t stride_t, int64_t stride_h, const int64_t *slots, int64_t num_slots,
+                            uint8_t *k_cont, uint16_t *k_norm, uint8_t *v_cont, uint16_t *v_norm,
+                            dq_stats *k_stats, dq_stats *v_stats, dq_stream_t stream) {
+  if (!ck || !cv || ck->t.hkv != cv->t.hkv) return DQ_ERR_INVALID;
+  dq::EncodeArgs ak{}, av{};
+  int st = encode_args(ck, k, T, stride_t, stride_h, slots, num_slots, k_cont, k_norm, k_stats, &ak);
+  if (st) return st;
+  st = encode_args(cv, v, T, stride_t, stride_h, slots, num_slots, v_cont, v_norm, v_stats, &av);
+  if (st || T == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dq::Tables &tk = ck->t, &tv = cv->t;
+  if (wave_path(tk, T) && wave_path(tv, T) && tk.order == tv.order) {
+    const int64_t nbk = (T * (int64_t)tk.hkv + dq::kWaveVecs - 1) / dq::kWaveVecs;
+    const dim3 grid((unsigned)(2 * nbk)), block(64 * dq::kWaveVecs);
+    if (tk.order == 1) hipLaunchKernelGGL(dq::encode_wave_kv_kernel<true>, grid, block, 0, s, ak, tk, av, tv, nbk);
+    else hipLaunchKernelGGL(dq::encode_wave_kv_kernel<false>, grid, block, 0, s, ak, tk, av, tv, nbk);
+    return hipGetLastError() == hipSuccess ? DQ_OK : DQ_ERR_HIP;
+  }
+  if (launch_encode(ak, tk, s) != hipSuccess) return DQ_ERR_HIP;
+  return launch_encode(av, tv, s) == hipSuccess ? DQ_OK : DQ_ERR_HIP;
 }

@@ -606,3 +606,31 @@ def test_encode_extreme_codecs(oracle_lib, encode_path, levels, C, step64):
         x = synth.kv_tensor(kind, 150, 2, seed=78, device=DEV)
         slots = torch.arange(150, dtype=torch.int64, device=DEV)
         _assert_encode_equal(*_encode_both(O, gc, oc, x, slots, 150), f"extreme {levels}/{C}/{kind}")
+
+
+
+@pytest.mark.parametrize("T,order", [(128, 0), (100, 1), (5000, 0)])
+def test_encode_kv_matches_separate_calls(oracle_lib, T, order):
+    """One K+V call writes the same bytes and stats as two dq_encode calls
+    (fused launch for small batches, two launches above the threshold),
+    and both equal the oracle."""
+    O = oracle_lib
+    hkv = 8 if T <= 128 else 4
+    ck, ock = _codecs(O, 8, 34, seed=3, hkv=hkv, order=order)
+    cv, ocv = _codecs(O, 6, 34, seed=4, hkv=hkv, order=order)
+    k = synth.kv_tensor("outlier", T, hkv, seed=5, device=DEV)
+    v = synth.kv_tensor("outlier", T, hkv, seed=6, device=DEV)
+    slots = torch.randperm(T + 40, generator=torch.Generator().manual_seed(1))[:T].to(DEV)
+    pools = [dq.alloc_pool(c, T + 40, DEV) for c in (ck, cv)]
+    sts = [dq.new_stats(DEV), dq.new_stats(DEV)]
+    dq.encode_kv(ck, cv, k, v, slots, *pools[0], *pools[1], *sts)
+    torch.cuda.synchronize()
+    for (codec, oc, x), (cont, norm), st in zip(((ck, ock, k), (cv, ocv, v)), pools, sts):
+        c2, n2 = dq.alloc_pool(codec, T + 40, DEV)
+        s2 = dq.new_stats(DEV)
+        dq.encode(codec, x, slots, c2, n2, s2)
+        torch.cuda.synchronize()
+        assert torch.equal(cont, c2) and torch.equal(norm, n2)
+        assert dq.stats_dict(st) == dq.stats_dict(s2)
+        ocont, onorm, ost = O.encode(oc, _np_bits(x), slots.cpu().numpy(), num_slots=cont.shape[1])
+        _assert_encode_equal(cont, norm, st, ocont, onorm, ost, f"encode_kv T={T}")
