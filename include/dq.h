@@ -181,6 +181,9 @@ int dq_decode_symbols(dq_codec_t codec, const uint8_t *cont, int64_t num_slots,
  * store.
  *   q          device bf16 [B][Hq][128]
  *   seq_start  device int64[B]; seq_len device int32[B], 1 <= len <= max_len
+ *              (lengths live on the device and are not checked: a length
+ *              of 0 gives a zero output row, and tokens past max_len are
+ *              not read)
  *   max_len    host: upper bound of seq_len, used to plan the split
  *   sm_scale   softmax scale (e.g. 1/sqrt(128))
  *   out_dtype  0: fp32, 1: bf16

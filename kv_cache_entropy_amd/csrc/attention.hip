@@ -487,7 +487,7 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
     L += w * p[129];
     o += w * p[d];
   }
-  buf[d] = o / L;
+  buf[d] = L > 0.0f ? o / L : 0.0f;  // an empty sequence (a caller error) gives a zero row
   // inverse rotation: o = D_V * H * o' / 128 (H * H = 128 I)
 #pragma unroll
   for (int w = 1; w < kD; w <<= 1) {

@@ -276,6 +276,19 @@ def test_attention_timed_entry_point(oracle_lib):
     assert e0.elapsed_time(e1) > 0.0
 
 
+def test_attention_empty_sequence_gives_zero_row(oracle_lib):
+    """A sequence of length 0 (outside the documented range) yields a zero
+    output row and leaves every other row as it is with a valid length."""
+    O = oracle_lib
+    c = _attn_case(O, 3, 8, 2, [700, 90, 1300], seed=21)
+    ref = _gpu_attn(c)
+    c["sl"] = torch.tensor([700, 0, 1300], dtype=torch.int32, device=DEV)
+    got = _gpu_attn(c, max_len=1300)
+    assert torch.count_nonzero(got[1]).item() == 0
+    assert torch.isfinite(got).all().item()
+    assert torch.equal(got[0], ref[0]) and torch.equal(got[2], ref[2])
+
+
 def _paged_copy(c, rng, extra_pages=5):
     """The contiguous pools of an attention case re-laid as shuffled 64-token
     pages in a larger pool, with the page table that addresses them."""
