@@ -31,6 +31,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <utility>
+
 namespace dq {
 namespace {
 
@@ -168,108 +170,140 @@ __device__ __forceinline__ void commit(const TileRegs<NQ> &r, uint8_t *dst, int 
   }
 }
 
-// Byte renormalisation.  The next byte is loaded unconditionally (the load
-// is volatile so the compiler cannot sink it into a branch): the select then
-// stays branch-free and the load overlaps the table lookups of the step.
-__device__ __forceinline__ void renorm(uint32_t &x, const uint8_t *&p, uint32_t byte) {
-  const bool need = x < kLow;
-  x = need ? ((x << 8) | byte) : x;
-  p += need ? 1 : 0;
-}
-typedef const volatile __attribute__((address_space(3))) uint8_t lds_byte;
-__device__ __forceinline__ uint32_t next_byte(const uint8_t *p) {
-  return *(lds_byte *)p;  // p points into LDS (a container staged by this wave)
-}
-
 struct DecTab {
   const uint8_t *sym8;
   const uint2 *symtab;
 };
 
+// Byte renormalisation.  Stream positions are 32-bit LDS addresses.  The
+// next byte is loaded unconditionally (the load is volatile so the compiler
+// cannot sink it into a branch): the select then stays branch-free and the
+// load overlaps the table lookups of the step.  The empty asm makes each new
+// position an opaque value, so every step advances the pointer with one
+// add-with-carry instead of re-deriving it from older positions.
+typedef const __attribute__((address_space(3))) uint8_t lds_u8;
+typedef const volatile __attribute__((address_space(3))) uint8_t lds_byte;
+__device__ __forceinline__ lds_u8 *to_lds(const uint8_t *p) {
+  return (lds_u8 *)p;  // p points into LDS (a container staged by this wave)
+}
+__device__ __forceinline__ uint32_t next_byte(lds_u8 *p) { return *(lds_byte *)p; }
+__device__ __forceinline__ void renorm(uint32_t &x, lds_u8 *&p, uint32_t byte) {
+  const bool need = x < kLow;
+  x = need ? ((x << 8) | byte) : x;
+  p += need ? 1 : 0;
+  asm("" : "+v"(p));
+}
+
+// The two table reads of a decode step (slot -> 8 * symbol, then the symbol
+// entry), volatile so that their order across chains is kept.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef const volatile __attribute__((address_space(3))) u32x2 lds_u32x2;
+__device__ __forceinline__ uint32_t lookup_sym8(const DecTab &t, uint32_t x) {
+  return *(lds_byte *)to_lds(t.sym8 + (x & (kM - 1)));
+}
+__device__ __forceinline__ uint2 lookup_symtab(const DecTab &t, uint32_t s8) {
+  const u32x2 e = *(lds_u32x2 *)to_lds(reinterpret_cast<const uint8_t *>(t.symtab) + s8);
+  return make_uint2(e.x, e.y);
+}
+
+// f(std::integral_constant<int, i>()) for i = 0 .. N-1, so that i can feed
+// the constant operands of a builtin (the MFMA broadcast block)
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_impl(F &f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F &&f) {
+  unroll_impl(f, std::make_integer_sequence<int, N>());
+}
+
+
 // Decodes one K tile (scores into sc) and/or one V tile (PV into acc),
 // interleaving the two independent rANS chains of each lane.
-// K: after every 4 symbols, sc += q~[4 heads][4 dims] x levels[4 dims]
-//   on a 4x4x4 MFMA whose A operand (the query, hi then lo) is broadcast
-//   from block 0 (cbsz 4), so only lanes 0..3 read it from LDS; the lane's
-//   own 4 levels are the B column, and the lane ends with its token's
-//   scores for the 4 heads.
+// K: after every 4 symbols (dim group G), sc += q~[4 heads][4 dims] x
+//   levels[4 dims] on a 4x4x4 MFMA.  The query of group G sits in block
+//   G mod 16 of register set G / 16 (lanes 4b .. 4b + 3 hold groups b and
+//   16 + b, one head each, hi then lo) and is broadcast to every block
+//   (cbsz 4, abid G mod 16).  The lane's own 4 levels are the B column, and
+//   the lane ends with its token's scores for the 4 heads.
 // V: levels go to the transposed LDS tile, 32 dims per pass; each pass is
 //   contracted with P (hi, then lo) by 16 MFMAs whose blocks are (8 dim
-//   quads) x (2 token halves); P is broadcast per half (cbsz 3), read by
-//   lanes 0..3, 32..35.
+//   quads) x (2 token halves).  P of token quad 8 h + c sits in block c of
+//   half h and is broadcast within the half (cbsz 3, abid c); it is read
+//   from LDS once per tile.
 template <bool DK, bool DV>
 __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
-                                          const uint8_t *vb, const uint4 *qg, const uint16_t *pl,
+                                          const uint8_t *vb, const uint4 (&qreg)[2], const uint16_t *pl,
                                           uint16_t *vt, floatx4 &sc, floatx4 (&acc)[8], int lane) {
   const int th = lane >> 5, row = lane & 31;
-  const bool qlane = lane < 4, plane = (lane & 31) < 4;
-  // rotated query (global, 2 KB per item, cache resident): lanes 0..3 load
-  // the 16 bytes of their head for the next group one group ahead
-  uint4 qnext = make_uint4(0, 0, 0, 0);
-  if (DK && qlane) qnext = qg[lane];
+  uint4 pq = make_uint4(0, 0, 0, 0);
+  if (DV) pq = *reinterpret_cast<const uint4 *>(pl + ((lane & 3) * 16 + th * 8 + (row >> 2)) * 8);
+  const half4 Ph = __builtin_bit_cast(half4, make_uint2(pq.x, pq.y));
+  const half4 Pl = __builtin_bit_cast(half4, make_uint2(pq.z, pq.w));
+  const uint32_t *vrow = reinterpret_cast<const uint32_t *>(vt) + row * (kVtStride / 2) + th * 16;
   uint32_t xk = 0, xv = 0;
-  const uint8_t *pk = kb, *pv = vb;
+  lds_u8 *pk = nullptr, *pv = nullptr;
   if (DK) {
     xk = load_le32(kb);
-    pk = kb + 4;
+    pk = to_lds(kb + 4);
   }
   if (DV) {
     xv = load_le32(vb);
-    pv = vb + 4;
+    pv = to_lds(vb + 4);
   }
   uint16_t *col = vt + lane;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    for (int gq = 0; gq < kPass / 4; ++gq) {
-      const uint4 qv = qnext;
-      const int gnext = p * (kPass / 4) + gq + 1;
-      if (DK && qlane && gnext < 32) qnext = qg[gnext * 4 + lane];
+  unroll<4>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    unroll<kPass / 4>([&](auto gc) {
+      constexpr int gq = decltype(gc)::value;
+      constexpr int G = p * (kPass / 4) + gq;
       uint32_t lv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t bk = 0, bv = 0;
+        // the two chains' loads are issued in this order (volatile), so
+        // each LDS round trip of one chain overlaps the other's
+        uint32_t bk = 0, bv = 0, sk = 0, sv = 0;
+        uint2 ek = make_uint2(0, 0), ev = make_uint2(0, 0);
         if (DK) bk = next_byte(pk);
         if (DV) bv = next_byte(pv);
+        if (DK) sk = lookup_sym8(tk, xk);
+        if (DV) sv = lookup_sym8(tv, xv);
+        if (DK) ek = lookup_symtab(tk, sk);
+        if (DV) ev = lookup_symtab(tv, sv);
         if (DK) {
-          uint32_t sy;
-          const uint2 e = rans_step(xk, tk.sym8, tk.symtab, sy);
+          xk = rans_advance(xk, ek);
           renorm(xk, pk, bk);
-          lv[j] = e.y;
+          lv[j] = ek.y;
         }
         if (DV) {
-          uint32_t sy;
-          const uint2 e = rans_step(xv, tv.sym8, tv.symtab, sy);
+          xv = rans_advance(xv, ev);
           renorm(xv, pv, bv);
-          col[(gq * 4 + j) * kVtStride] = (uint16_t)(e.y >> 16);
+          col[(gq * 4 + j) * kVtStride] = (uint16_t)(ev.y >> 16);
         }
       }
       if (DK) {
         const uint32_t b01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
         const uint32_t b23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
         const half4 Bk = __builtin_bit_cast(half4, make_uint2(b01, b23));
-        sc = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(qv.x, qv.y)), Bk, sc, 4, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(qv.z, qv.w)), Bk, sc, 4, 0, 0);
+        const uint4 &q = qreg[G >> 4];
+        sc = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(q.x, q.y)), Bk, sc, 4,
+                                                G & 15, 0);
+        sc = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(q.z, q.w)), Bk, sc, 4,
+                                                G & 15, 0);
       }
-    }
+    });
     if (DV) {
       wave_sync();
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        uint2 pa = make_uint2(0, 0), pb = make_uint2(0, 0);
-        if (plane) {
-          const uint4 pp = *reinterpret_cast<const uint4 *>(pl + ((lane & 3) * 16 + th * 8 + c) * 8);
-          pa = make_uint2(pp.x, pp.y);
-          pb = make_uint2(pp.z, pp.w);
-        }
-        const uint32_t *r = reinterpret_cast<const uint32_t *>(vt) + row * (kVtStride / 2) + th * 16 + 2 * c;
-        const half4 V = __builtin_bit_cast(half4, make_uint2(r[0], r[1]));
+      unroll<8>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        const half4 V = __builtin_bit_cast(half4, make_uint2(vrow[2 * c], vrow[2 * c + 1]));
         // hi and lo accumulate separately: two independent MFMA chains
-        acc[p] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, pa), V, acc[p], 3, 0, 0);
-        acc[4 + p] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, pb), V, acc[4 + p], 3, 0, 0);
-      }
+        acc[p] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ph, V, acc[p], 3, c, 0);
+        acc[4 + p] = __builtin_amdgcn_mfma_f32_4x4x4f16(Pl, V, acc[4 + p], 3, c, 0);
+      });
       wave_sync();
     }
-  }
+  });
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -376,7 +410,10 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
     };
 
     wave_sync();  // the previous item's LDS reads are done
+    // rotated query of this (sequence, kv head): lane l holds dim groups
+    // l / 4 and 16 + l / 4 of head l mod 4 (8 VGPRs for the whole item)
     const uint4 *qr = reinterpret_cast<const uint4 *>(a.qrot + bg * kQrotPerBG);
+    const uint4 qreg[2] = {qr[lane], qr[64 + lane]};
 
     // this lane's token norms for a tile (0 outside the pool plane)
     auto norms = [&](int64_t tbase, uint32_t &nk, uint32_t &nv) {
@@ -412,7 +449,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 #pragma unroll
     for (int p = 0; p < 8; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
     floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-    tile_pass<true, false>(dk, dv, kst + koff0 + lane * Ck, nullptr, qr, pl, vt, sc, acc, lane);
+    tile_pass<true, false>(dk, dv, kst + koff0 + lane * Ck, nullptr, qreg, pl, vt, sc, acc, lane);
     softmax_tile(sc, nk0, nv0, lane < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
 
     for (int j = 0; j < ntiles; ++j) {
@@ -437,10 +474,10 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
       }
       if (next) {
         sc = floatx4{0.f, 0.f, 0.f, 0.f};
-        tile_pass<true, true>(dk, dv, kst + koff + lane * Ck, vst + voff + lane * Cv, qr, pl, vt, sc, acc, lane);
+        tile_pass<true, true>(dk, dv, kst + koff + lane * Ck, vst + voff + lane * Cv, qreg, pl, vt, sc, acc, lane);
         softmax_tile(sc, nk1, nv1, (j + 1) * kTile + lane < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
       } else {
-        tile_pass<false, true>(dk, dv, nullptr, vst + voff + lane * Cv, qr, pl, vt, sc, acc, lane);
+        tile_pass<false, true>(dk, dv, nullptr, vst + voff + lane * Cv, qreg, pl, vt, sc, acc, lane);
       }
       nk1 = nk2;
       nv1 = nv2;
@@ -596,14 +633,14 @@ __device__ __forceinline__ void prefill_tile_pass(const DecTab tk, const DecTab 
     for (int rg = 0; rg < 4; ++rg) qn[rg] = qg[lane * 4 + rg];
   }
   uint32_t xk = 0, xv = 0;
-  const uint8_t *pk = kb, *pv = vb;
+  lds_u8 *pk = nullptr, *pv = nullptr;
   if (DK) {
     xk = load_le32(kb);
-    pk = kb + 4;
+    pk = to_lds(kb + 4);
   }
   if (DV) {
     xv = load_le32(vb);
-    pv = vb + 4;
+    pv = to_lds(vb + 4);
   }
   uint16_t *col = vt + lane;
 #pragma unroll
@@ -613,20 +650,25 @@ __device__ __forceinline__ void prefill_tile_pass(const DecTab tk, const DecTab 
       uint32_t lv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t bk = 0, bv = 0;
+        // the two chains' loads are issued in this order (volatile), so
+        // each LDS round trip of one chain overlaps the other's
+        uint32_t bk = 0, bv = 0, sk = 0, sv = 0;
+        uint2 ek = make_uint2(0, 0), ev = make_uint2(0, 0);
         if (DK) bk = next_byte(pk);
         if (DV) bv = next_byte(pv);
+        if (DK) sk = lookup_sym8(tk, xk);
+        if (DV) sv = lookup_sym8(tv, xv);
+        if (DK) ek = lookup_symtab(tk, sk);
+        if (DV) ev = lookup_symtab(tv, sv);
         if (DK) {
-          uint32_t sy;
-          const uint2 e = rans_step(xk, tk.sym8, tk.symtab, sy);
+          xk = rans_advance(xk, ek);
           renorm(xk, pk, bk);
-          lv[j] = e.y;
+          lv[j] = ek.y;
         }
         if (DV) {
-          uint32_t sy;
-          const uint2 e = rans_step(xv, tv.sym8, tv.symtab, sy);
+          xv = rans_advance(xv, ev);
           renorm(xv, pv, bv);
-          col[(gq * 4 + j) * kVtStride] = (uint16_t)(e.y >> 16);
+          col[(gq * 4 + j) * kVtStride] = (uint16_t)(ev.y >> 16);
         }
       }
       if (DK) {

@@ -36,14 +36,19 @@ __device__ __forceinline__ void build_tables(uint8_t *sym8, uint2 *symtab, const
                                  : make_uint2(0u, 0u);
 }
 
+// The state update of a decode step, given the symbol-table entry e of the
+// symbol that x's slot selects.
+__device__ __forceinline__ uint32_t rans_advance(uint32_t x, uint2 e) {
+  return __umul24(e.x, x >> kMBits) + ((x & (kM - 1)) - (e.y & 0xFFFFu));
+}
+
 // One decode step without the renormalisation; returns the symbol-table
 // entry (.y >> 16 = fp16 level) and the symbol.
 __device__ __forceinline__ uint2 rans_step(uint32_t &x, const uint8_t *sym8, const uint2 *symtab, uint32_t &s) {
-  const uint32_t slot = x & (kM - 1);
-  const uint32_t s8 = sym8[slot];
+  const uint32_t s8 = sym8[x & (kM - 1)];
   s = s8 >> 3;
   const uint2 e = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(symtab) + s8);
-  x = __umul24(e.x, x >> kMBits) + (slot - (e.y & 0xFFFFu));
+  x = rans_advance(x, e);
   return e;
 }
 
