@@ -12,7 +12,9 @@ Untimed setup: draw K/V, encode the whole prompt into the compressed pools
   launch), then dq_attn_decode for every sequence over its grown context.
 `value` = compressed KV bytes (containers + fp16 norms) read by attention per
 step / wall time per step.  The roofline entry measures the attention call
-alone with HIP events on its stream inside the timed region.
+alone with HIP events on its stream inside the timed region.  The same steps
+are then timed as one launch each (dq_attn_decode_append), also at batch 1
+and 4, next to the two-launch form.
 
     python bench.py [--steps 16] [--warmup 3] [--workload NAME]
 """
@@ -32,7 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 COUNTERS = os.path.join(ROOT, "profiles", "attn_splitk_llama31_8b_b128_8k_counters.json")
 ATTN_SOURCES = ["kv_cache_entropy_amd/csrc/attention.hip", "kv_cache_entropy_amd/csrc/decode_common.h",
-                "kv_cache_entropy_amd/csrc/dq_internal.h"]
+                "kv_cache_entropy_amd/csrc/dq_internal.h", "kv_cache_entropy_amd/csrc/encode_wave.h"]
 
 
 def log(msg):
@@ -71,11 +73,11 @@ PROFILE_CMDS = {
     "fetch": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
               "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'attn_splitk|copyBuffer' --output-format csv "
               "-d $R/" + PROF + "/fetch -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline "
-              "--copy-calibration > $R/" + PROF + "/fetch_bench.json"),
+              "--no-fused --copy-calibration > $R/" + PROF + "/fetch_bench.json"),
     "write": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
               "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'attn_splitk|copyBuffer' --output-format csv "
               "-d $R/" + PROF + "/write -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline "
-              "--copy-calibration > $R/" + PROF + "/write_bench.json"),
+              "--no-fused --copy-calibration > $R/" + PROF + "/write_bench.json"),
 }
 
 
@@ -122,7 +124,9 @@ def summarize_profiles(d):
         rows.append((float(r["TotalDurationNs"]), short, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
                      float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     rows.sort(reverse=True)
-    split = [r for r in rows if "attn_splitk_kernel" in r[1]]
+    # the decode kernel without the append (the fused-append timing launches
+    # attn_splitk_kernel<3, true>)
+    split = [r for r in rows if "attn_splitk_kernel" in r[1] and "false>" in r[1]]
     lines = [f"# Kernel trace: decode step, {wl}", "",
              "Batch 128, 32 q / 8 kv heads, 8K context, K 8 levels / V 6 levels in 34-byte containers; "
              "the default bench command (prefill encode, 3 warm-up and 16 timed decode steps, oracle timing "
@@ -135,7 +139,7 @@ def summarize_profiles(d):
     if split:
         sp = split[0]
         lines += ["", f"Split-K kernel: rocprofv3 average {sp[3]:.1f} us over {sp[2]} launches (warm-up and the "
-                  f"paged-pool timing included); the same run's bench line measured "
+                  f"paged-pool timing included, the fused-append launches not); the same run's bench line measured "
                   f"{rl['avg_launch_ms'] * 1e3:.1f} us with HIP "
                   f"events around the kernel over the timed steps, {rl['achieved']:.1f} GB/s of compressed "
                   f"bytes = {rl['frac']:.2%} of 8 TB/s.",
@@ -149,7 +153,8 @@ def summarize_profiles(d):
         rows = [r for r in rows if r["Counter_Name"] == counter]
         copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
         cal = max(copies, key=lambda r: float(r["Counter_Value"]))
-        att = [float(r["Counter_Value"]) for r in rows if "attn_splitk_kernel" in r["Kernel_Name"]]
+        att = [float(r["Counter_Value"]) for r in rows
+               if "attn_splitk_kernel" in r["Kernel_Name"] and "false>" in r["Kernel_Name"]]
         bl = _bench_line(os.path.join(d, f"{kind}_bench.json"))
         if bl.get("attn_source_sha256_16") != src:
             raise SystemExit(f"{kind} run was made on a different attention source")
@@ -239,6 +244,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-pool attention timing")
+    ap.add_argument("--no-fused", action="store_true", help="skip the one-launch decode-with-append timing")
     ap.add_argument("--no-rd", action="store_true", help="skip the rate-distortion drift-order encode")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill attention timing")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -384,6 +390,53 @@ def main():
         f"attention {att_avg_ms:.3f} ms of which split-K {split_avg_ms:.3f} ms), {value:.1f} GB/s step, "
         f"split-K kernel {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of HBM peak")
 
+    # the same decode steps as one launch each (dq_attn_decode_append: the
+    # append's encode runs inside the attention launch); re-encoding the same
+    # tokens into the same slots writes the same bytes.  Also at small batch
+    # (the first sequences), where the saved launch matters most.
+    fused = None
+    if not args.no_fused:
+        def fused_ms(nb, fused_call):
+            qb = [qs[s][:nb].contiguous() for s in range(nsteps)]
+            kb = [Kn[s][:nb] for s in range(nsteps)]
+            vb = [Vn[s][:nb] for s in range(nsteps)]
+            lb = [lens_s[s][:nb].contiguous() for s in range(nsteps)]
+            sb = [slots_s[s][:nb].contiguous() for s in range(nsteps)]
+            stb = st_t[:nb].contiguous()
+            mlb = int(ctx[:nb].max()) + nsteps
+            wsb = torch.empty(dq.attn_workspace_bytes(nb, Hq, Hkv, mlb), dtype=torch.uint8, device=dev)
+            ob = torch.empty((nb, Hq, 128), dtype=torch.float32, device=dev)
+
+            def one(s):
+                if fused_call:
+                    dq.attn_decode_append(ck, cv, qb[s], kb[s], vb[s], kc, kn, vc, vn, stb, lb[s], mlb, out=ob,
+                                          workspace=wsb)
+                else:
+                    dq.encode_kv(ck, cv, kb[s], vb[s], sb[s], kc, kn, vc, vn)
+                    dq.attn_decode(ck, cv, qb[s], kc, kn, vc, vn, stb, lb[s], mlb, out=ob, workspace=wsb)
+            for s in range(args.warmup):
+                one(s)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for k in range(args.steps):
+                one(args.warmup + k)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+
+        f_ms = fused_ms(B, True)
+        small = {}
+        for nb in (1, 4):
+            small[str(nb)] = {"fused_ms": round(fused_ms(nb, True), 4),
+                              "separate_ms": round(fused_ms(nb, False), 4)}
+        fused = {"batch": B, "ms_per_step": round(f_ms, 4), "gbps": round(alg_bytes / (f_ms / 1e3) / 1e9, 2),
+                 "separate_ms_per_step": round(ms_per_step, 4), "small_batch": small,
+                 "call": "dq_attn_decode_append"}
+        log(f"[bench] fused append: {f_ms:.3f} ms/step ({fused['gbps']:.1f} GB/s) vs {ms_per_step:.3f} ms as two "
+            f"launches; batch 1: {small['1']['fused_ms']:.4f} vs {small['1']['separate_ms']:.4f} ms, batch 4: "
+            f"{small['4']['fused_ms']:.4f} vs {small['4']['separate_ms']:.4f} ms")
+
     # the same caches re-laid as shuffled 64-token pages (page-table pool)
     paged = None
     if not args.no_paged:
@@ -487,6 +540,7 @@ def main():
         "attn_call_ms": round(att_avg_ms, 4),
         "attn_call_gbps": round(alg_bytes / (att_avg_ms / 1e3) / 1e9, 2),
         "paged_attn": paged,
+        "fused_append": fused,
         "rd_drift_order": rd,
         "prefill_attn": prefill,
         "cpu_baseline": cpu,

@@ -49,7 +49,8 @@ typedef void *dq_stream_t; /* hipStream_t */
 /* Human-readable text for a status code (static storage). */
 const char *dq_status_string(int status);
 
-/* ABI version: 100 * major + minor (101: dq_codec_desc.drift_order). */
+/* ABI version: 100 * major + minor (101: dq_codec_desc.drift_order; 102: decode
+ * with append). */
 int dq_version(void);
 
 /* ------------------------------------------------------------------------ */
@@ -268,6 +269,56 @@ int dq_attn_decode_timed(dq_codec_t ck, dq_codec_t cv, const void *q,
                          void *out, void *workspace, size_t ws_bytes,
                          dq_stream_t stream, void *split_begin,
                          void *split_end);
+
+/* Decode step with append, in one launch: the step's new token of every
+ * sequence is encoded into the pools (as dq_encode would write it) and
+ * attended to in the same call.  This is the fused append of the decode
+ * step ("D-Quant: Entropy Coding Meets KV Cache at 2.26 Bits", The Numbers:
+ * entropy coding costs the most at small batch, where a launch per step
+ * matters).  The launch's first waves encode the new K and V vectors, one
+ * wave per vector, while the others attend to the older tokens; each
+ * encoding wave also writes the new token's own attention partial from the
+ * symbols it chose, and the combine merges it with the older tokens'
+ * partials.
+ *   k_new, v_new  device bf16: the new token of sequence b, kv head g, at
+ *                 element b * new_stride_b + g * new_stride_h (128
+ *                 contiguous values; 2-byte aligned)
+ *   seq_len       includes the new token, which is at position
+ *                 seq_len[b] - 1: slot seq_start[b] + seq_len[b] - 1 of
+ *                 every kv head's plane (>= 1; the slot must be in the pool:
+ *                 a slot outside it is not written)
+ *   k_cont ...    the pools, written at the new slots and read elsewhere
+ *   k_stats, v_stats  device dq_stats of the two encodes, may be NULL
+ * The containers, norms and stats equal those of dq_encode_kv on the same
+ * tokens.  The output is that of dq_attn_decode after that encode up to
+ * floating-point order (the new token enters through the final merge).
+ * Workspace: dq_attn_decode_workspace for the same shape. */
+int dq_attn_decode_append(dq_codec_t ck, dq_codec_t cv, const void *q,
+                          int32_t B, int32_t Hq, const void *k_new,
+                          const void *v_new, int64_t new_stride_b,
+                          int64_t new_stride_h, uint8_t *k_cont,
+                          uint16_t *k_norm, uint8_t *v_cont, uint16_t *v_norm,
+                          int64_t num_slots, const int64_t *seq_start,
+                          const int32_t *seq_len, int64_t max_len,
+                          float sm_scale, int32_t out_dtype, void *out,
+                          void *workspace, size_t ws_bytes, dq_stats *k_stats,
+                          dq_stats *v_stats, dq_stream_t stream);
+
+/* dq_attn_decode_append over a paged pool (pages and max_pages as for
+ * dq_attn_decode_paged): the new token of sequence b goes to slot
+ * pages[b * max_pages + p / 64] * 64 + p % 64, p = seq_len[b] - 1. */
+int dq_attn_decode_paged_append(dq_codec_t ck, dq_codec_t cv, const void *q,
+                                int32_t B, int32_t Hq, const void *k_new,
+                                const void *v_new, int64_t new_stride_b,
+                                int64_t new_stride_h, uint8_t *k_cont,
+                                uint16_t *k_norm, uint8_t *v_cont,
+                                uint16_t *v_norm, int64_t num_slots,
+                                const int32_t *pages, int32_t max_pages,
+                                const int32_t *seq_len, int64_t max_len,
+                                float sm_scale, int32_t out_dtype, void *out,
+                                void *workspace, size_t ws_bytes,
+                                dq_stats *k_stats, dq_stats *v_stats,
+                                dq_stream_t stream);
 
 #ifdef __cplusplus
 }

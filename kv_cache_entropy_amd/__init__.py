@@ -305,6 +305,79 @@ def attn_decode_paged(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_c
     return out
 
 
+def _attn_decode_append(ck: Codec, cv: Codec, q, k_new, v_new, k_cont, k_norm, v_cont, v_norm,
+                        loc, seq_len, max_len, sm_scale, out, out_dtype, workspace, k_stats, v_stats,
+                        paged: bool):
+    _need_cuda("q", q, torch.bfloat16)
+    loc_name, loc_dt = ("pages", torch.int32) if paged else ("seq_start", torch.int64)
+    for name, t, dt in (("k_cont", k_cont, torch.uint8), ("v_cont", v_cont, torch.uint8),
+                        ("k_norm", k_norm, torch.float16), ("v_norm", v_norm, torch.float16),
+                        (loc_name, loc, loc_dt), ("seq_len", seq_len, torch.int32)):
+        _need_cuda(name, t, dt)
+        if not t.is_contiguous():
+            raise DQError(f"{name} must be contiguous")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise DQError("q must be a contiguous bf16 [B, Hq, 128]")
+    B, Hq, _ = q.shape
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        _need_cuda(name, x, torch.bfloat16)
+        if tuple(x.shape) != (B, ck.kv_heads, HEAD_DIM) or x.stride(2) != 1:
+            raise DQError(f"{name} must be [B, {ck.kv_heads}, 128] with unit inner stride")
+    if k_new.stride() != v_new.stride():
+        raise DQError("k_new and v_new must have the same strides")
+    if paged and (loc.dim() != 2 or loc.shape[0] != B):
+        raise DQError("pages must be int32 [B, max_pages]")
+    if k_cont.shape[1] != v_cont.shape[1]:
+        raise DQError("K and V pools must have the same slot count")
+    for st in (k_stats, v_stats):
+        if st is not None:
+            _need_cuda("stats", st, torch.int64)
+            if st.numel() != NSTATS or not st.is_contiguous():
+                raise DQError(f"stats must be a contiguous int64 [{NSTATS}]")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise DQError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, Hq, HEAD_DIM) or not out.is_contiguous():
+        raise DQError("out has the wrong shape or dtype")
+    need = attn_workspace_bytes(B, Hq, ck.kv_heads, max_len)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if sm_scale is None:
+        sm_scale = HEAD_DIM ** -0.5
+    head = (ck.handle, cv.handle, _ptr(q), B, Hq, _ptr(k_new), _ptr(v_new), k_new.stride(0),
+            k_new.stride(1), _ptr(k_cont), _ptr(k_norm), _ptr(v_cont), _ptr(v_norm), k_cont.shape[1])
+    where = (_ptr(loc), loc.shape[1]) if paged else (_ptr(loc),)
+    tail = (_ptr(seq_len), max_len, ctypes.c_float(sm_scale), 0 if out_dtype == torch.float32 else 1,
+            _ptr(out), _ptr(workspace), workspace.numel(), _ptr(k_stats), _ptr(v_stats), _stream(q.device))
+    fn = "dq_attn_decode_paged_append" if paged else "dq_attn_decode_append"
+    _check(getattr(_lib.lib(), fn)(*head, *where, *tail), fn)
+    return out
+
+
+def attn_decode_append(ck: Codec, cv: Codec, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       k_cont, k_norm, v_cont, v_norm, seq_start: torch.Tensor, seq_len: torch.Tensor,
+                       max_len: int, sm_scale: float | None = None, out: torch.Tensor | None = None,
+                       out_dtype=torch.float32, workspace: torch.Tensor | None = None,
+                       k_stats: torch.Tensor | None = None, v_stats: torch.Tensor | None = None):
+    """A decode step with append in one launch: k_new, v_new bf16 [B, Hkv, 128]
+    are encoded into slot seq_start[b] + seq_len[b] - 1 (seq_len counts the
+    new token) and attended to with the rest of the cache.  Returns out
+    [B, Hq, 128]; the pools are updated in place."""
+    return _attn_decode_append(ck, cv, q, k_new, v_new, k_cont, k_norm, v_cont, v_norm, seq_start, seq_len,
+                               max_len, sm_scale, out, out_dtype, workspace, k_stats, v_stats, paged=False)
+
+
+def attn_decode_paged_append(ck: Codec, cv: Codec, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                             k_cont, k_norm, v_cont, v_norm, pages: torch.Tensor, seq_len: torch.Tensor,
+                             max_len: int, sm_scale: float | None = None, out: torch.Tensor | None = None,
+                             out_dtype=torch.float32, workspace: torch.Tensor | None = None,
+                             k_stats: torch.Tensor | None = None, v_stats: torch.Tensor | None = None):
+    """attn_decode_append over a paged pool (pages int32 [B, max_pages])."""
+    return _attn_decode_append(ck, cv, q, k_new, v_new, k_cont, k_norm, v_cont, v_norm, pages, seq_len,
+                               max_len, sm_scale, out, out_dtype, workspace, k_stats, v_stats, paged=True)
+
+
 def attn_prefill_workspace_bytes(B: int, Tq: int, Hq: int, Hkv: int, max_len: int) -> int:
     n = ctypes.c_size_t()
     _check(_lib.lib().dq_attn_prefill_workspace(B, Tq, Hq, Hkv, max_len, ctypes.byref(n)),

@@ -46,10 +46,17 @@ def lib():
                                       ctypes.c_float, i32, vp, vp, ctypes.c_size_t, vp]
         L.dq_attn_decode_paged.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, i32, vp,
                                            i64, ctypes.c_float, i32, vp, vp, ctypes.c_size_t, vp]
+        # (ck, cv, q, B, Hq, k_new, v_new, stride_b, stride_h, kc, kn, vc, vn, S) + where +
+        # (seq_len, max_len, sm_scale, out_dtype, out, ws, ws_bytes, k_stats, v_stats, stream)
+        app_head = [vp, vp, vp, i32, i32, vp, vp, i64, i64, vp, vp, vp, vp, i64]
+        app_tail = [vp, i64, ctypes.c_float, i32, vp, vp, ctypes.c_size_t, vp, vp, vp]
+        L.dq_attn_decode_append.argtypes = app_head + [vp] + app_tail
+        L.dq_attn_decode_paged_append.argtypes = app_head + [vp, i32] + app_tail
         for f in ("dq_codec_create", "dq_codec_destroy", "dq_codec_info", "dq_codec_tables",
                   "dq_encode", "dq_encode_kv", "dq_decode_symbols", "dq_attn_decode_workspace",
                   "dq_attn_decode", "dq_attn_decode_timed", "dq_attn_decode_paged",
-                  "dq_attn_prefill_workspace", "dq_attn_prefill"):
+                  "dq_attn_prefill_workspace", "dq_attn_prefill", "dq_attn_decode_append",
+                  "dq_attn_decode_paged_append"):
             getattr(L, f).restype = ctypes.c_int
         del u64
         _handle = L

@@ -26,6 +26,7 @@
 //  3. combine: log-sum-exp merge of an item's chunks, then the inverse
 //     rotation D_V * H / 128 and the store.
 #include "decode_common.h"
+#include "encode_wave.h"
 
 #include <math.h>
 #include <stdint.h>
@@ -46,6 +47,9 @@ constexpr int kPass = 32;        // dims per V-tile pass
 constexpr int kPart = 132;       // floats per (item, head): acc[128], m, l, pad
 constexpr int kQrotPerBG = 32 * 4 * 8;  // halves per (b, kv head): [chunk][head][hi4 lo4]
 constexpr int kLutBytes = 2 * kDecodeTableBytes;  // K and V decode tables
+// K and V encoder constants of the append (etab, rdtab), static too
+constexpr int kAppendLdsBytes = 2 * (kMaxLevels * 16 + kMaxHalf * 8);
+constexpr int kStaticLds = kLutBytes + kAppendLdsBytes;
 
 struct AttnArgs {
   const uint16_t *q;
@@ -68,6 +72,15 @@ struct AttnArgs {
   int out_bf16;
   int waves_per_block;
   int Tq, tb, nqb;  // prefill: query tokens, tokens per 16-row block, blocks per sequence
+  // decode with append: the new token of sequence b (bf16 [128] at
+  // k_new / v_new + b * new_stride_b + g * new_stride_h) sits at position
+  // seq_len[b] - 1 and is encoded into the pools by the launch itself
+  const uint16_t *k_new, *v_new;
+  int64_t new_stride_b, new_stride_h;
+  uint8_t *kc_w, *vc_w;  // the pools, writable
+  uint16_t *kn_w, *vn_w;
+  dq_stats *k_stats, *v_stats;
+  float *part_new;  // [B][Hkv][4][kPart]: the new token's own partial
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -364,16 +377,91 @@ __device__ __forceinline__ void softmax_tile(const floatx4 &sc, uint32_t nk_bits
   }
 }
 
-template <int NQ>
+// Append: one wave encodes the new token's K (isv false) or V vector of
+// (b, g) into the pool and writes that token's own attention partial from
+// the symbols it chose: the K wave the scores (m = s_h, l = 1), the V wave
+// n_v * level (p = 1).  The chunk items then cover the older tokens only,
+// and the combine merges this partial like any other, so no item waits for
+// the encode.  scratch: the wave's LDS slice.
+template <bool RD>
+__device__ __forceinline__ void append_vector(const AttnArgs &a, const Tables &t, const uint4 *etab,
+                                              const float2 *rdtab, uint8_t *scratch, bool isv, int b, int g,
+                                              int lane) {
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+  const int pos = a.seq_len[b] - 1;
+  int64_t slot = -1;
+  if (pos >= 0) {
+    if (!a.pages) slot = a.seq_start[b] + pos;
+    else if (pos / kTile < a.max_pages) slot = (int64_t)a.pages[(int64_t)b * a.max_pages + pos / kTile] * kTile + pos % kTile;
+  }
+  const uint16_t *xp = (isv ? a.v_new : a.k_new) + (int64_t)b * a.new_stride_b + (int64_t)g * a.new_stride_h;
+  const WaveEncodeScratch L{reinterpret_cast<uint32_t *>(scratch), reinterpret_cast<float *>(scratch + 4 * kD),
+                            scratch + 8 * kD, scratch + 9 * kD, min(kWaveScr, t.C - 3)};
+  WaveEncodeResult r;
+  wave_encode_vector<RD, true>(xp, g, t, etab, rdtab, L, lane, r);
+  if (r.win >= 0 && slot >= 0 && slot < a.S) {
+    const int64_t idx = (int64_t)g * a.S + slot;
+    wave_store_container(r, L, t.C, (isv ? a.vc_w : a.kc_w) + idx * t.C, (isv ? a.vn_w : a.kn_w) + idx, lane);
+  }
+  dq_stats *st = isv ? a.v_stats : a.k_stats;
+  if (st && lane == 0) {
+    unsigned long long *gs = reinterpret_cast<unsigned long long *>(st);
+    atomicAdd(gs + 0, 1ull);
+    if (r.moves) {
+      atomicAdd(gs + 1, 1ull);
+      atomicAdd(gs + 2, (unsigned long long)r.moves);
+    }
+    if (r.passes) atomicAdd(gs + 3, (unsigned long long)r.passes);
+    if (r.bad) atomicAdd(gs + 4, 1ull);
+    if (r.zero) atomicAdd(gs + 5, 1ull);
+    atomicAdd(gs + 6 + 4 + r.okB, 1ull);
+  }
+  if (pos < 0) return;
+  float *P = a.part_new + bg * 4 * kPart;
+  const float n = half_to_float(r.nh);
+  const float lam0 = half_to_float(t.recon[r.sym[0]]), lam1 = half_to_float(t.recon[r.sym[1]]);
+  if (!isv) {
+    // s_h = q~_h . levels * n_k * scale; q~ is stored [dim group][head][hi x4, lo x4]
+    const uint16_t *qr = a.qrot + bg * kQrotPerBG;
+    const int d1 = lane + 64;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int i0 = ((lane >> 2) * 4 + h) * 8 + (lane & 3), i1 = ((d1 >> 2) * 4 + h) * 8 + (d1 & 3);
+      const float q0 = half_to_float(qr[i0]) + half_to_float(qr[i0 + 4]);
+      const float q1 = half_to_float(qr[i1]) + half_to_float(qr[i1 + 4]);
+      float dot = q0 * lam0 + q1 * lam1;
+#pragma unroll
+      for (int w = 1; w < 64; w <<= 1) dot += __shfl_xor(dot, w);
+      if (lane == h) {
+        P[h * kPart + 128] = dot * n * a.qk_scale;
+        P[h * kPart + 129] = 1.0f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      P[h * kPart + lane] = n * lam0;
+      P[h * kPart + lane + 64] = n * lam1;
+    }
+  }
+}
+
+template <int NQ, bool APPEND>
 __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnArgs a, Tables tk, Tables tv) {
   // decode tables at fixed LDS addresses (static), per-wave slices after them
   __shared__ uint8_t sym8[2][kM];
   __shared__ uint2 symtab[2][kMaxLevels];
+  __shared__ uint4 etab[2][APPEND ? kMaxLevels : 1];
+  __shared__ float2 rdtab[2][APPEND ? kMaxHalf : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const DecTab dk{sym8[0], symtab[0]};
   const DecTab dv{sym8[1], symtab[1]};
   build_tables(sym8[0], symtab[0], tk, threadIdx.x, blockDim.x);
   build_tables(sym8[1], symtab[1], tv, threadIdx.x, blockDim.x);
+  if (APPEND) {
+    wave_encode_tables(tk, etab[0], rdtab[0], threadIdx.x);
+    wave_encode_tables(tv, etab[1], rdtab[1], threadIdx.x);
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -390,12 +478,34 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
   const uint8_t *vpool_end = a.vc + (size_t)a.Hkv * a.S * Cv;
   const int64_t W = (int64_t)gridDim.x * a.waves_per_block;
 
-  for (int64_t item = (int64_t)blockIdx.x * a.waves_per_block + wave; item < a.n_items; item += W) {
+  // items [0, n_enc): the append's encodes (K of every (b, g), then V);
+  // then the attention items, each one chunk of one (b, g)
+  const int64_t n_enc = APPEND ? 2 * (int64_t)a.B * a.Hkv : 0;
+  int64_t it = (int64_t)blockIdx.x * a.waves_per_block + wave;
+  for (; APPEND && it < n_enc; it += W) {
+    const bool isv = it >= n_enc / 2;
+    const int64_t e = isv ? it - n_enc / 2 : it;
+    const int b = (int)(e / a.Hkv), g = (int)(e - (int64_t)(e / a.Hkv) * a.Hkv);
+    wave_sync();  // the slice is free
+    // one call per kernel argument: a reference chosen at run time would put
+    // both tables in scratch memory
+    if (isv) {
+      if (tv.order == 1) append_vector<true>(a, tv, etab[1], rdtab[1], base, true, b, g, lane);
+      else append_vector<false>(a, tv, etab[1], rdtab[1], base, true, b, g, lane);
+    } else {
+      if (tk.order == 1) append_vector<true>(a, tk, etab[0], rdtab[0], base, false, b, g, lane);
+      else append_vector<false>(a, tk, etab[0], rdtab[0], base, false, b, g, lane);
+    }
+  }
+  for (; it < n_enc + a.n_items; it += W) {
+    const int64_t item = it - n_enc;
     const int c = (int)(item % a.nc);
     const int64_t bg = item / a.nc;
     const int b = (int)(bg / a.Hkv), g = (int)(bg - (int64_t)b * a.Hkv);
-    // a paged sequence never reads past its row of the page table
-    const int len = a.pages ? min(a.seq_len[b], a.max_pages * kTile) : a.seq_len[b];
+    // a paged sequence never reads past its row of the page table; with an
+    // append the newest token is not part of any chunk
+    const int len0 = a.seq_len[b] - (APPEND ? 1 : 0);
+    const int len = a.pages ? min(len0, a.max_pages * kTile) : len0;
     const int t0 = c * a.chunk;
     if (t0 >= len) continue;
     const int t1 = min(t0 + a.chunk, len);
@@ -513,9 +623,14 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
   const int b = blockIdx.x / a.Hq, h = blockIdx.x - b * a.Hq;
   const int g = h / a.group, hh = h - g * a.group;
   const int len = a.seq_len[b];
-  const int n = min((len + a.chunk - 1) / a.chunk, a.nc);
+  // with an append the chunks hold the len - 1 older tokens and the new
+  // token's partial sits apart
+  const bool extra = a.part_new != nullptr && len >= 1;
+  const int lc = a.part_new != nullptr ? len - 1 : len;
+  const int n = min((lc + a.chunk - 1) / a.chunk, a.nc);
   const float *src = a.part + (((int64_t)b * a.Hkv + g) * a.nc) * 4 * kPart + hh * kPart;
-  float M = -__builtin_inff();
+  const float *pe = extra ? a.part_new + ((int64_t)b * a.Hkv + g) * 4 * kPart + hh * kPart : nullptr;
+  float M = extra ? pe[128] : -__builtin_inff();
   for (int c = 0; c < n; ++c) M = fmaxf(M, src[(int64_t)c * 4 * kPart + 128]);
   float L = 0.0f, o = 0.0f;
   for (int c = 0; c < n; ++c) {
@@ -523,6 +638,11 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
     const float w = exp2f(p[128] - M);
     L += w * p[129];
     o += w * p[d];
+  }
+  if (extra) {
+    const float w = exp2f(pe[128] - M);
+    L += w * pe[129];
+    o += w * pe[d];
   }
   buf[d] = L > 0.0f ? o / L : 0.0f;  // an empty sequence (a caller error) gives a zero row
   // inverse rotation: o = D_V * H * o' / 128 (H * H = 128 I)
@@ -938,9 +1058,9 @@ __global__ void __launch_bounds__(128) prefill_combine_kernel(AttnArgs a, uint64
 
 // ---------------------------------------------------------------- planning
 struct Plan {
-  int chunk, nc, waves_per_block, blocks, nq;
+  int chunk, nc, waves_per_block, blocks_cap, nq;
   int64_t n_items;
-  size_t lds, qrot_bytes, part_bytes, total;
+  size_t lds, qrot_bytes, part_bytes, part_new_bytes, total;
 };
 
 // CU count of the current device, read once per process (thread-safe static
@@ -994,8 +1114,8 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   const int wb = wave_layout(Ck, Cv).bytes;
   const int lds_cap = 160 * 1024;
   int wpb = pl->nq == 3 ? 12 : 4;  // three waves per SIMD when the LDS allows (larger C: fewer)
-  while (wpb > 1 && kLutBytes + wpb * wb > lds_cap) wpb -= wpb > 4 ? 4 : 1;
-  if (kLutBytes + wpb * wb > lds_cap) return DQ_ERR_UNSUPPORTED;
+  while (wpb > 1 && kStaticLds + wpb * wb > lds_cap) wpb -= wpb > 4 ? 4 : 1;
+  if (kStaticLds + wpb * wb > lds_cap) return DQ_ERR_UNSUPPORTED;
   // chunk: aim for ~8 items per resident wave (8 waves per CU) if every
   // sequence were max_len; independent of C so the workspace size is too
   const int64_t chunk = choose_chunk((int64_t)B * Hkv, max_len, (int64_t)cus * 12);
@@ -1005,23 +1125,27 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   pl->waves_per_block = wpb;
   pl->n_items = (int64_t)B * Hkv * nc;
   pl->lds = (size_t)wpb * wb;  // dynamic part; the decode tables are static
-  const int64_t want_blocks = (pl->n_items + wpb - 1) / wpb;
-  pl->blocks = (int)(want_blocks < cus ? want_blocks : cus);
+  pl->blocks_cap = cus;  // one block per CU at most; fewer when the items are few
   pl->qrot_bytes = ((size_t)B * Hkv * kQrotPerBG * 2 + 255) & ~(size_t)255;
-  pl->part_bytes = (size_t)pl->n_items * 4 * kPart * sizeof(float);
-  pl->total = pl->qrot_bytes + pl->part_bytes;
+  pl->part_bytes = ((size_t)pl->n_items * 4 * kPart * sizeof(float) + 255) & ~(size_t)255;
+  pl->part_new_bytes = (size_t)B * Hkv * 4 * kPart * sizeof(float);  // the append's own partials
+  pl->total = pl->qrot_bytes + pl->part_bytes + pl->part_new_bytes;
   return DQ_OK;
 }
 
-template <int NQ>
+template <int NQ, bool APPEND>
 hipError_t launch_splitk(const Plan &pl, const AttnArgs &a, const Tables &tk, const Tables &tv, hipStream_t s) {
   // dynamic LDS beyond the default limit, requested once (thread-safe static)
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     160 * 1024 - kLutBytes);
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ, APPEND>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kStaticLds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(attn_splitk_kernel<NQ>, dim3((unsigned)pl.blocks), dim3(64 * pl.waves_per_block), pl.lds, s,
-                     a, tk, tv);
+  // the append's encode items come first, one per wave
+  const int64_t n = a.n_items + (APPEND ? 2 * (int64_t)a.B * a.Hkv : 0);
+  const int64_t want = (n + pl.waves_per_block - 1) / pl.waves_per_block;
+  const int blocks = (int)(want < pl.blocks_cap ? want : pl.blocks_cap);
+  hipLaunchKernelGGL((attn_splitk_kernel<NQ, APPEND>), dim3((unsigned)blocks), dim3(64 * pl.waves_per_block), pl.lds,
+                     s, a, tk, tv);
   return hipGetLastError();
 }
 
@@ -1159,14 +1283,24 @@ extern "C" int dq_attn_decode_workspace(int32_t B, int32_t Hq, int32_t Hkv, int6
   return DQ_OK;
 }
 
+// The new tokens of a decode step with append (null: no append).
+struct AppendArgs {
+  const void *k_new, *v_new;
+  int64_t stride_b, stride_h;
+  dq_stats *k_stats, *v_stats;
+};
+
 static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq, const uint8_t *k_cont,
                        const uint16_t *k_norm, const uint8_t *v_cont, const uint16_t *v_norm, int64_t num_slots,
                        const int64_t *seq_start, const int32_t *pages, int32_t max_pages,
                        const int32_t *seq_len, int64_t max_len, float sm_scale, int32_t out_dtype, void *out,
                        void *workspace, size_t ws_bytes, dq_stream_t stream, hipEvent_t split_begin,
-                       hipEvent_t split_end) {
+                       hipEvent_t split_end, const AppendArgs *app = nullptr) {
   if (!ck || !cv || !q || !k_cont || !k_norm || !v_cont || !v_norm || (!seq_start && !pages) || !seq_len ||
       !out || !workspace)
+    return DQ_ERR_INVALID;
+  if (app && (!app->k_new || !app->v_new || (reinterpret_cast<uintptr_t>(app->k_new) & 1u) ||
+              (reinterpret_cast<uintptr_t>(app->v_new) & 1u)))
     return DQ_ERR_INVALID;
   if (pages && (max_pages < 1 || max_len > (int64_t)max_pages * dq::kTile)) return DQ_ERR_INVALID;
   const int Hkv = ck->t.hkv;
@@ -1212,12 +1346,32 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
   a.out = out;
   a.out_bf16 = out_dtype;
   a.waves_per_block = pl.waves_per_block;
+  if (app) {
+    a.k_new = static_cast<const uint16_t *>(app->k_new);
+    a.v_new = static_cast<const uint16_t *>(app->v_new);
+    a.new_stride_b = app->stride_b;
+    a.new_stride_h = app->stride_h;
+    // the append entry points take the pools as writable
+    a.kc_w = const_cast<uint8_t *>(k_cont);
+    a.vc_w = const_cast<uint8_t *>(v_cont);
+    a.kn_w = const_cast<uint16_t *>(k_norm);
+    a.vn_w = const_cast<uint16_t *>(v_norm);
+    a.k_stats = app->k_stats;
+    a.v_stats = app->v_stats;
+    a.part_new = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.qrot_bytes + pl.part_bytes);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(dq::rotate_q_kernel, dim3((unsigned)(B * Hkv * 4)), dim3(64), 0, s, a, ck->t.seed);
   if (split_begin && hipEventRecord(split_begin, s) != hipSuccess) return DQ_ERR_HIP;
-  hipError_t e = pl.nq == 3   ? dq::launch_splitk<3>(pl, a, ck->t, cv->t, s)
-                 : pl.nq == 5 ? dq::launch_splitk<5>(pl, a, ck->t, cv->t, s)
-                              : dq::launch_splitk<9>(pl, a, ck->t, cv->t, s);
+  hipError_t e;
+  if (app)
+    e = pl.nq == 3   ? dq::launch_splitk<3, true>(pl, a, ck->t, cv->t, s)
+        : pl.nq == 5 ? dq::launch_splitk<5, true>(pl, a, ck->t, cv->t, s)
+                     : dq::launch_splitk<9, true>(pl, a, ck->t, cv->t, s);
+  else
+    e = pl.nq == 3   ? dq::launch_splitk<3, false>(pl, a, ck->t, cv->t, s)
+        : pl.nq == 5 ? dq::launch_splitk<5, false>(pl, a, ck->t, cv->t, s)
+                     : dq::launch_splitk<9, false>(pl, a, ck->t, cv->t, s);
   if (e != hipSuccess) return DQ_ERR_HIP;
   if (split_end && hipEventRecord(split_end, s) != hipSuccess) return DQ_ERR_HIP;
   hipLaunchKernelGGL(dq::combine_kernel, dim3((unsigned)(B * Hq)), dim3(128), 0, s, a, cv->t.seed);
@@ -1253,4 +1407,31 @@ extern "C" int dq_attn_decode_timed(dq_codec_t ck, dq_codec_t cv, const void *q,
   return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, nullptr, 0, seq_len,
                      max_len, sm_scale, out_dtype, out, workspace, ws_bytes, stream,
                      static_cast<hipEvent_t>(split_begin), static_cast<hipEvent_t>(split_end));
+}
+
+extern "C" int dq_attn_decode_append(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,
+                                     const void *k_new, const void *v_new, int64_t new_stride_b,
+                                     int64_t new_stride_h, uint8_t *k_cont, uint16_t *k_norm, uint8_t *v_cont,
+                                     uint16_t *v_norm, int64_t num_slots, const int64_t *seq_start,
+                                     const int32_t *seq_len, int64_t max_len, float sm_scale, int32_t out_dtype,
+                                     void *out, void *workspace, size_t ws_bytes, dq_stats *k_stats,
+                                     dq_stats *v_stats, dq_stream_t stream) {
+  const AppendArgs app{k_new, v_new, new_stride_b, new_stride_h, k_stats, v_stats};
+  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, nullptr, 0, seq_len,
+                     max_len, sm_scale, out_dtype, out, workspace, ws_bytes, stream, nullptr, nullptr, &app);
+}
+
+extern "C" int dq_attn_decode_paged_append(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,
+                                           const void *k_new, const void *v_new, int64_t new_stride_b,
+                                           int64_t new_stride_h, uint8_t *k_cont, uint16_t *k_norm,
+                                           uint8_t *v_cont, uint16_t *v_norm, int64_t num_slots,
+                                           const int32_t *pages, int32_t max_pages, const int32_t *seq_len,
+                                           int64_t max_len, float sm_scale, int32_t out_dtype, void *out,
+                                           void *workspace, size_t ws_bytes, dq_stats *k_stats,
+                                           dq_stats *v_stats, dq_stream_t stream) {
+  if (!pages) return DQ_ERR_INVALID;
+  const AppendArgs app{k_new, v_new, new_stride_b, new_stride_h, k_stats, v_stats};
+  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, nullptr, pages, max_pages,
+                     seq_len, max_len, sm_scale, out_dtype, out, workspace, ws_bytes, stream, nullptr, nullptr,
+                     &app);
 }

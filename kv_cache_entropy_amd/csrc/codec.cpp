@@ -143,7 +143,7 @@ const char *dq_status_string(int status) {
   }
 }
 
-int dq_version(void) { return 101; }
+int dq_version(void) { return 102; }
 
 int dq_codec_create(const dq_codec_desc *desc, dq_codec_t *out) {
   if (!desc || !out) return DQ_ERR_INVALID;

@@ -34,6 +34,7 @@
 #include <cstdlib>
 
 #include "dq_internal.h"
+#include "encode_wave.h"
 
 namespace dq {
 namespace {
@@ -50,43 +51,6 @@ struct EncodeArgs {
   uint16_t *norm;
   dq_stats *stats;
 };
-
-__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
-  uint64_t z = seed + (n + 1) * 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-
-__device__ __forceinline__ float half_to_float(uint32_t h) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-
-// fp16 nearest to sqrt(S) (ties to even), exactly: a candidate from the
-// hardware square root and conversion, then corrected against the squared
-// midpoints to its neighbours.  Midpoints of adjacent fp16 values have at
-// most 12 significant bits, so mid * mid is exact in fp32 and the compares
-// decide the rounding of the exact square root.
-__device__ __forceinline__ uint32_t norm_half(float S) {
-  if (S != S) return 0x7E00u;
-  if (S == __builtin_inff()) return 0x7C00u;
-  uint32_t hb = __builtin_bit_cast(uint16_t, (_Float16)__builtin_sqrtf(S));
-  if (hb < 0x7C00u) {
-    const float hv = half_to_float(hb);
-    const float up = hb == 0x7BFFu ? 65536.0f : half_to_float(hb + 1);
-    const float mid = (hv + up) * 0.5f;
-    const float m2 = mid * mid;
-    if (S > m2 || (S == m2 && (hb & 1u))) ++hb;
-  }
-  if (hb > 0u) {
-    const float hv = hb == 0x7C00u ? 65536.0f : half_to_float(hb);
-    const float lo = half_to_float(hb - 1);
-    const float mid = (lo + hv) * 0.5f;
-    const float m2 = mid * mid;
-    if (S < m2 || (S == m2 && (hb & 1u))) --hb;
-  }
-  return hb;
-}
 
 __device__ __forceinline__ uint32_t nib(const uint32_t (&w)[16], int i) {
   return (w[i >> 3] >> (4 * (i & 7))) & 15u;
@@ -236,8 +200,8 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
     const int64_t slot = a.slots[tok];
     const bool in_pool = slot >= 0 && slot < a.num_slots;  // out-of-range slots write nothing
     const uint4 *src = reinterpret_cast<const uint4 *>(a.x + tok * a.stride_t + (int64_t)g * a.stride_h);
-    const uint64_t s0 = splitmix64(t.seed, 2ull * (uint64_t)g);
-    const uint64_t s1 = splitmix64(t.seed, 2ull * (uint64_t)g + 1ull);
+    const uint64_t s0 = dev_splitmix64(t.seed, 2ull * (uint64_t)g);
+    const uint64_t s1 = dev_splitmix64(t.seed, 2ull * (uint64_t)g + 1ull);
 
     // ---- drift.  I(k), the ideal code length of the symbols after the
     // first k moves (sum of log2(4096 / f), fixed point), decides whether
@@ -475,202 +439,39 @@ constexpr int kWaveVecs = 4;  // vectors (waves) per block
 template <bool RD>  // drift order: rate-distortion (true) or magnitude (false)
 __device__ __forceinline__ void wave_encode_block(const EncodeArgs &a, const Tables &t, int64_t block) {
   __shared__ uint4 etab[kMaxLevels];
-  __shared__ uint32_t ent[kWaveVecs][kD];          // s0 | sd << 8 | rank << 16
-  __shared__ float yabs[kWaveVecs][kD];
+  __shared__ float2 rdtab[kMaxHalf];
+  __shared__ uint32_t ent[kWaveVecs][kD];
+  __shared__ float key[kWaveVecs][kD];
   __shared__ uint8_t mag[kWaveVecs][kD];
-  __shared__ uint8_t scr[kWaveVecs][kScr * 64];   // renorm bytes, lane-minor
-  __shared__ float2 rdtab[kMaxHalf];              // {l_m + l_{m-1}, w_m} for the rate-distortion key
-  __shared__ uint32_t bstat[6 + kMaxC + 1];       // per-block stats, flushed once
+  __shared__ uint8_t scr[kWaveVecs][kWaveScr * 64];
+  __shared__ uint32_t bstat[6 + kMaxC + 1];  // per-block stats, flushed once
   const int tid = threadIdx.x;
   for (int k = tid; k < 6 + kMaxC + 1; k += 64 * kWaveVecs) bstat[k] = 0u;
-  if (tid < t.levels) {
-    const uint32_t f = t.freq[tid];
-    etab[tid] = make_uint4(f << 19, t.magic[tid], t.cum[tid], (kM - f) | ((uint32_t)t.shift[tid] << 16));
-  }
-  if (tid >= 1 && tid < t.half)
-    rdtab[tid] = make_float2(half_to_float(t.recon[t.half + tid]) + half_to_float(t.recon[t.half + tid - 1]),
-                             t.rd_w[tid]);
+  wave_encode_tables(t, etab, rdtab, tid);
   __syncthreads();
   const int w = tid >> 6, lane = tid & 63;
   const int64_t nvec = a.T * (int64_t)t.hkv;
   const int64_t vid = block * kWaveVecs + w;
   if (vid < nvec) {  // whole waves; every wave reaches the block barrier below
-    const int h = t.half, C = t.C;
     const int g = (int)(vid / a.T);
     const int64_t tok = vid - (int64_t)g * a.T;
     const int64_t slot = a.slots[tok];
-    const uint16_t *xp = a.x + tok * a.stride_t + (int64_t)g * a.stride_h;
-    const float x0 = __uint_as_float((uint32_t)xp[lane] << 16);
-    const float x1 = __uint_as_float((uint32_t)xp[lane + 64] << 16);
-
-    // ||x||^2: level 64 in-lane, then levels 32 .. 1 across lanes
-    float sq = x0 * x0 + x1 * x1;
-#pragma unroll
-    for (int wd = 32; wd >= 1; wd >>= 1) {
-      const float o = __shfl_down(sq, wd);
-      if (lane < wd) sq = sq + o;
-    }
-    const float S = __shfl(sq, 0);
-
-    // y = H * D * x
-    const uint64_t s0w = splitmix64(t.seed, 2ull * (uint64_t)g);
-    const uint64_t s1w = splitmix64(t.seed, 2ull * (uint64_t)g + 1ull);
-    float u0 = ((s0w >> lane) & 1ull) ? -x0 : x0;
-    float u1 = ((s1w >> lane) & 1ull) ? -x1 : x1;
-#pragma unroll
-    for (int wd = 1; wd < 64; wd <<= 1) {
-      const float p0 = __shfl_xor(u0, wd), p1 = __shfl_xor(u1, wd);
-      const bool hi = lane & wd;
-      u0 = hi ? p0 - u0 : u0 + p0;
-      u1 = hi ? p1 - u1 : u1 + p1;
-    }
-    {
-      const float p = u0, q = u1;
-      u0 = p + q;
-      u1 = p - q;
-    }
-
-    const uint32_t nh = norm_half(S);
-    const float nf = half_to_float(nh);
-    const bool zero = nh == 0u;
-    const bool bad = (nh & 0x7C00u) == 0x7C00u;
-    const bool degenerate = zero || bad;
-    float thr[kMaxHalf];
-#pragma unroll
-    for (int k = 1; k < kMaxHalf; ++k)
-      thr[k] = (k < h && !degenerate) ? (float)(k * t.step64) * nf * 0.015625f : __builtin_inff();
-    uint32_t sA[2], mA[2];
-    float yA[2];
-    const float ys[2] = {u0, u1};
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float ay = degenerate ? 0.0f : __builtin_fabsf(ys[e]);
-      uint32_t m = 0;
-#pragma unroll
-      for (int k = 1; k < kMaxHalf; ++k) m += ay >= thr[k] ? 1u : 0u;
-      sA[e] = (degenerate || ys[e] >= 0.0f) ? (uint32_t)h + m : (uint32_t)(h - 1) - m;
-      mA[e] = m;
-      yA[e] = ay;
-    }
-    uint32_t *E = ent[w];
-    float *Y = yabs[w];
-    uint8_t *Mg = mag[w];
-    uint8_t *scol = scr[w];
-
-    int moves = 0, passes = 0, okB = 0;
-    uint32_t okx = 0;
-    int win = -1;
-    for (int outer = 0; outer < 2 * kD && win < 0; ++outer) {
-      // ranks of the candidates (magnitude >= 1) in drift order.  Magnitude
-      // order compares (m desc, |y| asc); rate-distortion order compares its
-      // key (2|y| - n (l_m + l_{m-1})) * w_m ascending, n (l_m + l_{m-1})
-      // being exact in fp32.  Both then break ties by index.
-      constexpr bool rd = RD;
-      float kA[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        float key = yA[e];
-        if (rd && mA[e] >= 1u) {
-          const float2 r = rdtab[mA[e]];
-          const float tt = nf * r.x;
-          key = (2.0f * yA[e] - tt) * r.y;
-        }
-        kA[e] = key;
-      }
-      Mg[lane] = (uint8_t)mA[0];
-      Mg[lane + 64] = (uint8_t)mA[1];
-      Y[lane] = kA[0];
-      Y[lane + 64] = kA[1];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      int rank[2] = {0, 0};
-      for (int j = 0; j < kD; ++j) {
-        const uint32_t mj = Mg[j];
-        const float yj = Y[j];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int i = lane + 64 * e;
-          const bool tie_first = yj < kA[e] || (yj == kA[e] && j < i);
-          const bool before = mj >= 1u && (rd ? tie_first : (mj > mA[e] || (mj == mA[e] && tie_first)));
-          rank[e] += before ? 1 : 0;
-        }
-      }
-      int total = 0;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) total += __popcll(__ballot(mA[e] >= 1u));
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t sd = mA[e] >= 1u ? (sA[e] >= (uint32_t)h ? sA[e] - 1u : sA[e] + 1u) : sA[e];
-        const uint32_t rk = mA[e] >= 1u ? (uint32_t)rank[e] : 255u;
-        E[lane + 64 * e] = sA[e] | (sd << 8) | (rk << 16);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int k0 = 0; k0 <= total && win < 0; k0 += 64) {
-        const uint32_t k = (uint32_t)(k0 + lane);
-        uint32_t x = kLow;
-        int pos = kScr - 1;
-        for (int i = kD - 1; i >= 0; --i) {
-          const uint32_t en = E[i];
-          const uint32_t s = ((en >> 16) & 0xFFu) < k ? ((en >> 8) & 0xFFu) : (en & 0xFFu);
-          const uint4 c = etab[s];
-          scol[pos * 64 + lane] = (uint8_t)x;
-          const bool emit = x >= c.x;
-          x = emit ? x >> 8 : x;
-          pos -= emit ? 1 : 0;
-          const uint32_t q = __umulhi(x, c.y) >> (c.w >> 16);
-          x = x + c.z + __umul24(q, c.w & 0xFFFFu);
-        }
-        const int B = kScr - 1 - pos;
-        const bool fits = 4 + B <= C && (int)k <= total;
-        const uint64_t vote = __ballot(fits);
-        if (vote) {
-          win = __ffsll((unsigned long long)vote) - 1;
-          okB = __shfl(B, win);
-          okx = (uint32_t)__shfl((int)x, win);
-          moves += k0 + win;
-        }
-      }
-      if (win < 0) {
-        // every candidate moved and the stream still does not fit: keep the
-        // moves and rank again on the new symbols
-        moves += total;
-        ++passes;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          if (mA[e] >= 1u) {
-            sA[e] = sA[e] >= (uint32_t)h ? sA[e] - 1u : sA[e] + 1u;
-            mA[e] -= 1u;
-          }
-        }
-      }
-    }
-
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (win >= 0 && slot >= 0 && slot < a.num_slots) {
-      uint8_t *dst = a.cont + ((int64_t)g * a.num_slots + slot) * C;
-      for (int j = lane; j < C; j += 64) {
-        uint8_t b;
-        if (j < 4) b = (uint8_t)(okx >> (8 * j));
-        else b = (j - 4 < okB) ? scol[(kScr - okB + (j - 4)) * 64 + win] : (uint8_t)0;
-        dst[j] = b;
-      }
-      if (lane == 0) a.norm[(int64_t)g * a.num_slots + slot] = (uint16_t)nh;
-    }
+    const WaveEncodeScratch L{ent[w], key[w], mag[w], scr[w], kWaveScr};
+    WaveEncodeResult r;
+    wave_encode_vector<RD, false>(a.x + tok * a.stride_t + (int64_t)g * a.stride_h, g, t, etab, rdtab, L, lane, r);
+    if (r.win >= 0 && slot >= 0 && slot < a.num_slots)
+      wave_store_container(r, L, t.C, a.cont + ((int64_t)g * a.num_slots + slot) * t.C,
+                           a.norm + (int64_t)g * a.num_slots + slot, lane);
     if (a.stats && lane == 0) {
       atomicAdd(&bstat[0], 1u);
-      if (moves) {
+      if (r.moves) {
         atomicAdd(&bstat[1], 1u);
-        atomicAdd(&bstat[2], (uint32_t)moves);
+        atomicAdd(&bstat[2], (uint32_t)r.moves);
       }
-      if (passes) atomicAdd(&bstat[3], (uint32_t)passes);
-      if (bad) atomicAdd(&bstat[4], 1u);
-      if (zero) atomicAdd(&bstat[5], 1u);
-      atomicAdd(&bstat[6 + 4 + okB], 1u);
+      if (r.passes) atomicAdd(&bstat[3], (uint32_t)r.passes);
+      if (r.bad) atomicAdd(&bstat[4], 1u);
+      if (r.zero) atomicAdd(&bstat[5], 1u);
+      atomicAdd(&bstat[6 + 4 + r.okB], 1u);
     }
   }
   if (a.stats) {

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     L = _lib.lib()
-    assert L.dq_version() == 101
+    assert L.dq_version() == 102
     assert L.dq_status_string(0) == b"ok"
     for code in (-1, -2, -3, -4, -5):
         assert L.dq_status_string(code) not in (b"ok", b"unknown status")
@@ -161,6 +161,33 @@ def test_paged_attention_argument_checks():
     short = list(base)
     short[13] = 129  # max_len > max_pages * 64
     assert L.dq_attn_decode_paged(*short) == -1
+
+
+def test_append_argument_checks():
+    """The decode-with-append entry points reject missing or misaligned new
+    tokens and a missing page table before touching the device."""
+    L = _lib.lib()
+    c = dq.Codec(8, 34, seed=1, kv_heads=2)
+    v = dq.Codec(6, 34, seed=2, kv_heads=2)
+    vp = ctypes.c_void_p
+    fake = vp(256)
+    # ck cv q B Hq k_new v_new stride_b stride_h kc kn vc vn S seq_start seq_len max_len
+    # sm_scale out_dtype out ws ws_bytes k_stats v_stats stream
+    base = [c.handle, v.handle, fake, 1, 4, fake, fake, 256, 128, fake, fake, fake, fake, 64, fake, fake, 128,
+            ctypes.c_float(0.1), 0, fake, fake, 1 << 20, None, None, None]
+    for idx in (5, 6):
+        bad = list(base)
+        bad[idx] = None
+        assert L.dq_attn_decode_append(*bad) == -1
+        bad[idx] = vp(257)  # bf16 needs 2-byte alignment
+        assert L.dq_attn_decode_append(*bad) == -1
+    paged = base[:14] + [fake, 2] + base[15:]
+    nopages = list(paged)
+    nopages[14] = None
+    assert L.dq_attn_decode_paged_append(*nopages) == -1
+    short = list(paged)
+    short[17] = 129  # max_len > max_pages * 64
+    assert L.dq_attn_decode_paged_append(*short) == -1
 
 
 def test_drift_order_codec():

@@ -179,9 +179,9 @@ def test_decode_symbols_bit_exact(oracle_lib, levels, C):
 
 
 def _attn_case(O, B, Hq, hkv, lens, kinds=("outlier", "outlier"), C=(34, 34), seed=0, gap=5,
-               levels=(8, 6), step64=(0, 0)):
-    ck, ock = _codecs(O, levels[0], C[0], seed=seed + 1, hkv=hkv, step64=step64[0])
-    cv, ocv = _codecs(O, levels[1], C[1], seed=seed + 2, hkv=hkv, step64=step64[1])
+               levels=(8, 6), step64=(0, 0), order=(0, 0)):
+    ck, ock = _codecs(O, levels[0], C[0], seed=seed + 1, hkv=hkv, step64=step64[0], order=order[0])
+    cv, ocv = _codecs(O, levels[1], C[1], seed=seed + 2, hkv=hkv, step64=step64[1], order=order[1])
     starts, s = [], 0
     for L in lens:
         starts.append(s)
@@ -289,6 +289,61 @@ def test_attention_empty_sequence_gives_zero_row(oracle_lib):
     assert torch.equal(got[0], ref[0]) and torch.equal(got[2], ref[2])
 
 
+def _append_both(c, k_new, v_new, max_len):
+    """One decode step with append two ways on copies of the pools:
+    dq.encode_kv then dq.attn_decode, and dq.attn_decode_append.  Returns
+    (pools, stats, out) of each."""
+    lens = c["lens"] + 1
+    sl = torch.from_numpy(lens.astype(np.int32)).to(DEV)
+    slots = torch.from_numpy((c["starts"] + c["lens"]).astype(np.int64)).to(DEV)
+    res = []
+    for fused in (False, True):
+        pools = [t.clone() for t in (c["kc"], c["kn"], c["vc"], c["vn"])]
+        st = (dq.new_stats(DEV), dq.new_stats(DEV))
+        if fused:
+            out = dq.attn_decode_append(c["ck"], c["cv"], c["q"], k_new, v_new, *pools, c["ss"], sl, max_len,
+                                        k_stats=st[0], v_stats=st[1])
+        else:
+            dq.encode_kv(c["ck"], c["cv"], k_new, v_new, slots, *pools, k_stats=st[0], v_stats=st[1])
+            out = dq.attn_decode(c["ck"], c["cv"], c["q"], *pools, c["ss"], sl, max_len)
+        torch.cuda.synchronize()
+        res.append((pools, st, out))
+    return res, lens
+
+
+@pytest.mark.parametrize("Hq,hkv,lens,order,C,split", [
+    (8, 2, [0, 1, 63, 64, 65, 300, 1408, 2000], (0, 0), (34, 34), None),
+    (4, 4, [0, 127, 128, 129, 1500], (1, 1), (34, 34), 128),
+    (4, 2, [4095, 4096, 700], (0, 1), (29, 29), None),
+    (1, 1, [640, 5], (1, 0), (34, 29), 192),
+])
+def test_attention_append(oracle_lib, monkeypatch, Hq, hkv, lens, order, C, split):
+    """Decode with append in one launch: the new containers, norms and stats
+    equal those of dq_encode_kv bit for bit, the output matches encode-then-
+    attention up to fp32 order and the fp64 oracle within tolerance.  Old
+    lengths 0 (the new token alone) and chunk boundaries at the new token
+    (forced splits of 128 and 192 tokens) included."""
+    O = oracle_lib
+    if split:
+        monkeypatch.setenv("DQ_SPLIT_TOKENS", str(split))
+    c = _attn_case(O, len(lens), Hq, hkv, lens, C=C, seed=61 + Hq, order=order)
+    B = len(lens)
+    k_new = synth.kv_tensor("outlier", B, hkv, seed=71 + Hq, device=DEV)
+    v_new = synth.kv_tensor("student_t5", B, hkv, seed=72 + Hq, device=DEV)
+    max_len = max(lens) + 1
+    (pa, sa, oa), (pb, sb, ob) = _append_both(c, k_new, v_new, max_len)[0]
+    for x, y, name in zip(pa, pb, ("k_cont", "k_norm", "v_cont", "v_norm")):
+        assert torch.equal(x, y), f"append: {name} differs from dq_encode_kv"
+    for x, y in zip(sa, sb):
+        assert dq.stats_dict(x) == dq.stats_dict(y)
+    assert dq.stats_dict(sb[0])["vectors"] == B * hkv
+    diff = float((oa - ob).abs().max())
+    _say(f"append vs encode-then-attention: max-abs {diff:.3e}")
+    assert diff <= 1e-5
+    c2 = dict(c, kc=pb[0], kn=pb[1], vc=pb[2], vn=pb[3], lens=np.array(lens, np.int32) + 1)
+    _assert_close(ob.cpu().numpy(), _oracle_attn(O, c2), f"append Hq={Hq} hkv={hkv}")
+
+
 def _paged_copy(c, rng, extra_pages=5):
     """The contiguous pools of an attention case re-laid as shuffled 64-token
     pages in a larger pool, with the page table that addresses them."""
@@ -338,6 +393,38 @@ def test_attention_paged_pool(oracle_lib):
                                 _np_bits(pools["K"][1]), pools["V"][0].cpu().numpy(),
                                 _np_bits(pools["V"][1]), pages, c["lens"])
         _assert_close(out.cpu().numpy(), ref, f"paged Hq={Hq} hkv={hkv}")
+
+
+def test_attention_paged_append(oracle_lib):
+    """Decode with append over shuffled 64-token pages: each new token lands
+    in its page's slot with the bytes of the contiguous append (also when it
+    opens a new page), and the output equals the contiguous one bit for
+    bit."""
+    O = oracle_lib
+    rng = np.random.default_rng(23)
+    lens = [0, 63, 64, 65, 300, 127]
+    B = len(lens)
+    c = _attn_case(O, B, 8, 2, lens, seed=44, gap=64)
+    k_new = synth.kv_tensor("outlier", B, 2, seed=81, device=DEV)
+    v_new = synth.kv_tensor("outlier", B, 2, seed=82, device=DEV)
+    max_len = max(lens) + 1
+    (_, _, _), (pb, sb, ob) = _append_both(c, k_new, v_new, max_len)[0]
+    pools, pages = _paged_copy(dict(c, lens=c["lens"] + 1), rng)
+    pg = torch.from_numpy(pages).to(DEV)
+    sl = torch.from_numpy((c["lens"] + 1).astype(np.int32)).to(DEV)
+    st = (dq.new_stats(DEV), dq.new_stats(DEV))
+    outp = dq.attn_decode_paged_append(c["ck"], c["cv"], c["q"], k_new, v_new, *pools["K"], *pools["V"], pg, sl,
+                                       max_len, k_stats=st[0], v_stats=st[1])
+    torch.cuda.synchronize()
+    assert torch.equal(outp, ob), "paged and contiguous append results differ"
+    P = dq.PAGE_TOKENS
+    for b, L in enumerate(lens):
+        sp = int(pages[b, L // P]) * P + L % P
+        sc = int(c["starts"][b]) + L
+        for (cont, norm), cc, nc in ((pools["K"], pb[0], pb[1]), (pools["V"], pb[2], pb[3])):
+            assert torch.equal(cont[:, sp], cc[:, sc]) and torch.equal(norm[:, sp], nc[:, sc])
+    for x, y in zip(st, sb):
+        assert dq.stats_dict(x) == dq.stats_dict(y)
 
 
 def test_attention_paged_ids_outside_pool_read_zeros(oracle_lib):
@@ -507,6 +594,30 @@ def test_llama31_b128_8k_bench_configuration(oracle_lib):
                                 lens.to(torch.int32).to(DEV), int(c["ctx"].max()) + 19)
     torch.cuda.synchronize()
     assert torch.equal(outp, out), "paged pool differs from the contiguous pool at full size"
+    # the next decode step as one launch (append + attention): the new
+    # containers, norms and stats bit-exact against the oracle's encode,
+    # sampled rows within tolerance of the oracle's attention
+    w = c["w"]
+    k_new = synth.kv_tensor(w.kind, B, w.hkv, seed=w.seed + 30, device=DEV)
+    v_new = synth.kv_tensor(w.kind, B, w.hkv, seed=w.seed + 31, device=DEV)
+    lens2 = lens + 1
+    slots_np = (c["starts"] + lens.numpy()).astype(np.int64)
+    kc, kn = c["pools"]["K"]
+    vc, vn = c["pools"]["V"]
+    st = (dq.new_stats(DEV), dq.new_stats(DEV))
+    out2 = dq.attn_decode_append(c["ck"], c["cv"], q, k_new, v_new, kc, kn, vc, vn,
+                                 torch.from_numpy(c["starts"]).to(DEV), lens2.to(torch.int32).to(DEV),
+                                 int(c["ctx"].max()) + 19, k_stats=st[0], v_stats=st[1])
+    torch.cuda.synchronize()
+    for x, oc, (cont, norm), s in ((k_new, c["ock"], (kc, kn), st[0]), (v_new, c["ocv"], (vc, vn), st[1])):
+        ocont, onorm, ost = O.encode(oc, _np_bits(x), slots_np, num_slots=cont.shape[1])
+        assert (cont[:, slots_np].cpu().numpy() == ocont[:, slots_np]).all(), "fused append containers differ"
+        assert (_np_bits(norm[:, slots_np]) == onorm[:, slots_np]).all()
+        assert dq.stats_dict(s) == O_stats(ost)
+    rows = [3, 64, 126]
+    ref = O.attention(c["ock"], c["ocv"], _np_bits(q)[rows], kc.cpu().numpy(), _np_bits(kn), vc.cpu().numpy(),
+                      _np_bits(vn), c["starts"][rows], lens2.numpy().astype(np.int32)[rows])
+    _assert_close(out2.cpu().numpy()[rows], ref, f"llama31 b128 fused append rows {rows}")
 
 
 def test_longctx_b4_64k_c29(oracle_lib):
