@@ -617,8 +617,70 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 }
 
 // ---------------------------------------------------------------- combine
+// Log-sum-exp merge of a row's partials for the 128 threads of a block
+// (thread d owns dim d): partial c sits at src + c * stride floats (acc
+// [0, 128), m at 128, l at 129), plus an optional extra one (pe).  Returns
+// sum_c w_c acc_c[d] / sum_c w_c l_c with w_c = 2^(m_c - M), M the largest
+// m; a partial with m = -inf (no visible token) weighs nothing.  The maxima
+// and weights are taken 128 partials at a time, one per thread, so the
+// latency is that of a few loads, not of n dependent ones; each thread then
+// sums its dim in partial order.
+__device__ __forceinline__ float lse_merge(const float *src, int64_t stride, int n, const float *pe, float *red,
+                                           float *wts) {
+  const int d = threadIdx.x;
+  float M = pe ? pe[128] : -__builtin_inff();
+  for (int c = d; c < n; c += kD) M = fmaxf(M, src[(int64_t)c * stride + 128]);
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w));
+  if ((d & 63) == 0) red[d >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  float Lp = 0.0f, o = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += kD) {
+    const int cnt = min(kD, n - c0);
+    float w = 0.0f;
+    if (d < cnt) {
+      const float *p = src + (int64_t)(c0 + d) * stride;
+      const float m = p[128];
+      if (m != -__builtin_inff()) {
+        w = exp2f(m - M);
+        Lp += w * p[129];
+      }
+    }
+    __syncthreads();  // the previous round's weights are read
+    wts[d] = w;
+    __syncthreads();
+    const float *p = src + (int64_t)c0 * stride + d;
+    int j = 0;
+    for (; j + 4 <= cnt; j += 4) {
+      const float a0 = p[(int64_t)j * stride], a1 = p[(int64_t)(j + 1) * stride];
+      const float a2 = p[(int64_t)(j + 2) * stride], a3 = p[(int64_t)(j + 3) * stride];
+      if (wts[j] != 0.0f) o += wts[j] * a0;
+      if (wts[j + 1] != 0.0f) o += wts[j + 1] * a1;
+      if (wts[j + 2] != 0.0f) o += wts[j + 2] * a2;
+      if (wts[j + 3] != 0.0f) o += wts[j + 3] * a3;
+    }
+    for (; j < cnt; ++j)
+      if (wts[j] != 0.0f) o += wts[j] * p[(int64_t)j * stride];
+  }
+  if (pe) {
+    const float w = exp2f(pe[128] - M);
+    if (d == 0) Lp += w * pe[129];
+    o += w * pe[d];
+  }
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) Lp += __shfl_xor(Lp, w);
+  __syncthreads();  // red[0..1] and wts are free again
+  if ((d & 63) == 0) red[d >> 6] = Lp;
+  __syncthreads();
+  const float L = red[0] + red[1];
+  return L > 0.0f ? o / L : 0.0f;  // an empty row (a caller error) gives zeros
+}
+
 __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed) {
   __shared__ float buf[kD];
+  __shared__ float wts[kD];
+  __shared__ float red[2];
   const int d = threadIdx.x;
   const int b = blockIdx.x / a.Hq, h = blockIdx.x - b * a.Hq;
   const int g = h / a.group, hh = h - g * a.group;
@@ -627,24 +689,10 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
   // token's partial sits apart
   const bool extra = a.part_new != nullptr && len >= 1;
   const int lc = a.part_new != nullptr ? len - 1 : len;
-  const int n = min((lc + a.chunk - 1) / a.chunk, a.nc);
+  const int n = max(0, min((lc + a.chunk - 1) / a.chunk, a.nc));
   const float *src = a.part + (((int64_t)b * a.Hkv + g) * a.nc) * 4 * kPart + hh * kPart;
   const float *pe = extra ? a.part_new + ((int64_t)b * a.Hkv + g) * 4 * kPart + hh * kPart : nullptr;
-  float M = extra ? pe[128] : -__builtin_inff();
-  for (int c = 0; c < n; ++c) M = fmaxf(M, src[(int64_t)c * 4 * kPart + 128]);
-  float L = 0.0f, o = 0.0f;
-  for (int c = 0; c < n; ++c) {
-    const float *p = src + (int64_t)c * 4 * kPart;
-    const float w = exp2f(p[128] - M);
-    L += w * p[129];
-    o += w * p[d];
-  }
-  if (extra) {
-    const float w = exp2f(pe[128] - M);
-    L += w * pe[129];
-    o += w * pe[d];
-  }
-  buf[d] = L > 0.0f ? o / L : 0.0f;  // an empty sequence (a caller error) gives a zero row
+  buf[d] = lse_merge(src, 4 * kPart, n, pe, red, wts);  // an empty sequence (a caller error) gives a zero row
   // inverse rotation: o = D_V * H * o' / 128 (H * H = 128 I)
 #pragma unroll
   for (int w = 1; w < kD; w <<= 1) {
@@ -1013,6 +1061,8 @@ __global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk
 
 __global__ void __launch_bounds__(128) prefill_combine_kernel(AttnArgs a, uint64_t vseed) {
   __shared__ float buf[kD];
+  __shared__ float wts[kD];
+  __shared__ float red[2];
   const int d = threadIdx.x;
   int64_t blk = blockIdx.x;  // (b * Tq + tq) * Hq + h
   const int h = (int)(blk % a.Hq);
@@ -1024,17 +1074,8 @@ __global__ void __launch_bounds__(128) prefill_combine_kernel(AttnArgs a, uint64
   const int pos = a.seq_len[b] - a.Tq + tq;
   const int n = pos < 0 ? 0 : min(pos / a.chunk + 1, a.nc);
   const float *src = a.part + ((((int64_t)b * a.Hkv + g) * a.nqb + qb) * a.nc) * kRows * kPart + r * kPart;
-  float M = -__builtin_inff();
-  for (int c = 0; c < n; ++c) M = fmaxf(M, src[(int64_t)c * kRows * kPart + 128]);
-  float Ls = 0.0f, o = 0.0f;
-  for (int c = 0; c < n; ++c) {
-    const float *p = src + (int64_t)c * kRows * kPart;
-    if (p[128] == -__builtin_inff()) continue;  // no token of this chunk is visible to the row
-    const float w = exp2f(p[128] - M);
-    Ls += w * p[129];
-    o += w * p[d];
-  }
-  buf[d] = Ls > 0.0f ? o / Ls : 0.0f;
+  // a chunk with no token visible to the row has m = -inf and weighs nothing
+  buf[d] = lse_merge(src, kRows * kPart, n, nullptr, red, wts);
 #pragma unroll
   for (int w = 1; w < kD; w <<= 1) {
     __syncthreads();
@@ -1079,15 +1120,17 @@ int device_cus() {
 // `chunk` tokens) round-robin to W resident waves, so it takes about
 // ceil(units * nc / W) rounds of (chunk + c0) token-times, c0 being an
 // item's fixed cost (a K-only and a V-only tile pass and the partial; about
-// 32 tokens on MI355X).  The chunk (a multiple of the 64-token tile, 128 to
+// 32 tokens on MI355X).  The chunk (a multiple of the 64-token tile, 64 to
 // 2048: only max_len is known here, and ragged batches need the finer
 // items to balance) minimising that is chosen; W is a fixed function of the
-// CU count, so the workspace size depends only on the call's shape.
+// CU count, so the workspace size depends only on the call's shape.  Small
+// batches get one-tile chunks: an item is then a K pass and a V pass, the
+// shortest latency a wave can give a tile.
 // DQ_SPLIT_TOKENS forces a chunk (tests use it).
 int64_t choose_chunk(int64_t units, int64_t max_len, int64_t W) {
   const int64_t c0 = 32;
   int64_t best = 1024, best_cost = INT64_MAX;
-  for (int64_t chunk = 128; chunk <= 2048; chunk += kTile) {
+  for (int64_t chunk = kTile; chunk <= 2048; chunk += kTile) {
     const int64_t nc = (max_len + chunk - 1) / chunk;
     const int64_t span = nc == 1 ? ((max_len + kTile - 1) / kTile) * kTile : chunk;
     const int64_t rounds = (units * nc + W - 1) / W;
