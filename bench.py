@@ -14,7 +14,7 @@ Untimed setup: draw K/V, encode the whole prompt into the compressed pools
 step / wall time per step.  The roofline entry measures the attention call
 alone with HIP events on its stream inside the timed region.  The same steps
 are then timed as one launch each (dq_attn_decode_append), also at batch 1
-and 4, next to the two-launch form.
+and 4, next to the two-launch form, eagerly and as HIP-graph replays.
 
     python bench.py [--steps 16] [--warmup 3] [--workload NAME]
 """
@@ -408,7 +408,7 @@ def main():
     # (the first sequences), where the saved launch matters most.
     fused = None
     if not args.no_fused:
-        def fused_ms(nb, fused_call):
+        def fused_ms(nb, fused_call, graph=False):
             qb = [qs[s][:nb].contiguous() for s in range(nsteps)]
             kb = [Kn[s][:nb] for s in range(nsteps)]
             vb = [Vn[s][:nb] for s in range(nsteps)]
@@ -430,6 +430,26 @@ def main():
                 one(s)
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if graph:
+                # one step captured once (HIP graph), replayed: the launches
+                # cost no host time; the step re-encodes the same token
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    one(args.warmup)
+                torch.cuda.current_stream().wait_stream(side)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    one(args.warmup)
+                g.replay()
+                torch.cuda.synchronize()
+                e0.record()
+                for k in range(args.steps):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) / args.steps
             e0.record()
             for k in range(args.steps):
                 one(args.warmup + k)
@@ -441,13 +461,17 @@ def main():
         small = {}
         for nb in (1, 4):
             small[str(nb)] = {"fused_ms": round(fused_ms(nb, True), 4),
-                              "separate_ms": round(fused_ms(nb, False), 4)}
+                              "separate_ms": round(fused_ms(nb, False), 4),
+                              "fused_graph_ms": round(fused_ms(nb, True, graph=True), 4),
+                              "separate_graph_ms": round(fused_ms(nb, False, graph=True), 4)}
         fused = {"batch": B, "ms_per_step": round(f_ms, 4), "gbps": round(alg_bytes / (f_ms / 1e3) / 1e9, 2),
                  "separate_ms_per_step": round(ms_per_step, 4), "small_batch": small,
                  "call": "dq_attn_decode_append"}
         log(f"[bench] fused append: {f_ms:.3f} ms/step ({fused['gbps']:.1f} GB/s) vs {ms_per_step:.3f} ms as two "
-            f"launches; batch 1: {small['1']['fused_ms']:.4f} vs {small['1']['separate_ms']:.4f} ms, batch 4: "
-            f"{small['4']['fused_ms']:.4f} vs {small['4']['separate_ms']:.4f} ms")
+            f"launches; batch 1: {small['1']['fused_ms']:.4f} vs {small['1']['separate_ms']:.4f} ms (graph replay "
+            f"{small['1']['fused_graph_ms']:.4f} vs {small['1']['separate_graph_ms']:.4f}), batch 4: "
+            f"{small['4']['fused_ms']:.4f} vs {small['4']['separate_ms']:.4f} ms (graph replay "
+            f"{small['4']['fused_graph_ms']:.4f} vs {small['4']['separate_graph_ms']:.4f})")
 
     # the same caches re-laid as shuffled 64-token pages (page-table pool)
     paged = None

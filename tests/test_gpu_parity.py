@@ -344,6 +344,55 @@ def test_attention_append(oracle_lib, monkeypatch, Hq, hkv, lens, order, C, spli
     _assert_close(ob.cpu().numpy(), _oracle_attn(O, c2), f"append Hq={Hq} hkv={hkv}")
 
 
+def test_decode_step_graph_replay(oracle_lib):
+    """A decode step with append captured once in a HIP graph
+    (torch.cuda.CUDAGraph over the library's launches, which go to the
+    capturing stream) and replayed with new inputs: every replay, with eager
+    launches and synchronisations between replays, writes the same output
+    and pool bytes as the eager call on the same inputs."""
+    O = oracle_lib
+    lens = [700, 65, 1300, 1]
+    B, Hq, hkv = len(lens), 8, 2
+    c = _attn_case(O, B, Hq, hkv, lens, seed=91, gap=8)
+    ck, cv = c["ck"], c["cv"]
+    max_len = max(lens) + 1
+    ws = torch.empty(dq.attn_workspace_bytes(B, Hq, hkv, max_len), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
+    q = c["q"].clone()
+    k_new = synth.kv_tensor("outlier", B, hkv, seed=92, device=DEV)
+    v_new = synth.kv_tensor("outlier", B, hkv, seed=93, device=DEV)
+    sl = torch.from_numpy(np.array(lens, np.int32) + 1).to(DEV)
+    pools = [t.clone() for t in (c["kc"], c["kn"], c["vc"], c["vn"])]
+
+    def step():
+        dq.attn_decode_append(ck, cv, q, k_new, v_new, *pools, c["ss"], sl, max_len, out=out, workspace=ws)
+
+    side = torch.cuda.Stream()  # warm-up off the default stream, as torch asks before a capture
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        q.copy_(synth.q_tensor(B, Hq, seed=200 + r, device=DEV))
+        k_new.copy_(synth.kv_tensor("outlier", B, hkv, seed=210 + r, device=DEV))
+        v_new.copy_(synth.kv_tensor("student_t5", B, hkv, seed=220 + r, device=DEV))
+        ref_pools = [t.clone() for t in pools]
+        ref = dq.attn_decode_append(ck, cv, q, k_new, v_new, *ref_pools, c["ss"], sl, max_len)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r}: output differs from the eager call"
+        for x, y, name in zip(pools, ref_pools, ("k_cont", "k_norm", "v_cont", "v_norm")):
+            assert torch.equal(x, y), f"replay {r}: {name} differs from the eager call"
+    c2 = dict(c, kc=pools[0], kn=pools[1], vc=pools[2], vn=pools[3], q=q, lens=np.array(lens, np.int32) + 1)
+    _assert_close(out.cpu().numpy(), _oracle_attn(O, c2), "graph replay")
+
+
 def _paged_copy(c, rng, extra_pages=5):
     """The contiguous pools of an attention case re-laid as shuffled 64-token
     pages in a larger pool, with the page table that addresses them."""
