@@ -7,16 +7,18 @@ Workload (default): Llama-3.1-8B-shaped layer at its maximum batch -- batch
 outlier channels per head.  Synthetic data (synth/), no model weights.
 
 Untimed setup: draw K/V, encode the whole prompt into the compressed pools
-(timed separately for encode vectors/s).  One timed step = one decode step:
-  dq_encode_kv of the new token's K and V for every sequence (append, one
-  launch), then dq_attn_decode for every sequence over its grown context.
-`value` = compressed KV bytes (containers + fp16 norms) read by attention per
-step / wall time per step.  The roofline entry measures the attention call
-alone with HIP events on its stream inside the timed region.  The same steps
-are then timed as one launch each (dq_attn_decode_append), also at batch 1
-and 4, next to the two-launch form, eagerly and as HIP-graph replays.
+(timed separately for encode vectors/s).  One timed step = one decode step,
+one call of dq_attn_decode_append: the new token's K and V of every
+sequence encoded into the pools and attention of every sequence over its
+grown context (the call runs the encodes inside the attention launch at
+small batch, as a short launch of their own before it at this one).
+`value` = compressed KV bytes (containers + fp16 norms) read by attention
+per step / wall time per step.  The roofline entry measures that call's
+split-K kernel with HIP events on its stream inside the timed region.  The same steps are then
+timed as two launches (dq_encode_kv, then dq_attn_decode), and both forms at
+batch 1 and 4, eagerly and as HIP-graph replays.
 
-    python bench.py [--steps 16] [--warmup 3] [--workload NAME]
+    python bench.py [--steps 16] [--warmup 12] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -73,11 +75,11 @@ PROFILE_CMDS = {
     "fetch": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
               "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'attn_splitk|copyBuffer' --output-format csv "
               "-d $R/" + PROF + "/fetch -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline "
-              "--no-fused --copy-calibration > $R/" + PROF + "/fetch_bench.json"),
+              "--no-compare --copy-calibration > $R/" + PROF + "/fetch_bench.json"),
     "write": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
               "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'attn_splitk|copyBuffer' --output-format csv "
               "-d $R/" + PROF + "/write -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline "
-              "--no-fused --copy-calibration > $R/" + PROF + "/write_bench.json"),
+              "--no-compare --copy-calibration > $R/" + PROF + "/write_bench.json"),
 }
 
 
@@ -126,7 +128,7 @@ def summarize_profiles(d):
     rows.sort(reverse=True)
     lines = [f"# Kernel trace: decode step, {wl}", "",
              "Batch 128, 32 q / 8 kv heads, 8K context, K 8 levels / V 6 levels in 34-byte containers; "
-             "the default bench command (prefill encode, 3 warm-up and 16 timed decode steps, oracle timing "
+             "the default bench command (prefill encode, 12 warm-up and 16 timed decode steps, oracle timing "
              "on the host).", "",
              "Command (from the repository root):", "", "```", PROFILE_CMDS["trace"], "```", "",
              "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
@@ -134,8 +136,8 @@ def summarize_profiles(d):
         lines.append(f"| `{short}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.2f} |")
     rl = live["roofline"]
     # per-dispatch durations of the split-K kernels by launch shape: the bench
-    # also runs the kernel at batch 1 and 4 (the fused-append comparison), so
-    # the figure that must agree with the bench line is the one at its grid
+    # also runs them at batch 1 and 4 (the small-batch comparison), so the
+    # figure that must agree with the bench line is the one at its grid
     disp = {}
     for r in _csv(_find(os.path.join(d, "trace"), "kernel_trace.csv")):
         n = r["Kernel_Name"]
@@ -147,26 +149,30 @@ def summarize_profiles(d):
               "| kernel | blocks | launches | avg us | min us | max us |", "|---|---:|---:|---:|---:|---:|"]
     for (kname, blocks), v in sorted(disp.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
         lines.append(f"| `{kname}` | {blocks} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
-    head = [(k, v) for k, v in disp.items() if "false>" in k[0]]
+    # the decode step's split-K variant: the one launched most at the bench's
+    # shape (dq_attn_decode_append runs the attention without the encode loop
+    # when its items fill every round of waves, as at batch 128)
+    head = sorted(disp.items(), key=lambda kv: (kv[0][1], len(kv[1])))
+    kname = head[-1][0][0] if head else "attn_splitk_kernel"
     if head:
-        (kname, blocks), v = max(head, key=lambda kv: kv[0][1])
-        lines += ["", f"Split-K kernel at the bench's shape ({blocks} blocks): rocprofv3 average "
-                  f"{sum(v) / len(v):.1f} us over {len(v)} launches (warm-up and the paged-pool timing "
-                  f"included); the same run's bench line measured {rl['avg_launch_ms'] * 1e3:.1f} us with HIP "
+        (kname, blocks), v = head[-1]
+        lines += ["", f"`{kname}` (the decode step's split-K kernel) at the bench's shape "
+                  f"({blocks} blocks): rocprofv3 average "
+                  f"{sum(v) / len(v):.1f} us over {len(v)} launches (warm-up included); the same run's bench "
+                  f"line measured {rl['avg_launch_ms'] * 1e3:.1f} us with HIP "
                   f"events around the kernel over the timed steps, {rl['achieved']:.1f} GB/s of compressed "
                   f"bytes = {rl['frac']:.2%} of 8 TB/s."]
     lines += ["", "Bench line of this run:", "", "```", json.dumps(live), "```"]
     with open(os.path.join(out_dir, f"all_kernels_{wl}_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    # ---- HBM counters
+    # ---- HBM counters (of that kernel)
     def per_kernel(kind, counter):
         rows = _csv(_find(os.path.join(d, kind), "counter_collection.csv"))
         rows = [r for r in rows if r["Counter_Name"] == counter]
         copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
         cal = max(copies, key=lambda r: float(r["Counter_Value"]))
-        att = [float(r["Counter_Value"]) for r in rows
-               if "attn_splitk_kernel" in r["Kernel_Name"] and "false>" in r["Kernel_Name"]]
+        att = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]]
         bl = _bench_line(os.path.join(d, f"{kind}_bench.json"))
         if bl.get("attn_source_sha256_16") != src:
             raise SystemExit(f"{kind} run was made on a different attention source")
@@ -178,7 +184,7 @@ def summarize_profiles(d):
     fetch_b = sum(f_att) / len(f_att) * 1024 * f_scale
     write_b = sum(w_att) / len(w_att) * 1024 * w_scale
     alg = rl["alg_bytes_per_launch"]
-    rec = {"kernel": "attn_splitk_kernel", "workload": wl, "source_sha256_16": src,
+    rec = {"kernel": kname, "workload": wl, "source_sha256_16": src,
            "fetch_kib_per_launch_raw": sum(f_att) / len(f_att), "write_kib_per_launch_raw": sum(w_att) / len(w_att),
            "launches": [len(f_att), len(w_att)],
            "copy_1gib_fetch_kib": f_cal, "copy_1gib_write_kib": w_cal,
@@ -190,7 +196,7 @@ def summarize_profiles(d):
     with open(os.path.join(out_dir, f"attn_splitk_{wl}_counters.json"), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    md = [f"# HBM counters: attn_splitk_kernel, {wl}", "",
+    md = [f"# HBM counters: {kname}, {wl}", "",
           "Commands (from the repository root), one counter per run:", "", "```",
           PROFILE_CMDS["fetch"], PROFILE_CMDS["write"], "```", "",
           "| | FETCH_SIZE | WRITE_SIZE |", "|---|---:|---:|",
@@ -201,7 +207,8 @@ def summarize_profiles(d):
           f"| split-K kernel, scaled MB per launch | {fetch_b / 1e6:.1f} | {write_b / 1e6:.1f} |", "",
           f"Algorithmic bytes per launch (containers + fp16 norms of every context token, K and V): "
           f"{alg / 1e6:.1f} MB.  Measured traffic {(fetch_b + write_b) / 1e6:.1f} MB = "
-          f"{rec['traffic_over_alg']:.3f} x algorithmic; the writes are the split-K partial results.", ""]
+          f"{rec['traffic_over_alg']:.3f} x algorithmic; the writes are the split-K partial results and the "
+          f"appended tokens' containers.", ""]
     with open(os.path.join(out_dir, f"attn_splitk_{wl}_counters.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     print(f"wrote profiles for source {src}: traffic {(fetch_b + write_b) / 1e6:.1f} MB per launch")
@@ -251,12 +258,13 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=16)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=12)
     ap.add_argument("--workload", default="llama31_8b_b128_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-pool attention timing")
-    ap.add_argument("--no-fused", action="store_true", help="skip the one-launch decode-with-append timing")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the two-launch and small-batch timings of the decode step")
     ap.add_argument("--no-rd", action="store_true", help="skip the rate-distortion drift-order encode")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill attention timing")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -362,53 +370,82 @@ def main():
     per_tok = Hkv * (ck.C + 2 + cv.C + 2)
     bytes_s = [int((ctx + s + 1).sum()) * per_tok for s in range(nsteps)]
 
+    nq = 3 if max(ck.C, cv.C) <= 47 else (5 if max(ck.C, cv.C) <= 79 else 9)  # the kernel's tile pieces
+
     def step(s, ev=None):
+        # one decode step, one launch: the new token's K/V encoded into the
+        # pools inside the attention launch (dq_attn_decode_append)
         if ev is not None:
             ev[0].record()
-        dq.encode_kv(ck, cv, Kn[s], Vn[s], slots_s[s], kc, kn, vc, vn)
+        dq.attn_decode_append(ck, cv, qs[s], Kn[s], Vn[s], kc, kn, vc, vn, st_t, lens_s[s], max_len, out=out,
+                              workspace=ws, split_events=None if ev is None else (ev[1], ev[2]))
         if ev is not None:
-            ev[1].record()
-        dq.attn_decode(ck, cv, qs[s], kc, kn, vc, vn, st_t, lens_s[s], max_len, out=out, workspace=ws,
-                       split_events=None if ev is None else (ev[3], ev[4]))
-        if ev is not None:
-            ev[2].record()
+            ev[3].record()
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    # per step: [step start, encode done, attention done, split-K start, split-K done]; all on
-    # the current stream, which is the one every library launch goes to
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # per step: [step start, split-K start, split-K done, step done]; all on the
+    # current stream, which is the one every library launch goes to
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(args.warmup + k, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    enc_ms = [evs[k][0].elapsed_time(evs[k][1]) for k in range(args.steps)]
-    att_ms = [evs[k][1].elapsed_time(evs[k][2]) for k in range(args.steps)]
-    ev_total = evs[0][0].elapsed_time(evs[-1][2])
+    att_ms = [evs[k][0].elapsed_time(evs[k][3]) for k in range(args.steps)]
+    ev_total = evs[0][0].elapsed_time(evs[-1][3])
     total_s = max(wall, ev_total / 1e3)
     timed_bytes = sum(bytes_s[args.warmup:])
     ms_per_step = total_s * 1e3 / args.steps
     value = timed_bytes / total_s / 1e9
-    split_ms = [evs[k][3].elapsed_time(evs[k][4]) for k in range(args.steps)]
+    split_ms = [evs[k][1].elapsed_time(evs[k][2]) for k in range(args.steps)]
     att_avg_ms = sum(att_ms) / len(att_ms)
     split_avg_ms = sum(split_ms) / len(split_ms)
     alg_bytes = timed_bytes / args.steps
     achieved = alg_bytes / (split_avg_ms / 1e3) / 1e9
     ctx_tokens = sum(int((ctx + args.warmup + k + 1).sum()) for k in range(args.steps))
-    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (append encode {np.mean(enc_ms):.3f} ms, "
-        f"attention {att_avg_ms:.3f} ms of which split-K {split_avg_ms:.3f} ms), {value:.1f} GB/s step, "
-        f"split-K kernel {achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of HBM peak")
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (one dq_attn_decode_append call; split-K "
+        f"kernel {split_avg_ms:.3f} ms), {value:.1f} GB/s step, split-K kernel "
+        f"{achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of HBM peak")
 
-    # the same decode steps as one launch each (dq_attn_decode_append: the
-    # append's encode runs inside the attention launch); re-encoding the same
-    # tokens into the same slots writes the same bytes.  Also at small batch
-    # (the first sequences), where the saved launch matters most.
-    fused = None
-    if not args.no_fused:
-        def fused_ms(nb, fused_call, graph=False):
+    # the same steps as two launches (dq_encode_kv, then dq_attn_decode);
+    # re-encoding the same tokens into the same slots writes the same bytes.
+    # Then both forms at small batch (the first sequences), eagerly and as
+    # HIP-graph replays.
+    two = small = None
+    if not args.no_compare:
+        tev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+        def step2(s, ev=None):
+            if ev is not None:
+                ev[0].record()
+            dq.encode_kv(ck, cv, Kn[s], Vn[s], slots_s[s], kc, kn, vc, vn)
+            if ev is not None:
+                ev[1].record()
+            dq.attn_decode(ck, cv, qs[s], kc, kn, vc, vn, st_t, lens_s[s], max_len, out=out, workspace=ws,
+                           split_events=None if ev is None else (ev[3], ev[4]))
+            if ev is not None:
+                ev[2].record()
+        for s in range(args.warmup):
+            step2(s)
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            step2(args.warmup + k, tev[k])
+        torch.cuda.synchronize()
+        t_step = tev[0][0].elapsed_time(tev[-1][2]) / args.steps
+        t_enc = float(np.mean([e[0].elapsed_time(e[1]) for e in tev]))
+        t_att = float(np.mean([e[1].elapsed_time(e[2]) for e in tev]))
+        t_split = float(np.mean([e[3].elapsed_time(e[4]) for e in tev]))
+        two = {"ms_per_step": round(t_step, 4), "gbps": round(alg_bytes / (t_step / 1e3) / 1e9, 2),
+               "append_encode_ms": round(t_enc, 4), "attn_call_ms": round(t_att, 4),
+               "split_ms": round(t_split, 4), "split_gbps": round(alg_bytes / (t_split / 1e3) / 1e9, 2),
+               "kernel": f"attn_splitk_kernel<{nq}, false>"}
+        log(f"[bench] as dq_encode_kv then dq_attn_decode: {t_step:.3f} ms/step (append encode {t_enc:.3f} ms, attention {t_att:.3f} "
+            f"ms of which split-K {t_split:.3f} ms = {two['split_gbps']:.1f} GB/s)")
+
+        def small_ms(nb, fused_call, graph=False):
             qb = [qs[s][:nb].contiguous() for s in range(nsteps)]
             kb = [Kn[s][:nb] for s in range(nsteps)]
             vb = [Vn[s][:nb] for s in range(nsteps)]
@@ -431,7 +468,7 @@ def main():
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             if graph:
-                # one step captured once (HIP graph), replayed: the launches
+                # one step captured once (HIP graph) and replayed: the launches
                 # cost no host time; the step re-encodes the same token
                 side = torch.cuda.Stream()
                 side.wait_stream(torch.cuda.current_stream())
@@ -457,21 +494,17 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / args.steps
 
-        f_ms = fused_ms(B, True)
         small = {}
         for nb in (1, 4):
-            small[str(nb)] = {"fused_ms": round(fused_ms(nb, True), 4),
-                              "separate_ms": round(fused_ms(nb, False), 4),
-                              "fused_graph_ms": round(fused_ms(nb, True, graph=True), 4),
-                              "separate_graph_ms": round(fused_ms(nb, False, graph=True), 4)}
-        fused = {"batch": B, "ms_per_step": round(f_ms, 4), "gbps": round(alg_bytes / (f_ms / 1e3) / 1e9, 2),
-                 "separate_ms_per_step": round(ms_per_step, 4), "small_batch": small,
-                 "call": "dq_attn_decode_append"}
-        log(f"[bench] fused append: {f_ms:.3f} ms/step ({fused['gbps']:.1f} GB/s) vs {ms_per_step:.3f} ms as two "
-            f"launches; batch 1: {small['1']['fused_ms']:.4f} vs {small['1']['separate_ms']:.4f} ms (graph replay "
-            f"{small['1']['fused_graph_ms']:.4f} vs {small['1']['separate_graph_ms']:.4f}), batch 4: "
-            f"{small['4']['fused_ms']:.4f} vs {small['4']['separate_ms']:.4f} ms (graph replay "
-            f"{small['4']['fused_graph_ms']:.4f} vs {small['4']['separate_graph_ms']:.4f})")
+            small[str(nb)] = {"append_call_ms": round(small_ms(nb, True), 4),
+                              "encode_then_attn_ms": round(small_ms(nb, False), 4),
+                              "append_call_graph_ms": round(small_ms(nb, True, graph=True), 4),
+                              "encode_then_attn_graph_ms": round(small_ms(nb, False, graph=True), 4)}
+        log(f"[bench] batch 1: {small['1']['append_call_ms']:.4f} ms per step as one dq_attn_decode_append call vs "
+            f"{small['1']['encode_then_attn_ms']:.4f} as encode then attention (graph replay {small['1']['append_call_graph_ms']:.4f} vs "
+            f"{small['1']['encode_then_attn_graph_ms']:.4f}); batch 4: {small['4']['append_call_ms']:.4f} vs "
+            f"{small['4']['encode_then_attn_ms']:.4f} (graph replay {small['4']['append_call_graph_ms']:.4f} vs "
+            f"{small['4']['encode_then_attn_graph_ms']:.4f})")
 
     # the same caches re-laid as shuffled 64-token pages (page-table pool)
     paged = None
@@ -506,8 +539,8 @@ def main():
         paged_ms = sum(e[0].elapsed_time(e[1]) for e in pev) / args.steps
         paged = {"attn_call_ms": round(paged_ms, 4), "gbps": round(alg_bytes / (paged_ms / 1e3) / 1e9, 2),
                  "page_tokens": P, "layout": "pages shuffled over the pool"}
-        log(f"[bench] paged pool: attention call {paged_ms:.3f} ms ({paged['gbps']:.1f} GB/s) "
-            f"vs contiguous {att_avg_ms:.3f} ms")
+        contig = f"vs contiguous {two['attn_call_ms']:.3f} ms" if two else ""
+        log(f"[bench] paged pool: attention call {paged_ms:.3f} ms ({paged['gbps']:.1f} GB/s) {contig}")
         del pools
 
     # chunked prefill over the same caches: the first 16 sequences, their
@@ -573,15 +606,15 @@ def main():
                      "traffic": load_traffic(alg_bytes), "kernel": "attn_splitk_kernel",
                      "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(split_avg_ms, 4)},
         "attn_source_sha256_16": attn_source_hash(),
-        "attn_call_ms": round(att_avg_ms, 4),
-        "attn_call_gbps": round(alg_bytes / (att_avg_ms / 1e3) / 1e9, 2),
+        "step_call": "dq_attn_decode_append",
+        "step_call_ms": round(att_avg_ms, 4),
+        "encode_then_attn_step": two,
+        "small_batch_step": small,
         "paged_attn": paged,
-        "fused_append": fused,
         "rd_drift_order": rd,
         "prefill_attn": prefill,
         "cpu_baseline": cpu,
         "attn_context_tokens_per_s": round(ctx_tokens / (sum(att_ms) / 1e3), 1),
-        "append_encode_ms": round(float(np.mean(enc_ms)), 4),
         "prefill_encode_vectors_per_s": round(prefill_vps, 1),
         "drift_rate": {"k": round(drift_k, 5), "v": round(drift_v, 5)},
     }

@@ -279,7 +279,10 @@ int dq_attn_decode_timed(dq_codec_t ck, dq_codec_t cv, const void *q,
  * wave per vector, while the others attend to the older tokens; each
  * encoding wave also writes the new token's own attention partial from the
  * symbols it chose, and the combine merges it with the older tokens'
- * partials.
+ * partials.  When the attention items already fill every round of resident
+ * waves (large batches), the same encodes run as a short launch of their
+ * own before the attention instead, which then costs less; the results are
+ * the same either way.
  *   k_new, v_new  device bf16: the new token of sequence b, kv head g, at
  *                 element b * new_stride_b + g * new_stride_h (128
  *                 contiguous values; 2-byte aligned)
@@ -303,6 +306,24 @@ int dq_attn_decode_append(dq_codec_t ck, dq_codec_t cv, const void *q,
                           float sm_scale, int32_t out_dtype, void *out,
                           void *workspace, size_t ws_bytes, dq_stats *k_stats,
                           dq_stats *v_stats, dq_stream_t stream);
+
+/* dq_attn_decode_append plus the measurement hook of dq_attn_decode_timed:
+ * `split_begin` and `split_end` (hipEvent_t, either may be NULL) are
+ * recorded right before and after the split-K kernel, which here also runs
+ * the append's encodes. */
+int dq_attn_decode_append_timed(dq_codec_t ck, dq_codec_t cv, const void *q,
+                                int32_t B, int32_t Hq, const void *k_new,
+                                const void *v_new, int64_t new_stride_b,
+                                int64_t new_stride_h, uint8_t *k_cont,
+                                uint16_t *k_norm, uint8_t *v_cont,
+                                uint16_t *v_norm, int64_t num_slots,
+                                const int64_t *seq_start,
+                                const int32_t *seq_len, int64_t max_len,
+                                float sm_scale, int32_t out_dtype, void *out,
+                                void *workspace, size_t ws_bytes,
+                                dq_stats *k_stats, dq_stats *v_stats,
+                                dq_stream_t stream, void *split_begin,
+                                void *split_end);
 
 /* dq_attn_decode_append over a paged pool (pages and max_pages as for
  * dq_attn_decode_paged): the new token of sequence b goes to slot

@@ -257,12 +257,7 @@ def attn_decode(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_cont, v
     if split_events is None:
         _check(_lib.lib().dq_attn_decode(*args), "dq_attn_decode")
     else:
-        handles = []
-        for ev in split_events:
-            if ev.cuda_event == 0:  # torch creates the HIP event on first record
-                ev.record()
-            handles.append(ctypes.c_void_p(ev.cuda_event))
-        _check(_lib.lib().dq_attn_decode_timed(*args, *handles), "dq_attn_decode_timed")
+        _check(_lib.lib().dq_attn_decode_timed(*args, *_event_handles(split_events)), "dq_attn_decode_timed")
     return out
 
 
@@ -305,9 +300,18 @@ def attn_decode_paged(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_c
     return out
 
 
+def _event_handles(events):
+    handles = []
+    for ev in events:
+        if ev.cuda_event == 0:  # torch creates the HIP event on first record
+            ev.record()
+        handles.append(ctypes.c_void_p(ev.cuda_event))
+    return handles
+
+
 def _attn_decode_append(ck: Codec, cv: Codec, q, k_new, v_new, k_cont, k_norm, v_cont, v_norm,
                         loc, seq_len, max_len, sm_scale, out, out_dtype, workspace, k_stats, v_stats,
-                        paged: bool):
+                        paged: bool, split_events=None):
     _need_cuda("q", q, torch.bfloat16)
     loc_name, loc_dt = ("pages", torch.int32) if paged else ("seq_start", torch.int64)
     for name, t, dt in (("k_cont", k_cont, torch.uint8), ("v_cont", v_cont, torch.uint8),
@@ -350,6 +354,10 @@ def _attn_decode_append(ck: Codec, cv: Codec, q, k_new, v_new, k_cont, k_norm, v
     where = (_ptr(loc), loc.shape[1]) if paged else (_ptr(loc),)
     tail = (_ptr(seq_len), max_len, ctypes.c_float(sm_scale), 0 if out_dtype == torch.float32 else 1,
             _ptr(out), _ptr(workspace), workspace.numel(), _ptr(k_stats), _ptr(v_stats), _stream(q.device))
+    if split_events is not None and not paged:
+        _check(_lib.lib().dq_attn_decode_append_timed(*head, *where, *tail, *_event_handles(split_events)),
+               "dq_attn_decode_append_timed")
+        return out
     fn = "dq_attn_decode_paged_append" if paged else "dq_attn_decode_append"
     _check(getattr(_lib.lib(), fn)(*head, *where, *tail), fn)
     return out
@@ -359,13 +367,18 @@ def attn_decode_append(ck: Codec, cv: Codec, q: torch.Tensor, k_new: torch.Tenso
                        k_cont, k_norm, v_cont, v_norm, seq_start: torch.Tensor, seq_len: torch.Tensor,
                        max_len: int, sm_scale: float | None = None, out: torch.Tensor | None = None,
                        out_dtype=torch.float32, workspace: torch.Tensor | None = None,
-                       k_stats: torch.Tensor | None = None, v_stats: torch.Tensor | None = None):
+                       k_stats: torch.Tensor | None = None, v_stats: torch.Tensor | None = None,
+                       split_events=None):
     """A decode step with append in one launch: k_new, v_new bf16 [B, Hkv, 128]
     are encoded into slot seq_start[b] + seq_len[b] - 1 (seq_len counts the
     new token) and attended to with the rest of the cache.  Returns out
-    [B, Hq, 128]; the pools are updated in place."""
+    [B, Hq, 128]; the pools are updated in place.
+
+    split_events: optional (begin, end) torch.cuda.Event pair, recorded on
+    the current stream around the split-K kernel (which runs the encodes)."""
     return _attn_decode_append(ck, cv, q, k_new, v_new, k_cont, k_norm, v_cont, v_norm, seq_start, seq_len,
-                               max_len, sm_scale, out, out_dtype, workspace, k_stats, v_stats, paged=False)
+                               max_len, sm_scale, out, out_dtype, workspace, k_stats, v_stats, paged=False,
+                               split_events=split_events)
 
 
 def attn_decode_paged_append(ck: Codec, cv: Codec, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,

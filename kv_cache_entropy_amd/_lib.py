@@ -52,11 +52,12 @@ def lib():
         app_tail = [vp, i64, ctypes.c_float, i32, vp, vp, ctypes.c_size_t, vp, vp, vp]
         L.dq_attn_decode_append.argtypes = app_head + [vp] + app_tail
         L.dq_attn_decode_paged_append.argtypes = app_head + [vp, i32] + app_tail
+        L.dq_attn_decode_append_timed.argtypes = app_head + [vp] + app_tail + [vp, vp]
         for f in ("dq_codec_create", "dq_codec_destroy", "dq_codec_info", "dq_codec_tables",
                   "dq_encode", "dq_encode_kv", "dq_decode_symbols", "dq_attn_decode_workspace",
                   "dq_attn_decode", "dq_attn_decode_timed", "dq_attn_decode_paged",
                   "dq_attn_prefill_workspace", "dq_attn_prefill", "dq_attn_decode_append",
-                  "dq_attn_decode_paged_append"):
+                  "dq_attn_decode_paged_append", "dq_attn_decode_append_timed"):
             getattr(L, f).restype = ctypes.c_int
         del u64
         _handle = L

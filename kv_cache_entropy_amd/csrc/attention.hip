@@ -81,6 +81,8 @@ struct AttnArgs {
   uint16_t *kn_w, *vn_w;
   dq_stats *k_stats, *v_stats;
   float *part_new;  // [B][Hkv][4][kPart]: the new token's own partial
+  int64_t n_enc;    // encode items run by the split-K launch (0: a launch of their own ran them)
+  int skip_last;    // 1 with an append: the chunks cover the len - 1 older tokens
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -480,11 +482,12 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 
   // items [0, n_enc): the append's encodes (K of every (b, g), then V);
   // then the attention items, each one chunk of one (b, g)
-  const int64_t n_enc = APPEND ? 2 * (int64_t)a.B * a.Hkv : 0;
+  const int64_t n_enc = APPEND ? a.n_enc : 0;
+  const int64_t n_half = (int64_t)a.B * a.Hkv;
   int64_t it = (int64_t)blockIdx.x * a.waves_per_block + wave;
   for (; APPEND && it < n_enc; it += W) {
-    const bool isv = it >= n_enc / 2;
-    const int64_t e = isv ? it - n_enc / 2 : it;
+    const bool isv = it >= n_half;
+    const int64_t e = isv ? it - n_half : it;
     const int b = (int)(e / a.Hkv), g = (int)(e - (int64_t)(e / a.Hkv) * a.Hkv);
     wave_sync();  // the slice is free
     // one call per kernel argument: a reference chosen at run time would put
@@ -504,7 +507,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
     const int b = (int)(bg / a.Hkv), g = (int)(bg - (int64_t)b * a.Hkv);
     // a paged sequence never reads past its row of the page table; with an
     // append the newest token is not part of any chunk
-    const int len0 = a.seq_len[b] - (APPEND ? 1 : 0);
+    const int len0 = a.seq_len[b] - a.skip_last;
     const int len = a.pages ? min(len0, a.max_pages * kTile) : len0;
     const int t0 = c * a.chunk;
     if (t0 >= len) continue;
@@ -617,6 +620,40 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 }
 
 // ---------------------------------------------------------------- combine
+// The append's encodes as a launch of their own, for batches whose
+// attention items already fill every round of resident waves: one wave per
+// new vector (K of every (b, g), then V), each writing its container and
+// its token's own partial exactly as inside the split-K launch.
+constexpr int kAppendWaves = 4;  // waves per block
+__host__ __device__ inline int append_scratch_bytes(int C) {
+  const int rows = C - 3 < kWaveScr ? C - 3 : kWaveScr;
+  return 9 * kD + rows * 64;
+}
+__global__ void __launch_bounds__(64 * kAppendWaves) append_encode_kernel(AttnArgs a, Tables tk, Tables tv) {
+  __shared__ uint4 etab[2][kMaxLevels];
+  __shared__ float2 rdtab[2][kMaxHalf];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  wave_encode_tables(tk, etab[0], rdtab[0], threadIdx.x);
+  wave_encode_tables(tv, etab[1], rdtab[1], threadIdx.x);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n_half = (int64_t)a.B * a.Hkv;
+  const int64_t it = (int64_t)blockIdx.x * kAppendWaves + wave;
+  if (it >= 2 * n_half) return;  // whole waves; no block barrier follows
+  const bool isv = it >= n_half;
+  const int64_t e = isv ? it - n_half : it;
+  const int b = (int)(e / a.Hkv), g = (int)(e - (int64_t)(e / a.Hkv) * a.Hkv);
+  const int C = tk.C > tv.C ? tk.C : tv.C;
+  uint8_t *scratch = smem + (size_t)wave * ((append_scratch_bytes(C) + 15) & ~15);
+  if (isv) {
+    if (tv.order == 1) append_vector<true>(a, tv, etab[1], rdtab[1], scratch, true, b, g, lane);
+    else append_vector<false>(a, tv, etab[1], rdtab[1], scratch, true, b, g, lane);
+  } else {
+    if (tk.order == 1) append_vector<true>(a, tk, etab[0], rdtab[0], scratch, false, b, g, lane);
+    else append_vector<false>(a, tk, etab[0], rdtab[0], scratch, false, b, g, lane);
+  }
+}
+
 // Log-sum-exp merge of a row's partials for the 128 threads of a block
 // (thread d owns dim d): partial c sits at src + c * stride floats (acc
 // [0, 128), m at 128, l at 129), plus an optional extra one (pe).  Returns
@@ -1183,8 +1220,8 @@ hipError_t launch_splitk(const Plan &pl, const AttnArgs &a, const Tables &tk, co
       hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ, APPEND>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kStaticLds);
   if (attr != hipSuccess) return attr;
-  // the append's encode items come first, one per wave
-  const int64_t n = a.n_items + (APPEND ? 2 * (int64_t)a.B * a.Hkv : 0);
+  // the append's encode items (if this launch runs them) come first, one per wave
+  const int64_t n = a.n_items + (APPEND ? a.n_enc : 0);
   const int64_t want = (n + pl.waves_per_block - 1) / pl.waves_per_block;
   const int blocks = (int)(want < pl.blocks_cap ? want : pl.blocks_cap);
   hipLaunchKernelGGL((attn_splitk_kernel<NQ, APPEND>), dim3((unsigned)blocks), dim3(64 * pl.waves_per_block), pl.lds,
@@ -1402,12 +1439,30 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
     a.k_stats = app->k_stats;
     a.v_stats = app->v_stats;
     a.part_new = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.qrot_bytes + pl.part_bytes);
+    // The encodes ride in the split-K launch when they fit in the slack of
+    // its last round of resident waves (small batches: they are then free);
+    // otherwise they would lengthen every wave that takes one, and a launch
+    // of their own before the attention costs less.
+    const int64_t W = (int64_t)pl.blocks_cap * pl.waves_per_block;
+    const int64_t n_enc = 2 * (int64_t)B * Hkv;
+    bool fuse = (pl.n_items + n_enc + W - 1) / W == (pl.n_items + W - 1) / W;
+    if (const char *e = getenv("DQ_APPEND_FUSE")) fuse = e[0] == '1';  // tests force either way
+    a.n_enc = fuse ? n_enc : 0;
+    a.skip_last = 1;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(dq::rotate_q_kernel, dim3((unsigned)(B * Hkv * 4)), dim3(64), 0, s, a, ck->t.seed);
+  if (app && a.n_enc == 0) {
+    // the encodes need the rotated query (for the new token's scores): after rotate_q
+    const int C = ck->t.C > cv->t.C ? ck->t.C : cv->t.C;
+    const size_t lds = (size_t)dq::kAppendWaves * ((dq::append_scratch_bytes(C) + 15) & ~15);
+    const int64_t blocks = (2 * (int64_t)B * Hkv + dq::kAppendWaves - 1) / dq::kAppendWaves;
+    hipLaunchKernelGGL(dq::append_encode_kernel, dim3((unsigned)blocks), dim3(64 * dq::kAppendWaves), lds, s, a,
+                       ck->t, cv->t);
+  }
   if (split_begin && hipEventRecord(split_begin, s) != hipSuccess) return DQ_ERR_HIP;
   hipError_t e;
-  if (app)
+  if (app && a.n_enc > 0)  // the variant with the encode loop only when it has encodes to run
     e = pl.nq == 3   ? dq::launch_splitk<3, true>(pl, a, ck->t, cv->t, s)
         : pl.nq == 5 ? dq::launch_splitk<5, true>(pl, a, ck->t, cv->t, s)
                      : dq::launch_splitk<9, true>(pl, a, ck->t, cv->t, s);
@@ -1462,6 +1517,20 @@ extern "C" int dq_attn_decode_append(dq_codec_t ck, dq_codec_t cv, const void *q
   const AppendArgs app{k_new, v_new, new_stride_b, new_stride_h, k_stats, v_stats};
   return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, nullptr, 0, seq_len,
                      max_len, sm_scale, out_dtype, out, workspace, ws_bytes, stream, nullptr, nullptr, &app);
+}
+
+extern "C" int dq_attn_decode_append_timed(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,
+                                           const void *k_new, const void *v_new, int64_t new_stride_b,
+                                           int64_t new_stride_h, uint8_t *k_cont, uint16_t *k_norm,
+                                           uint8_t *v_cont, uint16_t *v_norm, int64_t num_slots,
+                                           const int64_t *seq_start, const int32_t *seq_len, int64_t max_len,
+                                           float sm_scale, int32_t out_dtype, void *out, void *workspace,
+                                           size_t ws_bytes, dq_stats *k_stats, dq_stats *v_stats,
+                                           dq_stream_t stream, void *split_begin, void *split_end) {
+  const AppendArgs app{k_new, v_new, new_stride_b, new_stride_h, k_stats, v_stats};
+  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, nullptr, 0, seq_len,
+                     max_len, sm_scale, out_dtype, out, workspace, ws_bytes, stream,
+                     static_cast<hipEvent_t>(split_begin), static_cast<hipEvent_t>(split_end), &app);
 }
 
 extern "C" int dq_attn_decode_paged_append(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,

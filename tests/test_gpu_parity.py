@@ -342,6 +342,17 @@ def test_attention_append(oracle_lib, monkeypatch, Hq, hkv, lens, order, C, spli
     assert diff <= 1e-5
     c2 = dict(c, kc=pb[0], kn=pb[1], vc=pb[2], vn=pb[3], lens=np.array(lens, np.int32) + 1)
     _assert_close(ob.cpu().numpy(), _oracle_attn(O, c2), f"append Hq={Hq} hkv={hkv}")
+    # the encodes inside the attention launch or in a launch of their own
+    # (the call picks by batch size): the same bytes and the same output
+    forced = []
+    for mode in ("1", "0"):
+        monkeypatch.setenv("DQ_APPEND_FUSE", mode)
+        forced.append(_append_both(c, k_new, v_new, max_len)[0][1])
+    monkeypatch.delenv("DQ_APPEND_FUSE")
+    (p1, s1, o1), (p0, s0, o0) = forced
+    assert torch.equal(o1, o0) and torch.equal(o1, ob)
+    for x, y in zip(list(p1) + list(s1), list(p0) + list(s0)):
+        assert torch.equal(x, y)
 
 
 def test_decode_step_graph_replay(oracle_lib):
@@ -611,16 +622,17 @@ def _sampled_attention(O, c, lens, max_len, rows, label):
 
 def test_llama31_b128_8k_bench_configuration(oracle_lib):
     """Batch 128 x 8192, 32 q / 8 kv heads, 34-byte containers, laid out as
-    the bench does (19 free slots per sequence): the full prompt encode
+    the bench does (28 free slots per sequence: 12 warm-up and 16 timed
+    steps): the full prompt encode
     bit-exact, one decode step's append bit-exact, and attention at the
-    bench's max_len (context + 19) on sampled sequences."""
+    bench's max_len (context + 28) on sampled sequences."""
     O = oracle_lib
-    c = _workload_case(O, "llama31_8b_b128_8k", cap_extra=19)
+    c = _workload_case(O, "llama31_8b_b128_8k", cap_extra=28)
     lens = _append_and_check(O, c, 1, seed=c["w"].seed + 20)
-    out = _sampled_attention(O, c, lens, int(c["ctx"].max()) + 19, [0, 77, 127], "llama31 b128")
+    out = _sampled_attention(O, c, lens, int(c["ctx"].max()) + 28, [0, 77, 127], "llama31 b128")
     # the same pools re-laid as shuffled 64-token pages: identical output
     P = dq.PAGE_TOKENS
-    cap = int(c["ctx"][0]) + 19
+    cap = int(c["ctx"][0]) + 28
     npg = (cap + P - 1) // P
     B = c["w"].batch
     rng = np.random.default_rng(8)
@@ -640,7 +652,7 @@ def test_llama31_b128_8k_bench_configuration(oracle_lib):
         paged[tag] = (cont2, norm2)
     q = synth.q_tensor(B, c["w"].hq, seed=c["w"].seed + 12, device=DEV)
     outp = dq.attn_decode_paged(c["ck"], c["cv"], q, *paged["K"], *paged["V"], pages,
-                                lens.to(torch.int32).to(DEV), int(c["ctx"].max()) + 19)
+                                lens.to(torch.int32).to(DEV), int(c["ctx"].max()) + 28)
     torch.cuda.synchronize()
     assert torch.equal(outp, out), "paged pool differs from the contiguous pool at full size"
     # the next decode step as one launch (append + attention): the new
@@ -656,7 +668,7 @@ def test_llama31_b128_8k_bench_configuration(oracle_lib):
     st = (dq.new_stats(DEV), dq.new_stats(DEV))
     out2 = dq.attn_decode_append(c["ck"], c["cv"], q, k_new, v_new, kc, kn, vc, vn,
                                  torch.from_numpy(c["starts"]).to(DEV), lens2.to(torch.int32).to(DEV),
-                                 int(c["ctx"].max()) + 19, k_stats=st[0], v_stats=st[1])
+                                 int(c["ctx"].max()) + 28, k_stats=st[0], v_stats=st[1])
     torch.cuda.synchronize()
     for x, oc, (cont, norm), s in ((k_new, c["ock"], (kc, kn), st[0]), (v_new, c["ocv"], (vc, vn), st[1])):
         ocont, onorm, ost = O.encode(oc, _np_bits(x), slots_np, num_slots=cont.shape[1])
