@@ -45,7 +45,6 @@ static_assert(kTile == DQ_PAGE_TOKENS, "a page is one attention tile");
 constexpr int kVtStride = 66;    // halves per V-tile row: 33 dwords, spreads LDS banks
 constexpr int kPass = 32;        // dims per V-tile pass
 constexpr int kPart = 132;       // floats per (item, head): acc[128], m, l, pad
-constexpr int kQrotPerBG = 32 * 4 * 8;  // halves per (b, kv head): [chunk][head][hi4 lo4]
 constexpr int kLutBytes = 2 * kDecodeTableBytes;  // K and V decode tables
 // K and V encoder constants of the append (etab, rdtab), static too
 constexpr int kAppendLdsBytes = 2 * (kMaxLevels * 16 + kMaxHalf * 8);
@@ -92,27 +91,16 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // ---------------------------------------------------------------- rotate q
-__global__ void __launch_bounds__(64) rotate_q_kernel(AttnArgs a, uint64_t kseed) {
-  const int lane = threadIdx.x;
-  const int bg = blockIdx.x >> 2, hh = blockIdx.x & 3;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  uint16_t *dst = a.qrot + (int64_t)bg * kQrotPerBG;
-  const int d0 = lane, d1 = lane + 64;
-  if (hh >= a.group) {
-    const int i0 = ((d0 >> 2) * 4 + hh) * 8 + (d0 & 3), i1 = ((d1 >> 2) * 4 + hh) * 8 + (d1 & 3);
-    dst[i0] = 0; dst[i0 + 4] = 0; dst[i1] = 0; dst[i1 + 4] = 0;
-    return;
-  }
-  const int h = g * a.group + hh;
-  const uint16_t *qp = a.q + ((int64_t)b * a.Hq + h) * kD;
-  const uint64_t w0 = dev_splitmix64(kseed, 2ull * (uint64_t)g);
-  const uint64_t w1 = dev_splitmix64(kseed, 2ull * (uint64_t)g + 1ull);
-  float v0 = __uint_as_float((uint32_t)qp[d0] << 16);
-  float v1 = __uint_as_float((uint32_t)qp[d1] << 16);
+// q~ = H * D_K * q for one query head, in fp32, by one wave: lane l ends with
+// dims l (v0) and l + 64 (v1).  Width 64 pairs d with d + 64 inside the lane;
+// widths 32..1 go across lanes.  w0, w1: the sign words of the kv group.
+__device__ __forceinline__ void rotate_q_head(const uint16_t *qp, uint64_t w0, uint64_t w1, int lane, float &v0,
+                                              float &v1) {
+  v0 = __uint_as_float((uint32_t)qp[lane] << 16);
+  v1 = __uint_as_float((uint32_t)qp[lane + 64] << 16);
   if ((w0 >> lane) & 1ull) v0 = -v0;
   if ((w1 >> lane) & 1ull) v1 = -v1;
-  // width 64 pairs d with d + 64 inside the lane; widths 32..1 across lanes
-  float t0 = v0 + v1, t1 = v0 - v1;
+  const float t0 = v0 + v1, t1 = v0 - v1;
   v0 = t0;
   v1 = t1;
 #pragma unroll
@@ -122,13 +110,42 @@ __global__ void __launch_bounds__(64) rotate_q_kernel(AttnArgs a, uint64_t kseed
     v0 = hi ? p0 - v0 : v0 + p0;
     v1 = hi ? p1 - v1 : v1 + p1;
   }
-  const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-  const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
-  const int i0 = ((d0 >> 2) * 4 + hh) * 8 + (d0 & 3), i1 = ((d1 >> 2) * 4 + hh) * 8 + (d1 & 3);
-  dst[i0] = __builtin_bit_cast(uint16_t, h0);
-  dst[i0 + 4] = __builtin_bit_cast(uint16_t, l0);
-  dst[i1] = __builtin_bit_cast(uint16_t, h1);
-  dst[i1 + 4] = __builtin_bit_cast(uint16_t, l1);
+}
+
+// The rotated query of kv group g of sequence b as the QK MFMAs read it: an
+// fp16 hi + lo pair per value, staged through `tmp` (2 KB of the wave's LDS
+// slice) as [dim group][head][hi x4, lo x4] and read back so that lane l
+// holds dim groups l / 4 and 16 + l / 4 of head l mod 4.  Heads past the
+// group size are zero.  Each split-K item rotates its own query (a few
+// hundred instructions against the item's tiles), so no launch precedes
+// the attention.
+__device__ __forceinline__ void rotate_q_wave(const AttnArgs &a, uint64_t kseed, int b, int g, uint16_t *tmp,
+                                              uint4 (&qreg)[2], int lane) {
+  const uint64_t w0 = dev_splitmix64(kseed, 2ull * (uint64_t)g);
+  const uint64_t w1 = dev_splitmix64(kseed, 2ull * (uint64_t)g + 1ull);
+  const int d0 = lane, d1 = lane + 64;
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    uint16_t h0 = 0, l0 = 0, h1 = 0, l1 = 0;
+    if (hh < a.group) {
+      float v0, v1;
+      rotate_q_head(a.q + ((int64_t)b * a.Hq + g * a.group + hh) * kD, w0, w1, lane, v0, v1);
+      const _Float16 f0 = (_Float16)v0, f1 = (_Float16)v1;
+      h0 = __builtin_bit_cast(uint16_t, f0);
+      h1 = __builtin_bit_cast(uint16_t, f1);
+      l0 = __builtin_bit_cast(uint16_t, (_Float16)(v0 - (float)f0));
+      l1 = __builtin_bit_cast(uint16_t, (_Float16)(v1 - (float)f1));
+    }
+    const int i0 = ((d0 >> 2) * 4 + hh) * 8 + (d0 & 3), i1 = ((d1 >> 2) * 4 + hh) * 8 + (d1 & 3);
+    tmp[i0] = h0;
+    tmp[i0 + 4] = l0;
+    tmp[i1] = h1;
+    tmp[i1 + 4] = l1;
+  }
+  wave_sync();
+  const uint4 *t4 = reinterpret_cast<const uint4 *>(tmp);
+  qreg[0] = t4[lane];
+  qreg[1] = t4[64 + lane];
 }
 
 __device__ __forceinline__ uint32_t load_le32(const uint8_t *p) {
@@ -423,14 +440,20 @@ __device__ __forceinline__ void append_vector(const AttnArgs &a, const Tables &t
   const float n = half_to_float(r.nh);
   const float lam0 = half_to_float(t.recon[r.sym[0]]), lam1 = half_to_float(t.recon[r.sym[1]]);
   if (!isv) {
-    // s_h = q~_h . levels * n_k * scale; q~ is stored [dim group][head][hi x4, lo x4]
-    const uint16_t *qr = a.qrot + bg * kQrotPerBG;
-    const int d1 = lane + 64;
+    // s_h = q~_h . levels * n_k * scale, with q~ as the QK MFMAs see it (the
+    // fp16 hi + lo pair of each rotated value); heads past the group: 0
+    const uint64_t w0 = dev_splitmix64(t.seed, 2ull * (uint64_t)g);
+    const uint64_t w1 = dev_splitmix64(t.seed, 2ull * (uint64_t)g + 1ull);
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const int i0 = ((lane >> 2) * 4 + h) * 8 + (lane & 3), i1 = ((d1 >> 2) * 4 + h) * 8 + (d1 & 3);
-      const float q0 = half_to_float(qr[i0]) + half_to_float(qr[i0 + 4]);
-      const float q1 = half_to_float(qr[i1]) + half_to_float(qr[i1 + 4]);
+      float q0 = 0.0f, q1 = 0.0f;
+      if (h < a.group) {
+        float v0, v1;
+        rotate_q_head(a.q + ((int64_t)b * a.Hq + g * a.group + h) * kD, w0, w1, lane, v0, v1);
+        const _Float16 f0 = (_Float16)v0, f1 = (_Float16)v1;
+        q0 = (float)f0 + (float)(_Float16)(v0 - (float)f0);
+        q1 = (float)f1 + (float)(_Float16)(v1 - (float)f1);
+      }
       float dot = q0 * lam0 + q1 * lam1;
 #pragma unroll
       for (int w = 1; w < 64; w <<= 1) dot += __shfl_xor(dot, w);
@@ -525,8 +548,8 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
     wave_sync();  // the previous item's LDS reads are done
     // rotated query of this (sequence, kv head): lane l holds dim groups
     // l / 4 and 16 + l / 4 of head l mod 4 (8 VGPRs for the whole item)
-    const uint4 *qr = reinterpret_cast<const uint4 *>(a.qrot + bg * kQrotPerBG);
-    const uint4 qreg[2] = {qr[lane], qr[64 + lane]};
+    uint4 qreg[2];
+    rotate_q_wave(a, tk.seed, b, g, vt, qreg, lane);
 
     // this lane's token norms for a tile (0 outside the pool plane)
     auto norms = [&](int64_t tbase, uint32_t &nk, uint32_t &nv) {
@@ -1206,7 +1229,7 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   pl->n_items = (int64_t)B * Hkv * nc;
   pl->lds = (size_t)wpb * wb;  // dynamic part; the decode tables are static
   pl->blocks_cap = cus;  // one block per CU at most; fewer when the items are few
-  pl->qrot_bytes = ((size_t)B * Hkv * kQrotPerBG * 2 + 255) & ~(size_t)255;
+  pl->qrot_bytes = 0;  // each item rotates its own query
   pl->part_bytes = ((size_t)pl->n_items * 4 * kPart * sizeof(float) + 255) & ~(size_t)255;
   pl->part_new_bytes = (size_t)B * Hkv * 4 * kPart * sizeof(float);  // the append's own partials
   pl->total = pl->qrot_bytes + pl->part_bytes + pl->part_new_bytes;
@@ -1421,7 +1444,7 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
   a.chunk = pl.chunk;
   a.nc = pl.nc;
   a.n_items = pl.n_items;
-  a.qrot = static_cast<uint16_t *>(workspace);
+  a.qrot = nullptr;  // the split-K items rotate their own queries
   a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.qrot_bytes);
   a.out = out;
   a.out_bf16 = out_dtype;
@@ -1451,9 +1474,7 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
     a.skip_last = 1;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(dq::rotate_q_kernel, dim3((unsigned)(B * Hkv * 4)), dim3(64), 0, s, a, ck->t.seed);
   if (app && a.n_enc == 0) {
-    // the encodes need the rotated query (for the new token's scores): after rotate_q
     const int C = ck->t.C > cv->t.C ? ck->t.C : cv->t.C;
     const size_t lds = (size_t)dq::kAppendWaves * ((dq::append_scratch_bytes(C) + 15) & ~15);
     const int64_t blocks = (2 * (int64_t)B * Hkv + dq::kAppendWaves - 1) / dq::kAppendWaves;
