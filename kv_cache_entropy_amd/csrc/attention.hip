@@ -157,13 +157,14 @@ __device__ __forceinline__ uint32_t load_le32(const uint8_t *p) {
 struct WaveLayout {
   int kst, vst, pl, vt, bytes;
 };
-__host__ __device__ inline WaveLayout wave_layout(int Ck, int Cv) {
+// full_v (latency mode): the V tile holds all 128 dims, not one 32-dim pass.
+__host__ __device__ inline WaveLayout wave_layout(int Ck, int Cv, bool full_v = false) {
   WaveLayout w;
   w.kst = 0;
   w.vst = w.kst + ((kTile * Ck + 31) & ~15);
   w.pl = w.vst + ((kTile * Cv + 31) & ~15);
   w.vt = w.pl + 2 * 4 * kTile * 2;  // P: [head][token quad][hi x4, lo x4] fp16
-  w.bytes = w.vt + kPass * kVtStride * 2;
+  w.bytes = w.vt + (full_v ? kD : kPass) * kVtStride * 2;
   w.bytes = (w.bytes + 15) & ~15;
   return w;
 }
@@ -250,6 +251,29 @@ __device__ __forceinline__ void unroll(F &&f) {
 }
 
 
+// P (hi, lo) x the 32 dims of V-tile rows starting at vrow: 16 MFMAs whose
+// blocks are (8 dim quads) x (2 token halves); token quad 8 h + c of P sits
+// in block c of half h and is broadcast within the half (cbsz 3, abid c).
+template <int P>
+__device__ __forceinline__ void pv_pass(const uint32_t *vrow, half4 Ph, half4 Pl, floatx4 (&acc)[8]) {
+  unroll<8>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    const half4 V = __builtin_bit_cast(half4, make_uint2(vrow[2 * c], vrow[2 * c + 1]));
+    // hi and lo accumulate separately: two independent MFMA chains
+    acc[P] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ph, V, acc[P], 3, c, 0);
+    acc[4 + P] = __builtin_amdgcn_mfma_f32_4x4x4f16(Pl, V, acc[4 + P], 3, c, 0);
+  });
+}
+
+// This lane's P operand: 16 bytes (hi x4, lo x4) of token quad 8 h + lane/4
+// mod 8 for head lane mod 4, read once per tile.
+__device__ __forceinline__ void load_p(const uint16_t *pl, int lane, half4 &Ph, half4 &Pl) {
+  const int th = lane >> 5, row = lane & 31;
+  const uint4 pq = *reinterpret_cast<const uint4 *>(pl + ((lane & 3) * 16 + th * 8 + (row >> 2)) * 8);
+  Ph = __builtin_bit_cast(half4, make_uint2(pq.x, pq.y));
+  Pl = __builtin_bit_cast(half4, make_uint2(pq.z, pq.w));
+}
+
 // Decodes one K tile (scores into sc) and/or one V tile (PV into acc),
 // interleaving the two independent rANS chains of each lane.
 // K: after every 4 symbols (dim group G), sc += q~[4 heads][4 dims] x
@@ -263,15 +287,17 @@ __device__ __forceinline__ void unroll(F &&f) {
 //   quads) x (2 token halves).  P of token quad 8 h + c sits in block c of
 //   half h and is broadcast within the half (cbsz 3, abid c); it is read
 //   from LDS once per tile.
-template <bool DK, bool DV>
+//
+// FULLV (latency mode): K and V of the same tile; the V levels of all 128
+// dims stay in the V tile for pv_full after the tile's softmax, and no PV
+// runs inside the pass.
+template <bool DK, bool DV, bool FULLV = false>
 __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
                                           const uint8_t *vb, const uint4 (&qreg)[2], const uint16_t *pl,
                                           uint16_t *vt, floatx4 &sc, floatx4 (&acc)[8], int lane) {
   const int th = lane >> 5, row = lane & 31;
-  uint4 pq = make_uint4(0, 0, 0, 0);
-  if (DV) pq = *reinterpret_cast<const uint4 *>(pl + ((lane & 3) * 16 + th * 8 + (row >> 2)) * 8);
-  const half4 Ph = __builtin_bit_cast(half4, make_uint2(pq.x, pq.y));
-  const half4 Pl = __builtin_bit_cast(half4, make_uint2(pq.z, pq.w));
+  half4 Ph = {}, Pl = {};
+  if (DV && !FULLV) load_p(pl, lane, Ph, Pl);
   const uint32_t *vrow = reinterpret_cast<const uint32_t *>(vt) + row * (kVtStride / 2) + th * 16;
   uint32_t xk = 0, xv = 0;
   lds_u8 *pk = nullptr, *pv = nullptr;
@@ -310,7 +336,7 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
         if (DV) {
           xv = rans_advance(xv, ev);
           renorm(xv, pv, bv);
-          col[(gq * 4 + j) * kVtStride] = (uint16_t)(ev.y >> 16);
+          col[((FULLV ? p * kPass : 0) + gq * 4 + j) * kVtStride] = (uint16_t)(ev.y >> 16);
         }
       }
       if (DK) {
@@ -324,17 +350,24 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
                                                 G & 15, 0);
       }
     });
-    if (DV) {
+    if (DV && !FULLV) {
       wave_sync();
-      unroll<8>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        const half4 V = __builtin_bit_cast(half4, make_uint2(vrow[2 * c], vrow[2 * c + 1]));
-        // hi and lo accumulate separately: two independent MFMA chains
-        acc[p] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ph, V, acc[p], 3, c, 0);
-        acc[4 + p] = __builtin_amdgcn_mfma_f32_4x4x4f16(Pl, V, acc[4 + p], 3, c, 0);
-      });
+      pv_pass<p>(vrow, Ph, Pl, acc);
       wave_sync();
     }
+  });
+}
+
+// Latency mode: PV of a whole tile whose V levels (128 dims) are in vt and
+// whose P is in pl.
+__device__ __forceinline__ void pv_full(const uint16_t *pl, const uint16_t *vt, floatx4 (&acc)[8], int lane) {
+  const int th = lane >> 5, row = lane & 31;
+  half4 Ph, Pl;
+  load_p(pl, lane, Ph, Pl);
+  const uint32_t *v32 = reinterpret_cast<const uint32_t *>(vt);
+  unroll<4>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    pv_pass<p>(v32 + (p * kPass + row) * (kVtStride / 2) + th * 16, Ph, Pl, acc);
   });
 }
 
@@ -393,6 +426,30 @@ __device__ __forceinline__ void softmax_tile(const floatx4 &sc, uint32_t nk_bits
     uint16_t *q8 = pl + (h * 16 + (lane >> 2)) * 8 + (lane & 3);
     q8[0] = __builtin_bit_cast(uint16_t, hi);
     q8[4] = __builtin_bit_cast(uint16_t, (_Float16)(pv - (float)hi));
+  }
+}
+
+// An item's partial: the two token halves of every dim are summed across
+// lanes l and l ^ 32; lanes 0..31 hold dims 32p + l.  Then m and the
+// wave-summed l of each head.
+__device__ __forceinline__ void write_partial(float *dst, const floatx4 (&acc)[8], const float (&m_run)[4],
+                                              const float (&l_lane)[4], int lane) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float a2 = acc[p][h] + acc[4 + p][h];
+      const float v = a2 + __shfl_xor(a2, 32);
+      if (lane < 32) dst[h * kPart + p * kPass + lane] = v;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float l = wave_sum(l_lane[h]);
+    if (lane == h) {
+      dst[h * kPart + 128] = m_run[h];
+      dst[h * kPart + 129] = l;
+    }
   }
 }
 
@@ -471,7 +528,12 @@ __device__ __forceinline__ void append_vector(const AttnArgs &a, const Tables &t
   }
 }
 
-template <int NQ, bool APPEND>
+// LAT (latency mode, for batches that leave waves idle): each tile's K and
+// V are decoded in one pass, then its softmax and PV; an item of n tiles
+// takes n passes instead of n + 1 (a K-only first and a V-only last), at
+// the price of a whole V tile in LDS and so fewer waves per CU.  The
+// arithmetic and its order are those of the pipelined mode.
+template <int NQ, bool APPEND, bool LAT = false>
 __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnArgs a, Tables tk, Tables tv) {
   // decode tables at fixed LDS addresses (static), per-wave slices after them
   __shared__ uint8_t sym8[2][kM];
@@ -492,7 +554,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int Ck = tk.C, Cv = tv.C;
-  const WaveLayout L = wave_layout(Ck, Cv);
+  const WaveLayout L = wave_layout(Ck, Cv, LAT);
   uint8_t *base = smem + (size_t)wave * L.bytes;
   uint8_t *kst = base + L.kst;
   uint8_t *vst = base + L.vst;
@@ -559,6 +621,45 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
       nv = ok ? a.vn[idx] : 0u;
     };
     TileRegs<NQ> rk, rv;
+    if (LAT) {
+      uint32_t nkc, nvc, nkn = 0, nvn = 0;  // norms of the current and the next tile
+      const int64_t base0 = tile_base(0);
+      fetch<NQ>(rk, a.kc + base0 * Ck, kTile * Ck, a.kc, kpool_end, lane);
+      fetch<NQ>(rv, a.vc + base0 * Cv, kTile * Cv, a.vc, vpool_end, lane);
+      norms(base0, nkc, nvc);
+      float m_run[4], l_lane[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        m_run[h] = -__builtin_inff();
+        l_lane[h] = 0.0f;
+      }
+      floatx4 acc[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < ntiles; ++j) {
+        wave_sync();  // every read of the staging buffers, P and the V tile is done
+        commit<NQ>(rk, kst, kTile * Ck, lane);
+        commit<NQ>(rv, vst, kTile * Cv, lane);
+        const int koff = rk.off, voff = rv.off;
+        wave_sync();
+        if (j + 1 < ntiles) {
+          const int64_t base1 = tile_base(j + 1);
+          fetch<NQ>(rk, a.kc + base1 * Ck, kTile * Ck, a.kc, kpool_end, lane);
+          fetch<NQ>(rv, a.vc + base1 * Cv, kTile * Cv, a.vc, vpool_end, lane);
+          norms(base1, nkn, nvn);
+        }
+        floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+        tile_pass<true, true, true>(dk, dv, kst + koff + lane * Ck, vst + voff + lane * Cv, qreg, pl, vt, sc, acc,
+                                    lane);
+        softmax_tile(sc, nkc, nvc, j * kTile + lane < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
+        wave_sync();  // P and the V tile are complete
+        pv_full(pl, vt, acc, lane);
+        nkc = nkn;
+        nvc = nvn;
+      }
+      write_partial(a.part + item * 4 * kPart, acc, m_run, l_lane, lane);
+      continue;
+    }
     uint32_t nk0, nv0, nk1 = 0, nv1 = 0;
     // prologue: K of tile 0
     const int64_t base0 = tile_base(0);
@@ -619,26 +720,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
       nv1 = nv2;
     }
 
-    // partial for this item: the two token halves of every dim are summed
-    // across lanes l and l ^ 32; lanes 0..31 hold dims 32p + l.
-    float *dst = a.part + item * 4 * kPart;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float a2 = acc[p][h] + acc[4 + p][h];
-        const float v = a2 + __shfl_xor(a2, 32);
-        if (lane < 32) dst[h * kPart + p * kPass + lane] = v;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float l = wave_sum(l_lane[h]);
-      if (lane == h) {
-        dst[h * kPart + 128] = m_run[h];
-        dst[h * kPart + 129] = l;
-      }
-    }
+    write_partial(a.part + item * 4 * kPart, acc, m_run, l_lane, lane);
   }
 }
 
@@ -1160,6 +1242,7 @@ __global__ void __launch_bounds__(128) prefill_combine_kernel(AttnArgs a, uint64
 // ---------------------------------------------------------------- planning
 struct Plan {
   int chunk, nc, waves_per_block, blocks_cap, nq;
+  bool lat;  // latency mode (whole V tiles in LDS, fewer waves per CU)
   int64_t n_items;
   size_t lds, qrot_bytes, part_bytes, part_new_bytes, total;
 };
@@ -1228,6 +1311,21 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   pl->waves_per_block = wpb;
   pl->n_items = (int64_t)B * Hkv * nc;
   pl->lds = (size_t)wpb * wb;  // dynamic part; the decode tables are static
+  // latency mode when its fewer resident waves still take every item in one
+  // round (small batches); DQ_LATENCY_MODE forces it on (1) or off (0)
+  pl->lat = false;
+  if (pl->nq == 3) {
+    const int lwb = wave_layout(Ck, Cv, true).bytes;
+    int lwpb = (lds_cap - kStaticLds) / lwb;
+    lwpb = lwpb > 12 ? 12 : lwpb;
+    bool lat = lwpb >= 1 && pl->n_items <= (int64_t)cus * lwpb;
+    if (const char *e = getenv("DQ_LATENCY_MODE")) lat = lwpb >= 1 && e[0] == '1';
+    if (lat) {
+      pl->lat = true;
+      pl->waves_per_block = lwpb;
+      pl->lds = (size_t)lwpb * lwb;
+    }
+  }
   pl->blocks_cap = cus;  // one block per CU at most; fewer when the items are few
   pl->qrot_bytes = 0;  // each item rotates its own query
   pl->part_bytes = ((size_t)pl->n_items * 4 * kPart * sizeof(float) + 255) & ~(size_t)255;
@@ -1236,19 +1334,19 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   return DQ_OK;
 }
 
-template <int NQ, bool APPEND>
+template <int NQ, bool APPEND, bool LAT = false>
 hipError_t launch_splitk(const Plan &pl, const AttnArgs &a, const Tables &tk, const Tables &tv, hipStream_t s) {
   // dynamic LDS beyond the default limit, requested once (thread-safe static)
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ, APPEND>),
+      hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ, APPEND, LAT>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kStaticLds);
   if (attr != hipSuccess) return attr;
   // the append's encode items (if this launch runs them) come first, one per wave
   const int64_t n = a.n_items + (APPEND ? a.n_enc : 0);
   const int64_t want = (n + pl.waves_per_block - 1) / pl.waves_per_block;
   const int blocks = (int)(want < pl.blocks_cap ? want : pl.blocks_cap);
-  hipLaunchKernelGGL((attn_splitk_kernel<NQ, APPEND>), dim3((unsigned)blocks), dim3(64 * pl.waves_per_block), pl.lds,
-                     s, a, tk, tv);
+  hipLaunchKernelGGL((attn_splitk_kernel<NQ, APPEND, LAT>), dim3((unsigned)blocks), dim3(64 * pl.waves_per_block),
+                     pl.lds, s, a, tk, tv);
   return hipGetLastError();
 }
 
@@ -1483,7 +1581,10 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
   }
   if (split_begin && hipEventRecord(split_begin, s) != hipSuccess) return DQ_ERR_HIP;
   hipError_t e;
-  if (app && a.n_enc > 0)  // the variant with the encode loop only when it has encodes to run
+  if (pl.lat)  // latency mode (only for the 3-piece tile fetch)
+    e = app && a.n_enc > 0 ? dq::launch_splitk<3, true, true>(pl, a, ck->t, cv->t, s)
+                           : dq::launch_splitk<3, false, true>(pl, a, ck->t, cv->t, s);
+  else if (app && a.n_enc > 0)  // the variant with the encode loop only when it has encodes to run
     e = pl.nq == 3   ? dq::launch_splitk<3, true>(pl, a, ck->t, cv->t, s)
         : pl.nq == 5 ? dq::launch_splitk<5, true>(pl, a, ck->t, cv->t, s)
                      : dq::launch_splitk<9, true>(pl, a, ck->t, cv->t, s);

@@ -441,8 +441,8 @@ __device__ __forceinline__ void wave_encode_block(const EncodeArgs &a, const Tab
   __shared__ uint4 etab[kMaxLevels];
   __shared__ float2 rdtab[kMaxHalf];
   __shared__ uint32_t ent[kWaveVecs][kD];
-  __shared__ float key[kWaveVecs][kD];
-  __shared__ uint8_t mag[kWaveVecs][kD];
+  __shared__ __attribute__((aligned(16))) float key[kWaveVecs][kD];  // read as float4
+  __shared__ __attribute__((aligned(16))) uint8_t mag[kWaveVecs][kD];  // read as words
   __shared__ uint8_t scr[kWaveVecs][kWaveScr * 64];
   __shared__ uint32_t bstat[6 + kMaxC + 1];  // per-block stats, flushed once
   const int tid = threadIdx.x;

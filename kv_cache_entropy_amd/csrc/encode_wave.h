@@ -80,8 +80,8 @@ __device__ __forceinline__ void wave_encode_tables(const Tables &t, uint4 *etab,
 // does not fit anyway, so only its length, not its bytes, must be right.
 struct WaveEncodeScratch {
   uint32_t *ent;  // [128] s0 | sd << 8 | rank << 16
-  float *key;     // [128] drift-order key
-  uint8_t *mag;   // [128] magnitude cell
+  float *key;     // [128] drift-order key (16-byte aligned: read as float4)
+  uint8_t *mag;   // [128] magnitude cell (4-byte aligned: read as words)
   uint8_t *scr;   // [rows][64] renorm bytes, lane-minor
   int rows;
 };
@@ -186,16 +186,28 @@ __device__ __forceinline__ void wave_encode_vector(const uint16_t *xp, int g, co
     Y[lane] = kA[0];
     Y[lane + 64] = kA[1];
     wave_sync_lds();
+    // four candidates per LDS read (a float4 of keys, a word of magnitudes),
+    // the tests combined without short-circuit branches
     int rank[2] = {0, 0};
-    for (int j = 0; j < kD; ++j) {
-      const uint32_t mj = Mg[j];
-      const float yj = Y[j];
+    const float4 *Y4 = reinterpret_cast<const float4 *>(Y);
+    const uint32_t *M4 = reinterpret_cast<const uint32_t *>(Mg);
+#pragma unroll 4
+    for (int j4 = 0; j4 < kD / 4; ++j4) {
+      const float4 y4 = Y4[j4];
+      const uint32_t m4 = M4[j4];
+      const float yv[4] = {y4.x, y4.y, y4.z, y4.w};
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int i = lane + 64 * e;
-        const bool tie_first = yj < kA[e] || (yj == kA[e] && j < i);
-        const bool before = mj >= 1u && (RD ? tie_first : (mj > mA[e] || (mj == mA[e] && tie_first)));
-        rank[e] += before ? 1 : 0;
+      for (int u = 0; u < 4; ++u) {
+        const int j = 4 * j4 + u;
+        const uint32_t mj = (m4 >> (8 * u)) & 0xFFu;
+        const float yj = yv[u];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = lane + 64 * e;
+          const bool tie_first = (yj < kA[e]) | ((yj == kA[e]) & (j < i));
+          const bool before = (mj >= 1u) & (RD ? tie_first : ((mj > mA[e]) | ((mj == mA[e]) & tie_first)));
+          rank[e] += before ? 1 : 0;
+        }
       }
     }
     int total = 0;
@@ -212,6 +224,9 @@ __device__ __forceinline__ void wave_encode_vector(const uint16_t *xp, int g, co
       const uint32_t k = (uint32_t)(k0 + lane);
       uint32_t x = kLow;
       int pos = rows - 1;
+      // the symbol and coder-constant reads of a step do not depend on the
+      // state: unrolled, they run ahead of the state chain
+#pragma unroll 8
       for (int i = kD - 1; i >= 0; --i) {
         const uint32_t en = E[i];
         const uint32_t s = ((en >> 16) & 0xFFu) < k ? ((en >> 8) & 0xFFu) : (en & 0xFFu);

@@ -355,6 +355,37 @@ def test_attention_append(oracle_lib, monkeypatch, Hq, hkv, lens, order, C, spli
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("Hq,hkv,lens,C,split", [
+    (8, 2, [1, 63, 64, 65, 300, 129, 2000], (34, 34), None),
+    (4, 4, [5000, 70], (29, 29), 640),
+    (1, 1, [128, 1], (34, 29), 64),
+])
+def test_attention_latency_mode_bit_identical(oracle_lib, monkeypatch, Hq, hkv, lens, C, split):
+    """Latency mode (each tile's K and V decoded in one pass, PV after the
+    tile's softmax) and the pipelined mode do the same arithmetic in the same
+    order: forced either way, plain decode and decode with append give the
+    same bytes; and the oracle agrees."""
+    O = oracle_lib
+    if split:
+        monkeypatch.setenv("DQ_SPLIT_TOKENS", str(split))
+    c = _attn_case(O, len(lens), Hq, hkv, lens, C=C, seed=101 + Hq)
+    B = len(lens)
+    k_new = synth.kv_tensor("outlier", B, hkv, seed=111, device=DEV)
+    v_new = synth.kv_tensor("outlier", B, hkv, seed=112, device=DEV)
+    res = {}
+    for mode in ("0", "1"):
+        monkeypatch.setenv("DQ_LATENCY_MODE", mode)
+        plain = _gpu_attn(c)
+        (_, _, _), (pb, sb, ob) = _append_both(c, k_new, v_new, max(lens) + 1)[0]
+        res[mode] = (plain, ob, pb)
+    monkeypatch.delenv("DQ_LATENCY_MODE")
+    assert torch.equal(res["0"][0], res["1"][0]), "plain decode differs between modes"
+    assert torch.equal(res["0"][1], res["1"][1]), "decode with append differs between modes"
+    for x, y in zip(res["0"][2], res["1"][2]):
+        assert torch.equal(x, y)
+    _assert_close(res["1"][0].cpu().numpy(), _oracle_attn(O, c), f"latency mode Hq={Hq} hkv={hkv}")
+
+
 def test_decode_step_graph_replay(oracle_lib):
     """A decode step with append captured once in a HIP graph
     (torch.cuda.CUDAGraph over the library's launches, which go to the
