@@ -373,8 +373,8 @@ def main():
     nq = 3 if max(ck.C, cv.C) <= 47 else (5 if max(ck.C, cv.C) <= 79 else 9)  # the kernel's tile pieces
 
     def step(s, ev=None):
-        # one decode step, one launch: the new token's K/V encoded into the
-        # pools inside the attention launch (dq_attn_decode_append)
+        # one decode step, one call: the new token's K/V encoded into the
+        # pools and attention over the grown contexts (dq_attn_decode_append)
         if ev is not None:
             ev[0].record()
         dq.attn_decode_append(ck, cv, qs[s], Kn[s], Vn[s], kc, kn, vc, vn, st_t, lens_s[s], max_len, out=out,

@@ -270,7 +270,7 @@ int dq_attn_decode_timed(dq_codec_t ck, dq_codec_t cv, const void *q,
                          dq_stream_t stream, void *split_begin,
                          void *split_end);
 
-/* Decode step with append, in one launch: the step's new token of every
+/* Decode step with append, in one call: the step's new token of every
  * sequence is encoded into the pools (as dq_encode would write it) and
  * attended to in the same call.  This is the fused append of the decode
  * step ("D-Quant: Entropy Coding Meets KV Cache at 2.26 Bits", The Numbers:

@@ -369,7 +369,7 @@ def attn_decode_append(ck: Codec, cv: Codec, q: torch.Tensor, k_new: torch.Tenso
                        out_dtype=torch.float32, workspace: torch.Tensor | None = None,
                        k_stats: torch.Tensor | None = None, v_stats: torch.Tensor | None = None,
                        split_events=None):
-    """A decode step with append in one launch: k_new, v_new bf16 [B, Hkv, 128]
+    """A decode step with append in one call: k_new, v_new bf16 [B, Hkv, 128]
     are encoded into slot seq_start[b] + seq_len[b] - 1 (seq_len counts the
     new token) and attended to with the rest of the cache.  Returns out
     [B, Hq, 128]; the pools are updated in place.
