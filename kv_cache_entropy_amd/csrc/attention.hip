@@ -872,7 +872,7 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
 //    tile (16 tokens x 16 dims); lane l ends with rows 4 (l / 16) + i of
 //    dim 16 db + l % 16.
 constexpr int kRows = 16;
-constexpr int kQrotPrefill = 32 * 4 * 4 * 8;  // halves per (b, g, block): [dim quad][lane][row group][hi4 lo4]
+constexpr int kQrotPrefill = 32 * 4 * 4 * 8;  // halves per (b, g, block): [dim quad][row group][row][hi4 lo4]
 
 typedef float floatx4v __attribute__((ext_vector_type(4)));
 
@@ -891,7 +891,7 @@ __global__ void __launch_bounds__(64) rotate_qp_kernel(AttnArgs a, uint64_t ksee
   const int r = tl * a.group + hh, i = r & 3, rg = r >> 2;
   uint16_t *dst = a.qrot + (((int64_t)b * a.Hkv + g) * a.nqb + qb) * kQrotPrefill;
   const int d0 = lane, d1 = lane + 64;
-  auto at = [&](int d) { return ((((d >> 2) * 4 + i) * 4 + rg) * 8) + (d & 3); };
+  auto at = [&](int d) { return ((((d >> 2) * 4 + rg) * 4 + i) * 8) + (d & 3); };
   if (tq >= a.Tq) {
     dst[at(d0)] = 0; dst[at(d0) + 4] = 0; dst[at(d1)] = 0; dst[at(d1) + 4] = 0;
     return;
@@ -936,12 +936,12 @@ template <bool DK, bool DV>
 __device__ __forceinline__ void prefill_tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
                                                   const uint8_t *vb, const uint4 *qg, const uint16_t *pl,
                                                   uint16_t *vt, floatx4 (&sc)[4], floatx4 (&acc)[8], int lane) {
-  const bool qlane = lane < 4;
-  uint4 qn[4] = {};
-  if (DK && qlane) {
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) qn[rg] = qg[lane * 4 + rg];
-  }
+  // query operands of a dim group: lane 4 r + i (r < 4) holds row i of row
+  // group r (hi x4, lo x4); each MFMA broadcasts block r (cbsz 4, abid r),
+  // so only lanes 0 .. 15 load (one 256-byte read per group)
+  const bool qlane = lane < 16;
+  uint4 qn = make_uint4(0, 0, 0, 0);
+  if (DK && qlane) qn = qg[lane];
   uint32_t xk = 0, xv = 0;
   lds_u8 *pk = nullptr, *pv = nullptr;
   if (DK) {
@@ -985,18 +985,15 @@ __device__ __forceinline__ void prefill_tile_pass(const DecTab tk, const DecTab 
         const uint32_t b01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
         const uint32_t b23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
         const half4 Bk = __builtin_bit_cast(half4, make_uint2(b01, b23));
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          sc[rg] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(qn[rg].x, qn[rg].y)), Bk,
-                                                      sc[rg], 4, 0, 0);
-          sc[rg] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(qn[rg].z, qn[rg].w)), Bk,
-                                                      sc[rg], 4, 0, 0);
-        }
+        const half4 Qh = __builtin_bit_cast(half4, make_uint2(qn.x, qn.y));
+        const half4 Ql = __builtin_bit_cast(half4, make_uint2(qn.z, qn.w));
         // next dim group's query operands, in flight during its decode
-        if (qlane && gnext < 32) {
-#pragma unroll
-          for (int rg = 0; rg < 4; ++rg) qn[rg] = qg[(gnext * 4 + lane) * 4 + rg];
-        }
+        if (qlane && gnext < 32) qn = qg[gnext * 16 + lane];
+        unroll<4>([&](auto rc) {
+          constexpr int rg = decltype(rc)::value;
+          sc[rg] = __builtin_amdgcn_mfma_f32_4x4x4f16(Qh, Bk, sc[rg], 4, rg, 0);
+          sc[rg] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ql, Bk, sc[rg], 4, rg, 0);
+        });
       }
     }
     if (DV) {
