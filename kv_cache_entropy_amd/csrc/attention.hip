@@ -553,6 +553,12 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  // lane l decodes token tok of each tile: the even tokens in lanes 0..31,
+  // the odd ones in 32..63.  The LDS serves a wave 32 lanes at a time, and
+  // the streams of one half then start 2 C bytes apart (17 dwords for C =
+  // 34), so their byte reads spread over the banks.  P and the V tile are
+  // indexed by lane: the token order inside a tile never shows.
+  const int tok = ((lane & 31) << 1) | (lane >> 5);
   const int Ck = tk.C, Cv = tv.C;
   const WaveLayout L = wave_layout(Ck, Cv, LAT);
   uint8_t *base = smem + (size_t)wave * L.bytes;
@@ -615,7 +621,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 
     // this lane's token norms for a tile (0 outside the pool plane)
     auto norms = [&](int64_t tbase, uint32_t &nk, uint32_t &nv) {
-      const int64_t idx = tbase + lane;
+      const int64_t idx = tbase + tok;
       const bool ok = idx >= (int64_t)g * a.S && idx < (int64_t)(g + 1) * a.S;
       nk = ok ? a.kn[idx] : 0u;
       nv = ok ? a.vn[idx] : 0u;
@@ -649,9 +655,9 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
           norms(base1, nkn, nvn);
         }
         floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-        tile_pass<true, true, true>(dk, dv, kst + koff + lane * Ck, vst + voff + lane * Cv, qreg, pl, vt, sc, acc,
+        tile_pass<true, true, true>(dk, dv, kst + koff + tok * Ck, vst + voff + tok * Cv, qreg, pl, vt, sc, acc,
                                     lane);
-        softmax_tile(sc, nkc, nvc, j * kTile + lane < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
+        softmax_tile(sc, nkc, nvc, j * kTile + tok < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
         wave_sync();  // P and the V tile are complete
         pv_full(pl, vt, acc, lane);
         nkc = nkn;
@@ -686,8 +692,8 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 #pragma unroll
     for (int p = 0; p < 8; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
     floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-    tile_pass<true, false>(dk, dv, kst + koff0 + lane * Ck, nullptr, qreg, pl, vt, sc, acc, lane);
-    softmax_tile(sc, nk0, nv0, lane < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
+    tile_pass<true, false>(dk, dv, kst + koff0 + tok * Ck, nullptr, qreg, pl, vt, sc, acc, lane);
+    softmax_tile(sc, nk0, nv0, tok < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
 
     for (int j = 0; j < ntiles; ++j) {
       const bool next = j + 1 < ntiles;
@@ -711,10 +717,10 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
       }
       if (next) {
         sc = floatx4{0.f, 0.f, 0.f, 0.f};
-        tile_pass<true, true>(dk, dv, kst + koff + lane * Ck, vst + voff + lane * Cv, qreg, pl, vt, sc, acc, lane);
-        softmax_tile(sc, nk1, nv1, (j + 1) * kTile + lane < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
+        tile_pass<true, true>(dk, dv, kst + koff + tok * Ck, vst + voff + tok * Cv, qreg, pl, vt, sc, acc, lane);
+        softmax_tile(sc, nk1, nv1, (j + 1) * kTile + tok < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
       } else {
-        tile_pass<false, true>(dk, dv, nullptr, vst + voff + lane * Cv, qreg, pl, vt, sc, acc, lane);
+        tile_pass<false, true>(dk, dv, nullptr, vst + voff + tok * Cv, qreg, pl, vt, sc, acc, lane);
       }
       nk1 = nk2;
       nv1 = nv2;
@@ -872,7 +878,7 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
 //    tile (16 tokens x 16 dims); lane l ends with rows 4 (l / 16) + i of
 //    dim 16 db + l % 16.
 constexpr int kRows = 16;
-constexpr int kQrotPrefill = 32 * 4 * 4 * 8;  // halves per (b, g, block): [dim quad][row group][row][hi4 lo4]
+constexpr int kQrotPrefill = 32 * 4 * 4 * 8;  // halves per (b, g, block): [dim quad][lane][row group][hi4 lo4]
 
 typedef float floatx4v __attribute__((ext_vector_type(4)));
 
@@ -891,7 +897,7 @@ __global__ void __launch_bounds__(64) rotate_qp_kernel(AttnArgs a, uint64_t ksee
   const int r = tl * a.group + hh, i = r & 3, rg = r >> 2;
   uint16_t *dst = a.qrot + (((int64_t)b * a.Hkv + g) * a.nqb + qb) * kQrotPrefill;
   const int d0 = lane, d1 = lane + 64;
-  auto at = [&](int d) { return ((((d >> 2) * 4 + rg) * 4 + i) * 8) + (d & 3); };
+  auto at = [&](int d) { return ((((d >> 2) * 4 + i) * 4 + rg) * 8) + (d & 3); };
   if (tq >= a.Tq) {
     dst[at(d0)] = 0; dst[at(d0) + 4] = 0; dst[at(d1)] = 0; dst[at(d1) + 4] = 0;
     return;
@@ -936,12 +942,12 @@ template <bool DK, bool DV>
 __device__ __forceinline__ void prefill_tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
                                                   const uint8_t *vb, const uint4 *qg, const uint16_t *pl,
                                                   uint16_t *vt, floatx4 (&sc)[4], floatx4 (&acc)[8], int lane) {
-  // query operands of a dim group: lane 4 r + i (r < 4) holds row i of row
-  // group r (hi x4, lo x4); each MFMA broadcasts block r (cbsz 4, abid r),
-  // so only lanes 0 .. 15 load (one 256-byte read per group)
-  const bool qlane = lane < 16;
-  uint4 qn = make_uint4(0, 0, 0, 0);
-  if (DK && qlane) qn = qg[lane];
+  const bool qlane = lane < 4;
+  uint4 qn[4] = {};
+  if (DK && qlane) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) qn[rg] = qg[lane * 4 + rg];
+  }
   uint32_t xk = 0, xv = 0;
   lds_u8 *pk = nullptr, *pv = nullptr;
   if (DK) {
@@ -985,15 +991,18 @@ __device__ __forceinline__ void prefill_tile_pass(const DecTab tk, const DecTab 
         const uint32_t b01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
         const uint32_t b23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
         const half4 Bk = __builtin_bit_cast(half4, make_uint2(b01, b23));
-        const half4 Qh = __builtin_bit_cast(half4, make_uint2(qn.x, qn.y));
-        const half4 Ql = __builtin_bit_cast(half4, make_uint2(qn.z, qn.w));
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          sc[rg] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(qn[rg].x, qn[rg].y)), Bk,
+                                                      sc[rg], 4, 0, 0);
+          sc[rg] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4, make_uint2(qn[rg].z, qn[rg].w)), Bk,
+                                                      sc[rg], 4, 0, 0);
+        }
         // next dim group's query operands, in flight during its decode
-        if (qlane && gnext < 32) qn = qg[gnext * 16 + lane];
-        unroll<4>([&](auto rc) {
-          constexpr int rg = decltype(rc)::value;
-          sc[rg] = __builtin_amdgcn_mfma_f32_4x4x4f16(Qh, Bk, sc[rg], 4, rg, 0);
-          sc[rg] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ql, Bk, sc[rg], 4, rg, 0);
-        });
+        if (qlane && gnext < 32) {
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) qn[rg] = qg[(gnext * 4 + lane) * 4 + rg];
+        }
       }
     }
     if (DV) {
@@ -1079,6 +1088,7 @@ __global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
+  const int tok = ((lane & 31) << 1) | (lane >> 5);  // this lane's token of a tile
   const int wave = threadIdx.x >> 6;
   const int Ck = tk.C, Cv = tv.C;
   const WaveLayout L = prefill_layout(Ck, Cv);
@@ -1110,7 +1120,7 @@ __global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk
     wave_sync();
     const uint4 *qr = reinterpret_cast<const uint4 *>(a.qrot + ((bg * a.nqb) + qb) * kQrotPrefill);
     auto norms = [&](int64_t tbase, uint32_t &nk, uint32_t &nv) {
-      const int64_t idx = tbase + lane;
+      const int64_t idx = tbase + tok;
       const bool ok = idx >= plane0 && idx < plane0 + a.S;
       nk = ok ? a.kn[idx] : 0u;
       nv = ok ? a.vn[idx] : 0u;
@@ -1143,8 +1153,8 @@ __global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk
     floatx4 sc[4];
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) sc[rg] = floatx4{0.f, 0.f, 0.f, 0.f};
-    prefill_tile_pass<true, false>(dk, dv, kst + koff0 + lane * Ck, nullptr, qr, pl, vt, sc, acc, lane);
-    prefill_softmax(sc, nk0, nv0, t0 + lane < t1, t0 + lane, pos0, a.group, a.qk_scale, m_run, l_lane, pl, acc,
+    prefill_tile_pass<true, false>(dk, dv, kst + koff0 + tok * Ck, nullptr, qr, pl, vt, sc, acc, lane);
+    prefill_softmax(sc, nk0, nv0, t0 + tok < t1, t0 + tok, pos0, a.group, a.qk_scale, m_run, l_lane, pl, acc,
                     lane);
 
     for (int j = 0; j < ntiles; ++j) {
@@ -1169,12 +1179,12 @@ __global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk
       if (next) {
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) sc[rg] = floatx4{0.f, 0.f, 0.f, 0.f};
-        prefill_tile_pass<true, true>(dk, dv, kst + koff + lane * Ck, vst + voff + lane * Cv, qr, pl, vt, sc, acc,
+        prefill_tile_pass<true, true>(dk, dv, kst + koff + tok * Ck, vst + voff + tok * Cv, qr, pl, vt, sc, acc,
                                       lane);
-        const int tp = t0 + (j + 1) * kTile + lane;
+        const int tp = t0 + (j + 1) * kTile + tok;
         prefill_softmax(sc, nk1, nv1, tp < t1, tp, pos0, a.group, a.qk_scale, m_run, l_lane, pl, acc, lane);
       } else {
-        prefill_tile_pass<false, true>(dk, dv, nullptr, vst + voff + lane * Cv, qr, pl, vt, sc, acc, lane);
+        prefill_tile_pass<false, true>(dk, dv, nullptr, vst + voff + tok * Cv, qr, pl, vt, sc, acc, lane);
       }
       nk1 = nk2;
       nv1 = nv2;
