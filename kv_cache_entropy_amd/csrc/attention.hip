@@ -177,6 +177,16 @@ struct TileRegs {
   int off;
 };
 
+// A 16-byte load from global memory, typed as such: a generic (flat) load
+// would also count on the LDS counter, and while one is in flight every
+// wait for an LDS result has to be a wait for all of them.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4 global_u32x4;
+__device__ __forceinline__ uint4 load_global16(uintptr_t p) {
+  const u32x4 v = *(global_u32x4 *)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int NQ>
 __device__ __forceinline__ void fetch(TileRegs<NQ> &r, const uint8_t *src, int nbytes, const uint8_t *pool,
                                       const uint8_t *pool_end, int lane) {
@@ -189,7 +199,7 @@ __device__ __forceinline__ void fetch(TileRegs<NQ> &r, const uint8_t *src, int n
   for (int k = 0; k < NQ; ++k) {
     const int i = lane + 64 * k;
     const uintptr_t p = a0 + 16 * (uintptr_t)i;
-    r.q[k] = (i < n16 && p >= beg && p + 16 <= end) ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
+    r.q[k] = (i < n16 && p >= beg && p + 16 <= end) ? load_global16(p) : make_uint4(0, 0, 0, 0);
   }
 }
 
