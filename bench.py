@@ -565,8 +565,10 @@ def main():
         torch.cuda.synchronize()
         pms = e0.elapsed_time(e1) / reps
         group = Hq // Hkv
-        tb = 16 // group
-        # compressed bytes the kernel reads: each block of tb queries reads its causal prefix
+        # compressed bytes the kernel reads: each item of query blocks reads its
+        # causal prefix once (8 blocks of 16 rows per item for containers of up
+        # to 43 bytes, one block otherwise)
+        tb = (16 // group) * (8 if max(ck.C, cv.C) <= 43 else 1)
         lens_np = lens_p.cpu().numpy().astype(np.int64)
         read = 0
         for L in lens_np:
@@ -574,7 +576,7 @@ def main():
                 read += (L - tq + min(tq, (qb + 1) * tb)) * Hkv * (ck.C + 2 + cv.C + 2)
         prefill = {"batch": nb, "chunk_tokens": tq, "context": int(lens_np.max()), "call_ms": round(pms, 3),
                    "query_tokens_per_s": round(nb * tq / (pms / 1e3), 1),
-                   "kv_bytes_read_gbps": round(read / (pms / 1e3) / 1e9, 1), "rows_per_item": 16}
+                   "kv_bytes_read_gbps": round(read / (pms / 1e3) / 1e9, 1), "rows_per_item": tb * group}
         log(f"[bench] chunked prefill: {nb} x {tq} queries over {prefill['context']} tokens in {pms:.2f} ms "
             f"({prefill['query_tokens_per_s'] / 1e3:.1f} K query tokens/s, {prefill['kv_bytes_read_gbps']} GB/s read)")
         del qp, wsp, outp

@@ -213,6 +213,12 @@ __device__ __forceinline__ void commit(const TileRegs<NQ> &r, uint8_t *dst, int 
   }
 }
 
+// The token of a 64-token tile that lane l decodes: the even tokens in
+// lanes 0..31, the odd ones in 32..63.  The LDS serves a wave 32 lanes at a
+// time, and the streams of one half then start 2 C bytes apart (17 dwords
+// for C = 34), so their byte reads spread over the banks.
+__device__ __forceinline__ int lane_token(int lane) { return ((lane & 31) << 1) | (lane >> 5); }
+
 struct DecTab {
   const uint8_t *sym8;
   const uint2 *symtab;
@@ -563,12 +569,8 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  // lane l decodes token tok of each tile: the even tokens in lanes 0..31,
-  // the odd ones in 32..63.  The LDS serves a wave 32 lanes at a time, and
-  // the streams of one half then start 2 C bytes apart (17 dwords for C =
-  // 34), so their byte reads spread over the banks.  P and the V tile are
-  // indexed by lane: the token order inside a tile never shows.
-  const int tok = ((lane & 31) << 1) | (lane >> 5);
+  // P and the V tile are indexed by lane: the token order inside a tile never shows
+  const int tok = lane_token(lane);
   const int Ck = tk.C, Cv = tv.C;
   const WaveLayout L = wave_layout(Ck, Cv, LAT);
   uint8_t *base = smem + (size_t)wave * L.bytes;
@@ -888,10 +890,16 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
 //    tile (16 tokens x 16 dims); lane l ends with rows 4 (l / 16) + i of
 //    dim 16 db + l % 16.
 constexpr int kRows = 16;
-constexpr int kQrotPrefill = 32 * 4 * 4 * 8;  // halves per (b, g, block): [dim quad][lane][row group][hi4 lo4]
+// rotated queries, halves per (b, g, block) in either layout:
+//   per-block decode: [dim quad][lane][row group][hi4 lo4]
+//   shared decode:    [16-dim block][lane][hi4 lo4], lane 16 k + r holding
+//                     dims 4 k .. 4 k + 3 of the block for row r (the B
+//                     operand of a 16x16x16 MFMA)
+constexpr int kQrotPrefill = 32 * 4 * 4 * 8;
 
 typedef float floatx4v __attribute__((ext_vector_type(4)));
 
+template <bool SHARED>
 __global__ void __launch_bounds__(64) rotate_qp_kernel(AttnArgs a, uint64_t kseed) {
   const int lane = threadIdx.x;
   // block = ((b * nqb + qb) * tb + tl) * Hq + h
@@ -907,7 +915,10 @@ __global__ void __launch_bounds__(64) rotate_qp_kernel(AttnArgs a, uint64_t ksee
   const int r = tl * a.group + hh, i = r & 3, rg = r >> 2;
   uint16_t *dst = a.qrot + (((int64_t)b * a.Hkv + g) * a.nqb + qb) * kQrotPrefill;
   const int d0 = lane, d1 = lane + 64;
-  auto at = [&](int d) { return ((((d >> 2) * 4 + i) * 4 + rg) * 8) + (d & 3); };
+  auto at = [&](int d) {
+    return SHARED ? (((d >> 4) * 64 + ((d & 15) >> 2) * 16 + r) * 8) + (d & 3)
+                  : ((((d >> 2) * 4 + i) * 4 + rg) * 8) + (d & 3);
+  };
   if (tq >= a.Tq) {
     dst[at(d0)] = 0; dst[at(d0) + 4] = 0; dst[at(d1)] = 0; dst[at(d1) + 4] = 0;
     return;
@@ -1098,7 +1109,7 @@ __global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const int tok = ((lane & 31) << 1) | (lane >> 5);  // this lane's token of a tile
+  const int tok = lane_token(lane);
   const int wave = threadIdx.x >> 6;
   const int Ck = tk.C, Cv = tv.C;
   const WaveLayout L = prefill_layout(Ck, Cv);
@@ -1213,6 +1224,262 @@ __global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk
       if (lane == r) {
         dst[r * kPart + 128] = m_run[r];
         dst[r * kPart + 129] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- prefill, shared decode
+// For containers of up to 47 bytes.  A block of kSbWaves waves takes an
+// item (sequence, kv head, kSbWaves consecutive query blocks of 16 rows,
+// context chunk).  The chunk goes by in rounds of kRoundTiles tiles: waves
+// 0..3 decode K of the round's tiles and waves 4..7 V, one container per
+// lane, into fp16 level tiles in LDS; then every wave runs its own 16 rows
+// over those tiles on 16x16x16 MFMAs.  A tile is decoded once for the
+// item's 128 rows instead of once per 16.
+//
+// Scores are formed transposed, S^T = K q~^T (tokens x rows), so that each
+// lane ends with 4 tokens of one row (lane l: row l mod 16, tokens 4 (l / 16)
+// .. + 3 of each 16-token block).  After the softmax that is, as it stands,
+// the B operand of O^T = V^T P^T, and the running max and sum are one value
+// per lane.
+constexpr int kSbWaves = 8;
+constexpr int kRoundTiles = 4;
+constexpr int kLvHalves = kTile * kD;  // one tile of K or V levels, fp16
+
+// K levels: [token][8-byte chunk c = dims 4 c .. 4 c + 3].  The chunk index
+// is swizzled so that the 16 tokens x 2 chunks a half-wave reads for an
+// MFMA operand, and the 32 tokens it writes at one chunk, all fall in
+// distinct banks.
+__device__ __forceinline__ int kl_off(int tok, int c) {
+  return tok * kD + ((c ^ ((tok & 15) << 1) ^ ((tok >> 4) & 3)) << 2);
+}
+// V levels: [dim][8-byte chunk of tokens 4 c .. 4 c + 3], swizzled likewise
+// for the operand reads (16 dims x 2 chunks) and the decode's writes (one
+// dim, 32 tokens).
+__device__ __forceinline__ int vl_off(int dim, int tok) {
+  return dim * kTile + ((((tok >> 2) ^ (((dim >> 1) & 7) << 1))) << 2) + (tok & 3);
+}
+
+__host__ __device__ inline size_t prefill_shared_lds(int Ck, int Cv) {
+  const int cmax = Ck > Cv ? Ck : Cv;
+  return (size_t)2 * kRoundTiles * kLvHalves * 2 + 2 * kRoundTiles * kTile * 4 +
+         (size_t)kSbWaves * ((kTile * cmax + 31) & ~15);
+}
+
+// One container per lane, a single rANS chain: K levels go to the K tile
+// four at a time, V levels one per step to the V tile.
+template <bool V>
+__device__ __forceinline__ void decode_levels(const DecTab t, const uint8_t *cb, uint16_t *dst, int tok) {
+  uint32_t x = load_le32(cb);
+  lds_u8 *p = to_lds(cb + 4);
+#pragma unroll
+  for (int G = 0; G < kD / 4; ++G) {
+    uint32_t lv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t bt = next_byte(p);
+      const uint32_t s8 = lookup_sym8(t, x);
+      const uint2 e = lookup_symtab(t, s8);
+      x = rans_advance(x, e);
+      renorm(x, p, bt);
+      lv[j] = e.y;
+      if (V) dst[vl_off(4 * G + j, tok)] = (uint16_t)(e.y >> 16);
+    }
+    if (!V) {
+      const uint32_t b01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
+      const uint32_t b23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
+      *reinterpret_cast<uint2 *>(dst + kl_off(tok, G)) = make_uint2(b01, b23);
+    }
+  }
+}
+
+// One decoded tile against this wave's 16 rows: S^T, the online softmax of
+// each row (lane l: row l mod 16), and O^T += V^T P^T.  tpos0 is the
+// position of the tile's first token; a token is visible to a row when it
+// lies before t1 and at or before the row's query position qpos.
+__device__ __forceinline__ void shared_tile(const uint16_t *kt, const uint16_t *vtl, const float *knl,
+                                            const float *vnl, const half4 (&qh)[8], const half4 (&ql)[8],
+                                            int tpos0, int t1, int qpos, float qk_scale, float &m_run,
+                                            float &l_run, floatx4 (&acc)[8], int lane) {
+  const int m = lane & 15, kq = lane >> 4;
+  floatx4 st[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) st[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < kD / 16; ++kb) {
+    half4 A[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) A[tb] = *reinterpret_cast<const half4 *>(kt + kl_off(16 * tb + m, 4 * kb + kq));
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) st[tb] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[tb], qh[kb], st[tb], 0, 0, 0);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) st[tb] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[tb], ql[kb], st[tb], 0, 0, 0);
+  }
+  float mx = -__builtin_inff();
+  bool vis[4][4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const float4 nk = *reinterpret_cast<const float4 *>(knl + 16 * tb + 4 * kq);
+    const float nkv[4] = {nk.x, nk.y, nk.z, nk.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tp = tpos0 + 16 * tb + 4 * kq + i;
+      vis[tb][i] = tp < t1 && tp <= qpos;
+      st[tb][i] = vis[tb][i] ? st[tb][i] * nkv[i] * qk_scale : -__builtin_inff();
+      mx = fmaxf(mx, st[tb][i]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  if (__builtin_amdgcn_read_exec() & __ballot(m_new > m_run)) {
+    const float alpha = m_new > m_run ? exp2f(m_run - m_new) : 1.0f;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+    m_run = m_new;
+  }
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const float4 nv = *reinterpret_cast<const float4 *>(vnl + 16 * tb + 4 * kq);
+    const float nvv[4] = {nv.x, nv.y, nv.z, nv.w};
+    half4 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = vis[tb][i] ? exp2f(st[tb][i] - m_run) : 0.0f;
+      l_run += p;
+      // P = p * n_v as an fp16 pair, as in decode attention
+      const float pv = p * nvv[i];
+      const _Float16 hi = (_Float16)pv;
+      ph[i] = hi;
+      pl[i] = (_Float16)(pv - (float)hi);
+    }
+    half4 A[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) A[db] = *reinterpret_cast<const half4 *>(vtl + vl_off(16 * db + m, 16 * tb + 4 * kq));
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[db], ph, acc[db], 0, 0, 0);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[db], pl, acc[db], 0, 0, 0);
+  }
+}
+
+template <int NQ>
+__global__ void __launch_bounds__(64 * kSbWaves) attn_prefill_shared_kernel(AttnArgs a, Tables tk, Tables tv) {
+  __shared__ uint8_t sym8[2][kM];
+  __shared__ uint2 symtab[2][kMaxLevels];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const DecTab dk{sym8[0], symtab[0]};
+  const DecTab dv{sym8[1], symtab[1]};
+  build_tables(sym8[0], symtab[0], tk, threadIdx.x, blockDim.x);
+  build_tables(sym8[1], symtab[1], tv, threadIdx.x, blockDim.x);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tok = lane_token(lane);
+  // decode role: K (waves 0..3) or V (4..7) of the round's tile wave mod 4
+  const bool isv = wave >= kRoundTiles;
+  const int dtile = wave & (kRoundTiles - 1);
+  const int C = isv ? tv.C : tk.C;
+  const int cmax = tk.C > tv.C ? tk.C : tv.C;
+  uint16_t *kl = reinterpret_cast<uint16_t *>(smem);
+  uint16_t *vl = kl + kRoundTiles * kLvHalves;
+  float *knl = reinterpret_cast<float *>(vl + kRoundTiles * kLvHalves);
+  float *vnl = knl + kRoundTiles * kTile;
+  uint8_t *stg = reinterpret_cast<uint8_t *>(vnl + kRoundTiles * kTile) + wave * ((kTile * cmax + 31) & ~15);
+  const uint8_t *pool = isv ? a.vc : a.kc;
+  const uint8_t *pool_end = pool + (size_t)a.Hkv * a.S * C;
+  const uint16_t *norm = isv ? a.vn : a.kn;
+  const int m = lane & 15, kq = lane >> 4;
+  const int nsb = (a.nqb + kSbWaves - 1) / kSbWaves;
+
+  for (int64_t item = blockIdx.x; item < a.n_items; item += gridDim.x) {
+    const int c = (int)(item % a.nc);
+    const int64_t rest = item / a.nc;
+    const int sb = (int)(rest % nsb);
+    const int64_t bg = rest / nsb;
+    const int b = (int)(bg / a.Hkv), g = (int)(bg - (int64_t)b * a.Hkv);
+    const int len = a.seq_len[b];
+    const int qb = sb * kSbWaves + wave;  // this wave's query block
+    const bool qvalid = qb < a.nqb;
+    const int qb_last = min(sb * kSbWaves + kSbWaves, a.nqb) - 1;
+    // position of the item's last query row, and of this wave's first and last
+    const int pmax = len - a.Tq + min(qb_last * a.tb + a.tb, a.Tq) - 1;
+    const int pos0 = len - a.Tq + qb * a.tb;
+    const int pend = pos0 + a.tb - 1;
+    const int t0 = c * a.chunk;
+    if (t0 > pmax || pmax < 0) continue;  // the same for the whole block
+    const int t1 = min(t0 + a.chunk, pmax + 1);
+    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+    const int64_t plane0 = (int64_t)g * a.S;
+    const int64_t sbase = plane0 + a.seq_start[b] + t0;  // pool index of token t0
+    const int qpos = pos0 + m / a.group;                   // query position of this lane's row
+
+    half4 qh[8], ql[8];
+    if (qvalid) {
+      const uint4 *qg = reinterpret_cast<const uint4 *>(a.qrot + ((bg * a.nqb) + qb) * kQrotPrefill);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const uint4 v = qg[kb * 64 + lane];
+        qh[kb] = __builtin_bit_cast(half4, make_uint2(v.x, v.y));
+        ql[kb] = __builtin_bit_cast(half4, make_uint2(v.z, v.w));
+      }
+    }
+    float m_run = -__builtin_inff(), l_run = 0.0f;
+    floatx4 acc[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    TileRegs<NQ> rr;
+    if (dtile < ntiles) fetch<NQ>(rr, pool + sbase * C + (int64_t)dtile * kTile * C, kTile * C, pool, pool_end, lane);
+    for (int r0 = 0; r0 < ntiles; r0 += kRoundTiles) {
+      const int tile = r0 + dtile;
+      if (tile < ntiles) {  // the same for the whole wave
+        commit<NQ>(rr, stg, kTile * C, lane);
+        const int off = rr.off;
+        wave_sync();
+        const int64_t idx = sbase + (int64_t)tile * kTile + tok;
+        const bool ok = idx >= plane0 && idx < plane0 + a.S;
+        const float nrm = ok ? (float)__builtin_bit_cast(_Float16, norm[idx]) : 0.0f;
+        if (tile + kRoundTiles < ntiles)
+          fetch<NQ>(rr, pool + (sbase + (int64_t)(tile + kRoundTiles) * kTile) * C, kTile * C, pool, pool_end, lane);
+        // one call per kernel argument (a table chosen at run time would go to scratch)
+        if (isv) {
+          decode_levels<true>(dv, stg + off + tok * C, vl + dtile * kLvHalves, tok);
+          vnl[dtile * kTile + tok] = nrm;
+        } else {
+          decode_levels<false>(dk, stg + off + tok * C, kl + dtile * kLvHalves, tok);
+          knl[dtile * kTile + tok] = nrm;
+        }
+      }
+      __syncthreads();  // the round's level tiles and norms are complete
+      if (qvalid) {
+        for (int tt = 0; tt < kRoundTiles; ++tt) {
+          const int tp0 = t0 + (r0 + tt) * kTile;
+          if (r0 + tt >= ntiles || tp0 > pend) break;  // later tiles are masked for every row
+          shared_tile(kl + tt * kLvHalves, vl + tt * kLvHalves, knl + tt * kTile, vnl + tt * kTile, qh, ql, tp0, t1,
+                      qpos, a.qk_scale, m_run, l_run, acc, lane);
+        }
+      }
+      __syncthreads();  // every read of the round's tiles is done
+    }
+
+    if (qvalid) {
+      // partial of (b, g, qb, c): lane l holds dims 16 db + 4 (l / 16) + i of row l mod 16
+      float *dst = a.part + ((((int64_t)b * a.Hkv + g) * a.nqb + qb) * a.nc + c) * kRows * kPart + m * kPart;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * db + 4 * kq + i] = acc[db][i];
+      float l = l_run + __shfl_xor(l_run, 16);
+      l += __shfl_xor(l, 32);
+      if (kq == 0) {
+        dst[128] = m_run;
+        dst[129] = l;
       }
     }
   }
@@ -1369,10 +1636,38 @@ hipError_t launch_splitk(const Plan &pl, const AttnArgs &a, const Tables &tk, co
 
 struct PrefillPlan {
   int chunk, nc, waves_per_block, blocks, nq, tb, nqb;
+  bool shared;  // shared-decode kernel (items of kSbWaves query blocks)
   int64_t n_items;
   size_t lds, qrot_bytes, part_bytes, total;
 };
 
+// Context split of the shared-decode kernel.  One block per CU takes items
+// (units x nc) in turn; an item of span s tokens costs about
+// ceil(s / 256) rounds of 4 tiles plus a fixed quarter round.  The chunk (a
+// multiple of 64) minimising ceil(items / CUs) x that is chosen.
+// DQ_SPLIT_TOKENS forces a chunk, as for decode.
+int64_t choose_prefill_chunk(int64_t units, int64_t max_len, int cus) {
+  const int64_t rt = (int64_t)kRoundTiles * kTile;
+  int64_t best = max_len, best_cost = INT64_MAX;
+  for (int64_t chunk = rt;; chunk += rt) {
+    const int64_t nc = (max_len + chunk - 1) / chunk;
+    const int64_t span = nc == 1 ? max_len : chunk;
+    const int64_t cost = ((units * nc + cus - 1) / cus) * (4 * ((span + rt - 1) / rt) + 1);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = nc == 1 ? ((max_len + kTile - 1) / kTile) * kTile : chunk;
+    }
+    if (nc == 1) break;
+  }
+  if (const char *e = getenv("DQ_SPLIT_TOKENS")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= kTile && v % kTile == 0) best = v;
+  }
+  return best;
+}
+
+// Ck, Cv pick the kernel: the shared-decode one when its LDS fits (C up to
+// 43), the per-block one otherwise.
 int make_prefill_plan(int B, int Tq, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, PrefillPlan *pl) {
   const int cus = device_cus();
   if (cus <= 0) return DQ_ERR_HIP;
@@ -1381,23 +1676,47 @@ int make_prefill_plan(int B, int Tq, int Hq, int Hkv, int64_t max_len, int Ck, i
   pl->nqb = (Tq + pl->tb - 1) / pl->tb;
   const int cmax = Ck > Cv ? Ck : Cv;
   pl->nq = cmax <= 47 ? 3 : (cmax <= 79 ? 5 : 9);
-  const int wb = prefill_layout(Ck, Cv).bytes;
-  int wpb = 8;
-  while (wpb > 1 && kLutBytes + wpb * wb > 160 * 1024) wpb -= 1;
-  if (kLutBytes + wpb * wb > 160 * 1024) return DQ_ERR_UNSUPPORTED;
-  const int64_t units = (int64_t)B * Hkv * pl->nqb;
-  const int64_t chunk = choose_chunk(units, max_len, (int64_t)cus * 8);
-  pl->chunk = (int)chunk;
-  pl->nc = (int)((max_len + chunk - 1) / chunk);
-  pl->waves_per_block = wpb;
-  pl->n_items = units * pl->nc;
-  pl->lds = (size_t)wpb * wb;
-  const int64_t want_blocks = (pl->n_items + wpb - 1) / wpb;
-  pl->blocks = (int)(want_blocks < cus ? want_blocks : cus);
-  pl->qrot_bytes = ((size_t)units * kQrotPrefill * 2 + 255) & ~(size_t)255;
-  pl->part_bytes = (size_t)pl->n_items * kRows * kPart * sizeof(float);
+  const int64_t qunits = (int64_t)B * Hkv * pl->nqb;  // (sequence, kv head, query block)
+  pl->shared = pl->nq == 3 && kLutBytes + prefill_shared_lds(Ck, Cv) <= 160 * 1024;
+  if (pl->shared) {
+    const int64_t units = (int64_t)B * Hkv * ((pl->nqb + kSbWaves - 1) / kSbWaves);
+    const int64_t chunk = choose_prefill_chunk(units, max_len, cus);
+    pl->chunk = (int)chunk;
+    pl->nc = (int)((max_len + chunk - 1) / chunk);
+    pl->waves_per_block = kSbWaves;
+    pl->n_items = units * pl->nc;
+    pl->lds = prefill_shared_lds(Ck, Cv);
+    pl->blocks = (int)(pl->n_items < cus ? pl->n_items : cus);
+  } else {
+    const int wb = prefill_layout(Ck, Cv).bytes;
+    int wpb = 8;
+    while (wpb > 1 && kLutBytes + wpb * wb > 160 * 1024) wpb -= 1;
+    if (kLutBytes + wpb * wb > 160 * 1024) return DQ_ERR_UNSUPPORTED;
+    const int64_t chunk = choose_chunk(qunits, max_len, (int64_t)cus * 8);
+    pl->chunk = (int)chunk;
+    pl->nc = (int)((max_len + chunk - 1) / chunk);
+    pl->waves_per_block = wpb;
+    pl->n_items = qunits * pl->nc;
+    pl->lds = (size_t)wpb * wb;
+    const int64_t want_blocks = (pl->n_items + wpb - 1) / wpb;
+    pl->blocks = (int)(want_blocks < cus ? want_blocks : cus);
+  }
+  pl->qrot_bytes = ((size_t)qunits * kQrotPrefill * 2 + 255) & ~(size_t)255;
+  pl->part_bytes = (size_t)qunits * pl->nc * kRows * kPart * sizeof(float);
   pl->total = pl->qrot_bytes + pl->part_bytes;
   return DQ_OK;
+}
+
+template <int NQ>
+hipError_t launch_prefill_shared(const PrefillPlan &pl, const AttnArgs &a, const Tables &tk, const Tables &tv,
+                                 hipStream_t s) {
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(attn_prefill_shared_kernel<NQ>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kLutBytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(attn_prefill_shared_kernel<NQ>, dim3((unsigned)pl.blocks), dim3(64 * kSbWaves), pl.lds, s, a,
+                     tk, tv);
+  return hipGetLastError();
 }
 
 template <int NQ>
@@ -1420,10 +1739,14 @@ extern "C" int dq_attn_prefill_workspace(int32_t B, int32_t Tq, int32_t Hq, int3
   if (!bytes || B < 1 || Tq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_len < Tq) return DQ_ERR_INVALID;
   const int group = Hq / Hkv;
   if (group != 1 && group != 2 && group != 4) return DQ_ERR_UNSUPPORTED;
-  dq::PrefillPlan pl;
-  const int st = dq::make_prefill_plan(B, Tq, Hq, Hkv, max_len, 34, 34, &pl);
+  // the kernel (and with it the split) depends on the container sizes, which
+  // this call does not know: the larger need of the two kernels
+  dq::PrefillPlan p1, p2;
+  int st = dq::make_prefill_plan(B, Tq, Hq, Hkv, max_len, 34, 34, &p1);
   if (st) return st;
-  *bytes = pl.total;
+  st = dq::make_prefill_plan(B, Tq, Hq, Hkv, max_len, 64, 64, &p2);
+  if (st) return st;
+  *bytes = p1.total > p2.total ? p1.total : p2.total;
   return DQ_OK;
 }
 
@@ -1481,10 +1804,16 @@ extern "C" int dq_attn_prefill(dq_codec_t ck, dq_codec_t cv, const void *q, int3
   a.nqb = pl.nqb;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t rot_blocks = (int64_t)B * pl.nqb * pl.tb * Hq;
-  hipLaunchKernelGGL(dq::rotate_qp_kernel, dim3((unsigned)rot_blocks), dim3(64), 0, s, a, ck->t.seed);
-  hipError_t e = pl.nq == 3   ? dq::launch_prefill<3>(pl, a, ck->t, cv->t, s)
-                 : pl.nq == 5 ? dq::launch_prefill<5>(pl, a, ck->t, cv->t, s)
-                              : dq::launch_prefill<9>(pl, a, ck->t, cv->t, s);
+  hipError_t e;
+  if (pl.shared) {
+    hipLaunchKernelGGL(dq::rotate_qp_kernel<true>, dim3((unsigned)rot_blocks), dim3(64), 0, s, a, ck->t.seed);
+    e = dq::launch_prefill_shared<3>(pl, a, ck->t, cv->t, s);
+  } else {
+    hipLaunchKernelGGL(dq::rotate_qp_kernel<false>, dim3((unsigned)rot_blocks), dim3(64), 0, s, a, ck->t.seed);
+    e = pl.nq == 3   ? dq::launch_prefill<3>(pl, a, ck->t, cv->t, s)
+        : pl.nq == 5 ? dq::launch_prefill<5>(pl, a, ck->t, cv->t, s)
+                     : dq::launch_prefill<9>(pl, a, ck->t, cv->t, s);
+  }
   if (e != hipSuccess) return DQ_ERR_HIP;
   hipLaunchKernelGGL(dq::prefill_combine_kernel, dim3((unsigned)((int64_t)B * Tq * Hq)), dim3(128), 0, s, a,
                      cv->t.seed);

@@ -763,6 +763,26 @@ def test_prefill_attention_small(oracle_lib, Hq, hkv, Tq):
     _assert_close(_gpu_prefill(c, q).cpu().numpy(), _oracle_prefill(O, c, q), f"prefill Hq={Hq} hkv={hkv} Tq={Tq}")
 
 
+@pytest.mark.parametrize("C,step64,Tq", [((44, 40), (30, 40), 21), ((60, 48), (30, 40), 9)])
+def test_prefill_attention_per_block_kernel(oracle_lib, C, step64, Tq):
+    """Containers too large for the shared-decode kernel's LDS (44 and 60
+    bytes) take the per-block kernel: every row against the oracle."""
+    O = oracle_lib
+    lens = [Tq, 200 + Tq, 70]
+    c, q = _prefill_case(O, lens, Tq, 8, 2, seed=31 + C[0], C=C, step64=step64)
+    _assert_close(_gpu_prefill(c, q).cpu().numpy(), _oracle_prefill(O, c, q), f"prefill C={C}")
+
+
+@pytest.mark.parametrize("Tq", [40, 129])
+def test_prefill_many_query_blocks(oracle_lib, Tq):
+    """More query blocks than one shared-decode item holds (8), a ragged
+    last item, and contexts of 1 to 6 rounds: every row against the oracle."""
+    O = oracle_lib
+    lens = [Tq, Tq + 1, 600, 1500]
+    c, q = _prefill_case(O, lens, Tq, 8, 2, seed=41 + Tq)
+    _assert_close(_gpu_prefill(c, q).cpu().numpy(), _oracle_prefill(O, c, q), f"prefill Tq={Tq}")
+
+
 def test_prefill_one_query_equals_decode(oracle_lib):
     O = oracle_lib
     lens = [1, 100, 777]
