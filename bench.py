@@ -567,8 +567,8 @@ def main():
         group = Hq // Hkv
         # compressed bytes the kernel reads: each item of query blocks reads its
         # causal prefix once (8 blocks of 16 rows per item for containers of up
-        # to 43 bytes, one block otherwise)
-        tb = (16 // group) * (8 if max(ck.C, cv.C) <= 43 else 1)
+        # to 35 bytes, one block otherwise)
+        tb = (16 // group) * (8 if max(ck.C, cv.C) <= 35 else 1)
         lens_np = lens_p.cpu().numpy().astype(np.int64)
         read = 0
         for L in lens_np:

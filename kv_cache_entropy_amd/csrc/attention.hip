@@ -1230,7 +1230,8 @@ __global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk
 }
 
 // ---------------------------------------------------------------- prefill, shared decode
-// For containers of up to 47 bytes.  A block of kSbWaves waves takes an
+// For containers of up to 35 bytes (the LDS holds 8 staging slices of 64
+// containers beside the level tiles).  A block of kSbWaves waves takes an
 // item (sequence, kv head, kSbWaves consecutive query blocks of 16 rows,
 // context chunk).  The chunk goes by in rounds of kRoundTiles tiles: waves
 // 0..3 decode K of the round's tiles and waves 4..7 V, one container per
@@ -1245,21 +1246,16 @@ __global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk
 // per lane.
 constexpr int kSbWaves = 8;
 constexpr int kRoundTiles = 4;
-constexpr int kLvHalves = kTile * kD;  // one tile of K or V levels, fp16
-
-// K levels: [token][8-byte chunk c = dims 4 c .. 4 c + 3].  The chunk index
-// is swizzled so that the 16 tokens x 2 chunks a half-wave reads for an
-// MFMA operand, and the 32 tokens it writes at one chunk, all fall in
-// distinct banks.
-__device__ __forceinline__ int kl_off(int tok, int c) {
-  return tok * kD + ((c ^ ((tok & 15) << 1) ^ ((tok >> 4) & 3)) << 2);
-}
-// V levels: [dim][8-byte chunk of tokens 4 c .. 4 c + 3], swizzled likewise
-// for the operand reads (16 dims x 2 chunks) and the decode's writes (one
-// dim, 32 tokens).
-__device__ __forceinline__ int vl_off(int dim, int tok) {
-  return dim * kTile + ((((tok >> 2) ^ (((dim >> 1) & 7) << 1))) << 2) + (tok & 3);
-}
+// Level tiles, fp16, rows padded by one dword pair (K) or one dword (V) so
+// that the 16 rows x 2 chunks a half-wave reads for an MFMA operand spread
+// over the banks (at most two-way), with every address a per-lane base plus
+// an immediate:
+//   K: [token][dims], 132 halves a row (8-byte operand reads stay aligned)
+//   V: [dim][tokens],  66 halves a row (operands read as two dwords)
+constexpr int kKlRow = kD + 4, kVlRow = kTile + 2;
+constexpr int kLvHalves = kTile * kKlRow;  // = kD * kVlRow: one K or V level tile
+static_assert(kTile * kKlRow == kD * kVlRow, "K and V level tiles share a size");
+typedef _Float16 half4a __attribute__((ext_vector_type(4), aligned(4)));
 
 __host__ __device__ inline size_t prefill_shared_lds(int Ck, int Cv) {
   const int cmax = Ck > Cv ? Ck : Cv;
@@ -1284,12 +1280,12 @@ __device__ __forceinline__ void decode_levels(const DecTab t, const uint8_t *cb,
       x = rans_advance(x, e);
       renorm(x, p, bt);
       lv[j] = e.y;
-      if (V) dst[vl_off(4 * G + j, tok)] = (uint16_t)(e.y >> 16);
+      if (V) dst[(4 * G + j) * kVlRow + tok] = (uint16_t)(e.y >> 16);
     }
     if (!V) {
       const uint32_t b01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
       const uint32_t b23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
-      *reinterpret_cast<uint2 *>(dst + kl_off(tok, G)) = make_uint2(b01, b23);
+      *reinterpret_cast<uint2 *>(dst + tok * kKlRow + 4 * G) = make_uint2(b01, b23);
     }
   }
 }
@@ -1300,7 +1296,7 @@ __device__ __forceinline__ void decode_levels(const DecTab t, const uint8_t *cb,
 // lies before t1 and at or before the row's query position qpos.
 __device__ __forceinline__ void shared_tile(const uint16_t *kt, const uint16_t *vtl, const float *knl,
                                             const float *vnl, const half4 (&qh)[8], const half4 (&ql)[8],
-                                            int tpos0, int t1, int qpos, float qk_scale, float &m_run,
+                                            int tpos0, int t1, int qpos, float &m_run,
                                             float &l_run, floatx4 (&acc)[8], int lane) {
   const int m = lane & 15, kq = lane >> 4;
   floatx4 st[4];
@@ -1310,23 +1306,22 @@ __device__ __forceinline__ void shared_tile(const uint16_t *kt, const uint16_t *
   for (int kb = 0; kb < kD / 16; ++kb) {
     half4 A[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) A[tb] = *reinterpret_cast<const half4 *>(kt + kl_off(16 * tb + m, 4 * kb + kq));
+    for (int tb = 0; tb < 4; ++tb) A[tb] = *reinterpret_cast<const half4 *>(kt + (16 * tb + m) * kKlRow + 16 * kb + 4 * kq);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) st[tb] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[tb], qh[kb], st[tb], 0, 0, 0);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) st[tb] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[tb], ql[kb], st[tb], 0, 0, 0);
   }
+  // token 16 tb + 4 kq + i of the tile is visible when 16 tb + i <= lim
+  const int lim = min(t1 - 1, qpos) - tpos0 - 4 * kq;
   float mx = -__builtin_inff();
-  bool vis[4][4];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const float4 nk = *reinterpret_cast<const float4 *>(knl + 16 * tb + 4 * kq);
+    const float4 nk = *reinterpret_cast<const float4 *>(knl + 16 * tb + 4 * kq);  // n_k * scale
     const float nkv[4] = {nk.x, nk.y, nk.z, nk.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tp = tpos0 + 16 * tb + 4 * kq + i;
-      vis[tb][i] = tp < t1 && tp <= qpos;
-      st[tb][i] = vis[tb][i] ? st[tb][i] * nkv[i] * qk_scale : -__builtin_inff();
+      st[tb][i] = 16 * tb + i <= lim ? st[tb][i] * nkv[i] : -__builtin_inff();
       mx = fmaxf(mx, st[tb][i]);
     }
   }
@@ -1342,6 +1337,8 @@ __device__ __forceinline__ void shared_tile(const uint16_t *kt, const uint16_t *
       for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
     m_run = m_new;
   }
+  // a row with nothing visible yet keeps m = -inf; its scores are -inf too
+  const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     const float4 nv = *reinterpret_cast<const float4 *>(vnl + 16 * tb + 4 * kq);
@@ -1349,7 +1346,7 @@ __device__ __forceinline__ void shared_tile(const uint16_t *kt, const uint16_t *
     half4 ph, pl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = vis[tb][i] ? exp2f(st[tb][i] - m_run) : 0.0f;
+      const float p = exp2f(st[tb][i] - m_use);
       l_run += p;
       // P = p * n_v as an fp16 pair, as in decode attention
       const float pv = p * nvv[i];
@@ -1359,7 +1356,10 @@ __device__ __forceinline__ void shared_tile(const uint16_t *kt, const uint16_t *
     }
     half4 A[8];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) A[db] = *reinterpret_cast<const half4 *>(vtl + vl_off(16 * db + m, 16 * tb + 4 * kq));
+    for (int db = 0; db < 8; ++db) {
+      const half4a v = *reinterpret_cast<const half4a *>(vtl + (16 * db + m) * kVlRow + 16 * tb + 4 * kq);
+      A[db] = half4{v[0], v[1], v[2], v[3]};
+    }
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[db], ph, acc[db], 0, 0, 0);
 #pragma unroll
@@ -1453,7 +1453,7 @@ __global__ void __launch_bounds__(64 * kSbWaves) attn_prefill_shared_kernel(Attn
           vnl[dtile * kTile + tok] = nrm;
         } else {
           decode_levels<false>(dk, stg + off + tok * C, kl + dtile * kLvHalves, tok);
-          knl[dtile * kTile + tok] = nrm;
+          knl[dtile * kTile + tok] = nrm * a.qk_scale;
         }
       }
       __syncthreads();  // the round's level tiles and norms are complete
@@ -1462,7 +1462,7 @@ __global__ void __launch_bounds__(64 * kSbWaves) attn_prefill_shared_kernel(Attn
           const int tp0 = t0 + (r0 + tt) * kTile;
           if (r0 + tt >= ntiles || tp0 > pend) break;  // later tiles are masked for every row
           shared_tile(kl + tt * kLvHalves, vl + tt * kLvHalves, knl + tt * kTile, vnl + tt * kTile, qh, ql, tp0, t1,
-                      qpos, a.qk_scale, m_run, l_run, acc, lane);
+                      qpos, m_run, l_run, acc, lane);
         }
       }
       __syncthreads();  // every read of the round's tiles is done
@@ -1667,7 +1667,7 @@ int64_t choose_prefill_chunk(int64_t units, int64_t max_len, int cus) {
 }
 
 // Ck, Cv pick the kernel: the shared-decode one when its LDS fits (C up to
-// 43), the per-block one otherwise.
+// 35), the per-block one otherwise.
 int make_prefill_plan(int B, int Tq, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, PrefillPlan *pl) {
   const int cus = device_cus();
   if (cus <= 0) return DQ_ERR_HIP;
