@@ -892,9 +892,9 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
 constexpr int kRows = 16;
 // rotated queries, halves per (b, g, block) in either layout:
 //   per-block decode: [dim quad][lane][row group][hi4 lo4]
-//   shared decode:    [16-dim block][lane][hi4 lo4], lane 16 k + r holding
-//                     dims 4 k .. 4 k + 3 of the block for row r (the B
-//                     operand of a 16x16x16 MFMA)
+//   shared decode:    [32-dim block][lane][hi8 lo8], lane 16 j + r holding
+//                     dims 8 j .. 8 j + 7 of the block for row r (the B
+//                     operand of a 16x16x32 MFMA)
 constexpr int kQrotPrefill = 32 * 4 * 4 * 8;
 
 typedef float floatx4v __attribute__((ext_vector_type(4)));
@@ -916,11 +916,12 @@ __global__ void __launch_bounds__(64) rotate_qp_kernel(AttnArgs a, uint64_t ksee
   uint16_t *dst = a.qrot + (((int64_t)b * a.Hkv + g) * a.nqb + qb) * kQrotPrefill;
   const int d0 = lane, d1 = lane + 64;
   auto at = [&](int d) {
-    return SHARED ? (((d >> 4) * 64 + ((d & 15) >> 2) * 16 + r) * 8) + (d & 3)
+    return SHARED ? (((d >> 5) * 64 + ((d & 31) >> 3) * 16 + r) * 16) + (d & 7)
                   : ((((d >> 2) * 4 + i) * 4 + rg) * 8) + (d & 3);
   };
+  const int lo = SHARED ? 8 : 4;  // offset of the lo half
   if (tq >= a.Tq) {
-    dst[at(d0)] = 0; dst[at(d0) + 4] = 0; dst[at(d1)] = 0; dst[at(d1) + 4] = 0;
+    dst[at(d0)] = 0; dst[at(d0) + lo] = 0; dst[at(d1)] = 0; dst[at(d1) + lo] = 0;
     return;
   }
   const uint16_t *qp = a.q + (((int64_t)b * a.Tq + tq) * a.Hq + h) * kD;
@@ -943,9 +944,9 @@ __global__ void __launch_bounds__(64) rotate_qp_kernel(AttnArgs a, uint64_t ksee
   const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
   const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
   dst[at(d0)] = __builtin_bit_cast(uint16_t, h0);
-  dst[at(d0) + 4] = __builtin_bit_cast(uint16_t, l0);
+  dst[at(d0) + lo] = __builtin_bit_cast(uint16_t, l0);
   dst[at(d1)] = __builtin_bit_cast(uint16_t, h1);
-  dst[at(d1) + 4] = __builtin_bit_cast(uint16_t, l1);
+  dst[at(d1) + lo] = __builtin_bit_cast(uint16_t, l1);
 }
 
 __host__ __device__ inline WaveLayout prefill_layout(int Ck, int Cv) {
@@ -1256,6 +1257,8 @@ constexpr int kKlRow = kD + 4, kVlRow = kTile + 2;
 constexpr int kLvHalves = kTile * kKlRow;  // = kD * kVlRow: one K or V level tile
 static_assert(kTile * kKlRow == kD * kVlRow, "K and V level tiles share a size");
 typedef _Float16 half4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half8a __attribute__((ext_vector_type(8), aligned(8)));
 
 __host__ __device__ inline size_t prefill_shared_lds(int Ck, int Cv) {
   const int cmax = Ck > Cv ? Ck : Cv;
@@ -1291,26 +1294,30 @@ __device__ __forceinline__ void decode_levels(const DecTab t, const uint8_t *cb,
 }
 
 // One decoded tile against this wave's 16 rows: S^T, the online softmax of
-// each row (lane l: row l mod 16), and O^T += V^T P^T.  tpos0 is the
-// position of the tile's first token; a token is visible to a row when it
-// lies before t1 and at or before the row's query position qpos.
+// each row (lane l: row l mod 16), and O^T += V^T P^T, on 16x16x32 MFMAs.
+// A lane's 8-value k group is 8 consecutive dims for S^T; for O^T it is the
+// 4 tokens 4 (l / 16) + i of each of two 16-token blocks, the tokens the
+// lane holds scores for (the order inside a group is free, as long as both
+// operands use the same one).  tpos0 is the position of the tile's first
+// token; a token is visible to a row when it lies before t1 and at or
+// before the row's query position qpos.
 __device__ __forceinline__ void shared_tile(const uint16_t *kt, const uint16_t *vtl, const float *knl,
-                                            const float *vnl, const half4 (&qh)[8], const half4 (&ql)[8],
-                                            int tpos0, int t1, int qpos, float &m_run,
-                                            float &l_run, floatx4 (&acc)[8], int lane) {
+                                            const float *vnl, const half8 (&qh)[4], const half8 (&ql)[4],
+                                            int tpos0, int t1, int qpos, float &m_run, float &l_run,
+                                            floatx4 (&acc)[8], int lane) {
   const int m = lane & 15, kq = lane >> 4;
   floatx4 st[4];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) st[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < kD / 16; ++kb) {
-    half4 A[4];
+  for (int kb = 0; kb < kD / 32; ++kb) {
+    half8 A[4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) A[tb] = *reinterpret_cast<const half4 *>(kt + (16 * tb + m) * kKlRow + 16 * kb + 4 * kq);
+    for (int tb = 0; tb < 4; ++tb) A[tb] = *reinterpret_cast<const half8a *>(kt + (16 * tb + m) * kKlRow + 32 * kb + 8 * kq);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) st[tb] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[tb], qh[kb], st[tb], 0, 0, 0);
+    for (int tb = 0; tb < 4; ++tb) st[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[tb], qh[kb], st[tb], 0, 0, 0);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) st[tb] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[tb], ql[kb], st[tb], 0, 0, 0);
+    for (int tb = 0; tb < 4; ++tb) st[tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[tb], ql[kb], st[tb], 0, 0, 0);
   }
   // token 16 tb + 4 kq + i of the tile is visible when 16 tb + i <= lim
   const int lim = min(t1 - 1, qpos) - tpos0 - 4 * kq;
@@ -1340,30 +1347,36 @@ __device__ __forceinline__ void shared_tile(const uint16_t *kt, const uint16_t *
   // a row with nothing visible yet keeps m = -inf; its scores are -inf too
   const float m_use = m_run == -__builtin_inff() ? 0.0f : m_run;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const float4 nv = *reinterpret_cast<const float4 *>(vnl + 16 * tb + 4 * kq);
-    const float nvv[4] = {nv.x, nv.y, nv.z, nv.w};
-    half4 ph, pl;
+  for (int h = 0; h < 2; ++h) {
+    half8 ph, pl;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = exp2f(st[tb][i] - m_use);
-      l_run += p;
-      // P = p * n_v as an fp16 pair, as in decode attention
-      const float pv = p * nvv[i];
-      const _Float16 hi = (_Float16)pv;
-      ph[i] = hi;
-      pl[i] = (_Float16)(pv - (float)hi);
+    for (int u = 0; u < 2; ++u) {
+      const int tb = 2 * h + u;
+      const float4 nv = *reinterpret_cast<const float4 *>(vnl + 16 * tb + 4 * kq);
+      const float nvv[4] = {nv.x, nv.y, nv.z, nv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(st[tb][i] - m_use);
+        l_run += p;
+        // P = p * n_v as an fp16 pair, as in decode attention
+        const float pv = p * nvv[i];
+        const _Float16 hi = (_Float16)pv;
+        ph[4 * u + i] = hi;
+        pl[4 * u + i] = (_Float16)(pv - (float)hi);
+      }
     }
-    half4 A[8];
+    half8 A[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const half4a v = *reinterpret_cast<const half4a *>(vtl + (16 * db + m) * kVlRow + 16 * tb + 4 * kq);
-      A[db] = half4{v[0], v[1], v[2], v[3]};
+      const uint16_t *row = vtl + (16 * db + m) * kVlRow + 32 * h + 4 * kq;
+      const half4a v0 = *reinterpret_cast<const half4a *>(row);
+      const half4a v1 = *reinterpret_cast<const half4a *>(row + 16);
+      A[db] = half8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     }
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[db], ph, acc[db], 0, 0, 0);
+    for (int db = 0; db < 8; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[db], ph, acc[db], 0, 0, 0);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(A[db], pl, acc[db], 0, 0, 0);
+    for (int db = 0; db < 8; ++db) acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[db], pl, acc[db], 0, 0, 0);
   }
 }
 
@@ -1419,14 +1432,13 @@ __global__ void __launch_bounds__(64 * kSbWaves) attn_prefill_shared_kernel(Attn
     const int64_t sbase = plane0 + a.seq_start[b] + t0;  // pool index of token t0
     const int qpos = pos0 + m / a.group;                   // query position of this lane's row
 
-    half4 qh[8], ql[8];
+    half8 qh[4], ql[4];
     if (qvalid) {
       const uint4 *qg = reinterpret_cast<const uint4 *>(a.qrot + ((bg * a.nqb) + qb) * kQrotPrefill);
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const uint4 v = qg[kb * 64 + lane];
-        qh[kb] = __builtin_bit_cast(half4, make_uint2(v.x, v.y));
-        ql[kb] = __builtin_bit_cast(half4, make_uint2(v.z, v.w));
+      for (int kb = 0; kb < 4; ++kb) {
+        qh[kb] = __builtin_bit_cast(half8, qg[(kb * 64 + lane) * 2]);
+        ql[kb] = __builtin_bit_cast(half8, qg[(kb * 64 + lane) * 2 + 1]);
       }
     }
     float m_run = -__builtin_inff(), l_run = 0.0f;
