@@ -26,9 +26,14 @@ constexpr int kDecodeTableBytes = (int)kM + kSymTabBytes;
 
 __device__ __forceinline__ void build_tables(uint8_t *sym8, uint2 *symtab, const Tables &t, int tid,
                                              int nthreads) {
+  // the symbol of slot u is the number of k >= 1 with cum[k] <= u (cum
+  // rises strictly): a count over uniform indices, so each cum[k] is a
+  // scalar read.  A search with a per-lane index into the argument block
+  // would be a chain of dependent memory loads per slot, 12 us per launch.
   for (int u = tid; u < (int)kM; u += nthreads) {
-    int s = 0;
-    while (s + 1 < t.levels && (int)t.cum[s + 1] <= u) ++s;
+    uint32_t s = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxLevels; ++k) s += (k < t.levels && (int)t.cum[k] <= u) ? 1u : 0u;
     sym8[u] = (uint8_t)(8 * s);
   }
   if (tid < kMaxLevels)
