@@ -181,35 +181,48 @@ __device__ __forceinline__ void wave_encode_vector(const uint16_t *xp, int g, co
       }
       kA[e] = key;
     }
-    Mg[lane] = (uint8_t)mA[0];
-    Mg[lane + 64] = (uint8_t)mA[1];
-    Y[lane] = kA[0];
-    Y[lane + 64] = kA[1];
-    wave_sync_lds();
-    // four candidates per LDS read (a float4 of keys, a word of magnitudes),
-    // the tests combined without short-circuit branches
-    int rank[2] = {0, 0};
-    const float4 *Y4 = reinterpret_cast<const float4 *>(Y);
-    const uint32_t *M4 = reinterpret_cast<const uint32_t *>(Mg);
-#pragma unroll 4
-    for (int j4 = 0; j4 < kD / 4; ++j4) {
-      const float4 y4 = Y4[j4];
-      const uint32_t m4 = M4[j4];
-      const float yv[4] = {y4.x, y4.y, y4.z, y4.w};
+    // Ranks by a bitonic sort of the wave's 128 (key, index) pairs, position
+    // lane + 64 e holding element e of the lane.  The 64-bit key orders
+    // non-candidates last, then (magnitude order) m descending, then the
+    // drift-order key ascending as sortable bits (-0 folded into +0, so that
+    // keys equal as floats tie), then the index: distinct keys, so a
+    // candidate's place is the number of candidates before it.
+    uint64_t v[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = 4 * j4 + u;
-        const uint32_t mj = (m4 >> (8 * u)) & 0xFFu;
-        const float yj = yv[u];
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t kb = __float_as_uint(kA[e] + 0.0f);
+      const uint32_t lo = (kb & 0x80000000u) ? ~kb : (kb | 0x80000000u);
+      const uint32_t cls = mA[e] >= 1u ? (RD ? 0u : 15u - mA[e]) : 16u;
+      v[e] = ((uint64_t)cls << 40) | ((uint64_t)lo << 8) | (uint64_t)(lane + 64 * e);
+    }
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int i = lane + 64 * e;
-          const bool tie_first = (yj < kA[e]) | ((yj == kA[e]) & (j < i));
-          const bool before = (mj >= 1u) & (RD ? tie_first : ((mj > mA[e]) | ((mj == mA[e]) & tie_first)));
-          rank[e] += before ? 1 : 0;
+    for (int k = 2; k <= kD; k <<= 1) {
+#pragma unroll
+      for (int j = k >> 1; j >= 1; j >>= 1) {
+        if (j == 64) {  // partners in the same lane (k = 128: ascending)
+          const uint64_t a0 = v[0], a1 = v[1];
+          v[0] = a0 < a1 ? a0 : a1;
+          v[1] = a0 < a1 ? a1 : a0;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int p = lane + 64 * e;
+            const uint32_t whi = (uint32_t)__shfl_xor((int)(uint32_t)(v[e] >> 32), j);
+            const uint32_t wlo = (uint32_t)__shfl_xor((int)(uint32_t)v[e], j);
+            const uint64_t w = ((uint64_t)whi << 32) | wlo;
+            const bool take_min = ((p & k) == 0) == ((p & j) == 0);
+            const bool less = v[e] < w;
+            v[e] = take_min == less ? v[e] : w;
+          }
         }
       }
     }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) Mg[(int)(v[e] & 0x7Fu)] = (uint8_t)(lane + 64 * e);
+    wave_sync_lds();
+    int rank[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) rank[e] = Mg[lane + 64 * e];
     int total = 0;
 #pragma unroll
     for (int e = 0; e < 2; ++e) total += __popcll(__ballot(mA[e] >= 1u));
