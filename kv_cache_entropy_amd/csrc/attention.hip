@@ -788,8 +788,24 @@ __global__ void __launch_bounds__(64 * kAppendWaves) append_encode_kernel(AttnAr
 __device__ __forceinline__ float lse_merge(const float *src, int64_t stride, int n, const float *pe, float *red,
                                            float *wts) {
   const int d = threadIdx.x;
+  // Every load that does not wait on the maximum is issued first: this
+  // dim's values of the first kD partials, and the (m, l) of the partials
+  // this thread weighs in the first two rounds.  A merge of up to kD
+  // partials then costs one memory round trip instead of three.
+  const int cnt0 = min(n, kD);
+  float av[kD];
+#pragma unroll
+  for (int j = 0; j < kD; ++j) av[j] = j < cnt0 ? src[(int64_t)j * stride + d] : 0.0f;
+  float mr[2] = {-__builtin_inff(), -__builtin_inff()}, lr[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (d + r * kD < n) {
+      mr[r] = src[(int64_t)(d + r * kD) * stride + 128];
+      lr[r] = src[(int64_t)(d + r * kD) * stride + 129];
+    }
   float M = pe ? pe[128] : -__builtin_inff();
-  for (int c = d; c < n; c += kD) M = fmaxf(M, src[(int64_t)c * stride + 128]);
+  M = fmaxf(M, fmaxf(mr[0], mr[1]));
+  for (int c = d + 2 * kD; c < n; c += kD) M = fmaxf(M, src[(int64_t)c * stride + 128]);
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w));
   if ((d & 63) == 0) red[d >> 6] = M;
@@ -801,15 +817,22 @@ __device__ __forceinline__ float lse_merge(const float *src, int64_t stride, int
     float w = 0.0f;
     if (d < cnt) {
       const float *p = src + (int64_t)(c0 + d) * stride;
-      const float m = p[128];
+      const bool held = c0 < 2 * kD;
+      const float m = held ? (c0 == 0 ? mr[0] : mr[1]) : p[128];
       if (m != -__builtin_inff()) {
         w = exp2f(m - M);
-        Lp += w * p[129];
+        Lp += w * (held ? (c0 == 0 ? lr[0] : lr[1]) : p[129]);
       }
     }
     __syncthreads();  // the previous round's weights are read
     wts[d] = w;
     __syncthreads();
+    if (c0 == 0) {
+#pragma unroll
+      for (int j = 0; j < kD; ++j)
+        if (j < cnt && wts[j] != 0.0f) o += wts[j] * av[j];
+      continue;
+    }
     const float *p = src + (int64_t)c0 * stride + d;
     int j = 0;
     for (; j + 4 <= cnt; j += 4) {
