@@ -1260,14 +1260,14 @@ __global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk
 // context chunk).  The chunk goes by in rounds of kRoundTiles tiles: waves
 // 0..3 decode K of the round's tiles and waves 4..7 V, one container per
 // lane, into fp16 level tiles in LDS; then every wave runs its own 16 rows
-// over those tiles on 16x16x16 MFMAs.  A tile is decoded once for the
+// over those tiles on 16x16x32 MFMAs.  A tile is decoded once for the
 // item's 128 rows instead of once per 16.
 //
 // Scores are formed transposed, S^T = K q~^T (tokens x rows), so that each
 // lane ends with 4 tokens of one row (lane l: row l mod 16, tokens 4 (l / 16)
-// .. + 3 of each 16-token block).  After the softmax that is, as it stands,
-// the B operand of O^T = V^T P^T, and the running max and sum are one value
-// per lane.
+// .. + 3 of each 16-token block).  After the softmax those values, two
+// 16-token blocks at a time, are as they stand the B operand of
+// O^T = V^T P^T, and the running max and sum are one value per lane.
 constexpr int kSbWaves = 8;
 constexpr int kRoundTiles = 4;
 // Level tiles, fp16, rows padded by one dword pair (K) or one dword (V) so
