@@ -233,6 +233,17 @@ def test_attention_ragged_small(oracle_lib, Hq, hkv):
     _assert_close(_gpu_attn(c).cpu().numpy(), _oracle_attn(O, c), f"ragged Hq={Hq} hkv={hkv}")
 
 
+def test_attention_many_partials(oracle_lib, monkeypatch):
+    """A 17000-token sequence in 64-token chunks: 266 partials, so the merge
+    takes the two rounds whose (m, l) it holds in registers and a third it
+    reads back; a short sequence beside it.  Against the oracle."""
+    O = oracle_lib
+    monkeypatch.setenv("DQ_SPLIT_TOKENS", "64")
+    lens = [17000, 300]
+    c = _attn_case(O, 2, 8, 2, lens, seed=13)
+    _assert_close(_gpu_attn(c).cpu().numpy(), _oracle_attn(O, c), "266 partials")
+
+
 def test_attention_split_invariance_and_bf16(oracle_lib):
     O = oracle_lib
     lens = [2000, 777, 1500]
