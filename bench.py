@@ -68,6 +68,10 @@ def load_traffic(bytes_per_launch_alg):
 # root on the GPU machine, one after the other), then
 # `python bench.py --summarize-profiles gpurun_out/prof` on any host.
 PROF = "gpurun_out/prof"
+# instruction mix and pipe activity (8 SQ counters and one GRBM counter: one
+# rocprofv3 pass)
+SQ_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU",
+               "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
 PROFILE_CMDS = {
     "trace": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -k 10 900 "
               "rocprofv3 --kernel-trace --stats --output-format csv -d $R/" + PROF + "/trace -o run -- "
@@ -80,6 +84,10 @@ PROFILE_CMDS = {
               "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'attn_splitk|copyBuffer' --output-format csv "
               "-d $R/" + PROF + "/write -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline "
               "--no-compare --copy-calibration > $R/" + PROF + "/write_bench.json"),
+    "sq": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
+           "rocprofv3 --pmc " + " ".join(SQ_COUNTERS) + " --kernel-include-regex 'attn_splitk|::encode_kernel<' "
+           "--output-format csv -d $R/" + PROF + "/sq -o run -- python3 $R/bench.py --steps 3 --warmup 1 "
+           "--no-cpu-baseline --no-compare --no-rd --no-paged --no-prefill > $R/" + PROF + "/sq_bench.json"),
 }
 
 
@@ -212,6 +220,80 @@ def summarize_profiles(d):
     with open(os.path.join(out_dir, f"attn_splitk_{wl}_counters.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     print(f"wrote profiles for source {src}: traffic {(fetch_b + write_b) / 1e6:.1f} MB per launch")
+    if os.path.isdir(os.path.join(d, "sq")):
+        summarize_sq(d, kname, wl, src)
+
+
+def summarize_sq(d, kname, wl, src):
+    """Pipe activity of the split-K kernel and the prompt encode from the SQ
+    counter pass.  Normalisation: 256 CUs, 1024 SIMDs; GRBM_GUI_ACTIVE sums
+    the 8 XCDs' busy cycles, so GRBM_GUI_ACTIVE / 8 is the dispatch's length
+    in cycles; a wave64 VALU instruction occupies its 16-lane SIMD 4 cycles."""
+    rows = _csv(_find(os.path.join(d, "sq"), "counter_collection.csv"))
+    bl = _bench_line(os.path.join(d, "sq_bench.json"))
+    if bl.get("attn_source_sha256_16") != src:
+        raise SystemExit("sq run was made on a different attention source")
+    disp = {}
+    for r in rows:
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]))
+        disp.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+
+    def table(sel):
+        n = len(sel)
+        avg = {c: sum(v[c] for v in sel) / n for c in SQ_COUNTERS}
+        cyc = avg["GRBM_GUI_ACTIVE"] / 8
+        return avg, {"dispatches": n, "cycles": cyc,
+                     "valu_busy": avg["SQ_ACTIVE_INST_VALU"] * 4 / 1024 / cyc,
+                     "lds_active": avg["SQ_LDS_IDX_ACTIVE"] / 256 / cyc,
+                     "bank_conflict_share": avg["SQ_LDS_BANK_CONFLICT"] / max(avg["SQ_LDS_IDX_ACTIVE"], 1.0)}
+
+    cmd = PROFILE_CMDS["sq"]
+    # split-K at the bench's grid
+    att = [(k, v) for k, v in disp.items() if kname in k[1]]
+    grid = max(k[2] for k, _ in att)
+    avg, der = table([v for k, v in att if k[2] == grid])
+    syms = bl["roofline"]["alg_bytes_per_launch"] / (bl["config"]["container_bytes"][0] + 2 +
+                                                     bl["config"]["container_bytes"][1] + 2) * 256
+    md = [f"# Pipe activity: {kname}, {wl}", "", "Command (from the repository root):", "", "```", cmd, "```", "",
+          f"Dispatches of `{kname}` at the bench's grid ({grid // 768} blocks): {der['dispatches']}, averaged.", "",
+          "| counter | per dispatch |", "|---|---:|"]
+    md += [f"| {c} | {avg[c]:.4g} |" for c in SQ_COUNTERS]
+    md += ["", f"Decoded symbols per dispatch (K and V, 128 per container): {syms:.4g}.", "",
+           "| derived | value |", "|---|---:|",
+           f"| dispatch length, cycles (GRBM_GUI_ACTIVE / 8 XCDs) | {der['cycles']:.4g} |",
+           f"| VALU busy (SQ_ACTIVE_INST_VALU x 4 / 1024 SIMDs / cycles) | {der['valu_busy']:.1%} |",
+           f"| LDS pipe active (SQ_LDS_IDX_ACTIVE / 256 CUs / cycles) | {der['lds_active']:.1%} |",
+           f"| bank-conflict cycles, share of LDS active | {der['bank_conflict_share']:.1%} |",
+           f"| VALU lane-ops per decoded symbol (SQ_INSTS_VALU x 64 / symbols) | "
+           f"{avg['SQ_INSTS_VALU'] * 64 / syms:.2f} |",
+           f"| LDS instructions per symbol step (SQ_INSTS_LDS x 64 / symbols) | "
+           f"{avg['SQ_INSTS_LDS'] * 64 / syms:.2f} |", ""]
+    with open(os.path.join(ROOT, "profiles", f"attn_splitk_{wl}_sq_counters.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    # prompt encode: the first two dispatches are K then V of the whole prompt
+    enc = sorted((k, v) for k, v in disp.items() if "::encode_kernel<" in k[1])
+    big = [(k, v) for k, v in enc if k[2] == max(kk[2] for kk, _ in enc)][:2]
+    md = [f"# Pipe activity: encode_kernel (prompt encode), {wl}", "", "Command (from the repository root):", "",
+          "```", cmd, "```", "",
+          "The prompt's K then V (one dispatch each, 8 kv heads x 1,048,576 tokens, one vector per lane).", "",
+          "| counter | K | V |", "|---|---:|---:|"]
+    tk, tv = table([big[0][1]]), table([big[1][1]])
+    md += [f"| {c} | {big[0][1][c]:.4g} | {big[1][1][c]:.4g} |" for c in SQ_COUNTERS]
+    nvec = bl["config"]["batch"] * bl["config"]["context"][1] * bl["config"]["kv_heads"]
+    md += ["", "| derived | K | V |", "|---|---:|---:|",
+           f"| dispatch length, cycles | {tk[1]['cycles']:.4g} | {tv[1]['cycles']:.4g} |",
+           f"| VALU busy | {tk[1]['valu_busy']:.1%} | {tv[1]['valu_busy']:.1%} |",
+           f"| VALU lane-ops per vector | {big[0][1]['SQ_INSTS_VALU'] * 64 / nvec:.0f} | "
+           f"{big[1][1]['SQ_INSTS_VALU'] * 64 / nvec:.0f} |", ""]
+    with open(os.path.join(ROOT, "profiles", f"encode_{wl}_sq_counters.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(f"wrote SQ counter summaries: split-K VALU {der['valu_busy']:.1%}, LDS {der['lds_active']:.1%}")
+
+
+def pct(xs):
+    """10th, 50th and 90th percentile of a list of times (nearest rank)."""
+    v = sorted(xs)
+    return [round(v[min(len(v) - 1, int(q * len(v)))], 4) for q in (0.1, 0.5, 0.9)]
 
 
 def cpu_baseline(w, ck, cv, kc, kn, vc, vn, q, starts, ctx, seconds):
@@ -321,8 +403,12 @@ def main():
     sk, sv = dq.stats_dict(stk), dq.stats_dict(stv)
     drift_k = sk["drifted_symbols"] / (128.0 * sk["vectors"])
     drift_v = sv["drifted_symbols"] / (128.0 * sv["vectors"])
+    # algorithmic bytes of the encode: the bf16 vector in, its container and
+    # fp16 norm out
+    enc_gbps = T_pre * Hkv * (2 * 256 + ck.C + 2 + cv.C + 2) / (prefill_ms / 1e3) / 1e9
     log(f"[bench] prefill encode {2 * T_pre * Hkv} vectors in {prefill_ms:.2f} ms "
-        f"({prefill_vps / 1e9:.2f} G vectors/s); drift K {drift_k:.3%} V {drift_v:.3%}")
+        f"({prefill_vps / 1e9:.2f} G vectors/s, {enc_gbps:.0f} GB/s = {enc_gbps / HBM_PEAK_GBPS:.1%} of HBM); "
+        f"drift K {drift_k:.3%} V {drift_v:.3%}")
 
     # the same prompt with the rate-distortion drift order (separate pools)
     rd = None
@@ -406,9 +492,23 @@ def main():
     alg_bytes = timed_bytes / args.steps
     achieved = alg_bytes / (split_avg_ms / 1e3) / 1e9
     ctx_tokens = sum(int((ctx + args.warmup + k + 1).sum()) for k in range(args.steps))
+    # a plain device copy on this GPU: what HBM sustains for a read + write
+    # stream, for the kernel's fraction of it
+    cpy_a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cpy_b = torch.empty_like(cpy_a)
+    cpy_b.copy_(cpy_a)
+    torch.cuda.synchronize()
+    e_a.record()
+    for _ in range(5):
+        cpy_b.copy_(cpy_a)
+    e_b.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * (1 << 30) / (e_a.elapsed_time(e_b) / 1e3) / 1e9
+    del cpy_a, cpy_b
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (one dq_attn_decode_append call; split-K "
         f"kernel {split_avg_ms:.3f} ms), {value:.1f} GB/s step, split-K kernel "
-        f"{achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of HBM peak")
+        f"{achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.1%} of HBM peak, {achieved / copy_gbps:.1%} of a "
+        f"device copy's {copy_gbps:.0f} GB/s")
 
     # the same steps as two launches (dq_encode_kv, then dq_attn_decode);
     # re-encoding the same tokens into the same slots writes the same bytes.
@@ -606,7 +706,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": load_traffic(alg_bytes), "kernel": "attn_splitk_kernel",
-                     "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(split_avg_ms, 4)},
+                     "alg_bytes_per_launch": alg_bytes, "avg_launch_ms": round(split_avg_ms, 4),
+                     "launch_ms_p10_p50_p90": pct(split_ms), "copy_gbps": round(copy_gbps, 1),
+                     "frac_of_copy": round(achieved / copy_gbps, 4)},
+        "step_ms_p10_p50_p90": pct(att_ms),
         "attn_source_sha256_16": attn_source_hash(),
         "step_call": "dq_attn_decode_append",
         "step_call_ms": round(att_avg_ms, 4),
@@ -618,6 +721,9 @@ def main():
         "cpu_baseline": cpu,
         "attn_context_tokens_per_s": round(ctx_tokens / (sum(att_ms) / 1e3), 1),
         "prefill_encode_vectors_per_s": round(prefill_vps, 1),
+        "prefill_encode_roofline": {"bound": "valu", "alg_gbps": round(enc_gbps, 1),
+                                    "hbm_frac": round(enc_gbps / HBM_PEAK_GBPS, 4),
+                                    "alg_bytes_per_vector": [256 + ck.C + 2, 256 + cv.C + 2]},
         "drift_rate": {"k": round(drift_k, 5), "v": round(drift_v, 5)},
     }
     print(json.dumps(rec), flush=True)
