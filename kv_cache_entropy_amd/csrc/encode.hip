@@ -41,6 +41,13 @@ namespace {
 
 constexpr int kThreads = 128;
 constexpr int kScr = 128;  // renorm bytes per lane and buffer: at most one per symbol
+// In-group selection keys: the offset of |y| bits above the group threshold
+// is clamped to a span (at most kKeySpan, so keys fit 32 bits); a clamped
+// key is (span + 1) * 128 + index, above every unclamped one.  Inner groups
+// never clamp at the full span: their |y| spans at most a factor 2, 2^23
+// bits of offset.  The outermost group's could reach 16 times its
+// threshold only for a norm rounded far down in fp16's subnormal range.
+constexpr uint32_t kKeySpan = (1u << 25) - 2u;
 
 struct EncodeArgs {
   const uint16_t *x;
@@ -50,6 +57,7 @@ struct EncodeArgs {
   uint8_t *cont;
   uint16_t *norm;
   dq_stats *stats;
+  uint32_t key_span;  // in-group key span; smaller values only to test the float-scan fallback
 };
 
 __device__ __forceinline__ uint32_t nib(const uint32_t (&w)[16], int i) {
@@ -312,16 +320,67 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
         }
         int nxt = -1;
         const bool want_next = undecided && sure;
-        if ((!full && rest > 0) || want_next) {
-          // the order inside a group needs |y|: rotate again rather than
-          // keep 128 values alive since quantisation
+        // The order inside a group needs |y|: the rotation runs again rather
+        // than keep 128 values alive since quantisation.  The boundary
+        // group's members first become integer keys, (|y| bits above the
+        // bits of the group's threshold) * 128 + 128 + index, 0 for the
+        // other coordinates.  Keys order as (|y|, index) do, so an
+        // extraction is one subtract and a minimum per coordinate.  The
+        // float scans remain for what the keys cannot rank: a next candidate
+        // from a lower group, and |y| far enough above the threshold that
+        // its key saturates (possible only in the outermost group).
+        bool scan = want_next && (full || rest == cnt[gb]);
+        const int want = full ? 0 : rest + (want_next && !scan ? 1 : 0);
+        int got = 0;
+        if (want > 0) {
           opaque(sym0);
+          float ay[kD];
+          rotate(src, s0, s1, ay, nullptr);
+          // the threshold of the members' magnitude before the rounds that
+          // moved every candidate, computed as quantisation did
+          const float nf = half_to_float(nh);
+          const uint32_t blo = __float_as_uint((float)((gb + passes) * t.step64) * nf * 0.015625f);
+          const uint32_t span = a.key_span, sat = (span << 7) + 128u;  // keys >= sat are clamped
+          uint32_t key[kD];
+#pragma unroll
+          for (int i = 0; i < kD; ++i) {
+            const uint32_t d = (__float_as_uint(ay[i]) & 0x7FFFFFFFu) - blo;  // members: |y| >= threshold
+            const uint32_t kv = (min(d, span) << 7) + (128u + (uint32_t)i);
+            const uint32_t mask = (uint32_t)__builtin_amdgcn_sbfe((int)gm[i >> 5], i & 31, 1);
+            key[i] = kv & mask;
+          }
+          uint32_t p1 = 1u;  // every key taken so far is below p1
+          for (int j = 0; j < want; ++j) {
+            // min over (key - p1) mod 2^32: a member not yet taken gives key
+            // - p1 < 2^32 - p1, the others give at least 2^32 - p1
+            uint32_t best = ~0u;
+#pragma unroll
+            for (int i = 0; i < kD; i += 2) best = min(best, min(key[i] - p1, key[i + 1] - p1));
+            const uint32_t kw = best + p1;
+            if (kw == 0u || kw >= sat) {
+              scan = true;
+              break;
+            }
+            p1 = kw + 1u;
+            const int i = (int)(kw & 127u);
+            if (j < rest) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) fl[q] |= ((i >> 5) == q) ? (1u << (i & 31)) : 0u;
+              ++got;
+            } else {
+              nxt = i;
+            }
+          }
+        }
+        if (scan) {
+          opaque(sym0);
+          opaque(fl);
           float ay[kD];
           rotate(src, s0, s1, ay, nullptr);
 #pragma unroll
           for (int i = 0; i < kD; ++i) ay[i] = __builtin_fabsf(ay[i]);
           if (!full)
-            for (int j = 0; j < rest; ++j) {
+            for (int j = got; j < rest; ++j) {
               const int i = next_in_group(ay, gm, fl);
 #pragma unroll
               for (int q = 0; q < 4; ++q) fl[q] |= ((i >> 5) == q) ? (1u << (i & 31)) : 0u;
@@ -526,7 +585,15 @@ static int encode_args(dq_codec_t codec, const void *x, int64_t T, int64_t strid
   // large-batch kernel's drift plan assumes it does not: it always takes
   // the wave-per-vector kernel, whose grid bounds the batch
   if (t.order == 1 && T * (int64_t)t.hkv > ((int64_t)1 << 30)) return DQ_ERR_UNSUPPORTED;
-  *a = dq::EncodeArgs{static_cast<const uint16_t *>(x), T, stride_t, stride_h, slots, num_slots, cont, norm, stats};
+  // DQ_ENCODE_KEY_SPAN narrows the in-group keys' span so that the float
+  // scans they fall back to run more often (same bytes either way)
+  uint32_t span = dq::kKeySpan;
+  if (const char *ev = getenv("DQ_ENCODE_KEY_SPAN")) {
+    const long long v = atoll(ev);
+    span = v < 0 ? 0u : (v < (long long)dq::kKeySpan ? (uint32_t)v : dq::kKeySpan);
+  }
+  *a = dq::EncodeArgs{static_cast<const uint16_t *>(x), T, stride_t, stride_h, slots, num_slots, cont, norm, stats,
+                      span};
   return DQ_OK;
 }
 

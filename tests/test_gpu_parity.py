@@ -120,6 +120,30 @@ def test_encode_adversarial(oracle_lib, encode_path, levels, C, step64):
     _assert_encode_equal(*_encode_both(O, gc, oc, x, slots, x.shape[0]), "adversarial")
 
 
+@pytest.mark.parametrize("span", [0, 1 << 21])
+@pytest.mark.parametrize("levels,C,step64", [(8, 34, 0), (6, 34, 0), (6, 29, 0), (16, 60, 25), (4, 30, 64)])
+def test_encode_in_group_scan_fallback(oracle_lib, monkeypatch, span, levels, C, step64):
+    """The lane encoder ranks a drift group's members by integer keys and
+    falls back to float scans for members past the keys' span.  Narrowed
+    spans force the fallback (span 0: from the first member on; 2^21: for
+    |y| above 2^(1/4) times the group's threshold, so it also starts
+    mid-way); the bytes must stay the oracle's."""
+    monkeypatch.setenv("DQ_ENCODE_WAVE_MAX", "0")
+    monkeypatch.setenv("DQ_ENCODE_KEY_SPAN", str(span))
+    O = oracle_lib
+    _say(f"in-group fallback span {span} {levels}/{C}/{step64}")
+    gc, oc = _codecs(O, levels, C, seed=41 + levels, hkv=2, step64=step64)
+    for kind in ("outlier", "student_t5"):
+        x = synth.kv_tensor(kind, 600, 2, seed=43, device=DEV)
+        slots = torch.arange(600, dtype=torch.int64, device=DEV)
+        _assert_encode_equal(*_encode_both(O, gc, oc, x, slots, 600), f"span {span} {levels}/{C}/{kind}")
+    rows = _adversarial_batch()
+    x = torch.from_numpy(rows).to(torch.bfloat16).reshape(-1, 1, 128).to(DEV)
+    ga, oa = _codecs(O, levels, C, seed=5, hkv=1, step64=step64)
+    slots = torch.arange(x.shape[0], dtype=torch.int64, device=DEV)
+    _assert_encode_equal(*_encode_both(O, ga, oa, x, slots, x.shape[0]), f"span {span} adversarial")
+
+
 @pytest.mark.parametrize("levels,C,step64", [(8, 34, 0), (6, 34, 0), (8, 29, 0), (6, 29, 0),
                                              (4, 30, 64), (10, 40, 34)])
 def test_encode_rate_distortion_order(oracle_lib, levels, C, step64):
