@@ -12,14 +12,13 @@
 // Two kernels write the same bytes:
 //  - encode_kernel (large batches, e.g. a prompt): one lane owns one vector
 //    end to end.  The rotation runs on the 128 coordinates in VGPRs (fully
-//    unrolled butterflies); the current symbols live in the lane's column of
-//    an LDS array, so a rANS pass is a straight chain of LDS byte reads and
-//    coder-constant lookups.  Renorm bytes go to a double-buffered LDS
-//    scratch, lane-minor, so the last fitting stream survives a later trial
-//    pass.  The drift search moves one candidate at a time around an
-//    estimate of the number of moves, so a drifted vector usually costs
-//    three passes.  Lanes of a wave take consecutive tokens of one kv head,
-//    so their containers are adjacent in the pool.
+//    unrolled butterflies); the symbols are packed 4 bits each in
+//    registers.  The drift is planned before any pass from the ideal code
+//    length, which decides whether a prefix of moves fits except inside a
+//    band narrower than one move's saving; then one rANS pass runs, or two
+//    when the undecided prefix is tried first.  Renorm bytes go to the
+//    lane's column of an LDS scratch.  Lanes of a wave take consecutive
+//    tokens of one kv head, so their containers are adjacent in the pool.
 //  - encode_wave_kernel (small batches, e.g. one appended token per
 //    sequence): one wave owns one vector, so the batch fills the chip with
 //    waves instead of lanes and the serial search becomes one parallel
@@ -487,7 +486,8 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
 //    the two values in a lane (the same fp32 operations in the same order as
 //    the per-lane path); the sum of squares follows the same halving tree;
 //  - every drift candidate gets its rank in the drift order (magnitude
-//    descending, |y| ascending, index ascending) by a broadcast scan;
+//    descending, |y| ascending, index ascending) from a bitonic sort of the
+//    wave's 128 (key, index) pairs;
 //  - lane l runs the rANS pass with the first k0 + l candidates moved one
 //    level inward; the lowest lane whose stream fits is the answer (the
 //    length never increases along the order, so every lower lane failed).
