@@ -66,8 +66,8 @@ def load_traffic(bytes_per_launch_alg):
 
 # The profiles under profiles/ come from these commands (run from the repo
 # root on the GPU machine, one after the other), then
-# `python bench.py --summarize-profiles gpurun_out/prof` on any host.
-PROF = "gpurun_out/prof"
+# `python bench.py --summarize-profiles prof_out` on any host.
+PROF = "prof_out"
 # instruction mix and pipe activity (8 SQ counters and one GRBM counter: one
 # rocprofv3 pass)
 SQ_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU",
@@ -359,7 +359,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 

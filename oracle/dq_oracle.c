@@ -345,8 +345,8 @@ typedef struct {
  * first k candidates one level inward fits.  If even all of them do not fit,
  * all are moved and the search repeats on the new symbols (a multilevel
  * event; the codec check guarantees the all-innermost vector fits). */
-/* Rate-distortion drift order (the pages point to the
- * rate-distortion toolbox of video coding [P1, So What]).  Moving |y| = a
+/* Rate-distortion drift order (an option beside the pages' order; the pages
+ * point to the rate-distortion toolbox of video coding [P1, So What]).  Moving |y| = a
  * from magnitude m to m - 1 adds n (l_m - l_{m-1}) (2a - n (l_m + l_{m-1}))
  * to the squared error (l = fp16 levels, n = stored norm); dropping the
  * common factor n and dividing by the bits saved gives the key
@@ -687,8 +687,8 @@ int dqo_attention(dqo_codec_args ka, dqo_codec_args va, int hkv,
                         seq_len, sm_scale, out, nthreads);
 }
 
-/* Chunked-prefill attention over the compressed cache (the
- * pages' serving figures include an 8K prompt [P1, The Numbers]).
+/* Chunked-prefill attention over the compressed cache (the pages' serving
+ * figures include an 8K prompt [P1, The Numbers]).
  * Reading: a chunk of Tq new tokens has already been encoded at the end of
  * each sequence, so the sequence holds seq_len[b] tokens of which the last
  * Tq are the chunk; query j of sequence b sits at position
