@@ -429,7 +429,7 @@ def main():
         rd = {"encode_vectors_per_s": round(2 * T_pre * Hkv / (rd_ms / 1e3), 1),
               "drift_rate": {"k": round(a_k["drifted_symbols"] / (128.0 * a_k["vectors"]), 5),
                              "v": round(a_v["drifted_symbols"] / (128.0 * a_v["vectors"]), 5)},
-              "kernel": "encode_wave_kernel"}
+              "kernel": "encode_kernel"}
         log(f"[bench] rate-distortion drift order: prefill encode {rd_ms:.1f} ms "
             f"({rd['encode_vectors_per_s'] / 1e9:.3f} G vectors/s); drift K {rd['drift_rate']['k']:.3%} "
             f"V {rd['drift_rate']['v']:.3%}")

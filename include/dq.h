@@ -91,7 +91,7 @@ typedef struct {
  *      once to fp32); the key is the added squared error per bit saved up to
  *      the vector's common factor n, evaluated in fp32 with one rounding for
  *      the difference and one for the product.  Lower distortion at the same
- *      budget; every batch size runs the small-batch encode kernel. */
+ *      budget, more moves. */
 
 /* Validates `desc`, builds the tables (host memory only) and returns a new
  * codec in *out.  DQ_ERR_BUDGET when a frequency would fall below 16, when
@@ -136,7 +136,7 @@ typedef struct {
  *   stats     device dq_stats, may be NULL
  * Vectors with a zero, inf or NaN norm are coded as all innermost-positive
  * symbols (norm stored as 0, inf or 0x7E00).  Duplicate slots race.
- * T = 0 is a no-op. */
+ * T = 0 is a no-op; T * Hkv above 2^38 gives DQ_ERR_UNSUPPORTED. */
 int dq_encode(dq_codec_t codec, const void *x, int64_t T, int64_t stride_t,
               int64_t stride_h, const int64_t *slots, int64_t num_slots,
               uint8_t *cont, uint16_t *norm, dq_stats *stats,

@@ -97,6 +97,30 @@ __device__ __forceinline__ int next_in_group(const float (&ay)[kD], const uint32
   return best[1] < best[0] ? 64 + bi[1] : bi[0];
 }
 
+// The candidate not yet in fl with the smallest (key, index), for the
+// rate-distortion order: rk holds each candidate's key as sortable bits
+// (below 2^32 - 1) and ~0 for the other coordinates; a taken candidate's
+// key is masked to ~0.  Halves as in next_in_group, so indices are inline
+// constants and a tie goes to the lower index.
+__device__ __forceinline__ int next_by_key(const uint32_t (&rk)[kD], const uint32_t (&fl)[4]) {
+  uint32_t best[2];
+  int bi[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    best[half] = ~0u;
+    bi[half] = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const int i = 64 * half + j;
+      const uint32_t v = rk[i] | (uint32_t)__builtin_amdgcn_sbfe((int)fl[i >> 5], i & 31, 1);
+      const bool take = v < best[half];
+      best[half] = take ? v : best[half];
+      bi[half] = take ? j : bi[half];
+    }
+  }
+  return best[1] < best[0] ? 64 + bi[1] : bi[0];
+}
+
 // One rANS pass over the packed symbols (pushed 127 -> 0).  Renorm bytes go
 // to the lane's scratch column from the end backwards (rows kScr - B ..
 // kScr - 1 are then in the decoder's reading order); the byte store is
@@ -183,9 +207,10 @@ __device__ __forceinline__ void rotate(const uint4 *src, uint64_t s0, uint64_t s
 
 __device__ __forceinline__ uint32_t inward(uint32_t s, int h) { return s >= (uint32_t)h ? s - 1u : s + 1u; }
 
-template <int MAXH>
+template <int MAXH, bool RD>  // RD: rate-distortion drift order
 __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Tables t) {
   __shared__ uint4 etab[kMaxLevels];
+  __shared__ float2 rdtab[kMaxLevels / 2];  // {l_m + l_{m-1}, w_m}; entry 0 unused
   __shared__ uint8_t scr[kScr * kThreads];  // renorm bytes, lane-minor
   __shared__ uint32_t bstat[6 + kMaxC + 1];
 
@@ -194,6 +219,11 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
     const uint32_t f = t.freq[lane];
     etab[lane] = make_uint4(f << 19, t.magic[lane], t.cum[lane], (kM - f) | ((uint32_t)t.shift[lane] << 16));
   }
+  if (RD && lane < kMaxLevels / 2)
+    rdtab[lane] = (lane >= 1 && lane < t.half)
+                      ? make_float2(half_to_float(t.recon[t.half + lane]) + half_to_float(t.recon[t.half + lane - 1]),
+                                    t.rd_w[lane])
+                      : make_float2(0.0f, 0.0f);
   for (int k = lane; k < 6 + kMaxC + 1; k += kThreads) bstat[k] = 0u;
   __syncthreads();
 
@@ -273,10 +303,11 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
       }
 
       opaque(sym0);
-      // plan: the smallest k with I(k) < sure_lo takes whole magnitude
-      // groups, outermost first, each move saving saving_fx[m]
       int ks = 0, total = 0;
       uint32_t Ik = I, Iprev = 0xFFFFFFFFu;  // I(ks), I(ks - 1)
+      if constexpr (!RD) {
+      // plan: the smallest k with I(k) < sure_lo takes whole magnitude
+      // groups, outermost first, each move saving saving_fx[m]
 #pragma unroll
       for (int m = MAXH - 1; m >= 1; --m) {
         if (m < h) {
@@ -429,6 +460,106 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
           nxt = -1;
         }
       }
+      } else {
+        // Rate-distortion order: candidates (m >= 1) ascending in the key
+        // (2|y| - n (l_m + l_{m-1})) * w_m, then in index, so the groups
+        // interleave.  I(every move) decides first whether any prefix can
+        // fit; otherwise candidates are taken in key order, each saving
+        // saving_fx[m], until I(k) < sure_lo.
+        uint32_t Iall = I;
+#pragma unroll
+        for (int m = 1; m < MAXH; ++m)
+          if (m < h) {
+            total += cnt[m];
+            Iall -= (uint32_t)cnt[m] * t.saving_fx[m];
+          }
+        uint32_t fl[4] = {0u, 0u, 0u, 0u};
+        int k = 0, nxt = -1;
+        bool go = true;
+        if (I < sure_lo) {
+          // fits as it is
+        } else if (Iall >= sure_hi) {
+          go = false;  // not even every move fits
+          Ik = Iall;
+        } else if (Iall >= sure_lo) {
+          // only the prefix of every move can fit
+          k = total;
+          Ik = Iall;
+#pragma unroll
+          for (int i = 0; i < kD; ++i) fl[i >> 5] |= (magnitude(nib(sym0, i), h) >= 1u ? 1u : 0u) << (i & 31);
+        } else {
+          opaque(sym0);
+          float ay[kD];
+          rotate(src, s0, s1, ay, nullptr);
+          const float nf = half_to_float(nh);
+          uint32_t rk[kD];
+#pragma unroll
+          for (int i = 0; i < kD; ++i) {
+            const uint32_t mg = magnitude(nib(sym0, i), h);
+            const float2 rr = rdtab[mg];
+            const float tt = nf * rr.x;  // exact: 11 x 12 significant bits
+            const float key = (2.0f * __builtin_fabsf(ay[i]) - tt) * rr.y;
+            const uint32_t kb = __float_as_uint(key + 0.0f);  // -0 -> +0
+            const uint32_t lo = (kb & 0x80000000u) ? ~kb : (kb | 0x80000000u);
+            rk[i] = mg >= 1u ? lo : ~0u;
+          }
+          int last = 0;
+          do {  // ends by the last candidate: I(every move) < sure_lo
+            const int c = next_by_key(rk, fl);
+            // c's magnitude: its packed word by selects (c varies by lane)
+            uint32_t w = sym0[0];
+#pragma unroll
+            for (int j = 1; j < 16; ++j) w = (c >> 3) == j ? sym0[j] : w;
+            const uint32_t mc = magnitude((w >> (4 * (c & 7))) & 15u, h);
+            uint32_t sv = 0u;
+#pragma unroll
+            for (int m = 1; m < MAXH; ++m) sv = mc == (uint32_t)m ? t.saving_fx[m] : sv;
+            Iprev = Ik;
+            Ik -= sv;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) fl[q] |= ((c >> 5) == q) ? (1u << (c & 31)) : 0u;
+            ++k;
+            last = c;
+          } while (Ik >= sure_lo);
+          if (Iprev < sure_hi) {
+            // prefix k - 1 may fit too: it is tried first
+#pragma unroll
+            for (int q = 0; q < 4; ++q) fl[q] &= ((last >> 5) == q) ? ~(1u << (last & 31)) : ~0u;
+            nxt = last;
+            --k;
+          }
+        }
+        if (go) {
+          opaque(sym0);
+          opaque(fl);
+          uint32_t sym[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sym[j] = 0u;
+#pragma unroll
+          for (int i = 0; i < kD; ++i) {
+            const uint32_t s = nib(sym0, i);
+            sym[i >> 3] |= (bit(fl, i) ? inward(s, h) : s) << (4 * (i & 7));
+          }
+          for (int attempt = 0; attempt < 2; ++attempt) {
+            uint32_t xf;
+            const int B = rans_pass(sym, etab, scr, lane, &xf);
+            if (4 + B <= C) {
+              okB = B;
+              okx = xf;
+              moves += k + attempt;
+              break;
+            }
+            if (nxt < 0) break;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int sh = 4 * (nxt & 7);
+              const uint32_t s = (sym[j] >> sh) & 15u;
+              sym[j] = ((nxt >> 3) == j) ? ((sym[j] & ~(15u << sh)) | (inward(s, h) << sh)) : sym[j];
+            }
+            nxt = -1;
+          }
+        }
+      }
       if (okB < 0) {
         // every candidate of the round moves one level inward; the plan is
         // made again on the new symbols (the all-innermost vector fits)
@@ -561,7 +692,8 @@ template <int MAXH>
 hipError_t launch(const EncodeArgs &a, const Tables &t, hipStream_t s) {
   const int64_t nvec = a.T * (int64_t)t.hkv;
   const unsigned blocks = (unsigned)((nvec + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(encode_kernel<MAXH>, dim3(blocks), dim3(kThreads), 0, s, a, t);
+  if (t.order == 1) hipLaunchKernelGGL((encode_kernel<MAXH, true>), dim3(blocks), dim3(kThreads), 0, s, a, t);
+  else hipLaunchKernelGGL((encode_kernel<MAXH, false>), dim3(blocks), dim3(kThreads), 0, s, a, t);
   return hipGetLastError();
 }
 
@@ -581,10 +713,8 @@ static int encode_args(dq_codec_t codec, const void *x, int64_t T, int64_t strid
       stride_h < 0)
     return DQ_ERR_INVALID;
   if (T > ((int64_t)1 << 40) / t.hkv || num_slots > ((int64_t)1 << 40) / t.C) return DQ_ERR_INVALID;
-  // the rate-distortion order interleaves magnitude groups, which the
-  // large-batch kernel's drift plan assumes it does not: it always takes
-  // the wave-per-vector kernel, whose grid bounds the batch
-  if (t.order == 1 && T * (int64_t)t.hkv > ((int64_t)1 << 30)) return DQ_ERR_UNSUPPORTED;
+  // one lane per vector in blocks of kThreads: the grid bounds the batch
+  if (T * (int64_t)t.hkv > ((int64_t)1 << 38)) return DQ_ERR_UNSUPPORTED;
   // DQ_ENCODE_KEY_SPAN narrows the in-group keys' span so that the float
   // scans they fall back to run more often (same bytes either way)
   uint32_t span = dq::kKeySpan;
@@ -604,7 +734,7 @@ static bool wave_path(const dq::Tables &t, int64_t T) {
   int64_t wave_max = dq::kWavePathMax;
   if (const char *ev = getenv("DQ_ENCODE_WAVE_MAX")) wave_max = atoll(ev);
   const int64_t nvec = T * (int64_t)t.hkv;
-  return (t.order == 1 || nvec <= wave_max) && nvec <= ((int64_t)1 << 30);
+  return nvec <= wave_max && nvec <= ((int64_t)1 << 30);
 }
 
 static hipError_t launch_encode(const dq::EncodeArgs &a, const dq::Tables &t, hipStream_t s) {

@@ -146,12 +146,12 @@ def test_encode_in_group_scan_fallback(oracle_lib, monkeypatch, span, levels, C,
 
 @pytest.mark.parametrize("levels,C,step64", [(8, 34, 0), (6, 34, 0), (8, 29, 0), (6, 29, 0),
                                              (4, 30, 64), (10, 40, 34)])
-def test_encode_rate_distortion_order(oracle_lib, levels, C, step64):
+def test_encode_rate_distortion_order(oracle_lib, encode_path, levels, C, step64):
     """Rate-distortion drift order: containers, norms and stats bit-exact on
     the four distributions and on the adversarial rows (ties, degenerate
-    norms, one-hot vectors)."""
+    norms, one-hot vectors), through both encode kernels."""
     O = oracle_lib
-    _say(f"rd order {levels}/{C}/{step64}")
+    _say(f"rd order {levels}/{C}/{step64} {encode_path}")
     gc, oc = _codecs(O, levels, C, seed=33 + levels, hkv=3, step64=step64, order=1)
     for kind in ("iid", "outlier", "student_t5", "iid_scaled"):
         x = synth.kv_tensor(kind, 200, 3, seed=71, device=DEV)
