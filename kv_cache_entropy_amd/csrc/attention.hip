@@ -64,6 +64,10 @@ struct AttnArgs {
   const int32_t *seq_len;
   float qk_scale;  // sm_scale * log2(e) / 128
   int chunk, nc;
+  // decode split: chunk c covers tiles [c cq + min(c, cr), (c + 1) cq +
+  // min(c + 1, cr)) of a sequence, so the nc chunks of a max_len sequence
+  // differ by at most one tile
+  int cq, cr;
   int64_t n_items;
   float *part;
   uint16_t *qrot;
@@ -487,8 +491,8 @@ __device__ __forceinline__ void append_vector(const AttnArgs &a, const Tables &t
     else if (pos / kTile < a.max_pages) slot = (int64_t)a.pages[(int64_t)b * a.max_pages + pos / kTile] * kTile + pos % kTile;
   }
   const uint16_t *xp = (isv ? a.v_new : a.k_new) + (int64_t)b * a.new_stride_b + (int64_t)g * a.new_stride_h;
-  const WaveEncodeScratch L{reinterpret_cast<uint32_t *>(scratch), reinterpret_cast<float *>(scratch + 4 * kD),
-                            scratch + 8 * kD, scratch + 9 * kD, min(kWaveScr, t.C - 3)};
+  const WaveEncodeScratch L{reinterpret_cast<uint32_t *>(scratch), scratch + 4 * kD, scratch + 5 * kD,
+                            min(kWaveScr, t.C - 3)};
   WaveEncodeResult r;
   wave_encode_vector<RD, true>(xp, g, t, etab, rdtab, L, lane, r);
   if (r.win >= 0 && slot >= 0 && slot < a.S) {
@@ -603,18 +607,23 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
       else append_vector<false>(a, tk, etab[0], rdtab[0], base, false, b, g, lane);
     }
   }
+  // items are chunk-major: a wave's items in successive rounds are chunks
+  // c, c + W / nbg, ..., which pairs the one-tile-longer first chunks with
+  // the shorter last ones when the items fill whole rounds
+  const int64_t nbg = (int64_t)a.B * a.Hkv;
   for (; it < n_enc + a.n_items; it += W) {
     const int64_t item = it - n_enc;
-    const int c = (int)(item % a.nc);
-    const int64_t bg = item / a.nc;
+    const int c = (int)(item / nbg);
+    const int64_t bg = item - (int64_t)c * nbg;
     const int b = (int)(bg / a.Hkv), g = (int)(bg - (int64_t)b * a.Hkv);
+    const int64_t pidx = bg * a.nc + c;  // the partial's slot
     // a paged sequence never reads past its row of the page table; with an
     // append the newest token is not part of any chunk
     const int len0 = a.seq_len[b] - a.skip_last;
     const int len = a.pages ? min(len0, a.max_pages * kTile) : len0;
-    const int t0 = c * a.chunk;
+    const int t0 = (c * a.cq + min(c, a.cr)) * kTile;
     if (t0 >= len) continue;
-    const int t1 = min(t0 + a.chunk, len);
+    const int t1 = min(t0 + (a.cq + (c < a.cr ? 1 : 0)) * kTile, len);
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
     const int64_t plane0 = (int64_t)g * a.S;
     // pool index of the first token of tile `tile` of this item: a page is
@@ -675,7 +684,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
         nkc = nkn;
         nvc = nvn;
       }
-      write_partial(a.part + item * 4 * kPart, acc, m_run, l_lane, lane);
+      write_partial(a.part + pidx * 4 * kPart, acc, m_run, l_lane, lane);
       continue;
     }
     uint32_t nk0, nv0, nk1 = 0, nv1 = 0;
@@ -738,7 +747,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
       nv1 = nv2;
     }
 
-    write_partial(a.part + item * 4 * kPart, acc, m_run, l_lane, lane);
+    write_partial(a.part + pidx * 4 * kPart, acc, m_run, l_lane, lane);
   }
 }
 
@@ -750,7 +759,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 constexpr int kAppendWaves = 4;  // waves per block
 __host__ __device__ inline int append_scratch_bytes(int C) {
   const int rows = C - 3 < kWaveScr ? C - 3 : kWaveScr;
-  return 9 * kD + rows * 64;
+  return 5 * kD + rows * 64;  // ent [128] words, mag [128] bytes, renorm rows
 }
 __global__ void __launch_bounds__(64 * kAppendWaves) append_encode_kernel(AttnArgs a, Tables tk, Tables tv) {
   __shared__ uint4 etab[2][kMaxLevels];
@@ -872,7 +881,10 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
   // token's partial sits apart
   const bool extra = a.part_new != nullptr && len >= 1;
   const int lc = a.part_new != nullptr ? len - 1 : len;
-  const int n = max(0, min((lc + a.chunk - 1) / a.chunk, a.nc));
+  // chunks holding tokens: those starting below tile L = ceil(lc / 64)
+  // (the first cr chunks have cq + 1 tiles, the others cq >= 1)
+  const int L = max(0, (lc + kTile - 1) / kTile), big = a.cr * (a.cq + 1);
+  const int n = min(a.nc, L <= big ? (L + a.cq) / (a.cq + 1) : a.cr + (L - big + a.cq - 1) / a.cq);
   const float *src = a.part + (((int64_t)b * a.Hkv + g) * a.nc) * 4 * kPart + hh * kPart;
   const float *pe = extra ? a.part_new + ((int64_t)b * a.Hkv + g) * 4 * kPart + hh * kPart : nullptr;
   buf[d] = lse_merge(src, 4 * kPart, n, pe, red, wts);  // an empty sequence (a caller error) gives a zero row
@@ -1560,7 +1572,7 @@ __global__ void __launch_bounds__(128) prefill_combine_kernel(AttnArgs a, uint64
 
 // ---------------------------------------------------------------- planning
 struct Plan {
-  int chunk, nc, waves_per_block, blocks_cap, nq;
+  int chunk, nc, cq, cr, waves_per_block, blocks_cap, nq;
   bool lat;  // latency mode (whole V tiles in LDS, fewer waves per CU)
   int64_t n_items;
   size_t lds, qrot_bytes, part_bytes, part_new_bytes, total;
@@ -1578,13 +1590,14 @@ int device_cus() {
   return cus;
 }
 
-// Context split.  A launch deals its items (units x nc, each covering up to
-// `chunk` tokens) round-robin to W resident waves, so it takes about
-// ceil(units * nc / W) rounds of (chunk + c0) token-times, c0 being an
-// item's fixed cost (a K-only and a V-only tile pass and the partial; about
-// 32 tokens on MI355X).  The chunk (a multiple of the 64-token tile, 64 to
-// 2048: only max_len is known here, and ragged batches need the finer
-// items to balance) minimising that is chosen; W is a fixed function of the
+// Context split.  A launch deals its items (units x nc, the nc chunks of a
+// max_len sequence balanced to within one tile) round-robin to W resident
+// waves, so it takes about ceil(units * nc / W) rounds of (longest chunk +
+// c0) token-times, c0 being an item's fixed cost (a K-only and a V-only tile
+// pass and the partial; about 32 tokens on MI355X).  The chunk count from a
+// chunk length of 64 to 2048 tokens (only max_len is known here, and ragged
+// batches need the finer items to balance) minimising that is chosen; W is a
+// fixed function of the
 // CU count, so the workspace size depends only on the call's shape.  Small
 // batches get one-tile chunks: an item is then a K pass and a V pass, the
 // shortest latency a wave can give a tile.
@@ -1594,7 +1607,8 @@ int64_t choose_chunk(int64_t units, int64_t max_len, int64_t W) {
   int64_t best = 1024, best_cost = INT64_MAX;
   for (int64_t chunk = kTile; chunk <= 2048; chunk += kTile) {
     const int64_t nc = (max_len + chunk - 1) / chunk;
-    const int64_t span = nc == 1 ? ((max_len + kTile - 1) / kTile) * kTile : chunk;
+    const int64_t tiles = (max_len + kTile - 1) / kTile;
+    const int64_t span = ((tiles + nc - 1) / nc) * kTile;  // the longest of nc balanced chunks
     const int64_t rounds = (units * nc + W - 1) / W;
     const int64_t cost = rounds * (span + c0);
     if (cost < best_cost) {
@@ -1625,8 +1639,11 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   // sequence were max_len; independent of C so the workspace size is too
   const int64_t chunk = choose_chunk((int64_t)B * Hkv, max_len, (int64_t)cus * 12);
   const int64_t nc = (max_len + chunk - 1) / chunk;
+  const int64_t tiles = (max_len + kTile - 1) / kTile;  // >= nc
   pl->chunk = (int)chunk;
   pl->nc = (int)nc;
+  pl->cq = nc > 0 ? (int)(tiles / nc) : 1;
+  pl->cr = nc > 0 ? (int)(tiles % nc) : 0;
   pl->waves_per_block = wpb;
   pl->n_items = (int64_t)B * Hkv * nc;
   pl->lds = (size_t)wpb * wb;  // dynamic part; the decode tables are static
@@ -1922,6 +1939,8 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
   a.qk_scale = sm_scale * 1.4426950408889634f / 128.0f;
   a.chunk = pl.chunk;
   a.nc = pl.nc;
+  a.cq = pl.cq;
+  a.cr = pl.cr;
   a.n_items = pl.n_items;
   a.qrot = nullptr;  // the split-K items rotate their own queries
   a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.qrot_bytes);

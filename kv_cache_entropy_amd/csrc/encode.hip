@@ -631,7 +631,6 @@ __device__ __forceinline__ void wave_encode_block(const EncodeArgs &a, const Tab
   __shared__ uint4 etab[kMaxLevels];
   __shared__ float2 rdtab[kMaxHalf];
   __shared__ uint32_t ent[kWaveVecs][kD];
-  __shared__ __attribute__((aligned(16))) float key[kWaveVecs][kD];  // read as float4
   __shared__ __attribute__((aligned(16))) uint8_t mag[kWaveVecs][kD];  // read as words
   __shared__ uint8_t scr[kWaveVecs][kWaveScr * 64];
   __shared__ uint32_t bstat[6 + kMaxC + 1];  // per-block stats, flushed once
@@ -646,7 +645,7 @@ __device__ __forceinline__ void wave_encode_block(const EncodeArgs &a, const Tab
     const int g = (int)(vid / a.T);
     const int64_t tok = vid - (int64_t)g * a.T;
     const int64_t slot = a.slots[tok];
-    const WaveEncodeScratch L{ent[w], key[w], mag[w], scr[w], kWaveScr};
+    const WaveEncodeScratch L{ent[w], mag[w], scr[w], kWaveScr};
     WaveEncodeResult r;
     wave_encode_vector<RD, false>(a.x + tok * a.stride_t + (int64_t)g * a.stride_h, g, t, etab, rdtab, L, lane, r);
     if (r.win >= 0 && slot >= 0 && slot < a.num_slots)

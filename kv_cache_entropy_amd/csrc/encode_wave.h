@@ -80,7 +80,6 @@ __device__ __forceinline__ void wave_encode_tables(const Tables &t, uint4 *etab,
 // does not fit anyway, so only its length, not its bytes, must be right.
 struct WaveEncodeScratch {
   uint32_t *ent;  // [128] s0 | sd << 8 | rank << 16
-  float *key;     // [128] drift-order key (16-byte aligned: read as float4)
   uint8_t *mag;   // [128] magnitude cell (4-byte aligned: read as words)
   uint8_t *scr;   // [rows][64] renorm bytes, lane-minor
   int rows;
@@ -157,7 +156,6 @@ __device__ __forceinline__ void wave_encode_vector(const uint16_t *xp, int g, co
     yA[e] = ay;
   }
   uint32_t *E = L.ent;
-  float *Y = L.key;
   uint8_t *Mg = L.mag;
   uint8_t *scol = L.scr;
   const int rows = L.rows;
