@@ -1605,11 +1605,15 @@ int device_cus() {
 int64_t choose_chunk(int64_t units, int64_t max_len, int64_t W) {
   const int64_t c0 = 32;
   int64_t best = 1024, best_cost = INT64_MAX;
-  for (int64_t chunk = kTile; chunk <= 2048; chunk += kTile) {
+  for (int64_t chunk = kTile; chunk <= 4096; chunk += kTile) {
     const int64_t nc = (max_len + chunk - 1) / chunk;
     const int64_t tiles = (max_len + kTile - 1) / kTile;
     const int64_t span = ((tiles + nc - 1) / nc) * kTile;  // the longest of nc balanced chunks
     const int64_t rounds = (units * nc + W - 1) / W;
+    // chunks past 2048 tokens only when the items then fill one round: a
+    // wave takes a single item, and a ragged batch's longest items are no
+    // longer than two of the finer split's would be together
+    if (chunk > 2048 && rounds > 1) continue;
     const int64_t cost = rounds * (span + c0);
     if (cost < best_cost) {
       best_cost = cost;
