@@ -50,8 +50,36 @@ typedef void *dq_stream_t; /* hipStream_t */
 const char *dq_status_string(int status);
 
 /* ABI version: 100 * major + minor (101: dq_codec_desc.drift_order; 102: decode
- * with append). */
+ * with append; 103: dq_set_knob). */
 int dq_version(void);
+
+/* Path overrides, for tests and tuning.  Every value the library can pick by
+ * itself gives the same results (the split length aside, which changes the
+ * floating-point order of the attention sums); these force one choice so
+ * that tests reach each code path.  Process-wide, thread-safe (atomic), read
+ * once per call that plans a launch; -1 restores the library's own choice.
+ *   DQ_KNOB_SPLIT_TOKENS     decode/prefill context chunk in tokens (a
+ *                            multiple of 64, >= 64; other values: ignored)
+ *   DQ_KNOB_LATENCY_MODE     1: decode in latency mode, 0: never
+ *   DQ_KNOB_APPEND_FUSE      1: a decode step's encodes inside the split-K
+ *                            launch, 0: in a launch of their own
+ *   DQ_KNOB_ENCODE_WAVE_MAX  batch size (vectors) up to which dq_encode uses
+ *                            the wave-per-vector kernel
+ *   DQ_KNOB_ENCODE_KEY_SPAN  span of the encoder's in-group integer keys
+ *                            (smaller spans take the float-scan fallback
+ *                            sooner; same bytes)
+ * dq_set_knob returns DQ_ERR_INVALID for an unknown knob or a value below
+ * -1; dq_get_knob returns the value (or DQ_ERR_INVALID). */
+enum {
+  DQ_KNOB_SPLIT_TOKENS = 1,
+  DQ_KNOB_LATENCY_MODE = 2,
+  DQ_KNOB_APPEND_FUSE = 3,
+  DQ_KNOB_ENCODE_WAVE_MAX = 4,
+  DQ_KNOB_ENCODE_KEY_SPAN = 5,
+  DQ_KNOB_COUNT = 6
+};
+int dq_set_knob(int knob, int64_t value);
+int64_t dq_get_knob(int knob);
 
 /* ------------------------------------------------------------------------ */
 /* Codec: the parameters of one coded stream (K or V).
@@ -156,7 +184,15 @@ int dq_encode_kv(dq_codec_t ck, dq_codec_t cv, const void *k, const void *v,
                  dq_stats *k_stats, dq_stats *v_stats, dq_stream_t stream);
 
 /* dq_decode_symbols: container -> the 128 symbols, for kv head `head` at n
- * slots (inspection and checking; attention decodes inside its own kernel).
+ * slots: the entropy decode alone, without dequantisation or attention, the
+ * per-stream inverse of dq_encode ("D-Quant: Entropy Coding Meets KV Cache at
+ * 2.26 Bits", intro: rANS coding of the quantised symbols; Drift: Bending
+ * Variable Back to Fixed: one fixed-size container per vector), for
+ * inspection and checking (attention decodes inside its own kernel).
+ *   cont         device uint8[Hkv][num_slots][C], read-only
+ *   slots        device int64[n]; a slot outside [0, num_slots) gives 128
+ *                zero symbols, final state 0 and 0 bytes consumed
+ *   head         kv head, 0 <= head < Hkv (else DQ_ERR_INVALID)
  *   sym_out      device uint8[n][128]
  *   final_state  device uint32[n] or NULL: decoder state after 128 symbols
  *                (2^23 for every container dq_encode wrote)

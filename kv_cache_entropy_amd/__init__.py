@@ -26,7 +26,7 @@ MAX_CONTAINER = 132
 PAGE_TOKENS = 64
 NSTATS = 6 + MAX_CONTAINER + 1
 
-__all__ = ["Codec", "alloc_pool", "encode", "encode_kv", "decode_symbols", "attn_decode", "attn_decode_paged",
+__all__ = ["Codec", "set_knob", "get_knob", "knobs", "alloc_pool", "encode", "encode_kv", "decode_symbols", "attn_decode", "attn_decode_paged",
            "attn_prefill", "attn_prefill_workspace_bytes",
            "attn_workspace_bytes", "new_stats", "stats_dict", "DQError", "library_path"]
 
@@ -43,6 +43,41 @@ def _check(status: int, what: str):
     if status != 0:
         msg = _lib.lib().dq_status_string(status).decode()
         raise DQError(f"{what}: {msg} ({status})")
+
+
+# Path overrides of the C ABI (dq_set_knob): -1 (or None) = the library's own
+# choice.  Tests force each code path with them; results do not depend on them
+# except for the split length (floating-point order of the attention sums).
+KNOBS = {"split_tokens": 1, "latency_mode": 2, "append_fuse": 3, "encode_wave_max": 4,
+         "encode_key_span": 5}
+
+
+def set_knob(name: str, value) -> None:
+    _check(_lib.lib().dq_set_knob(KNOBS[name], -1 if value is None else int(value)), f"dq_set_knob({name})")
+
+
+def get_knob(name: str) -> int:
+    return int(_lib.lib().dq_get_knob(KNOBS[name]))
+
+
+class knobs:
+    """Context manager: ``with knobs(split_tokens=64): ...`` forces the given
+    paths and restores the previous values on exit."""
+
+    def __init__(self, **kw):
+        self._kw = kw
+        self._old = {}
+
+    def __enter__(self):
+        for k, v in self._kw.items():
+            self._old[k] = get_knob(k)
+            set_knob(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k, v in self._old.items():
+            set_knob(k, v)
+        return False
 
 
 def _stream(device) -> ctypes.c_void_p:

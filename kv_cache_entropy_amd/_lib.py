@@ -30,6 +30,10 @@ def lib():
         L.dq_status_string.argtypes = [ctypes.c_int]
         L.dq_version.restype = ctypes.c_int
         L.dq_version.argtypes = []
+        L.dq_set_knob.restype = ctypes.c_int
+        L.dq_set_knob.argtypes = [ctypes.c_int, i64]
+        L.dq_get_knob.restype = i64
+        L.dq_get_knob.argtypes = [ctypes.c_int]
         L.dq_codec_create.argtypes = [ctypes.POINTER(CodecDesc), ctypes.POINTER(vp)]
         L.dq_codec_destroy.argtypes = [vp]
         L.dq_codec_info.argtypes = [vp, ctypes.POINTER(CodecDesc)]

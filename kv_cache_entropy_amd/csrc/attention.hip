@@ -6,25 +6,28 @@
 // Cache at 2.26 Bits" (intro, So What): the entropy decoder runs inside the
 // attention kernel.
 //
-// Three kernels on the caller's stream:
-//  1. rotate_q: q~ = H * D_K * q in fp32 for every query head, stored as an
-//     fp16 hi/lo pair (hi + lo carries ~22 bits) in the MFMA operand layout.
-//     Because H * H = 128 I, q . khat = q~ . (n * r(s)) / 128: scores are
-//     computed directly on the decoded levels, no inverse rotation of K.
-//  2. attn_splitk: persistent waves; a work item is (sequence, kv head,
-//     context chunk).  Per 64-token tile a wave copies the tile's K and V
-//     containers (64 * C contiguous bytes each, fixed stride) into its LDS
-//     slice with 16-byte loads; every lane then rANS-decodes one token's
+// Two kernels on the caller's stream (three when a decode step's appended
+// tokens are encoded by a launch of their own, append_encode_kernel):
+//  1. attn_splitk: persistent waves; a work item is (sequence, kv head,
+//     context chunk).  The item first rotates its own query, q~ = H * D_K *
+//     q in fp32, kept as an fp16 hi/lo pair (hi + lo carries ~22 bits) in
+//     the MFMA operand layout.  Because H * H = 128 I, q . khat = q~ . (n *
+//     r(s)) / 128: scores are computed directly on the decoded levels, no
+//     inverse rotation of K.  Per 64-token tile a wave copies the tile's K
+//     and V containers (64 * C contiguous bytes each, fixed stride) into its
+//     LDS slice with 16-byte loads; every lane then rANS-decodes one token's
 //     container through an LDS table (slot -> f, slot - cum, fp16 level).
-//     K: every 4 decoded symbols form the A operand of a 4x4x4 MFMA
+//     K: every 4 decoded symbols form the B operand of a 4x4x4 MFMA
 //     (16 blocks = the wave's 64 tokens) against q~ (4 heads), so the decoded
 //     keys never leave registers.  Online softmax in fp32 (exp2 domain).
 //     V: decoded levels are written transposed into an LDS tile [dim][token]
 //     and contracted with p * n_v (an fp16 hi/lo pair, so ~22 bits) by
 //     4x4x4 MFMAs whose 16 blocks cover 64 dims.  Each item leaves
 //     (m, l, acc[4][128]) in the workspace.
-//  3. combine: log-sum-exp merge of an item's chunks, then the inverse
+//  2. combine: log-sum-exp merge of an item's chunks, then the inverse
 //     rotation D_V * H / 128 and the store.
+// Chunked prefill (attn_prefill_shared_kernel, attn_prefill_kernel) reuses
+// the decode pieces with many query rows per decoded tile.
 #include "decode_common.h"
 #include "encode_wave.h"
 
@@ -1601,7 +1604,7 @@ int device_cus() {
 // CU count, so the workspace size depends only on the call's shape.  Small
 // batches get one-tile chunks: an item is then a K pass and a V pass, the
 // shortest latency a wave can give a tile.
-// DQ_SPLIT_TOKENS forces a chunk (tests use it).
+// DQ_KNOB_SPLIT_TOKENS forces a chunk (tests use it).
 int64_t choose_chunk(int64_t units, int64_t max_len, int64_t W) {
   const int64_t c0 = 32;
   int64_t best = 1024, best_cost = INT64_MAX;
@@ -1621,10 +1624,8 @@ int64_t choose_chunk(int64_t units, int64_t max_len, int64_t W) {
     }
     if (nc == 1) break;  // larger chunks change nothing
   }
-  if (const char *e = getenv("DQ_SPLIT_TOKENS")) {
-    const long v = strtol(e, nullptr, 10);
-    if (v >= kTile && v % kTile == 0) best = v;
-  }
+  const int64_t forced = knob(DQ_KNOB_SPLIT_TOKENS);
+  if (forced >= kTile && forced % kTile == 0) best = forced;
   return best;
 }
 
@@ -1652,14 +1653,15 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   pl->n_items = (int64_t)B * Hkv * nc;
   pl->lds = (size_t)wpb * wb;  // dynamic part; the decode tables are static
   // latency mode when its fewer resident waves still take every item in one
-  // round (small batches); DQ_LATENCY_MODE forces it on (1) or off (0)
+  // round (small batches); DQ_KNOB_LATENCY_MODE forces it on (1) or off (0)
   pl->lat = false;
   if (pl->nq == 3) {
     const int lwb = wave_layout(Ck, Cv, true).bytes;
     int lwpb = (lds_cap - kStaticLds) / lwb;
     lwpb = lwpb > 12 ? 12 : lwpb;
     bool lat = lwpb >= 1 && pl->n_items <= (int64_t)cus * lwpb;
-    if (const char *e = getenv("DQ_LATENCY_MODE")) lat = lwpb >= 1 && e[0] == '1';
+    const int64_t forced = knob(DQ_KNOB_LATENCY_MODE);
+    if (forced >= 0) lat = lwpb >= 1 && forced == 1;
     if (lat) {
       pl->lat = true;
       pl->waves_per_block = lwpb;
@@ -1701,7 +1703,7 @@ struct PrefillPlan {
 // (units x nc) in turn; an item of span s tokens costs about
 // ceil(s / 256) rounds of 4 tiles plus a fixed quarter round.  The chunk (a
 // multiple of 64) minimising ceil(items / CUs) x that is chosen.
-// DQ_SPLIT_TOKENS forces a chunk, as for decode.
+// DQ_KNOB_SPLIT_TOKENS forces a chunk, as for decode.
 int64_t choose_prefill_chunk(int64_t units, int64_t max_len, int cus) {
   const int64_t rt = (int64_t)kRoundTiles * kTile;
   int64_t best = max_len, best_cost = INT64_MAX;
@@ -1715,10 +1717,8 @@ int64_t choose_prefill_chunk(int64_t units, int64_t max_len, int cus) {
     }
     if (nc == 1) break;
   }
-  if (const char *e = getenv("DQ_SPLIT_TOKENS")) {
-    const long v = strtol(e, nullptr, 10);
-    if (v >= kTile && v % kTile == 0) best = v;
-  }
+  const int64_t forced = knob(DQ_KNOB_SPLIT_TOKENS);
+  if (forced >= kTile && forced % kTile == 0) best = forced;
   return best;
 }
 
@@ -1971,7 +1971,8 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
     const int64_t W = (int64_t)pl.blocks_cap * pl.waves_per_block;
     const int64_t n_enc = 2 * (int64_t)B * Hkv;
     bool fuse = (pl.n_items + n_enc + W - 1) / W == (pl.n_items + W - 1) / W;
-    if (const char *e = getenv("DQ_APPEND_FUSE")) fuse = e[0] == '1';  // tests force either way
+    const int64_t forced = dq::knob(DQ_KNOB_APPEND_FUSE);  // tests force either way
+    if (forced >= 0) fuse = forced == 1;
     a.n_enc = fuse ? n_enc : 0;
     a.skip_last = 1;
   }

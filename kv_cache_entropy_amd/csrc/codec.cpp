@@ -10,11 +10,19 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <new>
 
 #include "dq_internal.h"
 
 namespace dq {
+
+// Path overrides set through dq_set_knob: one relaxed atomic load per use,
+// so hot calls read no environment and race with nothing.
+static std::atomic<int64_t> g_knobs[DQ_KNOB_COUNT] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+static_assert(DQ_KNOB_COUNT == 6, "one initialiser per knob");
+
+int64_t knob(int k) { return g_knobs[k].load(std::memory_order_relaxed); }
 
 uint64_t host_splitmix64(uint64_t seed, uint64_t n) {
   // SplitMix64 (Steele, Lea & Flood, OOPSLA 2014), output n of the stream.
@@ -143,7 +151,18 @@ const char *dq_status_string(int status) {
   }
 }
 
-int dq_version(void) { return 102; }
+int dq_version(void) { return 103; }
+
+int dq_set_knob(int knob, int64_t value) {
+  if (knob < 1 || knob >= DQ_KNOB_COUNT || value < -1) return DQ_ERR_INVALID;
+  dq::g_knobs[knob].store(value, std::memory_order_relaxed);
+  return DQ_OK;
+}
+
+int64_t dq_get_knob(int knob) {
+  if (knob < 1 || knob >= DQ_KNOB_COUNT) return DQ_ERR_INVALID;
+  return dq::knob(knob);
+}
 
 int dq_codec_create(const dq_codec_desc *desc, dq_codec_t *out) {
   if (!desc || !out) return DQ_ERR_INVALID;

@@ -66,4 +66,5 @@ struct dq_codec {
 namespace dq {
 // host helpers implemented in codec.cpp
 uint64_t host_splitmix64(uint64_t seed, uint64_t n);
+int64_t knob(int k);  // value set by dq_set_knob, -1 when not forced
 }  // namespace dq

@@ -714,24 +714,22 @@ static int encode_args(dq_codec_t codec, const void *x, int64_t T, int64_t strid
   if (T > ((int64_t)1 << 40) / t.hkv || num_slots > ((int64_t)1 << 40) / t.C) return DQ_ERR_INVALID;
   // one lane per vector in blocks of kThreads: the grid bounds the batch
   if (T * (int64_t)t.hkv > ((int64_t)1 << 38)) return DQ_ERR_UNSUPPORTED;
-  // DQ_ENCODE_KEY_SPAN narrows the in-group keys' span so that the float
-  // scans they fall back to run more often (same bytes either way)
+  // DQ_KNOB_ENCODE_KEY_SPAN narrows the in-group keys' span so that the
+  // float scans they fall back to run more often (same bytes either way)
   uint32_t span = dq::kKeySpan;
-  if (const char *ev = getenv("DQ_ENCODE_KEY_SPAN")) {
-    const long long v = atoll(ev);
-    span = v < 0 ? 0u : (v < (long long)dq::kKeySpan ? (uint32_t)v : dq::kKeySpan);
-  }
+  const int64_t forced = dq::knob(DQ_KNOB_ENCODE_KEY_SPAN);
+  if (forced >= 0) span = forced < (int64_t)dq::kKeySpan ? (uint32_t)forced : dq::kKeySpan;
   *a = dq::EncodeArgs{static_cast<const uint16_t *>(x), T, stride_t, stride_h, slots, num_slots, cont, norm, stats,
                       span};
   return DQ_OK;
 }
 
 // Does a batch of this codec take the wave-per-vector kernel?
-// DQ_ENCODE_WAVE_MAX overrides the batch size (vectors) up to which it
-// does; both kernels write identical bytes.
+// DQ_KNOB_ENCODE_WAVE_MAX overrides the batch size (vectors) up to which
+// it does; both kernels write identical bytes.
 static bool wave_path(const dq::Tables &t, int64_t T) {
-  int64_t wave_max = dq::kWavePathMax;
-  if (const char *ev = getenv("DQ_ENCODE_WAVE_MAX")) wave_max = atoll(ev);
+  const int64_t forced = dq::knob(DQ_KNOB_ENCODE_WAVE_MAX);
+  const int64_t wave_max = forced >= 0 ? forced : dq::kWavePathMax;
   const int64_t nvec = T * (int64_t)t.hkv;
   return nvec <= wave_max && nvec <= ((int64_t)1 << 30);
 }

@@ -6,9 +6,10 @@
 // rotate (randomized Walsh-Hadamard), fp16 norm, quantise on the analytic
 // N(0,1) cells, rANS into the container, and drift the first candidates of
 // the fixed order one level inward until the stream fits.  Lane l holds
-// coordinates l and l + 64; the drift search is one parallel pass: every
-// candidate gets its rank in the drift order by a broadcast scan, and lane
-// l runs the rANS pass with the first k0 + l candidates moved, so the lowest
+// coordinates l and l + 64; the drift search is one parallel pass: a
+// bitonic sort of the wave's 128 (key, index) pairs gives every candidate
+// its rank in the drift order, and lane l runs the rANS pass with the first
+// k0 + l candidates moved, so the lowest
 // lane whose stream fits is the answer (the length never increases along
 // the order).
 //

@@ -33,3 +33,20 @@ def oracle_lib():
     import oracle
     oracle.build()
     return oracle
+
+
+@pytest.fixture
+def knob():
+    """knob(name, value) forces a library path (dq_set_knob) for one test;
+    every knob it touched is restored afterwards, pass or fail."""
+    import kv_cache_entropy_amd as dq
+    old = {}
+
+    def set_(name, value):
+        if name not in old:
+            old[name] = dq.get_knob(name)
+        dq.set_knob(name, value)
+
+    yield set_
+    for name, value in old.items():
+        dq.set_knob(name, value)

@@ -42,10 +42,23 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     L = _lib.lib()
-    assert L.dq_version() == 102
+    assert L.dq_version() == 103
     assert L.dq_status_string(0) == b"ok"
     for code in (-1, -2, -3, -4, -5):
         assert L.dq_status_string(code) not in (b"ok", b"unknown status")
+
+
+def test_knobs_set_get_and_reject():
+    """dq_set_knob stores a forced path per knob (host only, no GPU), -1
+    restores the default, and unknown knobs or values below -1 are rejected."""
+    for name in dq.KNOBS:
+        assert dq.get_knob(name) == -1
+    with dq.knobs(split_tokens=128, latency_mode=1):
+        assert dq.get_knob("split_tokens") == 128 and dq.get_knob("latency_mode") == 1
+    assert dq.get_knob("split_tokens") == -1 and dq.get_knob("latency_mode") == -1
+    L = _lib.lib()
+    assert L.dq_set_knob(0, 1) == -1 and L.dq_set_knob(99, 1) == -1 and L.dq_set_knob(1, -2) == -1
+    assert L.dq_get_knob(0) == -1
 
 
 @pytest.mark.parametrize("levels,C,step64", [

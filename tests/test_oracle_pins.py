@@ -713,3 +713,108 @@ def test_golden_fixtures_unchanged(oracle_lib):
         assert f.read() == mg.tables_text()
     with open(os.path.join(here, "small_encode.txt")) as f:
         assert f.read() == mg.small_encode_text()
+
+
+# ------------------------------------------------------------------ calibration and stats
+def _drift_rate(O, levels, C, step64, xbits):
+    codec = O.Codec(levels, C, seed=0, hkv=1, step64=step64)
+    _, _, st = O.encode(codec, xbits)
+    s = O.stats_dict(st)
+    return s["drifted_symbols"] / (128.0 * s["vectors"])
+
+
+def test_default_widths_follow_calibration_rule(oracle_lib):
+    """The default cell widths are the calibration rule applied again: on
+    2^16 i.i.d. N(0,1) vectors (the analytic model, seed 0), each default
+    is the admissible width within +-3 steps of 1/64 whose drift rate is
+    nearest the pages' rate for its stream, 0.75% of key symbols and 5.00%
+    of value symbols ("D-Quant: Entropy Coding Meets KV Cache at 2.26 Bits",
+    Drift: Bending Variable Back to Fixed); the 29-byte container uses the
+    same targets.  An off-by-one default fails here.  Keys at 29 bytes
+    cannot reach 0.75%: 83/64 is the widest width the table accepts (every
+    wider one floors both outer frequencies at 16, under the 1.15x rule),
+    so it is the default there."""
+    O = oracle_lib
+    xbits = synth.bf16_bits(synth.kv_tensor("iid", 1 << 16, 1, seed=0))
+    target = {8: 0.0075, 6: 0.05}
+    for (levels, C), s64 in sorted(O.DEFAULT_STEP64.items()):
+        rates = {w: _drift_rate(O, levels, C, w, xbits)
+                 for w in range(s64 - 3, s64 + 4) if O.codec_check(levels, w, C) == 0}
+        best = min(rates, key=lambda w: abs(rates[w] - target[levels]))
+        assert best == s64, (levels, C, s64, rates)
+    assert O.codec_check(8, 83, 29) == 0
+    assert all(O.codec_check(8, w, 29) != 0 for w in range(84, 256))
+    # the cap costs keys at 29 bytes their target: ~6.4% of symbols drift
+    assert 0.055 < _drift_rate(O, 8, 29, 83, xbits[:8192]) < 0.075
+
+
+def _mag(s, h):
+    return np.where(s >= h, s - h, h - 1 - s)
+
+
+@pytest.mark.parametrize("levels,C,step64,kind", [
+    (8, 34, 0, "outlier"), (6, 34, 0, "outlier"), (6, 29, 0, "student_t5"),
+    (8, 42, 32, "onehot")])
+def test_stats_are_sums_of_per_vector_results(oracle_lib, levels, C, step64, kind):
+    """Every field of the batch statistics (vectors, drifted vectors and
+    symbols, multilevel passes, degenerate norms, each stream-length bin)
+    equals the sum over the batch of quantities recomputed from each
+    vector's own encode: moves as the summed level distance between the
+    symbols before and after drift, extra passes as the largest distance
+    minus one (a symbol moved in pass p moved in every earlier pass), the
+    stream length as the length of a fresh rANS encode of the final symbols
+    (whose container decodes back to them), degenerate norms from the
+    stored fp16 bits.  The one-hot rows under an 8-level, 32/64-wide, 42-byte
+    codec put every coordinate at |y| = n, magnitude 2, where moving every
+    candidate once still overflows: that case exercises the multilevel
+    counter."""
+    O = oracle_lib
+    hkv = 2
+    codec = O.Codec(levels, C, seed=9, hkv=hkv, step64=step64)
+    t = codec.tables()
+    h = levels // 2
+    if kind == "onehot":
+        xf = np.zeros((40, hkv, D), np.float32)
+        for i in range(40):
+            xf[i, :, (7 * i) % D] = 0.25 * (1 + i % 5) * (1 if i % 3 else -1)
+        xf[:20, 1] = synth.kv_tensor("iid", 20, 1, seed=8)[:, 0].float().numpy()
+        xb = bits_bf16(xf)
+    else:
+        xb = synth.bf16_bits(synth.kv_tensor(kind, 40, hkv, seed=7))
+    # degenerate rows: zero, overflow to inf, NaN
+    extra = np.zeros((3, hkv, D), np.float32)
+    extra[1, :, 0] = np.inf
+    extra[2, :, :] = 1.0
+    extra[2, :, 3] = np.nan
+    xb = np.concatenate([xb, bits_bf16(extra)], axis=0)
+    _, _, st = O.encode(codec, xb)
+    s = O.stats_dict(st)
+    want = {"vectors": 0, "drifted_vectors": 0, "drifted_symbols": 0, "multilevel_events": 0,
+            "bad_norms": 0, "zero_norms": 0}
+    hist = np.zeros(len(s["len_hist"]), np.int64)
+    for tt in range(xb.shape[0]):
+        for g in range(hkv):
+            cont, d = O.encode_detail(codec, xb[tt, g], g)
+            s0 = np.array(d.sym0, np.int64)
+            s1 = np.array(d.sym, np.int64)
+            dist = np.abs(_mag(s0, h) - _mag(s1, h))
+            moves = int(dist.sum())
+            extra_passes = max(0, int(dist.max()) - 1)
+            n = len(O.rans_encode(s1.astype(np.uint8), t["freq"], t["cum"]))
+            dec, fs, _ = O.rans_decode(cont, C, t["freq"], t["cum"])
+            assert (dec == s1).all() and fs == 1 << 23
+            assert moves == d.moves and n == d.len
+            nb = int(d.norm)
+            want["vectors"] += 1
+            want["drifted_vectors"] += moves > 0
+            want["drifted_symbols"] += moves
+            want["multilevel_events"] += extra_passes
+            want["zero_norms"] += nb == 0
+            want["bad_norms"] += (nb & 0x7C00) == 0x7C00
+            hist[n] += 1
+    for k, v in want.items():
+        assert s[k] == v, (k, s[k], v)
+    assert list(s["len_hist"]) == hist.tolist()
+    if kind == "onehot":
+        assert s["multilevel_events"] > 0
+    assert s["zero_norms"] == hkv and s["bad_norms"] == 2 * hkv
