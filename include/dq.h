@@ -239,6 +239,31 @@ int dq_attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B,
                    int32_t out_dtype, void *out, void *workspace,
                    size_t ws_bytes, dq_stream_t stream);
 
+/* dq_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It calls no allocating routine.  The
+ * workspace is a library-held device array of DQ_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, reserved with the library's code on each GPU it runs on
+ * and held until the process ends; its address is looked up on the first
+ * call on a device (that device current).  A call whose workspace need
+ * (dq_attn_decode_workspace for the same B, Hq, Hkv, max_len) exceeds the
+ * array returns DQ_ERR_WORKSPACE and launches nothing; batch 128 x 8K and
+ * 32 sequences of up to 128K tokens (8 kv heads) fit.  Every call on one GPU
+ * shares its array: calls that overlap on one GPU (concurrent streams,
+ * threads) race and must be serialised by the caller.  Nothing in the array
+ * needs to start at zero: every partial a call reads back it wrote earlier
+ * in the same call.  `stream` must belong to the current device.  Every
+ * other argument, the checks and the result (bit for bit) are those of
+ * dq_attn_decode. */
+#define DQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+int dq_attn_decode_noalloc(dq_codec_t ck, dq_codec_t cv, const void *q,
+                           int32_t B, int32_t Hq, const uint8_t *k_cont,
+                           const uint16_t *k_norm, const uint8_t *v_cont,
+                           const uint16_t *v_norm, int64_t num_slots,
+                           const int64_t *seq_start, const int32_t *seq_len,
+                           int64_t max_len, float sm_scale, int32_t out_dtype,
+                           void *out, dq_stream_t stream);
+
 /* Chunked-prefill attention over the compressed cache.  A chunk of Tq new
  * tokens per sequence has been encoded with dq_encode at the end of the
  * sequence's slots, so seq_len[b] counts it; query j of sequence b sits at

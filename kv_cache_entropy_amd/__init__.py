@@ -26,7 +26,8 @@ MAX_CONTAINER = 132
 PAGE_TOKENS = 64
 NSTATS = 6 + MAX_CONTAINER + 1
 
-__all__ = ["Codec", "set_knob", "get_knob", "knobs", "alloc_pool", "encode", "encode_kv", "decode_symbols", "attn_decode", "attn_decode_paged",
+__all__ = ["Codec", "set_knob", "get_knob", "knobs", "alloc_pool", "encode", "encode_kv", "decode_symbols",
+           "attn_decode", "attn_decode_noalloc", "attn_decode_paged",
            "attn_prefill", "attn_prefill_workspace_bytes",
            "attn_workspace_bytes", "new_stats", "stats_dict", "DQError", "library_path"]
 
@@ -293,6 +294,41 @@ def attn_decode(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_cont, v
         _check(_lib.lib().dq_attn_decode(*args), "dq_attn_decode")
     else:
         _check(_lib.lib().dq_attn_decode_timed(*args, *_event_handles(split_events)), "dq_attn_decode_timed")
+    return out
+
+
+def attn_decode_noalloc(ck: Codec, cv: Codec, q: torch.Tensor, k_cont, k_norm, v_cont, v_norm,
+                        seq_start: torch.Tensor, seq_len: torch.Tensor, max_len: int,
+                        sm_scale: float | None = None, out: torch.Tensor | None = None,
+                        out_dtype=torch.float32):
+    """attn_decode through dq_attn_decode_noalloc: the library's own device
+    array is the workspace (no allocation in the call; pass `out` to keep
+    this wrapper from allocating the result).  Calls that overlap on one GPU
+    race; a shape whose workspace exceeds the array raises DQError."""
+    _need_cuda("q", q, torch.bfloat16)
+    for name, t, dt in (("k_cont", k_cont, torch.uint8), ("v_cont", v_cont, torch.uint8),
+                        ("k_norm", k_norm, torch.float16), ("v_norm", v_norm, torch.float16),
+                        ("seq_start", seq_start, torch.int64), ("seq_len", seq_len, torch.int32)):
+        _need_cuda(name, t, dt)
+        if not t.is_contiguous():
+            raise DQError(f"{name} must be contiguous")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise DQError("q must be a contiguous bf16 [B, Hq, 128]")
+    if k_cont.shape[1] != v_cont.shape[1]:
+        raise DQError("K and V pools must have the same slot count")
+    B, Hq, _ = q.shape
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise DQError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=out_dtype, device=q.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (B, Hq, HEAD_DIM) or not out.is_contiguous():
+        raise DQError("out has the wrong shape or dtype")
+    if sm_scale is None:
+        sm_scale = HEAD_DIM ** -0.5
+    _check(_lib.lib().dq_attn_decode_noalloc(
+        ck.handle, cv.handle, _ptr(q), B, Hq, _ptr(k_cont), _ptr(k_norm), _ptr(v_cont), _ptr(v_norm),
+        k_cont.shape[1], _ptr(seq_start), _ptr(seq_len), max_len, ctypes.c_float(sm_scale),
+        0 if out_dtype == torch.float32 else 1, _ptr(out), _stream(q.device)), "dq_attn_decode_noalloc")
     return out
 
 

@@ -45,6 +45,8 @@ def lib():
         L.dq_attn_decode.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, vp, i64,
                                      ctypes.c_float, i32, vp, vp, ctypes.c_size_t, vp]
         L.dq_attn_decode_timed.argtypes = L.dq_attn_decode.argtypes + [vp, vp]
+        L.dq_attn_decode_noalloc.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, i64, vp, vp, i64,
+                                             ctypes.c_float, i32, vp, vp]
         L.dq_attn_prefill_workspace.argtypes = [i32, i32, i32, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
         L.dq_attn_prefill.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, i64, vp, vp, i64,
                                       ctypes.c_float, i32, vp, vp, ctypes.c_size_t, vp]
@@ -59,7 +61,7 @@ def lib():
         L.dq_attn_decode_append_timed.argtypes = app_head + [vp] + app_tail + [vp, vp]
         for f in ("dq_codec_create", "dq_codec_destroy", "dq_codec_info", "dq_codec_tables",
                   "dq_encode", "dq_encode_kv", "dq_decode_symbols", "dq_attn_decode_workspace",
-                  "dq_attn_decode", "dq_attn_decode_timed", "dq_attn_decode_paged",
+                  "dq_attn_decode", "dq_attn_decode_timed", "dq_attn_decode_paged", "dq_attn_decode_noalloc",
                   "dq_attn_prefill_workspace", "dq_attn_prefill", "dq_attn_decode_append",
                   "dq_attn_decode_paged_append", "dq_attn_decode_append_timed"):
             getattr(L, f).restype = ctypes.c_int

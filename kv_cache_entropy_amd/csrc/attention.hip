@@ -35,6 +35,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
 #include <utility>
 
 namespace dq {
@@ -2073,4 +2075,51 @@ extern "C" int dq_attn_decode_paged_append(dq_codec_t ck, dq_codec_t cv, const v
   return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, nullptr, pages, max_pages,
                      seq_len, max_len, sm_scale, out_dtype, out, workspace, ws_bytes, stream, nullptr, nullptr,
                      &app);
+}
+
+// ---------------------------------------------------------------- no-alloc decode
+// dq_attn_decode_noalloc's workspace: a device array of fixed size, one copy
+// per GPU, held until the process ends.  Host code never passes `scratch`
+// itself (in host code the name is a stand-in, not a device address): the
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and only that address reaches the kernels.
+static __device__ __align__(256) uint8_t scratch[DQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (looked up on its first call).
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DQ_ERR_UNSUPPORTED;
+  void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DQ_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return DQ_OK;
+}
+}  // namespace
+
+extern "C" int dq_attn_decode_noalloc(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, int32_t Hq,
+                                      const uint8_t *k_cont, const uint16_t *k_norm, const uint8_t *v_cont,
+                                      const uint16_t *v_norm, int64_t num_slots, const int64_t *seq_start,
+                                      const int32_t *seq_len, int64_t max_len, float sm_scale,
+                                      int32_t out_dtype, void *out, dq_stream_t stream) {
+  void *ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st) return st;
+  // the same checks and kernels as dq_attn_decode; a call whose workspace
+  // need exceeds the array returns DQ_ERR_WORKSPACE before any launch
+  return attn_decode(ck, cv, q, B, Hq, k_cont, k_norm, v_cont, v_norm, num_slots, seq_start, nullptr, 0, seq_len,
+                     max_len, sm_scale, out_dtype, out, ws, (size_t)DQ_NOALLOC_SCRATCH_BYTES, stream, nullptr,
+                     nullptr);
 }
