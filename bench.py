@@ -336,6 +336,156 @@ def cpu_baseline(w, ck, cv, kc, kn, vc, vn, q, starts, ctx, seconds):
             "encode_vectors_per_s": xk.shape[0] * w.hkv / enc_s}
 
 
+OTHER_WORKLOADS = ["tiny_1seq_1k", "qwen3_8b_b16_8k", "longctx_b4_64k_c29", "ragged_32seq_4k_128k"]
+MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MB MALL: written between timed launches
+
+
+def oracle_attention_rate(w, ck, cv, kc, kn, vc, vn, q, starts, ctx, seconds):
+    """The oracle's fp64 decode attention on a bounded sample of a workload:
+    whole sequences in order until ~`seconds` of CPU work (at least one, cut
+    to its first 16384 tokens if longer), on the host cores this process may
+    use.  Returns (context tokens/s, threads, sample text)."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    ock = oracle.Codec(ck.levels, ck.C, seed=ck.seed, hkv=ck.kv_heads, step64=ck.step64)
+    ocv = oracle.Codec(cv.levels, cv.C, seed=cv.seed, hkv=cv.kv_heads, step64=cv.step64)
+    qb = synth.bf16_bits(q)
+    tokens, elapsed, n = 0, 0.0, 0
+    while (elapsed < seconds or n == 0) and n < len(ctx):
+        lo = int(starts[n])
+        L = min(int(ctx[n]), 16384)
+        kcs = np.ascontiguousarray(kc[:, lo:lo + L].cpu().numpy())
+        vcs = np.ascontiguousarray(vc[:, lo:lo + L].cpu().numpy())
+        kns, vns = synth.bf16_bits(kn[:, lo:lo + L]), synth.bf16_bits(vn[:, lo:lo + L])
+        t0 = time.perf_counter()
+        oracle.attention(ock, ocv, qb[n:n + 1], kcs, kns, vcs, vns, np.array([0]), np.array([L], np.int32),
+                         nthreads=threads)
+        elapsed += time.perf_counter() - t0
+        tokens += L
+        n += 1
+    return tokens / elapsed, threads, (f"fp64 decode attention of {n} sequence(s), {tokens} context tokens "
+                                       f"x {w.hkv} kv heads, {w.hq} q heads, in {elapsed:.1f} s")
+
+
+def measure_workload(name, steps, warmup, dev, flush, oracle_seconds, copy_gbps=None):
+    """Decode attention (dq_attn_decode) over one workload's prompt, each timed
+    launch preceded by a write of a 512 MB buffer so that no part of the
+    compressed cache is still in the 256 MB MALL; the split-K kernel is timed
+    with HIP events on its stream.  The ragged workload also times its
+    8192-token chunk encode per sequence; the tiny one is a latency figure."""
+    import numpy as np
+    import torch
+
+    import kv_cache_entropy_amd as dq
+    import synth
+    w = synth.workloads()[name]
+    B, Hq, Hkv = w.batch, w.hq, w.hkv
+    ctx = np.array(w.ctx, np.int64)
+    cap = ctx + w.append_tokens + 1
+    starts = np.concatenate([[0], np.cumsum(cap)[:-1]])
+    ck = dq.Codec(w.levels_k, w.container_k, seed=w.seed, kv_heads=Hkv)
+    cv = dq.Codec(w.levels_v, w.container_v, seed=w.seed + 1, kv_heads=Hkv)
+    S = int(cap.sum())
+    kc, kn = dq.alloc_pool(ck, S, dev)
+    vc, vn = dq.alloc_pool(cv, S, dev)
+    T = int(ctx.sum())
+    slots = torch.from_numpy(np.concatenate([np.arange(a, a + L) for a, L in zip(starts, ctx)])).to(dev)
+    for cont, norm, codec, sd in ((kc, kn, ck, 10), (vc, vn, cv, 11)):
+        x = synth.kv_tensor(w.kind, T, Hkv, seed=w.seed + sd, device=dev)
+        dq.encode(codec, x, slots, cont, norm)
+        del x
+    del slots
+    q = synth.q_tensor(B, Hq, seed=w.seed + 100, device=dev)
+    ss = torch.from_numpy(starts).to(dev)
+    sl = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+    max_len = int(ctx.max())
+    # sized for one more token: the tiny workload also times a step with append
+    ws = torch.empty(dq.attn_workspace_bytes(B, Hq, Hkv, max_len + 1), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    alg = T * Hkv * (ck.C + 2 + cv.C + 2)
+    for _ in range(warmup):
+        dq.attn_decode(ck, cv, q, kc, kn, vc, vn, ss, sl, max_len, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    call, split = [], []
+    for _ in range(steps):
+        flush.zero_()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        dq.attn_decode(ck, cv, q, kc, kn, vc, vn, ss, sl, max_len, out=out, workspace=ws,
+                       split_events=(ev[1], ev[2]))
+        ev[3].record()
+        torch.cuda.synchronize()
+        call.append(ev[0].elapsed_time(ev[3]))
+        split.append(ev[1].elapsed_time(ev[2]))
+    call_ms, split_ms = float(np.median(call)), float(np.median(split))
+    achieved = alg / (split_ms / 1e3) / 1e9
+    rec = {"batch": B, "q_heads": Hq, "kv_heads": Hkv, "context": [int(ctx.min()), int(ctx.max())],
+           "context_tokens": T, "container_bytes": [ck.C, cv.C], "kv_distribution": w.kind,
+           "alg_bytes_per_launch": alg, "attn_call_ms": round(call_ms, 4), "split_ms": round(split_ms, 4),
+           "split_ms_p10_p50_p90": pct(split), "call_gbps": round(alg / (call_ms / 1e3) / 1e9, 2),
+           "split_gbps": round(achieved, 2), "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4),
+           "context_tokens_per_s": round(T / (call_ms / 1e3), 1), "timing": "median of "
+           f"{steps} launches, each after a {MALL_FLUSH_BYTES >> 20} MB write that evicts the MALL"}
+    if copy_gbps:
+        rec["frac_of_copy"] = round(achieved / copy_gbps, 4)
+    if name == "tiny_1seq_1k":
+        # latency: the decode step with append in one call, no flush needed
+        k_new = synth.kv_tensor(w.kind, B, Hkv, seed=w.seed + 20, device=dev)
+        v_new = synth.kv_tensor(w.kind, B, Hkv, seed=w.seed + 21, device=dev)
+        sl1 = sl + 1
+        for _ in range(warmup):
+            dq.attn_decode_append(ck, cv, q, k_new, v_new, kc, kn, vc, vn, ss, sl1, max_len + 1, out=out,
+                                  workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            dq.attn_decode_append(ck, cv, q, k_new, v_new, kc, kn, vc, vn, ss, sl1, max_len + 1, out=out,
+                                  workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        rec["append_step_us"] = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+        rec["attn_call_us"] = round(call_ms * 1e3, 2)
+    if w.append_tokens:
+        # the prefill chunk: append_tokens new tokens per sequence, K and V
+        n_app = w.append_tokens
+        aslots = torch.from_numpy(np.concatenate([np.arange(a + L, a + L + n_app)
+                                                  for a, L in zip(starts, ctx)])).to(dev)
+        xk = synth.kv_tensor(w.kind, B * n_app, Hkv, seed=w.seed + 30, device=dev)
+        xv = synth.kv_tensor(w.kind, B * n_app, Hkv, seed=w.seed + 31, device=dev)
+        dq.encode_kv(ck, cv, xk, xv, aslots, kc, kn, vc, vn)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dq.encode_kv(ck, cv, xk, xv, aslots, kc, kn, vc, vn)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ems = float(np.median(times))
+        rec["append_encode"] = {"tokens_per_seq": n_app, "vectors": 2 * B * n_app * Hkv, "ms": round(ems, 3),
+                                "vectors_per_s": round(2 * B * n_app * Hkv / (ems / 1e3), 1)}
+        del xk, xv, aslots
+    if oracle_seconds > 0:
+        rate, thr, sample = oracle_attention_rate(w, ck, cv, kc, kn, vc, vn, q, starts, ctx, oracle_seconds)
+        rec["cpu_oracle"] = {"context_tokens_per_s": round(rate, 1), "cores": thr, "kind": "oracle",
+                             "sample": sample}
+    log(f"[bench] {name}: attention {call_ms:.4f} ms per call (split-K {split_ms:.4f} ms = "
+        f"{achieved:.1f} GB/s = {achieved / HBM_PEAK_GBPS:.2%} of HBM), "
+        f"{rec['context_tokens_per_s'] / 1e9:.3f} G context-tokens/s"
+        + (f"; oracle {rec['cpu_oracle']['context_tokens_per_s']:.0f} context-tokens/s" if "cpu_oracle" in rec else "")
+        + (f"; chunk encode {rec['append_encode']['vectors_per_s'] / 1e9:.2f} G vectors/s"
+           if "append_encode" in rec else "")
+        + (f"; append step {rec['append_step_us']} us" if "append_step_us" in rec else ""))
+    del kc, kn, vc, vn, ws, out, q
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +499,12 @@ def main():
                     help="skip the two-launch and small-batch timings of the decode step")
     ap.add_argument("--no-rd", action="store_true", help="skip the rate-distortion drift-order encode")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill attention timing")
+    ap.add_argument("--splitk-waves", type=int, default=None,
+                    help="resident waves per CU of the split-K kernel (occupancy study; default: the library's)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the decode-attention timings of the other workloads")
+    ap.add_argument("--others-only", metavar="NAME", nargs="*",
+                    help="time only these other workloads (all four if none named) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter scale for rocprofv3)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -371,6 +527,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.splitk_waves:
+        dq.set_knob("splitk_waves", args.splitk_waves)
+    if args.others_only is not None:
+        flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        res = {n: measure_workload(n, args.steps, args.warmup, dev, flush, 0.0)
+               for n in (args.others_only or OTHER_WORKLOADS)}
+        print(json.dumps({"workloads": res, "attn_source_sha256_16": attn_source_hash()}), flush=True)
+        return
     w = synth.workloads()[args.workload]
     B, Hq, Hkv = w.batch, w.hq, w.hkv
     ctx = np.array(w.ctx, np.int64)
@@ -674,12 +838,40 @@ def main():
         for L in lens_np:
             for qb in range((tq + tb - 1) // tb):
                 read += (L - tq + min(tq, (qb + 1) * tb)) * Hkv * (ck.C + 2 + cv.C + 2)
+        # the method's flops, counted once: every query row against its
+        # causal prefix, QK and PV, 2 flops per multiply-add, all Hq heads
+        flops = 0
+        for L in lens_np:
+            vis = np.arange(L - tq + 1, L + 1, dtype=np.int64)  # keys each query row sees
+            flops += int(vis.sum()) * Hq * 128 * 2 * 2
+        syms = read // (ck.C + 2 + cv.C + 2) * 256  # K and V symbols the kernel decodes
+        tflops = flops / (pms / 1e3) / 1e12
         prefill = {"batch": nb, "chunk_tokens": tq, "context": int(lens_np.max()), "call_ms": round(pms, 3),
                    "query_tokens_per_s": round(nb * tq / (pms / 1e3), 1),
-                   "kv_bytes_read_gbps": round(read / (pms / 1e3) / 1e9, 1), "rows_per_item": tb * group}
+                   "kv_bytes_read_gbps": round(read / (pms / 1e3) / 1e9, 1), "rows_per_item": tb * group,
+                   "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0,
+                                "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
+                                "flops_per_call": flops, "dtype": "fp16 (hi/lo pairs: 2 MFMAs per product)",
+                                "kernel": "attn_prefill_shared_kernel" if max(ck.C, cv.C) <= 35
+                                else "attn_prefill_kernel"},
+                   "decoded_symbols_per_s": round(syms / (pms / 1e3), 1)}
         log(f"[bench] chunked prefill: {nb} x {tq} queries over {prefill['context']} tokens in {pms:.2f} ms "
-            f"({prefill['query_tokens_per_s'] / 1e3:.1f} K query tokens/s, {prefill['kv_bytes_read_gbps']} GB/s read)")
+            f"({prefill['query_tokens_per_s'] / 1e3:.1f} K query tokens/s, {prefill['kv_bytes_read_gbps']} GB/s read, "
+            f"{tflops:.1f} TFLOP/s = {tflops / 2500.0:.2%} of fp16 MFMA peak, "
+            f"{syms / (pms / 1e3) / 1e9:.1f} G symbols/s decoded)")
         del qp, wsp, outp
+
+    # the other workloads: decode attention over each prompt, the MALL
+    # evicted before every timed launch, with the oracle on a bounded sample
+    others = None
+    if not args.no_others:
+        del ws
+        torch.cuda.empty_cache()
+        flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        others = {n: measure_workload(n, max(args.steps, 10), 3, dev, flush,
+                                      0.0 if args.no_cpu_baseline else 2.0, copy_gbps)
+                  for n in OTHER_WORKLOADS}
+        del flush
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -718,6 +910,7 @@ def main():
         "paged_attn": paged,
         "rd_drift_order": rd,
         "prefill_attn": prefill,
+        "workloads": others,
         "cpu_baseline": cpu,
         "attn_context_tokens_per_s": round(ctx_tokens / (sum(att_ms) / 1e3), 1),
         "prefill_encode_vectors_per_s": round(prefill_vps, 1),

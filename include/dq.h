@@ -50,7 +50,7 @@ typedef void *dq_stream_t; /* hipStream_t */
 const char *dq_status_string(int status);
 
 /* ABI version: 100 * major + minor (101: dq_codec_desc.drift_order; 102: decode
- * with append; 103: dq_set_knob). */
+ * with append; 103: dq_set_knob, dq_attn_decode_noalloc). */
 int dq_version(void);
 
 /* Path overrides, for tests and tuning.  Every value the library can pick by
@@ -68,6 +68,13 @@ int dq_version(void);
  *   DQ_KNOB_ENCODE_KEY_SPAN  span of the encoder's in-group integer keys
  *                            (smaller spans take the float-scan fallback
  *                            sooner; same bytes)
+ *   DQ_KNOB_SPLITK_WAVES     resident waves per CU of the decode split-K
+ *                            kernel, 1..11 (fewer than the library's 12:
+ *                            occupancy studies; same bytes)
+ *   DQ_KNOB_WORK_QUEUE       1: split-K waves take their items from a device
+ *                            work queue, 0: by the static deal (the library
+ *                            uses the queue when the items take several
+ *                            rounds of resident waves; same bytes)
  * dq_set_knob returns DQ_ERR_INVALID for an unknown knob or a value below
  * -1; dq_get_knob returns the value (or DQ_ERR_INVALID). */
 enum {
@@ -76,7 +83,9 @@ enum {
   DQ_KNOB_APPEND_FUSE = 3,
   DQ_KNOB_ENCODE_WAVE_MAX = 4,
   DQ_KNOB_ENCODE_KEY_SPAN = 5,
-  DQ_KNOB_COUNT = 6
+  DQ_KNOB_SPLITK_WAVES = 6,
+  DQ_KNOB_WORK_QUEUE = 7,
+  DQ_KNOB_COUNT = 8
 };
 int dq_set_knob(int knob, int64_t value);
 int64_t dq_get_knob(int knob);

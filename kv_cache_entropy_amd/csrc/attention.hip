@@ -91,6 +91,9 @@ struct AttnArgs {
   float *part_new;  // [B][Hkv][4][kPart]: the new token's own partial
   int64_t n_enc;    // encode items run by the split-K launch (0: a launch of their own ran them)
   int skip_last;    // 1 with an append: the chunks cover the len - 1 older tokens
+  // work queue: null, or a counter (zero at launch) from which each wave
+  // takes its next item, for launches whose items take several rounds
+  unsigned int *queue;
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -596,8 +599,19 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
   // then the attention items, each one chunk of one (b, g)
   const int64_t n_enc = APPEND ? a.n_enc : 0;
   const int64_t n_half = (int64_t)a.B * a.Hkv;
-  int64_t it = (int64_t)blockIdx.x * a.waves_per_block + wave;
-  for (; APPEND && it < n_enc; it += W) {
+  // items in turn: statically every W-th one, or from the work queue.  The
+  // static deal suits one round of equal items; a ragged batch over several
+  // rounds would leave one wave all the chunks of a long sequence (the
+  // deal repeats with period W, a multiple of B * Hkv), so there each wave
+  // takes the next item from the queue when it is done with one.
+  auto grab = [&](int64_t cur) -> int64_t {
+    if (!a.queue) return cur + W;
+    unsigned int t = 0u;
+    if (lane == 0) t = atomicAdd(a.queue, 1u);
+    return (int64_t)(unsigned int)__shfl((int)t, 0);
+  };
+  int64_t it = a.queue ? grab(0) : (int64_t)blockIdx.x * a.waves_per_block + wave;
+  for (; APPEND && it < n_enc; it = grab(it)) {
     const bool isv = it >= n_half;
     const int64_t e = isv ? it - n_half : it;
     const int b = (int)(e / a.Hkv), g = (int)(e - (int64_t)(e / a.Hkv) * a.Hkv);
@@ -616,7 +630,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
   // c, c + W / nbg, ..., which pairs the one-tile-longer first chunks with
   // the shorter last ones when the items fill whole rounds
   const int64_t nbg = (int64_t)a.B * a.Hkv;
-  for (; it < n_enc + a.n_items; it += W) {
+  for (; it < n_enc + a.n_items; it = grab(it)) {
     const int64_t item = it - n_enc;
     const int c = (int)(item / nbg);
     const int64_t bg = item - (int64_t)c * nbg;
@@ -754,6 +768,12 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 
     write_partial(a.part + pidx * 4 * kPart, acc, m_run, l_lane, lane);
   }
+}
+
+// Zeroes the split-K work queue's counter (a kernel, not a memset, so the
+// call stays capturable in a HIP graph).
+__global__ void __launch_bounds__(64) queue_reset_kernel(unsigned int *counter) {
+  if (threadIdx.x == 0) *counter = 0u;
 }
 
 // ---------------------------------------------------------------- combine
@@ -1580,7 +1600,7 @@ struct Plan {
   int chunk, nc, cq, cr, waves_per_block, blocks_cap, nq;
   bool lat;  // latency mode (whole V tiles in LDS, fewer waves per CU)
   int64_t n_items;
-  size_t lds, qrot_bytes, part_bytes, part_new_bytes, total;
+  size_t lds, qrot_bytes, part_bytes, part_new_bytes, queue_bytes, total;
 };
 
 // CU count of the current device, read once per process (thread-safe static
@@ -1640,6 +1660,8 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   const int wb = wave_layout(Ck, Cv).bytes;
   const int lds_cap = 160 * 1024;
   int wpb = pl->nq == 3 ? 12 : 4;  // three waves per SIMD when the LDS allows (larger C: fewer)
+  const int64_t forced_w = knob(DQ_KNOB_SPLITK_WAVES);
+  if (forced_w >= 1 && forced_w < wpb) wpb = (int)forced_w;
   while (wpb > 1 && kStaticLds + wpb * wb > lds_cap) wpb -= wpb > 4 ? 4 : 1;
   if (kStaticLds + wpb * wb > lds_cap) return DQ_ERR_UNSUPPORTED;
   // chunk: aim for ~8 items per resident wave (8 waves per CU) if every
@@ -1674,7 +1696,8 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   pl->qrot_bytes = 0;  // each item rotates its own query
   pl->part_bytes = ((size_t)pl->n_items * 4 * kPart * sizeof(float) + 255) & ~(size_t)255;
   pl->part_new_bytes = (size_t)B * Hkv * 4 * kPart * sizeof(float);  // the append's own partials
-  pl->total = pl->qrot_bytes + pl->part_bytes + pl->part_new_bytes;
+  pl->queue_bytes = 256;  // the work queue's counter
+  pl->total = pl->qrot_bytes + pl->part_bytes + pl->part_new_bytes + pl->queue_bytes;
   return DQ_OK;
 }
 
@@ -1978,7 +2001,18 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
     a.n_enc = fuse ? n_enc : 0;
     a.skip_last = 1;
   }
+  // the work queue when the items take several rounds of resident waves
+  {
+    const int64_t W = (int64_t)pl.blocks_cap * pl.waves_per_block;
+    bool queue = !pl.lat && pl.n_items + a.n_enc > W;
+    const int64_t forced = dq::knob(DQ_KNOB_WORK_QUEUE);  // tests force either way
+    if (forced >= 0) queue = forced == 1;
+    if (queue)
+      a.queue = reinterpret_cast<unsigned int *>(static_cast<uint8_t *>(workspace) + pl.qrot_bytes +
+                                                 pl.part_bytes + pl.part_new_bytes);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.queue) hipLaunchKernelGGL(dq::queue_reset_kernel, dim3(1), dim3(64), 0, s, a.queue);
   if (app && a.n_enc == 0) {
     const int C = ck->t.C > cv->t.C ? ck->t.C : cv->t.C;
     const size_t lds = (size_t)dq::kAppendWaves * ((dq::append_scratch_bytes(C) + 15) & ~15);

@@ -420,6 +420,41 @@ def test_attention_latency_mode_bit_identical(oracle_lib, knob, Hq, hkv, lens, C
     _assert_close(res["1"][0].cpu().numpy(), _oracle_attn(O, c), f"latency mode Hq={Hq} hkv={hkv}")
 
 
+@pytest.mark.parametrize("Hq,hkv,lens,split", [
+    (32, 8, [6400, 70, 3000, 1], 64),
+    (8, 2, [20000, 640, 5, 12000, 129], 64),
+    (4, 4, [9000, 9001, 64, 65], 128),
+])
+def test_attention_work_queue(oracle_lib, knob, Hq, hkv, lens, split):
+    """Ragged batches whose items take several rounds of resident waves:
+    split-K waves taking items from the device work queue give the same
+    bytes as the static deal (each item's arithmetic does not depend on the
+    wave that runs it), plain and with append (the queue also hands out the
+    encode items when they ride in the launch), and match the oracle."""
+    O = oracle_lib
+    knob("split_tokens", split)
+    c = _attn_case(O, len(lens), Hq, hkv, lens, seed=151 + Hq)
+    B = len(lens)
+    k_new = synth.kv_tensor("outlier", B, hkv, seed=161, device=DEV)
+    v_new = synth.kv_tensor("outlier", B, hkv, seed=162, device=DEV)
+    res = {}
+    for mode in (0, 1):
+        knob("work_queue", mode)
+        plain = _gpu_attn(c)
+        fused = []
+        for fuse in (0, 1):
+            knob("append_fuse", fuse)
+            (_, _, _), (pb, sb, ob) = _append_both(c, k_new, v_new, max(lens) + 1)[0]
+            fused.append((ob, pb))
+        res[mode] = (plain, fused)
+    assert torch.equal(res[0][0], res[1][0]), "queue and static deal differ"
+    for (o0, p0), (o1, p1) in zip(res[0][1], res[1][1]):
+        assert torch.equal(o0, o1)
+        for x, y in zip(p0, p1):
+            assert torch.equal(x, y)
+    _assert_close(res[1][0].cpu().numpy(), _oracle_attn(O, c), f"work queue Hq={Hq} hkv={hkv}")
+
+
 def test_decode_step_graph_replay(oracle_lib):
     """A decode step with append captured once in a HIP graph
     (torch.cuda.CUDAGraph over the library's launches, which go to the
