@@ -501,6 +501,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill attention timing")
     ap.add_argument("--splitk-waves", type=int, default=None,
                     help="resident waves per CU of the split-K kernel (occupancy study; default: the library's)")
+    ap.add_argument("--knob", action="append", default=[], metavar="NAME=VALUE",
+                    help="force a library path (dq_set_knob) for a study, e.g. slot_table=0")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the decode-attention timings of the other workloads")
     ap.add_argument("--others-only", metavar="NAME", nargs="*",
@@ -529,6 +531,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.splitk_waves:
         dq.set_knob("splitk_waves", args.splitk_waves)
+    for kv in args.knob:
+        name, value = kv.split("=")
+        dq.set_knob(name, int(value))
     if args.others_only is not None:
         flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device=dev)
         res = {n: measure_workload(n, args.steps, args.warmup, dev, flush, 0.0)

@@ -75,6 +75,9 @@ int dq_version(void);
  *                            work queue, 0: by the static deal (the library
  *                            uses the queue when the items take several
  *                            rounds of resident waves; same bytes)
+ *   DQ_KNOB_SLOT_TABLE       0: decode steps read the slot's symbol, then its
+ *                            entry (two LDS round trips); 1 (default where
+ *                            the 64 KB fit): one per-slot entry (same bytes)
  * dq_set_knob returns DQ_ERR_INVALID for an unknown knob or a value below
  * -1; dq_get_knob returns the value (or DQ_ERR_INVALID). */
 enum {
@@ -85,7 +88,8 @@ enum {
   DQ_KNOB_ENCODE_KEY_SPAN = 5,
   DQ_KNOB_SPLITK_WAVES = 6,
   DQ_KNOB_WORK_QUEUE = 7,
-  DQ_KNOB_COUNT = 8
+  DQ_KNOB_SLOT_TABLE = 8,
+  DQ_KNOB_COUNT = 9
 };
 int dq_set_knob(int knob, int64_t value);
 int64_t dq_get_knob(int knob);

@@ -48,12 +48,18 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kTile = 64;
 static_assert(kTile == DQ_PAGE_TOKENS, "a page is one attention tile");
 constexpr int kVtStride = 66;    // halves per V-tile row: 33 dwords, spreads LDS banks
-constexpr int kPass = 32;        // dims per V-tile pass
+constexpr int kPass = 32;        // dims per V-tile pass (per-block prefill)
+constexpr int kDPass = 16;       // dims per V-tile pass (decode attention)
 constexpr int kPart = 132;       // floats per (item, head): acc[128], m, l, pad
 constexpr int kLutBytes = 2 * kDecodeTableBytes;  // K and V decode tables
 // K and V encoder constants of the append (etab, rdtab), static too
 constexpr int kAppendLdsBytes = 2 * (kMaxLevels * 16 + kMaxHalf * 8);
 constexpr int kStaticLds = kLutBytes + kAppendLdsBytes;
+// Per-slot decode tables (slot -> {f, cum | fp16 level << 16}), 32 KB per
+// codec: one LDS read per decode step instead of a byte read and a
+// dependent entry read.
+constexpr int kSlotTableBytes = (int)kM * 8;
+constexpr int kSlotLds = 2 * kSlotTableBytes + 2 * kSymTabBytes + kAppendLdsBytes + 16;
 
 struct AttnArgs {
   const uint16_t *q;
@@ -176,7 +182,7 @@ __host__ __device__ inline WaveLayout wave_layout(int Ck, int Cv, bool full_v = 
   w.vst = w.kst + ((kTile * Ck + 31) & ~15);
   w.pl = w.vst + ((kTile * Cv + 31) & ~15);
   w.vt = w.pl + 2 * 4 * kTile * 2;  // P: [head][token quad][hi x4, lo x4] fp16
-  w.bytes = w.vt + (full_v ? kD : kPass) * kVtStride * 2;
+  w.bytes = w.vt + (full_v ? kD : kDPass) * kVtStride * 2;
   w.bytes = (w.bytes + 15) & ~15;
   return w;
 }
@@ -234,6 +240,7 @@ __device__ __forceinline__ int lane_token(int lane) { return ((lane & 31) << 1) 
 struct DecTab {
   const uint8_t *sym8;
   const uint2 *symtab;
+  const uint2 *ent;  // per-slot entries (null: sym8 and symtab)
 };
 
 // Byte renormalisation.  Stream positions are 32-bit LDS addresses.  The
@@ -266,6 +273,11 @@ __device__ __forceinline__ uint2 lookup_symtab(const DecTab &t, uint32_t s8) {
   const u32x2 e = *(lds_u32x2 *)to_lds(reinterpret_cast<const uint8_t *>(t.symtab) + s8);
   return make_uint2(e.x, e.y);
 }
+// The entry of x's slot from the per-slot table: one read per step.
+__device__ __forceinline__ uint2 lookup_slot(const DecTab &t, uint32_t x) {
+  const u32x2 e = *(lds_u32x2 *)to_lds(reinterpret_cast<const uint8_t *>(t.ent) + ((x & (kM - 1)) << 3));
+  return make_uint2(e.x, e.y);
+}
 
 // f(std::integral_constant<int, i>()) for i = 0 .. N-1, so that i can feed
 // the constant operands of a builtin (the MFMA broadcast block)
@@ -279,22 +291,29 @@ __device__ __forceinline__ void unroll(F &&f) {
 }
 
 
-// P (hi, lo) x the 32 dims of V-tile rows starting at vrow: 16 MFMAs whose
-// blocks are (8 dim quads) x (2 token halves); token quad 8 h + c of P sits
-// in block c of half h and is broadcast within the half (cbsz 3, abid c).
+// P (hi, lo) x the 16 dims of a V-tile pass: 8 MFMAs whose blocks are (4
+// dim quads) x (4 token quarters).  Token quad 4 q + c of P sits in block c
+// of quarter q and is broadcast within the quarter (cbsz 2, abid c); vrow is
+// this lane's row (dim lane mod 16) at its quarter's tokens (16 (lane / 16)
+// onwards).  The hi and lo products accumulate into the same registers, hi
+// first: the partial of each dim is summed over the quarters at the end.
 template <int P>
 __device__ __forceinline__ void pv_pass(const uint32_t *vrow, half4 Ph, half4 Pl, floatx4 (&acc)[8]) {
-  unroll<8>([&](auto cc) {
+  // the pass's four operands are read first: one LDS round trip, not four
+  half4 V[4];
+  unroll<4>([&](auto cc) {
     constexpr int c = decltype(cc)::value;
-    const half4 V = __builtin_bit_cast(half4, make_uint2(vrow[2 * c], vrow[2 * c + 1]));
-    // hi and lo accumulate separately: two independent MFMA chains
-    acc[P] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ph, V, acc[P], 3, c, 0);
-    acc[4 + P] = __builtin_amdgcn_mfma_f32_4x4x4f16(Pl, V, acc[4 + P], 3, c, 0);
+    V[c] = __builtin_bit_cast(half4, make_uint2(vrow[2 * c], vrow[2 * c + 1]));
+  });
+  unroll<4>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    acc[P] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ph, V[c], acc[P], 2, c, 0);
+    acc[P] = __builtin_amdgcn_mfma_f32_4x4x4f16(Pl, V[c], acc[P], 2, c, 0);
   });
 }
 
-// This lane's P operand: 16 bytes (hi x4, lo x4) of token quad 8 h + lane/4
-// mod 8 for head lane mod 4, read once per tile.
+// This lane's P operand: 16 bytes (hi x4, lo x4) of token quad lane / 4 for
+// head lane mod 4, read once per tile.
 __device__ __forceinline__ void load_p(const uint16_t *pl, int lane, half4 &Ph, half4 &Pl) {
   const int th = lane >> 5, row = lane & 31;
   const uint4 pq = *reinterpret_cast<const uint4 *>(pl + ((lane & 3) * 16 + th * 8 + (row >> 2)) * 8);
@@ -310,23 +329,22 @@ __device__ __forceinline__ void load_p(const uint16_t *pl, int lane, half4 &Ph, 
 //   16 + b, one head each, hi then lo) and is broadcast to every block
 //   (cbsz 4, abid G mod 16).  The lane's own 4 levels are the B column, and
 //   the lane ends with its token's scores for the 4 heads.
-// V: levels go to the transposed LDS tile, 32 dims per pass; each pass is
-//   contracted with P (hi, then lo) by 16 MFMAs whose blocks are (8 dim
-//   quads) x (2 token halves).  P of token quad 8 h + c sits in block c of
-//   half h and is broadcast within the half (cbsz 3, abid c); it is read
-//   from LDS once per tile.
+// V: levels go to the transposed LDS tile, 16 dims per pass; each pass is
+//   contracted with P (hi, then lo) by pv_pass.  P is read from LDS once
+//   per tile.
+// SLOT: each step reads its entry from the per-slot table (one LDS round
+// trip); otherwise the slot's symbol, then the symbol's entry.
 //
 // FULLV (latency mode): K and V of the same tile; the V levels of all 128
 // dims stay in the V tile for pv_full after the tile's softmax, and no PV
 // runs inside the pass.
-template <bool DK, bool DV, bool FULLV = false>
+template <bool DK, bool DV, bool FULLV = false, bool SLOT = false>
 __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
                                           const uint8_t *vb, const uint4 (&qreg)[2], const uint16_t *pl,
                                           uint16_t *vt, floatx4 &sc, floatx4 (&acc)[8], int lane) {
-  const int th = lane >> 5, row = lane & 31;
   half4 Ph = {}, Pl = {};
   if (DV && !FULLV) load_p(pl, lane, Ph, Pl);
-  const uint32_t *vrow = reinterpret_cast<const uint32_t *>(vt) + row * (kVtStride / 2) + th * 16;
+  const uint32_t *vrow = reinterpret_cast<const uint32_t *>(vt) + (lane & 15) * (kVtStride / 2) + (lane >> 4) * 8;
   uint32_t xk = 0, xv = 0;
   lds_u8 *pk = nullptr, *pv = nullptr;
   if (DK) {
@@ -338,24 +356,30 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
     pv = to_lds(vb + 4);
   }
   uint16_t *col = vt + lane;
-  unroll<4>([&](auto pc) {
+  unroll<kD / kDPass>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
-    unroll<kPass / 4>([&](auto gc) {
+    unroll<kDPass / 4>([&](auto gc) {
       constexpr int gq = decltype(gc)::value;
-      constexpr int G = p * (kPass / 4) + gq;
+      constexpr int G = p * (kDPass / 4) + gq;
       uint32_t lv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // the two chains' loads are issued in this order (volatile), so
         // each LDS round trip of one chain overlaps the other's
-        uint32_t bk = 0, bv = 0, sk = 0, sv = 0;
+        uint32_t bk = 0, bv = 0;
         uint2 ek = make_uint2(0, 0), ev = make_uint2(0, 0);
         if (DK) bk = next_byte(pk);
         if (DV) bv = next_byte(pv);
-        if (DK) sk = lookup_sym8(tk, xk);
-        if (DV) sv = lookup_sym8(tv, xv);
-        if (DK) ek = lookup_symtab(tk, sk);
-        if (DV) ev = lookup_symtab(tv, sv);
+        if (SLOT) {
+          if (DK) ek = lookup_slot(tk, xk);
+          if (DV) ev = lookup_slot(tv, xv);
+        } else {
+          uint32_t sk = 0, sv = 0;
+          if (DK) sk = lookup_sym8(tk, xk);
+          if (DV) sv = lookup_sym8(tv, xv);
+          if (DK) ek = lookup_symtab(tk, sk);
+          if (DV) ev = lookup_symtab(tv, sv);
+        }
         if (DK) {
           xk = rans_advance(xk, ek);
           renorm(xk, pk, bk);
@@ -364,7 +388,7 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
         if (DV) {
           xv = rans_advance(xv, ev);
           renorm(xv, pv, bv);
-          col[((FULLV ? p * kPass : 0) + gq * 4 + j) * kVtStride] = (uint16_t)(ev.y >> 16);
+          col[((FULLV ? p * kDPass : 0) + gq * 4 + j) * kVtStride] = (uint16_t)(ev.y >> 16);
         }
       }
       if (DK) {
@@ -389,13 +413,12 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
 // Latency mode: PV of a whole tile whose V levels (128 dims) are in vt and
 // whose P is in pl.
 __device__ __forceinline__ void pv_full(const uint16_t *pl, const uint16_t *vt, floatx4 (&acc)[8], int lane) {
-  const int th = lane >> 5, row = lane & 31;
   half4 Ph, Pl;
   load_p(pl, lane, Ph, Pl);
   const uint32_t *v32 = reinterpret_cast<const uint32_t *>(vt);
-  unroll<4>([&](auto pc) {
+  unroll<kD / kDPass>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
-    pv_pass<p>(v32 + (p * kPass + row) * (kVtStride / 2) + th * 16, Ph, Pl, acc);
+    pv_pass<p>(v32 + (p * kDPass + (lane & 15)) * (kVtStride / 2) + (lane >> 4) * 8, Ph, Pl, acc);
   });
 }
 
@@ -457,18 +480,19 @@ __device__ __forceinline__ void softmax_tile(const floatx4 &sc, uint32_t nk_bits
   }
 }
 
-// An item's partial: the two token halves of every dim are summed across
-// lanes l and l ^ 32; lanes 0..31 hold dims 32p + l.  Then m and the
-// wave-summed l of each head.
+// An item's partial: the four token quarters of every dim are summed
+// across lanes l, l ^ 16, l ^ 32, l ^ 48; lanes 0..15 hold dims 16p + l.
+// Then m and the wave-summed l of each head.
 __device__ __forceinline__ void write_partial(float *dst, const floatx4 (&acc)[8], const float (&m_run)[4],
                                               const float (&l_lane)[4], int lane) {
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
+  for (int p = 0; p < kD / kDPass; ++p) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float a2 = acc[p][h] + acc[4 + p][h];
-      const float v = a2 + __shfl_xor(a2, 32);
-      if (lane < 32) dst[h * kPart + p * kPass + lane] = v;
+      float v = acc[p][h];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 16) dst[h * kPart + p * kDPass + lane] = v;
     }
   }
 #pragma unroll
@@ -561,18 +585,27 @@ __device__ __forceinline__ void append_vector(const AttnArgs &a, const Tables &t
 // takes n passes instead of n + 1 (a K-only first and a V-only last), at
 // the price of a whole V tile in LDS and so fewer waves per CU.  The
 // arithmetic and its order are those of the pipelined mode.
-template <int NQ, bool APPEND, bool LAT = false>
+// SLOT: the per-slot decode tables (64 KB for K and V), so a decode step is
+// one LDS round trip; otherwise the byte table and the symbol entries.
+template <int NQ, bool APPEND, bool LAT = false, bool SLOT = false>
 __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnArgs a, Tables tk, Tables tv) {
+  static_assert(!(LAT && SLOT), "latency mode keeps the byte tables: its whole V tiles leave no room");
   // decode tables at fixed LDS addresses (static), per-wave slices after them
-  __shared__ uint8_t sym8[2][kM];
+  __shared__ uint2 slot_ent[2][SLOT ? kM : 1];
+  __shared__ uint8_t sym8[2][SLOT ? 1 : kM];
   __shared__ uint2 symtab[2][kMaxLevels];
   __shared__ uint4 etab[2][APPEND ? kMaxLevels : 1];
   __shared__ float2 rdtab[2][APPEND ? kMaxHalf : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const DecTab dk{sym8[0], symtab[0]};
-  const DecTab dv{sym8[1], symtab[1]};
-  build_tables(sym8[0], symtab[0], tk, threadIdx.x, blockDim.x);
-  build_tables(sym8[1], symtab[1], tv, threadIdx.x, blockDim.x);
+  const DecTab dk{sym8[0], symtab[0], SLOT ? slot_ent[0] : nullptr};
+  const DecTab dv{sym8[1], symtab[1], SLOT ? slot_ent[1] : nullptr};
+  if (SLOT) {
+    build_slot_tables(slot_ent[0], symtab[0], tk, threadIdx.x, blockDim.x);
+    build_slot_tables(slot_ent[1], symtab[1], tv, threadIdx.x, blockDim.x);
+  } else {
+    build_tables(sym8[0], symtab[0], tk, threadIdx.x, blockDim.x);
+    build_tables(sym8[1], symtab[1], tv, threadIdx.x, blockDim.x);
+  }
   if (APPEND) {
     wave_encode_tables(tk, etab[0], rdtab[0], threadIdx.x);
     wave_encode_tables(tv, etab[1], rdtab[1], threadIdx.x);
@@ -732,7 +765,7 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 #pragma unroll
     for (int p = 0; p < 8; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
     floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-    tile_pass<true, false>(dk, dv, kst + koff0 + tok * Ck, nullptr, qreg, pl, vt, sc, acc, lane);
+    tile_pass<true, false, false, SLOT>(dk, dv, kst + koff0 + tok * Ck, nullptr, qreg, pl, vt, sc, acc, lane);
     softmax_tile(sc, nk0, nv0, tok < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
 
     for (int j = 0; j < ntiles; ++j) {
@@ -757,10 +790,11 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
       }
       if (next) {
         sc = floatx4{0.f, 0.f, 0.f, 0.f};
-        tile_pass<true, true>(dk, dv, kst + koff + tok * Ck, vst + voff + tok * Cv, qreg, pl, vt, sc, acc, lane);
+        tile_pass<true, true, false, SLOT>(dk, dv, kst + koff + tok * Ck, vst + voff + tok * Cv, qreg, pl, vt, sc,
+                                           acc, lane);
         softmax_tile(sc, nk1, nv1, (j + 1) * kTile + tok < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
       } else {
-        tile_pass<false, true>(dk, dv, nullptr, vst + voff + tok * Cv, qreg, pl, vt, sc, acc, lane);
+        tile_pass<false, true, false, SLOT>(dk, dv, nullptr, vst + voff + tok * Cv, qreg, pl, vt, sc, acc, lane);
       }
       nk1 = nk2;
       nv1 = nv2;
@@ -1598,7 +1632,8 @@ __global__ void __launch_bounds__(128) prefill_combine_kernel(AttnArgs a, uint64
 // ---------------------------------------------------------------- planning
 struct Plan {
   int chunk, nc, cq, cr, waves_per_block, blocks_cap, nq;
-  bool lat;  // latency mode (whole V tiles in LDS, fewer waves per CU)
+  bool lat;   // latency mode (whole V tiles in LDS, fewer waves per CU)
+  bool slot;  // per-slot decode tables (one LDS round trip per decode step)
   int64_t n_items;
   size_t lds, qrot_bytes, part_bytes, part_new_bytes, queue_bytes, total;
 };
@@ -1692,6 +1727,16 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
       pl->lds = (size_t)lwpb * lwb;
     }
   }
+  // per-slot tables where their 64 KB fit beside the waves' slices
+  // (containers up to 38 bytes at 12 waves); DQ_KNOB_SLOT_TABLE forces them
+  // off (0) or on (1, where they fit)
+  pl->slot = false;
+  if (!pl->lat && pl->nq == 3) {
+    bool slot = kSlotLds + pl->waves_per_block * wb <= lds_cap;
+    const int64_t forced = knob(DQ_KNOB_SLOT_TABLE);
+    if (forced == 0) slot = false;
+    pl->slot = slot;
+  }
   pl->blocks_cap = cus;  // one block per CU at most; fewer when the items are few
   pl->qrot_bytes = 0;  // each item rotates its own query
   pl->part_bytes = ((size_t)pl->n_items * 4 * kPart * sizeof(float) + 255) & ~(size_t)255;
@@ -1701,19 +1746,19 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   return DQ_OK;
 }
 
-template <int NQ, bool APPEND, bool LAT = false>
+template <int NQ, bool APPEND, bool LAT = false, bool SLOT = false>
 hipError_t launch_splitk(const Plan &pl, const AttnArgs &a, const Tables &tk, const Tables &tv, hipStream_t s) {
   // dynamic LDS beyond the default limit, requested once (thread-safe static)
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ, APPEND, LAT>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kStaticLds);
+      hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ, APPEND, LAT, SLOT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - (SLOT ? kSlotLds : kStaticLds));
   if (attr != hipSuccess) return attr;
   // the append's encode items (if this launch runs them) come first, one per wave
   const int64_t n = a.n_items + (APPEND ? a.n_enc : 0);
   const int64_t want = (n + pl.waves_per_block - 1) / pl.waves_per_block;
   const int blocks = (int)(want < pl.blocks_cap ? want : pl.blocks_cap);
-  hipLaunchKernelGGL((attn_splitk_kernel<NQ, APPEND, LAT>), dim3((unsigned)blocks), dim3(64 * pl.waves_per_block),
-                     pl.lds, s, a, tk, tv);
+  hipLaunchKernelGGL((attn_splitk_kernel<NQ, APPEND, LAT, SLOT>), dim3((unsigned)blocks),
+                     dim3(64 * pl.waves_per_block), pl.lds, s, a, tk, tv);
   return hipGetLastError();
 }
 
@@ -2025,6 +2070,9 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
   if (pl.lat)  // latency mode (only for the 3-piece tile fetch)
     e = app && a.n_enc > 0 ? dq::launch_splitk<3, true, true>(pl, a, ck->t, cv->t, s)
                            : dq::launch_splitk<3, false, true>(pl, a, ck->t, cv->t, s);
+  else if (pl.slot)  // three-piece tile fetch with the per-slot tables
+    e = app && a.n_enc > 0 ? dq::launch_splitk<3, true, false, true>(pl, a, ck->t, cv->t, s)
+                           : dq::launch_splitk<3, false, false, true>(pl, a, ck->t, cv->t, s);
   else if (app && a.n_enc > 0)  // the variant with the encode loop only when it has encodes to run
     e = pl.nq == 3   ? dq::launch_splitk<3, true>(pl, a, ck->t, cv->t, s)
         : pl.nq == 5 ? dq::launch_splitk<5, true>(pl, a, ck->t, cv->t, s)

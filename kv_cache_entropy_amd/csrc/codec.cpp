@@ -19,8 +19,8 @@ namespace dq {
 
 // Path overrides set through dq_set_knob: one relaxed atomic load per use,
 // so hot calls read no environment and race with nothing.
-static std::atomic<int64_t> g_knobs[DQ_KNOB_COUNT] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
-static_assert(DQ_KNOB_COUNT == 8, "one initialiser per knob");
+static std::atomic<int64_t> g_knobs[DQ_KNOB_COUNT] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+static_assert(DQ_KNOB_COUNT == 9, "one initialiser per knob");
 
 int64_t knob(int k) { return g_knobs[k].load(std::memory_order_relaxed); }
 

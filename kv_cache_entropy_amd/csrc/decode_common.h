@@ -41,6 +41,23 @@ __device__ __forceinline__ void build_tables(uint8_t *sym8, uint2 *symtab, const
                                  : make_uint2(0u, 0u);
 }
 
+// Per-slot tables: slot u -> the entry of its symbol, {f, cum | fp16 level
+// << 16}.  The 16 entries go to `symtab` first; after a barrier each slot
+// copies its symbol's (the symbol counted as in build_tables).
+__device__ __forceinline__ void build_slot_tables(uint2 *ent, uint2 *symtab, const Tables &t, int tid,
+                                                  int nthreads) {
+  if (tid < kMaxLevels)
+    symtab[tid] = tid < t.levels ? make_uint2(t.freq[tid], (uint32_t)t.cum[tid] | ((uint32_t)t.recon[tid] << 16))
+                                 : make_uint2(0u, 0u);
+  __syncthreads();
+  for (int u = tid; u < (int)kM; u += nthreads) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxLevels; ++k) s += (k < t.levels && (int)t.cum[k] <= u) ? 1u : 0u;
+    ent[u] = symtab[s];
+  }
+}
+
 // The state update of a decode step, given the symbol-table entry e of the
 // symbol that x's slot selects.
 __device__ __forceinline__ uint32_t rans_advance(uint32_t x, uint2 e) {

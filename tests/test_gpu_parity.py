@@ -455,6 +455,43 @@ def test_attention_work_queue(oracle_lib, knob, Hq, hkv, lens, split):
     _assert_close(res[1][0].cpu().numpy(), _oracle_attn(O, c), f"work queue Hq={Hq} hkv={hkv}")
 
 
+@pytest.mark.parametrize("Hq,hkv,lens,C,step64,split", [
+    (8, 2, [1, 63, 64, 65, 300, 129, 2000], (34, 34), (0, 0), None),
+    (4, 4, [5000, 70], (29, 29), (0, 0), 640),
+    (1, 1, [128, 1], (34, 29), (0, 0), 64),
+    (4, 2, [3000, 4097], (38, 29), (66, 0), None),  # the largest container the per-slot tables allow
+])
+def test_attention_slot_tables_bit_identical(oracle_lib, knob, Hq, hkv, lens, C, step64, split):
+    """The per-slot decode tables (one LDS read per step) and the byte table
+    plus symbol entries (two dependent reads) hold the same entries: the
+    pipelined kernel gives the same bytes either way, plain, with append and
+    over a paged pool; and the oracle agrees."""
+    O = oracle_lib
+    knob("latency_mode", 0)
+    if split:
+        knob("split_tokens", split)
+    c = _attn_case(O, len(lens), Hq, hkv, lens, C=C, step64=step64, seed=171 + Hq, gap=64)
+    B = len(lens)
+    k_new = synth.kv_tensor("outlier", B, hkv, seed=181, device=DEV)
+    v_new = synth.kv_tensor("student_t5", B, hkv, seed=182, device=DEV)
+    pools, pages = _paged_copy(c, np.random.default_rng(5))
+    pg = torch.from_numpy(pages).to(DEV)
+    res = {}
+    for mode in (0, 1):
+        knob("slot_table", mode)
+        plain = _gpu_attn(c)
+        (_, _, _), (pb, sb, ob) = _append_both(c, k_new, v_new, max(lens) + 1)[0]
+        paged = dq.attn_decode_paged(c["ck"], c["cv"], c["q"], *pools["K"], *pools["V"], pg, c["sl"],
+                                     int(c["lens"].max()))
+        torch.cuda.synchronize()
+        res[mode] = (plain, ob, paged, pb)
+    for x, y, name in zip(res[0][:3], res[1][:3], ("plain", "append", "paged")):
+        assert torch.equal(x, y), f"{name} differs between table kinds"
+    for x, y in zip(res[0][3], res[1][3]):
+        assert torch.equal(x, y)
+    _assert_close(res[1][0].cpu().numpy(), _oracle_attn(O, c), f"slot tables Hq={Hq} hkv={hkv}")
+
+
 def test_decode_step_graph_replay(oracle_lib):
     """A decode step with append captured once in a HIP graph
     (torch.cuda.CUDAGraph over the library's launches, which go to the
