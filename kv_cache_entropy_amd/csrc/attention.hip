@@ -273,10 +273,18 @@ __device__ __forceinline__ uint2 lookup_symtab(const DecTab &t, uint32_t s8) {
   const u32x2 e = *(lds_u32x2 *)to_lds(reinterpret_cast<const uint8_t *>(t.symtab) + s8);
   return make_uint2(e.x, e.y);
 }
-// The entry of x's slot from the per-slot table: one read per step.
-__device__ __forceinline__ uint2 lookup_slot(const DecTab &t, uint32_t x) {
-  const u32x2 e = *(lds_u32x2 *)to_lds(reinterpret_cast<const uint8_t *>(t.ent) + ((x & (kM - 1)) << 3));
+// The entry of a slot from the per-slot table: one read per step.
+__device__ __forceinline__ uint2 lookup_slot(const DecTab &t, uint32_t slot) {
+  const u32x2 e = *(lds_u32x2 *)to_lds(reinterpret_cast<const uint8_t *>(t.ent) + (slot << 3));
   return make_uint2(e.x, e.y);
+}
+// x's slot, as an opaque value: the table address (slot * 8) and the state
+// update (slot - cum) then share one AND instead of the compiler's
+// (x << 3) & 0x7FF8 beside x & 0xFFF.
+__device__ __forceinline__ uint32_t slot_of(uint32_t x) {
+  uint32_t s = x & (kM - 1);
+  asm("" : "+v"(s));
+  return s;
 }
 
 // f(std::integral_constant<int, i>()) for i = 0 .. N-1, so that i can feed
@@ -366,13 +374,15 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
       for (int j = 0; j < 4; ++j) {
         // the two chains' loads are issued in this order (volatile), so
         // each LDS round trip of one chain overlaps the other's
-        uint32_t bk = 0, bv = 0;
+        uint32_t bk = 0, bv = 0, ak = 0, av = 0;
         uint2 ek = make_uint2(0, 0), ev = make_uint2(0, 0);
         if (DK) bk = next_byte(pk);
         if (DV) bv = next_byte(pv);
         if (SLOT) {
-          if (DK) ek = lookup_slot(tk, xk);
-          if (DV) ev = lookup_slot(tv, xv);
+          if (DK) ak = slot_of(xk);
+          if (DV) av = slot_of(xv);
+          if (DK) ek = lookup_slot(tk, ak);
+          if (DV) ev = lookup_slot(tv, av);
         } else {
           uint32_t sk = 0, sv = 0;
           if (DK) sk = lookup_sym8(tk, xk);
@@ -381,12 +391,12 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
           if (DV) ev = lookup_symtab(tv, sv);
         }
         if (DK) {
-          xk = rans_advance(xk, ek);
+          xk = SLOT ? rans_advance_slot(xk, ak, ek) : rans_advance(xk, ek);
           renorm(xk, pk, bk);
           lv[j] = ek.y;
         }
         if (DV) {
-          xv = rans_advance(xv, ev);
+          xv = SLOT ? rans_advance_slot(xv, av, ev) : rans_advance(xv, ev);
           renorm(xv, pv, bv);
           col[((FULLV ? p * kDPass : 0) + gq * 4 + j) * kVtStride] = (uint16_t)(ev.y >> 16);
         }

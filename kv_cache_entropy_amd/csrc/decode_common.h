@@ -64,6 +64,11 @@ __device__ __forceinline__ uint32_t rans_advance(uint32_t x, uint2 e) {
   return __umul24(e.x, x >> kMBits) + ((x & (kM - 1)) - (e.y & 0xFFFFu));
 }
 
+// The same update with the slot (x mod 4096) already at hand.
+__device__ __forceinline__ uint32_t rans_advance_slot(uint32_t x, uint32_t slot, uint2 e) {
+  return __umul24(e.x, x >> kMBits) + (slot - (e.y & 0xFFFFu));
+}
+
 // One decode step without the renormalisation; returns the symbol-table
 // entry (.y >> 16 = fp16 level) and the symbol.
 __device__ __forceinline__ uint2 rans_step(uint32_t &x, const uint8_t *sym8, const uint2 *symtab, uint32_t &s) {
