@@ -79,15 +79,20 @@ PROFILE_CMDS = {
     "fetch": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
               "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'attn_splitk|copyBuffer' --output-format csv "
               "-d $R/" + PROF + "/fetch -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline "
-              "--no-compare --copy-calibration > $R/" + PROF + "/fetch_bench.json"),
+              "--no-compare --no-others --copy-calibration > $R/" + PROF + "/fetch_bench.json"),
     "write": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
               "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'attn_splitk|copyBuffer' --output-format csv "
               "-d $R/" + PROF + "/write -o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline "
-              "--no-compare --copy-calibration > $R/" + PROF + "/write_bench.json"),
+              "--no-compare --no-others --copy-calibration > $R/" + PROF + "/write_bench.json"),
     "sq": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 "
            "rocprofv3 --pmc " + " ".join(SQ_COUNTERS) + " --kernel-include-regex 'attn_splitk|::encode_kernel<' "
            "--output-format csv -d $R/" + PROF + "/sq -o run -- python3 $R/bench.py --steps 3 --warmup 1 "
-           "--no-cpu-baseline --no-compare --no-rd --no-paged --no-prefill > $R/" + PROF + "/sq_bench.json"),
+           "--no-cpu-baseline --no-compare --no-rd --no-paged --no-prefill --no-others > $R/" + PROF
+           + "/sq_bench.json"),
+    # the 64K-context workload alone (its split-K launches, MALL evicted before each)
+    "trace_c4": ("R=$PWD && mkdir -p $R/" + PROF + " && cd /tmp && export TMPDIR=/tmp && timeout -k 10 600 "
+                 "rocprofv3 --kernel-trace --stats --output-format csv -d $R/" + PROF + "/trace_c4 -o run -- "
+                 "python3 $R/bench.py --others-only longctx_b4_64k_c29 > $R/" + PROF + "/trace_c4_bench.json"),
 }
 
 
@@ -146,29 +151,36 @@ def summarize_profiles(d):
     # per-dispatch durations of the split-K kernels by launch shape: the bench
     # also runs them at batch 1 and 4 (the small-batch comparison), so the
     # figure that must agree with the bench line is the one at its grid
-    disp = {}
+    disp, seqd = {}, {}
     for r in _csv(_find(os.path.join(d, "trace"), "kernel_trace.csv")):
         n = r["Kernel_Name"]
         if "attn_splitk_kernel" not in n:
             continue
         key = (n[n.index("attn_splitk_kernel"):n.index(">") + 1], int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
-        disp.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        disp.setdefault(key, []).append(dur)
+        seqd.setdefault(key, []).append((int(r["Start_Timestamp"]), dur))
     lines += ["", "Split-K kernels per launch shape (rocprofv3 kernel trace, one record per dispatch):", "",
               "| kernel | blocks | launches | avg us | min us | max us |", "|---|---:|---:|---:|---:|---:|"]
     for (kname, blocks), v in sorted(disp.items(), key=lambda kv: (kv[0][0], -kv[0][1])):
         lines.append(f"| `{kname}` | {blocks} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
     # the decode step's split-K variant: the one launched most at the bench's
     # shape (dq_attn_decode_append runs the attention without the encode loop
-    # when its items fill every round of waves, as at batch 128)
+    # when its items fill every round of waves, as at batch 128); the timed
+    # steps are its launches number warmup .. warmup + steps - 1 at that shape
+    # (the two-launch and paged comparisons and the other workloads follow)
     head = sorted(disp.items(), key=lambda kv: (kv[0][1], len(kv[1])))
     kname = head[-1][0][0] if head else "attn_splitk_kernel"
     if head:
-        (kname, blocks), v = head[-1]
+        (kname, blocks), _ = head[-1]
+        seq = sorted(seqd[(kname, blocks)])
+        w0, ns = live["warmup"], live["steps"]
+        v = [dur for _, dur in seq[w0:w0 + ns]]
         lines += ["", f"`{kname}` (the decode step's split-K kernel) at the bench's shape "
-                  f"({blocks} blocks): rocprofv3 average "
-                  f"{sum(v) / len(v):.1f} us over {len(v)} launches (warm-up included); the same run's bench "
-                  f"line measured {rl['avg_launch_ms'] * 1e3:.1f} us with HIP "
-                  f"events around the kernel over the timed steps, {rl['achieved']:.1f} GB/s of compressed "
+                  f"({blocks} blocks), the bench's {ns} timed steps (its launches {w0} .. {w0 + ns - 1} at "
+                  f"that shape): rocprofv3 average {sum(v) / len(v):.1f} us (min {min(v):.1f}, max "
+                  f"{max(v):.1f}); the same run's bench line measured {rl['avg_launch_ms'] * 1e3:.1f} us with "
+                  f"HIP events around the kernel over those steps, {rl['achieved']:.1f} GB/s of compressed "
                   f"bytes = {rl['frac']:.2%} of 8 TB/s."]
     lines += ["", "Bench line of this run:", "", "```", json.dumps(live), "```"]
     with open(os.path.join(out_dir, f"all_kernels_{wl}_trace.md"), "w") as f:
@@ -222,6 +234,45 @@ def summarize_profiles(d):
     print(f"wrote profiles for source {src}: traffic {(fetch_b + write_b) / 1e6:.1f} MB per launch")
     if os.path.isdir(os.path.join(d, "sq")):
         summarize_sq(d, kname, wl, src)
+    if os.path.isdir(os.path.join(d, "trace_c4")):
+        summarize_trace_workload(d, "trace_c4", "longctx_b4_64k_c29", src)
+
+
+def summarize_trace_workload(d, sub, name, src):
+    """Kernel trace of one of the other workloads (`--others-only NAME`):
+    its split-K launches against the bench's own HIP-event figure."""
+    live = _bench_line(os.path.join(d, f"{sub}_bench.json"))
+    if live.get("attn_source_sha256_16") != src:
+        raise SystemExit(f"{sub} run was made on a different attention source")
+    wrec = live["workloads"][name]
+    stats = _csv(_find(os.path.join(d, sub), "kernel_stats.csv"))
+    rows = sorted(((float(r["TotalDurationNs"]), r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
+                    .replace("void ", "").strip(), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                    float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])) for r in stats),
+                  reverse=True)
+    lines = [f"# Kernel trace: decode attention, {name}", "",
+             f"Batch {wrec['batch']}, {wrec['q_heads']} q / {wrec['kv_heads']} kv heads, context "
+             f"{wrec['context'][1]}, containers {wrec['container_bytes'][0]}/{wrec['container_bytes'][1]} bytes, "
+             f"{wrec['kv_distribution']} data; each timed launch preceded by a 512 MB write that evicts the MALL.",
+             "", "Command (from the repository root):", "", "```", PROFILE_CMDS[sub], "```", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for tot, short, calls, avg, mn, mx, pct_ in rows[:10]:
+        lines.append(f"| `{short}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct_:.2f} |")
+    durs = {}
+    for r in _csv(_find(os.path.join(d, sub), "kernel_trace.csv")):
+        n = r["Kernel_Name"]
+        if "attn_splitk_kernel" in n:
+            k = n[n.index("attn_splitk_kernel"):n.index(">") + 1]
+            durs.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    for k, v in sorted(durs.items()):
+        lines += ["", f"`{k}`: {len(v)} launches, rocprofv3 median {sorted(v)[len(v) // 2]:.1f} us (min "
+                  f"{min(v):.1f}, max {max(v):.1f}); the bench's median of its timed launches (HIP events) was "
+                  f"{wrec['split_ms'] * 1e3:.1f} us: {wrec['split_gbps']:.1f} GB/s of compressed bytes = "
+                  f"{wrec['hbm_frac']:.2%} of 8 TB/s."]
+    lines += ["", "Bench output of this run:", "", "```", json.dumps(wrec), "```"]
+    with open(os.path.join(ROOT, "profiles", f"attn_splitk_{name}_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote the {name} trace summary")
 
 
 def summarize_sq(d, kname, wl, src):
