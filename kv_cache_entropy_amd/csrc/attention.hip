@@ -1202,8 +1202,10 @@ __device__ __forceinline__ void prefill_softmax(const floatx4 (&sc)[4], uint32_t
   }
 }
 
+// Larger containers (NQ 5, 9) hold more tile bytes per lane: those variants
+// run one wave per SIMD, with the whole register file, so nothing spills.
 template <int NQ>
-__global__ void __launch_bounds__(512) attn_prefill_kernel(AttnArgs a, Tables tk, Tables tv) {
+__global__ void __launch_bounds__(NQ == 3 ? 512 : 256) attn_prefill_kernel(AttnArgs a, Tables tk, Tables tv) {
   __shared__ uint8_t sym8[2][kM];
   __shared__ uint2 symtab[2][kMaxLevels];
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -1825,7 +1827,7 @@ int make_prefill_plan(int B, int Tq, int Hq, int Hkv, int64_t max_len, int Ck, i
     pl->blocks = (int)(pl->n_items < cus ? pl->n_items : cus);
   } else {
     const int wb = prefill_layout(Ck, Cv).bytes;
-    int wpb = 8;
+    int wpb = pl->nq == 3 ? 8 : 4;  // the kernel's launch bounds
     while (wpb > 1 && kLutBytes + wpb * wb > 160 * 1024) wpb -= 1;
     if (kLutBytes + wpb * wb > 160 * 1024) return DQ_ERR_UNSUPPORTED;
     const int64_t chunk = choose_chunk(qunits, max_len, (int64_t)cus * 8);
