@@ -249,6 +249,8 @@ struct DecTab {
 // load overlaps the table lookups of the step.  The empty asm makes each new
 // position an opaque value, so every step advances the pointer with one
 // add-with-carry instead of re-deriving it from older positions.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef const __attribute__((address_space(3))) uint8_t lds_u8;
 typedef const volatile __attribute__((address_space(3))) uint8_t lds_byte;
 __device__ __forceinline__ lds_u8 *to_lds(const uint8_t *p) {
@@ -262,9 +264,28 @@ __device__ __forceinline__ void renorm(uint32_t &x, lds_u8 *&p, uint32_t byte) {
   asm("" : "+v"(p));
 }
 
+// Renormalisation four steps at a time.  A step shifts in at most one byte,
+// so the 4 stream bytes at p cover a group of 4 steps: they are read once
+// (two aligned dwords, then a byte shift) and each step takes the next one
+// of them.  sel is the v_perm selector of (x << 8) | window byte k: its low
+// byte is k, the number of bytes the group has taken so far.
+typedef const volatile __attribute__((address_space(3))) u32x2_a4 lds_u32x2_a4;
+constexpr uint32_t kSel0 = 0x06050400u;
+__device__ __forceinline__ uint32_t byte_window(lds_u8 *p) {
+  const uint32_t a = (uint32_t)(uintptr_t)p;
+  const u32x2_a4 d = *(lds_u32x2_a4 *)(uintptr_t)(a & ~3u);
+  return __builtin_amdgcn_alignbyte(d.y, d.x, a);  // bytes a .. a + 3
+}
+__device__ __forceinline__ void renorm_window(uint32_t &x, uint32_t w, uint32_t &sel) {
+  const bool need = x < kLow;
+  const uint32_t y = __builtin_amdgcn_perm(x, w, sel);
+  x = need ? y : x;
+  sel += need ? 1u : 0u;
+  asm("" : "+v"(sel));  // one add-with-carry per step; the group's count is sel - kSel0
+}
+
 // The two table reads of a decode step (slot -> 8 * symbol, then the symbol
 // entry), volatile so that their order across chains is kept.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef const volatile __attribute__((address_space(3))) u32x2 lds_u32x2;
 __device__ __forceinline__ uint32_t lookup_sym8(const DecTab &t, uint32_t x) {
   return *(lds_byte *)to_lds(t.sym8 + (x & (kM - 1)));
@@ -370,14 +391,16 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
       constexpr int gq = decltype(gc)::value;
       constexpr int G = p * (kDPass / 4) + gq;
       uint32_t lv[4];
+      // the group's renormalisation bytes (volatile loads, issued first)
+      uint32_t wk = 0, wv = 0, selk = kSel0, selv = kSel0;
+      if (DK) wk = byte_window(pk);
+      if (DV) wv = byte_window(pv);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // the two chains' loads are issued in this order (volatile), so
         // each LDS round trip of one chain overlaps the other's
-        uint32_t bk = 0, bv = 0, ak = 0, av = 0;
+        uint32_t ak = 0, av = 0;
         uint2 ek = make_uint2(0, 0), ev = make_uint2(0, 0);
-        if (DK) bk = next_byte(pk);
-        if (DV) bv = next_byte(pv);
         if (SLOT) {
           if (DK) ak = slot_of(xk);
           if (DV) av = slot_of(xv);
@@ -392,15 +415,17 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
         }
         if (DK) {
           xk = SLOT ? rans_advance_slot(xk, ak, ek) : rans_advance(xk, ek);
-          renorm(xk, pk, bk);
+          renorm_window(xk, wk, selk);
           lv[j] = ek.y;
         }
         if (DV) {
           xv = SLOT ? rans_advance_slot(xv, av, ev) : rans_advance(xv, ev);
-          renorm(xv, pv, bv);
+          renorm_window(xv, wv, selv);
           col[((FULLV ? p * kDPass : 0) + gq * 4 + j) * kVtStride] = (uint16_t)(ev.y >> 16);
         }
       }
+      if (DK) pk += selk - kSel0;
+      if (DV) pv += selv - kSel0;
       if (DK) {
         const uint32_t b01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
         const uint32_t b23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
