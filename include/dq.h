@@ -50,7 +50,8 @@ typedef void *dq_stream_t; /* hipStream_t */
 const char *dq_status_string(int status);
 
 /* ABI version: 100 * major + minor (101: dq_codec_desc.drift_order; 102: decode
- * with append; 103: dq_set_knob, dq_attn_decode_noalloc). */
+ * with append; 103: dq_set_knob, dq_attn_decode_noalloc; 104:
+ * DQ_KNOB_ENCODE_TWO_PASS). */
 int dq_version(void);
 
 /* Path overrides, for tests and tuning.  Every value the library can pick by
@@ -78,6 +79,11 @@ int dq_version(void);
  *   DQ_KNOB_SLOT_TABLE       0: decode steps read the slot's symbol, then its
  *                            entry (two LDS round trips); 1 (default where
  *                            the 64 KB fit): one per-slot entry (same bytes)
+ *   DQ_KNOB_ENCODE_TWO_PASS  0: dq_encode's lane-per-vector path runs the
+ *                            drift search inline, in one kernel; 1 (default):
+ *                            a first kernel encodes the vectors that need no
+ *                            drift and a second runs the search on the rest
+ *                            (same bytes, norms and stats)
  * dq_set_knob returns DQ_ERR_INVALID for an unknown knob or a value below
  * -1; dq_get_knob returns the value (or DQ_ERR_INVALID). */
 enum {
@@ -89,7 +95,8 @@ enum {
   DQ_KNOB_SPLITK_WAVES = 6,
   DQ_KNOB_WORK_QUEUE = 7,
   DQ_KNOB_SLOT_TABLE = 8,
-  DQ_KNOB_COUNT = 9
+  DQ_KNOB_ENCODE_TWO_PASS = 9,
+  DQ_KNOB_COUNT = 10
 };
 int dq_set_knob(int knob, int64_t value);
 int64_t dq_get_knob(int knob);

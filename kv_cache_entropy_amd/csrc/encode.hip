@@ -207,31 +207,43 @@ __device__ __forceinline__ void rotate(const uint4 *src, uint64_t s0, uint64_t s
 
 __device__ __forceinline__ uint32_t inward(uint32_t s, int h) { return s >= (uint32_t)h ? s - 1u : s + 1u; }
 
-template <int MAXH, bool RD>  // RD: rate-distortion drift order
-__global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Tables t) {
-  __shared__ uint4 etab[kMaxLevels];
-  __shared__ float2 rdtab[kMaxLevels / 2];  // {l_m + l_{m-1}, w_m}; entry 0 unused
-  __shared__ uint8_t scr[kScr * kThreads];  // renorm bytes, lane-minor
-  __shared__ uint32_t bstat[6 + kMaxC + 1];
+constexpr int kStatWords = 6 + kMaxC + 1;  // per-block stats, flushed once
 
-  const int lane = threadIdx.x;
+// The block's coder tables (and rate-distortion terms when RD), stats zeroed.
+template <bool RD>
+__device__ __forceinline__ void block_setup(const Tables &t, uint4 *etab, float2 *rdtab, uint32_t *bstat,
+                                            int lane) {
   if (lane < t.levels) {
     const uint32_t f = t.freq[lane];
     etab[lane] = make_uint4(f << 19, t.magic[lane], t.cum[lane], (kM - f) | ((uint32_t)t.shift[lane] << 16));
   }
-  if (RD && lane < kMaxLevels / 2)
+  if (RD && lane < kMaxHalf)
     rdtab[lane] = (lane >= 1 && lane < t.half)
                       ? make_float2(half_to_float(t.recon[t.half + lane]) + half_to_float(t.recon[t.half + lane - 1]),
                                     t.rd_w[lane])
                       : make_float2(0.0f, 0.0f);
-  for (int k = lane; k < 6 + kMaxC + 1; k += kThreads) bstat[k] = 0u;
+  for (int k = lane; k < kStatWords; k += kThreads) bstat[k] = 0u;
   __syncthreads();
+}
 
+__device__ __forceinline__ void flush_stats(const EncodeArgs &a, const uint32_t *bstat, int lane) {
+  if (a.stats) {
+    __syncthreads();
+    unsigned long long *gs = reinterpret_cast<unsigned long long *>(a.stats);
+    for (int q = lane; q < kStatWords; q += kThreads)
+      if (bstat[q]) atomicAdd(gs + q, (unsigned long long)bstat[q]);
+  }
+}
+
+// The serial encode of vector vid by one lane, drift search included; lane
+// is also its column of the renorm scratch.  Stats go to the block's bstat.
+template <int MAXH, bool RD>  // RD: rate-distortion drift order
+__device__ __forceinline__ void encode_vector(const EncodeArgs &a, const Tables &t, int64_t vid,
+                                              const uint4 *etab, const float2 *rdtab, uint8_t *scr,
+                                              uint32_t *bstat, int lane) {
   const int h = t.half;
   const int C = t.C;
-  const int64_t nvec = a.T * (int64_t)t.hkv;
-  const int64_t vid = (int64_t)blockIdx.x * kThreads + lane;
-  if (vid < nvec) {
+  {
     const int g = (int)(vid / a.T);
     const int64_t tok = vid - (int64_t)g * a.T;
     const int64_t slot = a.slots[tok];
@@ -601,12 +613,343 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
       atomicAdd(&bstat[6 + 4 + (okB < 0 ? 0 : okB)], 1u);
     }
   }
-  if (a.stats) {
-    __syncthreads();
-    unsigned long long *gs = reinterpret_cast<unsigned long long *>(a.stats);
-    for (int q = lane; q < 6 + kMaxC + 1; q += kThreads)
-      if (bstat[q]) atomicAdd(gs + q, (unsigned long long)bstat[q]);
+}
+
+// Single pass: one lane per vector, the drift search inline.
+template <int MAXH, bool RD>
+__global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Tables t) {
+  __shared__ uint4 etab[kMaxLevels];
+  __shared__ float2 rdtab[kMaxHalf];        // {l_m + l_{m-1}, w_m}; entry 0 unused
+  __shared__ uint8_t scr[kScr * kThreads];  // renorm bytes, lane-minor
+  __shared__ uint32_t bstat[kStatWords];
+  const int lane = threadIdx.x;
+  block_setup<RD>(t, etab, rdtab, bstat, lane);
+  const int64_t nvec = a.T * (int64_t)t.hkv;
+  const int64_t vid = (int64_t)blockIdx.x * kThreads + lane;
+  if (vid < nvec) encode_vector<MAXH, RD>(a, t, vid, etab, rdtab, scr, bstat, lane);
+  flush_stats(a, bstat, lane);
+}
+
+// Two passes for large batches.  encode_vector keeps neither the rotated
+// coordinates nor the plan across its rounds: its in-group order needs |y|
+// again, so it rotates a second time, and a wave runs every path that one of
+// its lanes takes.  Nearly every value vector and about half the keys drift
+// at the default widths, so:
+//  - encode_fast_kernel runs round 0 of the search with y kept in registers
+//    from the first rotation: the plan, the in-group keys made from y, the
+//    one or two rANS passes.  The cases it leaves are rare: a vector whose
+//    round 0 cannot fit (more rounds), a next candidate that has to come
+//    from a lower group (a float scan), a key at the span's clamp.  Those
+//    in-pool vectors get kPendingNorm in their norm slot;
+//  - encode_rest_kernel gathers the pending vectors of 8192 consecutive
+//    ones into a list and runs encode_vector on it.  Vectors outside the
+//    pool write nothing either way; with stats, the second pass counts them.
+// Round 0 makes the same choices in the same order as encode_vector, so
+// bytes, norms and stats are those of encode_kernel.  (Slots of one call are
+// distinct: with a slot given twice, which vector's container remains is
+// unspecified, as in one pass, and the stats may count only that one.)
+constexpr uint16_t kPendingNorm = 0xFFFFu;  // never a norm: norm_half gives NaN as 0x7E00
+constexpr int kRestRange = 8192;            // vectors per encode_rest_kernel block
+
+template <int MAXH, bool RD>
+__global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, Tables t) {
+  __shared__ uint4 etab[kMaxLevels];
+  __shared__ float2 rdtab[kMaxHalf];
+  __shared__ uint8_t scr[kScr * kThreads];
+  __shared__ uint32_t bstat[kStatWords];
+  const int lane = threadIdx.x;
+  block_setup<RD>(t, etab, rdtab, bstat, lane);
+  const int h = t.half;
+  const int C = t.C;
+  const int64_t nvec = a.T * (int64_t)t.hkv;
+  const int64_t vid = (int64_t)blockIdx.x * kThreads + lane;
+  if (vid < nvec) {
+    const int g = (int)(vid / a.T);
+    const int64_t tok = vid - (int64_t)g * a.T;
+    const int64_t slot = a.slots[tok];
+    if (slot >= 0 && slot < a.num_slots) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(a.x + tok * a.stride_t + (int64_t)g * a.stride_h);
+      const uint64_t s0 = dev_splitmix64(t.seed, 2ull * (uint64_t)g);
+      const uint64_t s1 = dev_splitmix64(t.seed, 2ull * (uint64_t)g + 1ull);
+      float y[kD], S;
+      rotate(src, s0, s1, y, &S);
+      const uint32_t nh = norm_half(S);
+      const bool zero = nh == 0u;
+      const bool bad = (nh & 0x7C00u) == 0x7C00u;
+      const bool degenerate = zero || bad;
+      // quantisation and the magnitude histogram, as in encode_vector
+      const float nf = half_to_float(nh);
+      float thr[MAXH];
+#pragma unroll
+      for (int k = 1; k < MAXH; ++k)
+        thr[k] = (k < h && !degenerate) ? (float)(k * t.step64) * nf * 0.015625f : __builtin_inff();
+      uint32_t sym0[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sym0[j] = 0u;
+      uint32_t hl = 0u, hh = 0u;
+#pragma unroll
+      for (int i = 0; i < kD; ++i) {
+        const float ay = degenerate ? 0.0f : __builtin_fabsf(y[i]);
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 1; k < MAXH; ++k) m += ay >= thr[k] ? 1u : 0u;
+        const uint32_t inc = 1u << (8 * (m & 3u));
+        hl += m < 4u ? inc : 0u;
+        hh += m < 4u ? 0u : inc;
+        const uint32_t sy = (degenerate || y[i] >= 0.0f) ? (uint32_t)h + m : (uint32_t)(h - 1) - m;
+        sym0[i >> 3] |= sy << (4 * (i & 7));
+        // finish each packed word and the counts here: otherwise the
+        // compiler keeps all 128 magnitudes, and y for their signs
+        if ((i & 7) == 7) asm volatile("" : "+v"(sym0[i >> 3]), "+v"(hl), "+v"(hh));
+      }
+      int cnt[MAXH];
+      uint32_t I = 0u;
+#pragma unroll
+      for (int m = 0; m < MAXH; ++m) {
+        const int c = (int)(((m < 4 ? hl : hh) >> (8 * (m & 3))) & 0xFFu);
+        cnt[m] = m >= 1 ? c : 0;
+        if (m < h) I += (uint32_t)c * t.cost_fx[h + m];
+      }
+      const uint32_t lim = (uint32_t)(8 * (C - 3)) << kCostFrac;
+      const uint32_t sure_lo = lim - kEpsHiFx;
+      const uint32_t sure_hi = lim + kEpsLoFx;
+
+      // round 0 of the search: the moved candidates fl, their count k, and
+      // nxt, the one more tried second when prefix k is undecided
+      bool pending = false;
+      uint32_t fl[4] = {0u, 0u, 0u, 0u};
+      int k = 0, nxt = -1, total = 0;
+      uint32_t Ik = I, Iprev = 0xFFFFFFFFu;
+      if constexpr (!RD) {
+        int ks = 0;
+#pragma unroll
+        for (int m = MAXH - 1; m >= 1; --m) {
+          if (m < h) {
+            total += cnt[m];
+            if (Ik >= sure_lo && cnt[m] > 0) {
+              const uint32_t sv = t.saving_fx[m];
+              const uint32_t need = (Ik - sure_lo) / sv + 1u;
+              const uint32_t take = need < (uint32_t)cnt[m] ? need : (uint32_t)cnt[m];
+              Iprev = Ik - (take - 1u) * sv;
+              Ik -= take * sv;
+              ks += (int)take;
+            }
+          }
+        }
+        const bool sure = Ik < sure_lo;
+        const bool undecided = sure ? (ks >= 1 && Iprev < sure_hi) : (Ik < sure_hi);
+        pending = !(sure || undecided);  // every move of the round is too long
+        k = undecided ? (sure ? ks - 1 : total) : ks;
+        int kk = k, rest = 0, gb = h - 1;
+        bool full = false;
+#pragma unroll
+        for (int m = MAXH - 1; m >= 1; --m) {
+          if (m < h && kk > 0) {
+            gb = m;
+            full = kk >= cnt[m];
+            rest = full ? cnt[m] : kk;
+            kk -= rest;
+          }
+        }
+        const bool want_next = undecided && sure;
+        // the next candidate from a lower group needs the float scan
+        pending = pending || (want_next && (full || rest == cnt[gb]));
+        const int want = pending || full ? 0 : rest + (want_next ? 1 : 0);
+        uint32_t gm[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < kD; ++i) {
+          const uint32_t mg = magnitude(nib(sym0, i), h);
+          fl[i >> 5] |= (mg > (uint32_t)gb || (full && mg == (uint32_t)gb) ? 1u : 0u) << (i & 31);
+          gm[i >> 5] |= (mg == (uint32_t)gb ? 1u : 0u) << (i & 31);
+        }
+        // the masks are read back bit by bit: not 128 compares kept alive
+        opaque(gm);
+        opaque(fl);
+        opaque(sym0);
+        if (want > 0) {
+          // in-group keys from y, as encode_vector makes them from its
+          // second rotation (the same bits)
+          const uint32_t blo = __float_as_uint((float)(gb * t.step64) * nf * 0.015625f);
+          const uint32_t span = a.key_span, sat = (span << 7) + 128u;
+          uint32_t key[kD];
+#pragma unroll
+          for (int i = 0; i < kD; ++i) {
+            const uint32_t d = (__float_as_uint(y[i]) & 0x7FFFFFFFu) - blo;
+            const uint32_t kv = (min(d, span) << 7) + (128u + (uint32_t)i);
+            const uint32_t mask = (uint32_t)__builtin_amdgcn_sbfe((int)gm[i >> 5], i & 31, 1);
+            key[i] = kv & mask;
+          }
+          uint32_t p1 = 1u;
+          for (int j = 0; j < want; ++j) {
+            uint32_t best = ~0u;
+#pragma unroll
+            for (int i = 0; i < kD; i += 2) best = min(best, min(key[i] - p1, key[i + 1] - p1));
+            const uint32_t kw = best + p1;
+            if (kw == 0u || kw >= sat) {
+              pending = true;  // a clamped key: the float scan ranks it
+              break;
+            }
+            p1 = kw + 1u;
+            const int i = (int)(kw & 127u);
+            if (j < rest) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) fl[q] |= ((i >> 5) == q) ? (1u << (i & 31)) : 0u;
+            } else {
+              nxt = i;
+            }
+          }
+        }
+      } else {
+        uint32_t Iall = I;
+#pragma unroll
+        for (int m = 1; m < MAXH; ++m)
+          if (m < h) {
+            total += cnt[m];
+            Iall -= (uint32_t)cnt[m] * t.saving_fx[m];
+          }
+        if (I < sure_lo) {
+          // fits as it is
+        } else if (Iall >= sure_hi) {
+          pending = true;  // not even every move fits: more rounds
+        } else if (Iall >= sure_lo) {
+          k = total;
+#pragma unroll
+          for (int i = 0; i < kD; ++i) fl[i >> 5] |= (magnitude(nib(sym0, i), h) >= 1u ? 1u : 0u) << (i & 31);
+        } else {
+          opaque(sym0);
+          uint32_t rk[kD];
+#pragma unroll
+          for (int i = 0; i < kD; ++i) {
+            const uint32_t mg = magnitude(nib(sym0, i), h);
+            const float2 rr = rdtab[mg];
+            const float tt = nf * rr.x;
+            const float key = (2.0f * __builtin_fabsf(y[i]) - tt) * rr.y;
+            const uint32_t kb = __float_as_uint(key + 0.0f);
+            const uint32_t lo = (kb & 0x80000000u) ? ~kb : (kb | 0x80000000u);
+            rk[i] = mg >= 1u ? lo : ~0u;
+          }
+          int last = 0;
+          do {
+            const int c = next_by_key(rk, fl);
+            uint32_t w = sym0[0];
+#pragma unroll
+            for (int j = 1; j < 16; ++j) w = (c >> 3) == j ? sym0[j] : w;
+            const uint32_t mc = magnitude((w >> (4 * (c & 7))) & 15u, h);
+            uint32_t sv = 0u;
+#pragma unroll
+            for (int m = 1; m < MAXH; ++m) sv = mc == (uint32_t)m ? t.saving_fx[m] : sv;
+            Iprev = Ik;
+            Ik -= sv;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) fl[q] |= ((c >> 5) == q) ? (1u << (c & 31)) : 0u;
+            ++k;
+            last = c;
+          } while (Ik >= sure_lo);
+          if (Iprev < sure_hi) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) fl[q] &= ((last >> 5) == q) ? ~(1u << (last & 31)) : ~0u;
+            nxt = last;
+            --k;
+          }
+        }
+      }
+
+      int okB = -1, moves = 0;
+      uint32_t okx = 0u;
+      if (!pending) {
+        opaque(sym0);
+        opaque(fl);
+        uint32_t sym[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sym[j] = 0u;
+#pragma unroll
+        for (int i = 0; i < kD; ++i) {
+          const uint32_t sv = nib(sym0, i);
+          sym[i >> 3] |= (bit(fl, i) ? inward(sv, h) : sv) << (4 * (i & 7));
+        }
+        for (int attempt = 0; attempt < 2; ++attempt) {
+          uint32_t xf;
+          const int B = rans_pass(sym, etab, scr, lane, &xf);
+          if (4 + B <= C) {
+            okB = B;
+            okx = xf;
+            moves = k + attempt;
+            break;
+          }
+          if (nxt < 0) break;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int sh = 4 * (nxt & 7);
+            const uint32_t sv = (sym[j] >> sh) & 15u;
+            sym[j] = ((nxt >> 3) == j) ? ((sym[j] & ~(15u << sh)) | (inward(sv, h) << sh)) : sym[j];
+          }
+          nxt = -1;
+        }
+      }
+      const int64_t at = (int64_t)g * a.num_slots + slot;
+      if (okB >= 0) {
+        uint8_t *dst = a.cont + at * C;
+        dst[0] = (uint8_t)okx;
+        dst[1] = (uint8_t)(okx >> 8);
+        dst[2] = (uint8_t)(okx >> 16);
+        dst[3] = (uint8_t)(okx >> 24);
+        for (int j = 0; j < C - 4; ++j) dst[4 + j] = j < okB ? scr[(kScr - okB + j) * kThreads + lane] : (uint8_t)0;
+        a.norm[at] = (uint16_t)nh;
+        if (a.stats) {
+          atomicAdd(&bstat[0], 1u);
+          if (moves) {
+            atomicAdd(&bstat[1], 1u);
+            atomicAdd(&bstat[2], (uint32_t)moves);
+          }
+          if (bad) atomicAdd(&bstat[4], 1u);
+          if (zero) atomicAdd(&bstat[5], 1u);
+          atomicAdd(&bstat[6 + 4 + okB], 1u);
+        }
+      } else {
+        a.norm[at] = kPendingNorm;  // more rounds: the second pass
+      }
+    }
   }
+  flush_stats(a, bstat, lane);
+}
+
+template <int MAXH, bool RD>
+__global__ void __launch_bounds__(kThreads, 2) encode_rest_kernel(EncodeArgs a, Tables t) {
+  __shared__ uint4 etab[kMaxLevels];
+  __shared__ float2 rdtab[kMaxHalf];
+  __shared__ uint8_t scr[kScr * kThreads];
+  __shared__ uint32_t bstat[kStatWords];
+  __shared__ uint16_t list[kRestRange];  // pending vectors, as offsets in the block's range
+  __shared__ uint32_t nlist;
+  const int lane = threadIdx.x;
+  if (lane == 0) nlist = 0u;
+  block_setup<RD>(t, etab, rdtab, bstat, lane);
+  const int64_t nvec = a.T * (int64_t)t.hkv;
+  const int64_t v0 = (int64_t)blockIdx.x * kRestRange;
+  const int64_t v1 = min(v0 + (int64_t)kRestRange, nvec);
+  for (int64_t c = v0; c < v1; c += kThreads) {
+    const int64_t vid = c + lane;
+    bool pend = false;
+    if (vid < v1) {
+      const int g = (int)(vid / a.T);
+      const int64_t tok = vid - (int64_t)g * a.T;
+      const int64_t slot = a.slots[tok];
+      pend = (slot >= 0 && slot < a.num_slots) ? a.norm[(int64_t)g * a.num_slots + slot] == kPendingNorm
+                                               : a.stats != nullptr;
+    }
+    // the wave's pending lanes take consecutive list entries
+    const uint64_t m = __ballot(pend);
+    uint32_t base = 0u;
+    if ((lane & 63) == 0 && m) base = atomicAdd(&nlist, (uint32_t)__popcll(m));
+    base = (uint32_t)__shfl((int)base, 0);
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (pend) list[base + rank] = (uint16_t)(vid - v0);
+  }
+  __syncthreads();
+  const int n = (int)nlist;
+  for (int j = 0; j < n; j += kThreads)
+    if (j + lane < n) encode_vector<MAXH, RD>(a, t, v0 + list[j + lane], etab, rdtab, scr, bstat, lane);
+  flush_stats(a, bstat, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -687,10 +1030,23 @@ __global__ void __launch_bounds__(64 * kWaveVecs) encode_wave_kv_kernel(EncodeAr
 
 constexpr int64_t kWavePathMax = 16384;  // vectors: below this, latency wins
 
+// One pass or two (DQ_KNOB_ENCODE_TWO_PASS: 0 one, 1 two; the library takes
+// two); the bytes are the same.
 template <int MAXH>
 hipError_t launch(const EncodeArgs &a, const Tables &t, hipStream_t s) {
   const int64_t nvec = a.T * (int64_t)t.hkv;
   const unsigned blocks = (unsigned)((nvec + kThreads - 1) / kThreads);
+  if (knob(DQ_KNOB_ENCODE_TWO_PASS) != 0) {
+    const unsigned rest = (unsigned)((nvec + kRestRange - 1) / kRestRange);
+    if (t.order == 1) {
+      hipLaunchKernelGGL((encode_fast_kernel<MAXH, true>), dim3(blocks), dim3(kThreads), 0, s, a, t);
+      hipLaunchKernelGGL((encode_rest_kernel<MAXH, true>), dim3(rest), dim3(kThreads), 0, s, a, t);
+    } else {
+      hipLaunchKernelGGL((encode_fast_kernel<MAXH, false>), dim3(blocks), dim3(kThreads), 0, s, a, t);
+      hipLaunchKernelGGL((encode_rest_kernel<MAXH, false>), dim3(rest), dim3(kThreads), 0, s, a, t);
+    }
+    return hipGetLastError();
+  }
   if (t.order == 1) hipLaunchKernelGGL((encode_kernel<MAXH, true>), dim3(blocks), dim3(kThreads), 0, s, a, t);
   else hipLaunchKernelGGL((encode_kernel<MAXH, false>), dim3(blocks), dim3(kThreads), 0, s, a, t);
   return hipGetLastError();

@@ -34,11 +34,14 @@ def _codecs(O, levels, C, seed, hkv, step64=0, order=0):
     return g, o
 
 
-@pytest.fixture(params=["wave", "lane"])
+@pytest.fixture(params=["wave", "lane", "lane_one_pass"])
 def encode_path(request, knob):
     """Small batches run the wave-per-vector kernel, large ones the
-    lane-per-vector kernel; force each in turn on the same inputs."""
+    lane-per-vector kernels (two passes by default: no-drift vectors first,
+    then the drift search on the rest; or the search inline in one pass);
+    force each in turn on the same inputs."""
     knob("encode_wave_max", "1000000000" if request.param == "wave" else "0")
+    knob("encode_two_pass", "0" if request.param == "lane_one_pass" else "-1")
     return request.param
 
 
@@ -174,6 +177,65 @@ def test_encode_strided_input_and_pool_slots(oracle_lib, encode_path):
     _assert_encode_equal(cont, norm, st, ocont, onorm, ost, "strided")
     # untouched slots stay zero
     assert int(cont[:, :1000].abs().sum()) == 0
+
+
+@pytest.mark.parametrize("levels,C,order", [(8, 34, 0), (6, 29, 0), (6, 29, 1), (8, 29, 1)])
+def test_encode_two_pass_many_blocks(oracle_lib, knob, levels, C, order):
+    """The two-pass lane encoder over several 8192-vector ranges of its
+    second pass (12288 vectors, heavy-tailed data so that many need the
+    drift search): bytes, norms and stats equal to the one-pass kernel's and
+    to the oracle's."""
+    O = oracle_lib
+    _say(f"two-pass {levels}/{C} order {order}")
+    T, hkv = 3072, 4
+    gc, oc = _codecs(O, levels, C, seed=211 + levels, hkv=hkv, order=order)
+    x = synth.kv_tensor("student_t5", T, hkv, seed=212, device=DEV)
+    slots = torch.randperm(T + 100, generator=torch.Generator().manual_seed(213))[:T].to(DEV)
+    knob("encode_wave_max", "0")
+    out = {}
+    for two in ("1", "0"):
+        knob("encode_two_pass", two)
+        cont, norm = dq.alloc_pool(gc, T + 100, DEV)
+        st = dq.new_stats(DEV)
+        dq.encode(gc, x, slots, cont, norm, st)
+        torch.cuda.synchronize()
+        out[two] = (cont, norm, st)
+    assert torch.equal(out["1"][0], out["0"][0]) and torch.equal(out["1"][1], out["0"][1])
+    assert dq.stats_dict(out["1"][2]) == dq.stats_dict(out["0"][2])
+    assert dq.stats_dict(out["1"][2])["drifted_vectors"] > 0
+    ocont, onorm, ost = O.encode(oc, _np_bits(x), slots.cpu().numpy(), num_slots=out["1"][0].shape[1])
+    _assert_encode_equal(*out["1"], ocont, onorm, ost, f"two-pass {levels}/{C}")
+
+
+def test_encode_slots_outside_pool(oracle_lib, encode_path):
+    """A vector whose slot is outside the pool (negative or past its end)
+    writes nothing; with stats it is still counted, as if it had a slot.
+    The in-pool vectors' containers and norms are those of a call without
+    the others."""
+    O = oracle_lib
+    T, hkv = 400, 2
+    gc, oc = _codecs(O, 6, 29, seed=15, hkv=hkv)
+    x = synth.kv_tensor("student_t5", T, hkv, seed=16, device=DEV)
+    cont, norm = dq.alloc_pool(gc, 500, DEV)
+    S = cont.shape[1]  # the pool as allocated (rounded up)
+    slots = torch.arange(T, dtype=torch.int64) + 50
+    slots[::7] = -1
+    slots[3::11] = S + 3
+    inside = (slots >= 0) & (slots < S)
+    st = dq.new_stats(DEV)
+    dq.encode(gc, x, slots.to(DEV), cont, norm, st)
+    torch.cuda.synchronize()
+    # stats: every vector, as encoded into a pool where each has a slot
+    full_slots = torch.arange(T, dtype=torch.int64, device=DEV)
+    c2, n2 = dq.alloc_pool(gc, T, DEV)
+    st2 = dq.new_stats(DEV)
+    dq.encode(gc, x, full_slots, c2, n2, st2)
+    torch.cuda.synchronize()
+    assert dq.stats_dict(st) == dq.stats_dict(st2)
+    idx = torch.nonzero(inside).flatten()
+    ocont, onorm, ost = O.encode(oc, _np_bits(x[idx.to(DEV)]), slots[idx].numpy(), num_slots=S)
+    gcont, gnorm = cont.cpu().numpy(), _np_bits(norm)
+    assert (gcont == ocont).all() and (gnorm == onorm).all()
 
 
 @pytest.mark.parametrize("levels,C", [(8, 34), (6, 29)])
