@@ -207,6 +207,19 @@ __device__ __forceinline__ void rotate(const uint4 *src, uint64_t s0, uint64_t s
 
 __device__ __forceinline__ uint32_t inward(uint32_t s, int h) { return s >= (uint32_t)h ? s - 1u : s + 1u; }
 
+// Moves packed symbol i (a per-lane index) one level inward: its word is
+// picked out by selects, updated, and put back by selects.
+__device__ __forceinline__ void move_inward(uint32_t (&sym)[16], int i, int h) {
+  const int wi = i >> 3, sh = 4 * (i & 7);
+  uint32_t w = sym[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) w = wi == j ? sym[j] : w;
+  const uint32_t sv = (w >> sh) & 15u;
+  w = (w & ~(15u << sh)) | (inward(sv, h) << sh);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sym[j] = wi == j ? w : sym[j];
+}
+
 constexpr int kStatWords = 6 + kMaxC + 1;  // per-block stats, flushed once
 
 // The block's coder tables (and rate-distortion terms when RD), stats zeroed.
@@ -717,7 +730,9 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
       // round 0 of the search: the moved candidates fl, their count k, and
       // nxt, the one more tried second when prefix k is undecided
       bool pending = false;
-      uint32_t fl[4] = {0u, 0u, 0u, 0u};
+      uint32_t sym[16];  // the symbols of prefix k
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sym[j] = 0u;
       int k = 0, nxt = -1, total = 0;
       uint32_t Ik = I, Iprev = 0xFFFFFFFFu;
       if constexpr (!RD) {
@@ -755,51 +770,42 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
         // the next candidate from a lower group needs the float scan
         pending = pending || (want_next && (full || rest == cnt[gb]));
         const int want = pending || full ? 0 : rest + (want_next ? 1 : 0);
-        uint32_t gm[4] = {0u, 0u, 0u, 0u};
+        // one pass: the symbols with the whole-group moves applied, and the
+        // boundary group's in-group keys made from y, as encode_vector makes
+        // them from its second rotation (the same bits); 0 for the others
+        const uint32_t blo = __float_as_uint((float)(gb * t.step64) * nf * 0.015625f);
+        const uint32_t span = a.key_span, sat = (span << 7) + 128u;  // keys >= sat are clamped
+        uint32_t key[kD];
 #pragma unroll
         for (int i = 0; i < kD; ++i) {
-          const uint32_t mg = magnitude(nib(sym0, i), h);
-          fl[i >> 5] |= (mg > (uint32_t)gb || (full && mg == (uint32_t)gb) ? 1u : 0u) << (i & 31);
-          gm[i >> 5] |= (mg == (uint32_t)gb ? 1u : 0u) << (i & 31);
+          const uint32_t sv = nib(sym0, i);
+          const uint32_t mg = magnitude(sv, h);
+          const bool move = mg > (uint32_t)gb || (full && mg == (uint32_t)gb);
+          sym[i >> 3] |= (move ? inward(sv, h) : sv) << (4 * (i & 7));
+          const uint32_t d = (__float_as_uint(y[i]) & 0x7FFFFFFFu) - blo;  // members: |y| >= threshold
+          key[i] = mg == (uint32_t)gb ? (min(d, span) << 7) + (128u + (uint32_t)i) : 0u;
+          asm volatile("" : "+v"(key[i]));  // made here, while mg is at hand
+          if ((i & 7) == 7) asm volatile("" : "+v"(sym[i >> 3]));
         }
-        // the masks are read back bit by bit: not 128 compares kept alive
-        opaque(gm);
-        opaque(fl);
-        opaque(sym0);
-        if (want > 0) {
-          // in-group keys from y, as encode_vector makes them from its
-          // second rotation (the same bits)
-          const uint32_t blo = __float_as_uint((float)(gb * t.step64) * nf * 0.015625f);
-          const uint32_t span = a.key_span, sat = (span << 7) + 128u;
-          uint32_t key[kD];
+        uint32_t p1 = 1u;  // every key taken so far is below p1
+        for (int j = 0; j < want; ++j) {
+          // min over (key - p1) mod 2^32: a member not yet taken gives key
+          // - p1 < 2^32 - p1, the others give at least 2^32 - p1
+          uint32_t best = ~0u;
 #pragma unroll
-          for (int i = 0; i < kD; ++i) {
-            const uint32_t d = (__float_as_uint(y[i]) & 0x7FFFFFFFu) - blo;
-            const uint32_t kv = (min(d, span) << 7) + (128u + (uint32_t)i);
-            const uint32_t mask = (uint32_t)__builtin_amdgcn_sbfe((int)gm[i >> 5], i & 31, 1);
-            key[i] = kv & mask;
+          for (int i = 0; i < kD; i += 2) best = min(best, min(key[i] - p1, key[i + 1] - p1));
+          const uint32_t kw = best + p1;
+          if (kw == 0u || kw >= sat) {
+            pending = true;  // a clamped key: the float scan ranks it
+            break;
           }
-          uint32_t p1 = 1u;
-          for (int j = 0; j < want; ++j) {
-            uint32_t best = ~0u;
-#pragma unroll
-            for (int i = 0; i < kD; i += 2) best = min(best, min(key[i] - p1, key[i + 1] - p1));
-            const uint32_t kw = best + p1;
-            if (kw == 0u || kw >= sat) {
-              pending = true;  // a clamped key: the float scan ranks it
-              break;
-            }
-            p1 = kw + 1u;
-            const int i = (int)(kw & 127u);
-            if (j < rest) {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) fl[q] |= ((i >> 5) == q) ? (1u << (i & 31)) : 0u;
-            } else {
-              nxt = i;
-            }
-          }
+          p1 = kw + 1u;
+          const int i = (int)(kw & 127u);
+          if (j < rest) move_inward(sym, i, h);
+          else nxt = i;
         }
       } else {
+        uint32_t fl[4] = {0u, 0u, 0u, 0u};
         uint32_t Iall = I;
 #pragma unroll
         for (int m = 1; m < MAXH; ++m)
@@ -852,21 +858,18 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
             --k;
           }
         }
-      }
-
-      int okB = -1, moves = 0;
-      uint32_t okx = 0u;
-      if (!pending) {
         opaque(sym0);
         opaque(fl);
-        uint32_t sym[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sym[j] = 0u;
 #pragma unroll
         for (int i = 0; i < kD; ++i) {
           const uint32_t sv = nib(sym0, i);
           sym[i >> 3] |= (bit(fl, i) ? inward(sv, h) : sv) << (4 * (i & 7));
         }
+      }
+
+      int okB = -1, moves = 0;
+      uint32_t okx = 0u;
+      if (!pending) {
         for (int attempt = 0; attempt < 2; ++attempt) {
           uint32_t xf;
           const int B = rans_pass(sym, etab, scr, lane, &xf);
@@ -877,12 +880,7 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
             break;
           }
           if (nxt < 0) break;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int sh = 4 * (nxt & 7);
-            const uint32_t sv = (sym[j] >> sh) & 15u;
-            sym[j] = ((nxt >> 3) == j) ? ((sym[j] & ~(15u << sh)) | (inward(sv, h) << sh)) : sym[j];
-          }
+          move_inward(sym, nxt, h);
           nxt = -1;
         }
       }
