@@ -20,6 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdq.so")
+PROBE = os.path.join(OBJ, "lds_gather_probe")
 SOURCES = ["codec.cpp", "encode.hip", "decode.hip", "attention.hip"]
 ARCH = "gfx950"
 
@@ -63,6 +64,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the LDS gather microbenchmark (a program of its own, not part of the library)
+    probe = [_hipcc(), "-O3", "-std=c++17", "-Wall"] + HIP_ONLY + [
+        "-x", "hip", os.path.join(CSRC, "probes", "lds_gather.hip"), "-o", PROBE]
+    if verbose:
+        print(" ".join(probe), flush=True)
+    r = subprocess.run(probe, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for probes/lds_gather.hip:\n{r.stderr}")
     return LIB
 
 
