@@ -354,15 +354,15 @@ def summarize_sq(d, kname, wl, src):
           "for the few it leaves.", "",
           "| counter | K first | K second | V first | V second |", "|---|---:|---:|---:|---:|"]
     md += [f"| {c} | " + " | ".join(f"{v[c]:.4g}" for _, v in enc) + " |" for c in SQ_COUNTERS]
-    der = [table([v])[1] for _, v in enc]
+    edr = [table([v])[1] for _, v in enc]
     md += ["", "| derived | K | V |", "|---|---:|---:|"]
-    cyc = [der[0]["cycles"] + der[1]["cycles"], der[2]["cycles"] + der[3]["cycles"]]
+    cyc = [edr[0]["cycles"] + edr[1]["cycles"], edr[2]["cycles"] + edr[3]["cycles"]]
     busy = [(enc[0][1]["SQ_ACTIVE_INST_VALU"] + enc[1][1]["SQ_ACTIVE_INST_VALU"]) * 4 / 1024 / cyc[0],
             (enc[2][1]["SQ_ACTIVE_INST_VALU"] + enc[3][1]["SQ_ACTIVE_INST_VALU"]) * 4 / 1024 / cyc[1]]
     ops = [(enc[0][1]["SQ_INSTS_VALU"] + enc[1][1]["SQ_INSTS_VALU"]) * 64 / nvec,
            (enc[2][1]["SQ_INSTS_VALU"] + enc[3][1]["SQ_INSTS_VALU"]) * 64 / nvec]
     md += [f"| both passes, cycles | {cyc[0]:.4g} | {cyc[1]:.4g} |",
-           f"| second pass, share of the cycles | {der[1]['cycles'] / cyc[0]:.1%} | {der[3]['cycles'] / cyc[1]:.1%} |",
+           f"| second pass, share of the cycles | {edr[1]['cycles'] / cyc[0]:.1%} | {edr[3]['cycles'] / cyc[1]:.1%} |",
            f"| VALU busy | {busy[0]:.1%} | {busy[1]:.1%} |",
            f"| VALU lane-ops per vector | {ops[0]:.0f} | {ops[1]:.0f} |", ""]
     with open(os.path.join(ROOT, "profiles", f"encode_{wl}_sq_counters.md"), "w") as f:
