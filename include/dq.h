@@ -183,7 +183,12 @@ typedef struct {
  *   norm      device uint16[Hkv][num_slots]     (fp16 bits)
  *   stats     device dq_stats, may be NULL
  * Vectors with a zero, inf or NaN norm are coded as all innermost-positive
- * symbols (norm stored as 0, inf or 0x7E00).  Duplicate slots race.
+ * symbols (norm stored as 0, inf or 0x7E00).  A slot outside [0, num_slots)
+ * writes nothing; the stats still count its vector.  Duplicate slots race:
+ * which vector's container remains is unspecified, and the stats may count
+ * only that one.  Until the call's work on `stream` completes, the norm of
+ * a vector still in the drift search may read 0xFFFF (large batches run the
+ * search's rare cases in a second kernel and mark them so).
  * T = 0 is a no-op; T * Hkv above 2^38 gives DQ_ERR_UNSUPPORTED. */
 int dq_encode(dq_codec_t codec, const void *x, int64_t T, int64_t stride_t,
               int64_t stride_h, const int64_t *slots, int64_t num_slots,

@@ -9,11 +9,13 @@
 //   -> if the stream does not fit, drift the first candidates of a fixed
 //   order one level inward until it does.
 //
-// Two kernels write the same bytes:
+// The kernels below write the same bytes:
 //  - encode_kernel (large batches, e.g. a prompt): one lane owns one vector
-//    end to end.  The rotation runs on the 128 coordinates in VGPRs (fully
-//    unrolled butterflies); the symbols are packed 4 bits each in
-//    registers.  The drift is planned before any pass from the ideal code
+//    end to end; encode_fast_kernel + encode_rest_kernel split the same
+//    lane-per-vector encode into two passes (round 0 of the search with the
+//    rotated coordinates kept, then the rare rest), the default.  The
+//    rotation runs on the 128 coordinates in VGPRs (fully unrolled
+//    butterflies); the symbols are packed 4 bits each in registers.  The drift is planned before any pass from the ideal code
 //    length, which decides whether a prefix of moves fits except inside a
 //    band narrower than one move's saving; then one rANS pass runs, or two
 //    when the undecided prefix is tried first.  Renorm bytes go to the
