@@ -9,13 +9,11 @@
 //   -> if the stream does not fit, drift the first candidates of a fixed
 //   order one level inward until it does.
 //
-// The kernels below write the same bytes:
+// Two kernels write the same bytes:
 //  - encode_kernel (large batches, e.g. a prompt): one lane owns one vector
-//    end to end; encode_fast_kernel + encode_rest_kernel split the same
-//    lane-per-vector encode into two passes (round 0 of the search with the
-//    rotated coordinates kept, then the rare rest), the default.  The
-//    rotation runs on the 128 coordinates in VGPRs (fully unrolled
-//    butterflies); the symbols are packed 4 bits each in registers.  The drift is planned before any pass from the ideal code
+//    end to end.  The rotation runs on the 128 coordinates in VGPRs (fully
+//    unrolled butterflies); the symbols are packed 4 bits each in
+//    registers.  The drift is planned before any pass from the ideal code
 //    length, which decides whether a prefix of moves fits except inside a
 //    band narrower than one move's saving; then one rANS pass runs, or two
 //    when the undecided prefix is tried first.  Renorm bytes go to the
@@ -128,7 +126,6 @@ __device__ __forceinline__ int next_by_key(const uint32_t (&rk)[kD], const uint3
 // kScr - 1 are then in the decoder's reading order); the byte store is
 // unconditional and simply overwritten when no byte is emitted.  The coder
 // constants do not depend on the state, so their loads run ahead of it.
-template <int NT = kThreads>  // lanes per block: the scratch's row stride
 __device__ __forceinline__ int rans_pass(const uint32_t (&sym)[16], const uint4 *etab, uint8_t *buf, int lane,
                                          uint32_t *xfinal) {
   uint32_t x = kLow;
@@ -136,7 +133,7 @@ __device__ __forceinline__ int rans_pass(const uint32_t (&sym)[16], const uint4 
 #pragma unroll
   for (int i = kD - 1; i >= 0; --i) {
     const uint4 e = etab[nib(sym, i)];  // {f << 19, magic, cum, (4096 - f) | shift << 16}
-    buf[pos * NT + lane] = (uint8_t)x;
+    buf[pos * kThreads + lane] = (uint8_t)x;
     const bool emit = x >= e.x;
     x = emit ? x >> 8 : x;
     pos -= emit ? 1 : 0;
@@ -226,7 +223,7 @@ __device__ __forceinline__ void move_inward(uint32_t (&sym)[16], int i, int h) {
 constexpr int kStatWords = 6 + kMaxC + 1;  // per-block stats, flushed once
 
 // The block's coder tables (and rate-distortion terms when RD), stats zeroed.
-template <bool RD, int NT = kThreads>
+template <bool RD>
 __device__ __forceinline__ void block_setup(const Tables &t, uint4 *etab, float2 *rdtab, uint32_t *bstat,
                                             int lane) {
   if (lane < t.levels) {
@@ -238,16 +235,15 @@ __device__ __forceinline__ void block_setup(const Tables &t, uint4 *etab, float2
                       ? make_float2(half_to_float(t.recon[t.half + lane]) + half_to_float(t.recon[t.half + lane - 1]),
                                     t.rd_w[lane])
                       : make_float2(0.0f, 0.0f);
-  for (int k = lane; k < kStatWords; k += NT) bstat[k] = 0u;
+  for (int k = lane; k < kStatWords; k += kThreads) bstat[k] = 0u;
   __syncthreads();
 }
 
-template <int NT = kThreads>
 __device__ __forceinline__ void flush_stats(const EncodeArgs &a, const uint32_t *bstat, int lane) {
   if (a.stats) {
     __syncthreads();
     unsigned long long *gs = reinterpret_cast<unsigned long long *>(a.stats);
-    for (int q = lane; q < kStatWords; q += NT)
+    for (int q = lane; q < kStatWords; q += kThreads)
       if (bstat[q]) atomicAdd(gs + q, (unsigned long long)bstat[q]);
   }
 }
@@ -667,55 +663,19 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
 // unspecified, as in one pass, and the stats may count only that one.)
 constexpr uint16_t kPendingNorm = 0xFFFFu;  // never a norm: norm_half gives NaN as 0x7E00
 constexpr int kRestRange = 8192;            // vectors per encode_rest_kernel block
-constexpr int kFastThreads = 256;           // lanes per encode_fast_kernel block
 
-// The container of a vector whose stream fits: final state, the B renorm
-// bytes from the lane's scratch column, zero padding; then its norm.
-template <int NT>
-__device__ __forceinline__ void store_container(const EncodeArgs &a, int C, int64_t at, uint32_t x, int B,
-                                                uint32_t nh, const uint8_t *scr, int lane) {
-  uint8_t *dst = a.cont + at * C;
-  dst[0] = (uint8_t)x;
-  dst[1] = (uint8_t)(x >> 8);
-  dst[2] = (uint8_t)(x >> 16);
-  dst[3] = (uint8_t)(x >> 24);
-  for (int j = 0; j < C - 4; ++j) dst[4 + j] = j < B ? scr[(kScr - B + j) * NT + lane] : (uint8_t)0;
-  a.norm[at] = (uint16_t)nh;
-}
-
-__device__ __forceinline__ void count_vector(uint32_t *bstat, int moves, bool bad, bool zero, int B) {
-  atomicAdd(&bstat[0], 1u);
-  if (moves) {
-    atomicAdd(&bstat[1], 1u);
-    atomicAdd(&bstat[2], (uint32_t)moves);
-  }
-  if (bad) atomicAdd(&bstat[4], 1u);
-  if (zero) atomicAdd(&bstat[5], 1u);
-  atomicAdd(&bstat[6 + 4 + B], 1u);
-}
-
-// The second rANS pass of round 0 (the undecided prefix k did not fit, so
-// k + 1 is tried) is needed by a few lanes of a block but would hold every
-// lane of their waves: those lanes queue their symbols in LDS, and after a
-// block barrier the first lanes of the block run the queued passes.
 template <int MAXH, bool RD>
-__global__ void __launch_bounds__(kFastThreads, 2) encode_fast_kernel(EncodeArgs a, Tables t) {
-  constexpr int NT = kFastThreads;
+__global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, Tables t) {
   __shared__ uint4 etab[kMaxLevels];
   __shared__ float2 rdtab[kMaxHalf];
-  __shared__ uint8_t scr[kScr * NT];
+  __shared__ uint8_t scr[kScr * kThreads];
   __shared__ uint32_t bstat[kStatWords];
-  __shared__ uint32_t qsym[NT][17];  // queued second passes: the symbols (row stride 17 words)
-  __shared__ int64_t qat[NT];        // their pool index
-  __shared__ uint32_t qinfo[NT];     // norm | bad << 16 | zero << 17 | moves << 18
-  __shared__ uint32_t nq;
   const int lane = threadIdx.x;
-  if (lane == 0) nq = 0u;
-  block_setup<RD, NT>(t, etab, rdtab, bstat, lane);
+  block_setup<RD>(t, etab, rdtab, bstat, lane);
   const int h = t.half;
   const int C = t.C;
   const int64_t nvec = a.T * (int64_t)t.hkv;
-  const int64_t vid = (int64_t)blockIdx.x * NT + lane;
+  const int64_t vid = (int64_t)blockIdx.x * kThreads + lane;
   if (vid < nvec) {
     const int g = (int)(vid / a.T);
     const int64_t tok = vid - (int64_t)g * a.T;
@@ -732,20 +692,17 @@ __global__ void __launch_bounds__(kFastThreads, 2) encode_fast_kernel(EncodeArgs
       const bool degenerate = zero || bad;
       // quantisation and the magnitude histogram, as in encode_vector
       const float nf = half_to_float(nh);
-      // a degenerate vector's thresholds are NaN, so every |y| (inf too)
-      // compares below them: all magnitudes 0, as encode_vector's |y| = 0
       float thr[MAXH];
 #pragma unroll
       for (int k = 1; k < MAXH; ++k)
-        thr[k] = degenerate ? __builtin_nanf("")
-                            : (k < h ? (float)(k * t.step64) * nf * 0.015625f : __builtin_inff());
+        thr[k] = (k < h && !degenerate) ? (float)(k * t.step64) * nf * 0.015625f : __builtin_inff();
       uint32_t sym0[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) sym0[j] = 0u;
       uint32_t hl = 0u, hh = 0u;
 #pragma unroll
       for (int i = 0; i < kD; ++i) {
-        const float ay = __builtin_fabsf(y[i]);
+        const float ay = degenerate ? 0.0f : __builtin_fabsf(y[i]);
         uint32_t m = 0;
 #pragma unroll
         for (int k = 1; k < MAXH; ++k) m += ay >= thr[k] ? 1u : 0u;
@@ -910,46 +867,48 @@ __global__ void __launch_bounds__(kFastThreads, 2) encode_fast_kernel(EncodeArgs
         }
       }
 
-      const int64_t at = (int64_t)g * a.num_slots + slot;
-      int B = -1;
-      uint32_t xf = 0u;
+      int okB = -1, moves = 0;
+      uint32_t okx = 0u;
       if (!pending) {
-        B = rans_pass<NT>(sym, etab, scr, lane, &xf);
-        if (4 + B > C) B = -1;
+        for (int attempt = 0; attempt < 2; ++attempt) {
+          uint32_t xf;
+          const int B = rans_pass(sym, etab, scr, lane, &xf);
+          if (4 + B <= C) {
+            okB = B;
+            okx = xf;
+            moves = k + attempt;
+            break;
+          }
+          if (nxt < 0) break;
+          move_inward(sym, nxt, h);
+          nxt = -1;
+        }
       }
-      if (B >= 0) {
-        store_container<NT>(a, C, at, xf, B, nh, scr, lane);
-        if (a.stats) count_vector(bstat, k, bad, zero, B);
-      } else if (!pending && nxt >= 0) {
-        // prefix k did not fit: prefix k + 1, queued for the block's second pass
-        move_inward(sym, nxt, h);
-        const uint32_t e = atomicAdd(&nq, 1u);
-#pragma unroll
-        for (int w = 0; w < 16; ++w) qsym[e][w] = sym[w];
-        qat[e] = at;
-        qinfo[e] = nh | (bad ? 1u << 16 : 0u) | (zero ? 1u << 17 : 0u) | ((uint32_t)(k + 1) << 18);
+      const int64_t at = (int64_t)g * a.num_slots + slot;
+      if (okB >= 0) {
+        uint8_t *dst = a.cont + at * C;
+        dst[0] = (uint8_t)okx;
+        dst[1] = (uint8_t)(okx >> 8);
+        dst[2] = (uint8_t)(okx >> 16);
+        dst[3] = (uint8_t)(okx >> 24);
+        for (int j = 0; j < C - 4; ++j) dst[4 + j] = j < okB ? scr[(kScr - okB + j) * kThreads + lane] : (uint8_t)0;
+        a.norm[at] = (uint16_t)nh;
+        if (a.stats) {
+          atomicAdd(&bstat[0], 1u);
+          if (moves) {
+            atomicAdd(&bstat[1], 1u);
+            atomicAdd(&bstat[2], (uint32_t)moves);
+          }
+          if (bad) atomicAdd(&bstat[4], 1u);
+          if (zero) atomicAdd(&bstat[5], 1u);
+          atomicAdd(&bstat[6 + 4 + okB], 1u);
+        }
       } else {
-        a.norm[at] = kPendingNorm;  // more rounds: the second kernel
+        a.norm[at] = kPendingNorm;  // more rounds: the second pass
       }
     }
   }
-  __syncthreads();
-  if ((uint32_t)lane < nq) {
-    uint32_t sym[16];
-#pragma unroll
-    for (int w = 0; w < 16; ++w) sym[w] = qsym[lane][w];
-    const int64_t at = qat[lane];
-    const uint32_t info = qinfo[lane];
-    uint32_t xf;
-    const int B = rans_pass<NT>(sym, etab, scr, lane, &xf);
-    if (4 + B <= t.C) {
-      store_container<NT>(a, t.C, at, xf, B, info & 0xFFFFu, scr, lane);
-      if (a.stats) count_vector(bstat, (int)(info >> 18), (info >> 16) & 1u, (info >> 17) & 1u, B);
-    } else {
-      a.norm[at] = kPendingNorm;
-    }
-  }
-  flush_stats<NT>(a, bstat, lane);
+  flush_stats(a, bstat, lane);
 }
 
 template <int MAXH, bool RD>
@@ -1076,13 +1035,12 @@ hipError_t launch(const EncodeArgs &a, const Tables &t, hipStream_t s) {
   const int64_t nvec = a.T * (int64_t)t.hkv;
   const unsigned blocks = (unsigned)((nvec + kThreads - 1) / kThreads);
   if (knob(DQ_KNOB_ENCODE_TWO_PASS) != 0) {
-    const unsigned fast = (unsigned)((nvec + kFastThreads - 1) / kFastThreads);
     const unsigned rest = (unsigned)((nvec + kRestRange - 1) / kRestRange);
     if (t.order == 1) {
-      hipLaunchKernelGGL((encode_fast_kernel<MAXH, true>), dim3(fast), dim3(kFastThreads), 0, s, a, t);
+      hipLaunchKernelGGL((encode_fast_kernel<MAXH, true>), dim3(blocks), dim3(kThreads), 0, s, a, t);
       hipLaunchKernelGGL((encode_rest_kernel<MAXH, true>), dim3(rest), dim3(kThreads), 0, s, a, t);
     } else {
-      hipLaunchKernelGGL((encode_fast_kernel<MAXH, false>), dim3(fast), dim3(kFastThreads), 0, s, a, t);
+      hipLaunchKernelGGL((encode_fast_kernel<MAXH, false>), dim3(blocks), dim3(kThreads), 0, s, a, t);
       hipLaunchKernelGGL((encode_rest_kernel<MAXH, false>), dim3(rest), dim3(kThreads), 0, s, a, t);
     }
     return hipGetLastError();
