@@ -13,10 +13,12 @@ sequence encoded into the pools and attention of every sequence over its
 grown context (the call runs the encodes inside the attention launch at
 small batch, as a short launch of their own before it at this one).
 `value` = compressed KV bytes (containers + fp16 norms) read by attention
-per step / wall time per step.  The roofline entry measures that call's
-split-K kernel with HIP events on its stream inside the timed region.  The same steps are then
-timed as two launches (dq_encode_kv, then dq_attn_decode), and both forms at
-batch 1 and 4, eagerly and as HIP-graph replays.
+per step / time per step, over the timed steps with one event pair around
+them all.  The same steps then run again with HIP events around each call's
+split-K kernel, on its stream, for the roofline entry (re-encoding a step's
+token into its slot writes the same bytes).  Then the steps as two launches
+(dq_encode_kv, then dq_attn_decode), and both forms at batch 1 and 4,
+eagerly and as HIP-graph replays.
 
     python bench.py [--steps 16] [--warmup 12] [--workload NAME]
 """
@@ -169,19 +171,22 @@ def summarize_profiles(d):
         lines.append(f"| `{kname}` | {blocks} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
     # the decode step's split-K variant: the one launched most at the bench's
     # shape (dq_attn_decode_append runs the attention without the encode loop
-    # when its items fill every round of waves, as at batch 128); the timed
-    # steps are its launches number warmup .. warmup + steps - 1 at that shape
-    # (the two-launch and paged comparisons and the other workloads follow)
+    # when its items fill every round of waves, as at batch 128).  The bench
+    # runs its timed steps twice, the second time with HIP events around
+    # each split-K launch: those are its launches number warmup + steps ..
+    # warmup + 2 steps - 1 at that shape (the two-launch and paged
+    # comparisons and the other workloads follow)
     head = sorted(disp.items(), key=lambda kv: (kv[0][1], len(kv[1])))
     kname = head[-1][0][0] if head else "attn_splitk_kernel"
     if head:
         (kname, blocks), _ = head[-1]
         seq = sorted(seqd[(kname, blocks)])
-        w0, ns = live["warmup"], live["steps"]
+        ns = live["steps"]
+        w0 = live["warmup"] + ns
         v = [dur for _, dur in seq[w0:w0 + ns]]
         lines += ["", f"`{kname}` (the decode step's split-K kernel) at the bench's shape "
-                  f"({blocks} blocks), the bench's {ns} timed steps (its launches {w0} .. {w0 + ns - 1} at "
-                  f"that shape): rocprofv3 average {sum(v) / len(v):.1f} us (min {min(v):.1f}, max "
+                  f"({blocks} blocks), the bench's {ns} event-timed steps (its launches {w0} .. {w0 + ns - 1} "
+                  f"at that shape): rocprofv3 average {sum(v) / len(v):.1f} us (min {min(v):.1f}, max "
                   f"{max(v):.1f}); the same run's bench line measured {rl['avg_launch_ms'] * 1e3:.1f} us with "
                   f"HIP events around the kernel over those steps, {rl['achieved']:.1f} GB/s of compressed "
                   f"bytes = {rl['frac']:.2%} of 8 TB/s."]
@@ -721,18 +726,28 @@ def main():
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    # per step: [step start, split-K start, split-K done, step done]; all on the
+    # the timed steps: one event pair around all of them, nothing recorded
+    # in between (an event between two kernels is a gap of its own)
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev_a.record()
+    for k in range(args.steps):
+        step(args.warmup + k)
+    ev_b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_s = max(wall, ev_a.elapsed_time(ev_b) / 1e3)
+    # the same steps again (re-encoding a step's tokens into the same slots
+    # writes the same bytes), now with events per step: [step start, split-K
+    # start, split-K done, step done], for the kernel's own time; all on the
     # current stream, which is the one every library launch goes to
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for k in range(args.steps):
         step(args.warmup + k, evs[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     att_ms = [evs[k][0].elapsed_time(evs[k][3]) for k in range(args.steps)]
-    ev_total = evs[0][0].elapsed_time(evs[-1][3])
-    total_s = max(wall, ev_total / 1e3)
     timed_bytes = sum(bytes_s[args.warmup:])
     ms_per_step = total_s * 1e3 / args.steps
     value = timed_bytes / total_s / 1e9
