@@ -643,6 +643,36 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
   flush_stats(a, bstat, lane);
 }
 
+// Quantisation of the rotated coordinates against thresholds thr[1..NK]
+// (the magnitude is the count of those |y| reaches), packed 4 bits per
+// symbol, with the magnitude histogram as 8-bit counters (m = 0..3 in hl,
+// 4..7 in hh).
+template <int NK, int MAXH>
+__device__ __forceinline__ void quantize(const float (&y)[kD], const float (&thr)[MAXH], int h, bool degenerate,
+                                         uint32_t (&sym0)[16], uint32_t &hl, uint32_t &hh) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sym0[j] = 0u;
+#pragma unroll
+  for (int i = 0; i < kD; ++i) {
+    const float ay = __builtin_fabsf(y[i]);
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 1; k <= NK; ++k) m += ay >= thr[k] ? 1u : 0u;
+    const uint32_t inc = 1u << (8 * (m & 3u));
+    if (NK < 4) {
+      hl += inc;
+    } else {
+      hl += m < 4u ? inc : 0u;
+      hh += m < 4u ? 0u : inc;
+    }
+    const uint32_t sy = (degenerate || y[i] >= 0.0f) ? (uint32_t)h + m : (uint32_t)(h - 1) - m;
+    sym0[i >> 3] |= sy << (4 * (i & 7));
+    // finish each packed word and the counts here: otherwise the compiler
+    // keeps all 128 magnitudes, and y for their signs
+    if ((i & 7) == 7) asm volatile("" : "+v"(sym0[i >> 3]), "+v"(hl), "+v"(hh));
+  }
+}
+
 // Two passes for large batches.  encode_vector keeps neither the rotated
 // coordinates nor the plan across its rounds: its in-group order needs |y|
 // again, so it rotates a second time, and a wave runs every path that one of
@@ -664,7 +694,9 @@ __global__ void __launch_bounds__(kThreads, 2) encode_kernel(EncodeArgs a, Table
 constexpr uint16_t kPendingNorm = 0xFFFFu;  // never a norm: norm_half gives NaN as 0x7E00
 constexpr int kRestRange = 8192;            // vectors per encode_rest_kernel block
 
-template <int MAXH, bool RD>
+// NK: the thresholds quantisation tests (h - 1 when the launch knows h,
+// as for 6 levels; MAXH - 1 covers every h up to MAXH)
+template <int MAXH, bool RD, int NK = MAXH - 1>
 __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, Tables t) {
   __shared__ uint4 etab[kMaxLevels];
   __shared__ float2 rdtab[kMaxHalf];
@@ -690,31 +722,18 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
       const bool zero = nh == 0u;
       const bool bad = (nh & 0x7C00u) == 0x7C00u;
       const bool degenerate = zero || bad;
-      // quantisation and the magnitude histogram, as in encode_vector
+      // quantisation and the magnitude histogram, as in encode_vector; a
+      // degenerate vector's thresholds are NaN, so every |y| (inf too)
+      // compares below them: all magnitudes 0, as encode_vector's |y| = 0
       const float nf = half_to_float(nh);
       float thr[MAXH];
 #pragma unroll
       for (int k = 1; k < MAXH; ++k)
-        thr[k] = (k < h && !degenerate) ? (float)(k * t.step64) * nf * 0.015625f : __builtin_inff();
+        thr[k] = degenerate ? __builtin_nanf("")
+                            : (k < h ? (float)(k * t.step64) * nf * 0.015625f : __builtin_inff());
       uint32_t sym0[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sym0[j] = 0u;
       uint32_t hl = 0u, hh = 0u;
-#pragma unroll
-      for (int i = 0; i < kD; ++i) {
-        const float ay = degenerate ? 0.0f : __builtin_fabsf(y[i]);
-        uint32_t m = 0;
-#pragma unroll
-        for (int k = 1; k < MAXH; ++k) m += ay >= thr[k] ? 1u : 0u;
-        const uint32_t inc = 1u << (8 * (m & 3u));
-        hl += m < 4u ? inc : 0u;
-        hh += m < 4u ? 0u : inc;
-        const uint32_t sy = (degenerate || y[i] >= 0.0f) ? (uint32_t)h + m : (uint32_t)(h - 1) - m;
-        sym0[i >> 3] |= sy << (4 * (i & 7));
-        // finish each packed word and the counts here: otherwise the
-        // compiler keeps all 128 magnitudes, and y for their signs
-        if ((i & 7) == 7) asm volatile("" : "+v"(sym0[i >> 3]), "+v"(hl), "+v"(hh));
-      }
+      quantize<NK>(y, thr, h, degenerate, sym0, hl, hh);
       int cnt[MAXH];
       uint32_t I = 0u;
 #pragma unroll
@@ -1036,11 +1055,18 @@ hipError_t launch(const EncodeArgs &a, const Tables &t, hipStream_t s) {
   const unsigned blocks = (unsigned)((nvec + kThreads - 1) / kThreads);
   if (knob(DQ_KNOB_ENCODE_TWO_PASS) != 0) {
     const unsigned rest = (unsigned)((nvec + kRestRange - 1) / kRestRange);
+    // 6 levels (h = 3) test two thresholds instead of MAXH - 1 = 3
+    bool six = false;
+    if constexpr (MAXH == 4) six = t.half == 3;
     if (t.order == 1) {
-      hipLaunchKernelGGL((encode_fast_kernel<MAXH, true>), dim3(blocks), dim3(kThreads), 0, s, a, t);
+      if constexpr (MAXH == 4)
+        if (six) hipLaunchKernelGGL((encode_fast_kernel<4, true, 2>), dim3(blocks), dim3(kThreads), 0, s, a, t);
+      if (!six) hipLaunchKernelGGL((encode_fast_kernel<MAXH, true>), dim3(blocks), dim3(kThreads), 0, s, a, t);
       hipLaunchKernelGGL((encode_rest_kernel<MAXH, true>), dim3(rest), dim3(kThreads), 0, s, a, t);
     } else {
-      hipLaunchKernelGGL((encode_fast_kernel<MAXH, false>), dim3(blocks), dim3(kThreads), 0, s, a, t);
+      if constexpr (MAXH == 4)
+        if (six) hipLaunchKernelGGL((encode_fast_kernel<4, false, 2>), dim3(blocks), dim3(kThreads), 0, s, a, t);
+      if (!six) hipLaunchKernelGGL((encode_fast_kernel<MAXH, false>), dim3(blocks), dim3(kThreads), 0, s, a, t);
       hipLaunchKernelGGL((encode_rest_kernel<MAXH, false>), dim3(rest), dim3(kThreads), 0, s, a, t);
     }
     return hipGetLastError();
