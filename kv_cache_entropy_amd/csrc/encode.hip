@@ -795,16 +795,52 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
         const uint32_t blo = __float_as_uint((float)(gb * t.step64) * nf * 0.015625f);
         const uint32_t span = a.key_span, sat = (span << 7) + 128u;  // keys >= sat are clamped
         uint32_t key[kD];
+        if constexpr (MAXH == 4) {
+          // up to 8 levels, symbols below 8: eight nibbles of a packed word
+          // at a time.  Per nibble, t = s + 8 - h has bit 3 iff s >= h, and
+          // its low 3 bits give the magnitude (s - h, or h - 1 - s flipped
+          // from them); a symbol moves iff its magnitude >= gb + (full ? 0
+          // : 1), one level inward (s + 1 below h, s - 1 from h on).  No
+          // nibble carries into the next: every sum stays below 16.
+          const uint32_t hb = 0x11111111u * (uint32_t)(8 - h);
+          const uint32_t tb = 0x11111111u * (uint32_t)(8 - (full ? gb : gb + 1));
+          const uint32_t gbb = 0x11111111u * (uint32_t)gb;
+          // 2 (|y| bits - blo): the shift drops y's sign bit; exact for
+          // members, whose |y| >= the threshold; keys as in the other loop
+          const uint32_t nblo2 = 0u - (blo << 1), span2 = span << 1;
 #pragma unroll
-        for (int i = 0; i < kD; ++i) {
-          const uint32_t sv = nib(sym0, i);
-          const uint32_t mg = magnitude(sv, h);
-          const bool move = mg > (uint32_t)gb || (full && mg == (uint32_t)gb);
-          sym[i >> 3] |= (move ? inward(sv, h) : sv) << (4 * (i & 7));
-          const uint32_t d = (__float_as_uint(y[i]) & 0x7FFFFFFFu) - blo;  // members: |y| >= threshold
-          key[i] = mg == (uint32_t)gb ? (min(d, span) << 7) + (128u + (uint32_t)i) : 0u;
-          asm volatile("" : "+v"(key[i]));  // made here, while mg is at hand
-          if ((i & 7) == 7) asm volatile("" : "+v"(sym[i >> 3]));
+          for (int w = 0; w < 16; ++w) {
+            const uint32_t x = sym0[w];
+            const uint32_t tt = x + hb;
+            const uint32_t gen = (tt >> 3) & 0x11111111u;  // 1 where s >= h
+            const uint32_t ltn = gen ^ 0x11111111u;        // 1 where s < h
+            const uint32_t mag = (tt ^ ((ltn << 3) - ltn)) & 0x77777777u;
+            const uint32_t mv = ((mag + tb) >> 3) & 0x11111111u;
+            sym[w] = x + (mv & ltn) - (mv & gen);
+            // bit 3 of each nibble: magnitude == gb (z == 0)
+            const uint32_t z = mag ^ gbb;
+            const uint32_t eq = ~((z | 0x88888888u) - 0x11111111u) & 0x88888888u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int i = 8 * w + j;
+              const uint32_t dd = min((__float_as_uint(y[i]) << 1) + nblo2, span2);
+              key[i] = ((dd << 6) + (128u + (uint32_t)i)) & (uint32_t)__builtin_amdgcn_sbfe((int)eq, 4 * j + 3, 1);
+              asm volatile("" : "+v"(key[i]));  // made here, while eq is at hand
+            }
+            asm volatile("" : "+v"(sym[w]));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < kD; ++i) {
+            const uint32_t sv = nib(sym0, i);
+            const uint32_t mg = magnitude(sv, h);
+            const bool move = mg > (uint32_t)gb || (full && mg == (uint32_t)gb);
+            sym[i >> 3] |= (move ? inward(sv, h) : sv) << (4 * (i & 7));
+            const uint32_t d = (__float_as_uint(y[i]) & 0x7FFFFFFFu) - blo;  // members: |y| >= threshold
+            key[i] = mg == (uint32_t)gb ? (min(d, span) << 7) + (128u + (uint32_t)i) : 0u;
+            asm volatile("" : "+v"(key[i]));  // made here, while mg is at hand
+            if ((i & 7) == 7) asm volatile("" : "+v"(sym[i >> 3]));
+          }
         }
         uint32_t p1 = 1u;  // every key taken so far is below p1
         for (int j = 0; j < want; ++j) {
