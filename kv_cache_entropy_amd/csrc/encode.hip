@@ -681,8 +681,7 @@ __device__ __forceinline__ void quantize(const float (&y)[kD], const float (&thr
 //  - encode_fast_kernel runs round 0 of the search with y kept in registers
 //    from the first rotation: the plan, the in-group keys made from y, the
 //    one or two rANS passes.  The cases it leaves are rare: a vector whose
-//    round 0 cannot fit (more rounds), a next candidate that has to come
-//    from a lower group (a float scan), a key at the span's clamp.  Those
+//    round 0 cannot fit (more rounds), a key at the span's clamp.  Those
 //    in-pool vectors get kPendingNorm in their norm slot;
 //  - encode_rest_kernel gathers the pending vectors of 8192 consecutive
 //    ones into a list and runs encode_vector on it.  Vectors outside the
@@ -786,13 +785,31 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
           }
         }
         const bool want_next = undecided && sure;
-        // the next candidate from a lower group needs the float scan
-        pending = pending || (want_next && (full || rest == cnt[gb]));
-        const int want = pending || full ? 0 : rest + (want_next ? 1 : 0);
+        // When the undecided prefix uses up the boundary group, the next
+        // candidate is the smallest |y| of the next lower non-empty group
+        // (encode_vector's float scan): every member of the boundary group
+        // moves, and the keys are made for that lower group (kg) instead,
+        // so one extraction gives it.  No such group: the second kernel.
+        const bool scan = want_next && (full || rest == cnt[gb]);
+        int kg = gb;
+        if (scan) {
+          const int start = k == 0 ? h - 1 : gb - 1;
+          bool found = false;
+#pragma unroll
+          for (int m = MAXH - 1; m >= 1; --m)
+            if (!found && m <= start && cnt[m] > 0) {
+              kg = m;
+              found = true;
+            }
+          pending = pending || !found;
+        }
+        const bool whole = full || scan;  // the boundary group moves whole
+        const int taken = scan ? 0 : rest;  // members taken in key order
+        const int want = pending ? 0 : (scan ? 1 : (full ? 0 : rest + (want_next ? 1 : 0)));
         // one pass: the symbols with the whole-group moves applied, and the
-        // boundary group's in-group keys made from y, as encode_vector makes
-        // them from its second rotation (the same bits); 0 for the others
-        const uint32_t blo = __float_as_uint((float)(gb * t.step64) * nf * 0.015625f);
+        // key group's in-group keys made from y, as encode_vector makes them
+        // from its second rotation (the same bits); 0 for the others
+        const uint32_t blo = __float_as_uint((float)(kg * t.step64) * nf * 0.015625f);
         const uint32_t span = a.key_span, sat = (span << 7) + 128u;  // keys >= sat are clamped
         uint32_t key[kD];
         if constexpr (MAXH == 4) {
@@ -803,8 +820,8 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
           // : 1), one level inward (s + 1 below h, s - 1 from h on).  No
           // nibble carries into the next: every sum stays below 16.
           const uint32_t hb = 0x11111111u * (uint32_t)(8 - h);
-          const uint32_t tb = 0x11111111u * (uint32_t)(8 - (full ? gb : gb + 1));
-          const uint32_t gbb = 0x11111111u * (uint32_t)gb;
+          const uint32_t tb = 0x11111111u * (uint32_t)(8 - (whole ? gb : gb + 1));
+          const uint32_t gbb = 0x11111111u * (uint32_t)kg;
           // 2 (|y| bits - blo): the shift drops y's sign bit; exact for
           // members, whose |y| >= the threshold; keys as in the other loop
           const uint32_t nblo2 = 0u - (blo << 1), span2 = span << 1;
@@ -817,7 +834,7 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
             const uint32_t mag = (tt ^ ((ltn << 3) - ltn)) & 0x77777777u;
             const uint32_t mv = ((mag + tb) >> 3) & 0x11111111u;
             sym[w] = x + (mv & ltn) - (mv & gen);
-            // bit 3 of each nibble: magnitude == gb (z == 0)
+            // bit 3 of each nibble: magnitude == kg (z == 0)
             const uint32_t z = mag ^ gbb;
             const uint32_t eq = ~((z | 0x88888888u) - 0x11111111u) & 0x88888888u;
 #pragma unroll
@@ -834,10 +851,10 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
           for (int i = 0; i < kD; ++i) {
             const uint32_t sv = nib(sym0, i);
             const uint32_t mg = magnitude(sv, h);
-            const bool move = mg > (uint32_t)gb || (full && mg == (uint32_t)gb);
+            const bool move = mg > (uint32_t)gb || (whole && mg == (uint32_t)gb);
             sym[i >> 3] |= (move ? inward(sv, h) : sv) << (4 * (i & 7));
             const uint32_t d = (__float_as_uint(y[i]) & 0x7FFFFFFFu) - blo;  // members: |y| >= threshold
-            key[i] = mg == (uint32_t)gb ? (min(d, span) << 7) + (128u + (uint32_t)i) : 0u;
+            key[i] = mg == (uint32_t)kg ? (min(d, span) << 7) + (128u + (uint32_t)i) : 0u;
             asm volatile("" : "+v"(key[i]));  // made here, while mg is at hand
             if ((i & 7) == 7) asm volatile("" : "+v"(sym[i >> 3]));
           }
@@ -856,7 +873,7 @@ __global__ void __launch_bounds__(kThreads, 2) encode_fast_kernel(EncodeArgs a, 
           }
           p1 = kw + 1u;
           const int i = (int)(kw & 127u);
-          if (j < rest) move_inward(sym, i, h);
+          if (j < taken) move_inward(sym, i, h);
           else nxt = i;
         }
       } else {
