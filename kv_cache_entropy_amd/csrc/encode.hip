@@ -997,23 +997,48 @@ __global__ void __launch_bounds__(kThreads, 2) encode_rest_kernel(EncodeArgs a, 
   const int64_t nvec = a.T * (int64_t)t.hkv;
   const int64_t v0 = (int64_t)blockIdx.x * kRestRange;
   const int64_t v1 = min(v0 + (int64_t)kRestRange, nvec);
-  for (int64_t c = v0; c < v1; c += kThreads) {
-    const int64_t vid = c + lane;
-    bool pend = false;
-    if (vid < v1) {
-      const int g = (int)(vid / a.T);
-      const int64_t tok = vid - (int64_t)g * a.T;
-      const int64_t slot = a.slots[tok];
-      pend = (slot >= 0 && slot < a.num_slots) ? a.norm[(int64_t)g * a.num_slots + slot] == kPendingNorm
-                                               : a.stats != nullptr;
+  // (head, token) of the range's first vector once; the others step from
+  // it (no division per vector when a head holds at least a range), four
+  // vectors per lane per round so that their loads overlap
+  const int64_t g0 = v0 / a.T, r0 = v0 - g0 * a.T;
+  constexpr int kU = 4;
+  for (int64_t c = 0; c < v1 - v0; c += kU * kThreads) {
+    int64_t slot[kU], head[kU];
+    bool live[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t off = c + u * kThreads + lane;
+      live[u] = off < v1 - v0;
+      int64_t r = r0 + off, g = g0;
+      if (a.T >= kRestRange) {
+        if (r >= a.T) {  // the range spans at most two heads
+          r -= a.T;
+          ++g;
+        }
+      } else {
+        g += r / a.T;
+        r -= (r / a.T) * a.T;
+      }
+      head[u] = g;
+      slot[u] = live[u] ? a.slots[r] : -1;
     }
-    // the wave's pending lanes take consecutive list entries
-    const uint64_t m = __ballot(pend);
-    uint32_t base = 0u;
-    if ((lane & 63) == 0 && m) base = atomicAdd(&nlist, (uint32_t)__popcll(m));
-    base = (uint32_t)__shfl((int)base, 0);
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-    if (pend) list[base + rank] = (uint16_t)(vid - v0);
+    bool pend[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      pend[u] = live[u] && ((slot[u] >= 0 && slot[u] < a.num_slots)
+                                ? a.norm[head[u] * a.num_slots + slot[u]] == kPendingNorm
+                                : a.stats != nullptr);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      // the wave's pending lanes take consecutive list entries
+      const uint64_t m = __ballot(pend[u]);
+      uint32_t base = 0u;
+      if ((lane & 63) == 0 && m) base = atomicAdd(&nlist, (uint32_t)__popcll(m));
+      base = (uint32_t)__shfl((int)base, 0);
+      const uint32_t rank =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (pend[u]) list[base + rank] = (uint16_t)(c + u * kThreads + lane);
+    }
   }
   __syncthreads();
   const int n = (int)nlist;

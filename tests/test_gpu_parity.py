@@ -179,15 +179,16 @@ def test_encode_strided_input_and_pool_slots(oracle_lib, encode_path):
     assert int(cont[:, :1000].abs().sum()) == 0
 
 
-@pytest.mark.parametrize("levels,C,order", [(8, 34, 0), (6, 29, 0), (6, 29, 1), (8, 29, 1)])
-def test_encode_two_pass_many_blocks(oracle_lib, knob, levels, C, order):
+@pytest.mark.parametrize("levels,C,order,T,hkv", [(8, 34, 0, 3072, 4), (6, 29, 0, 3072, 4), (6, 29, 1, 3072, 4),
+                                                  (8, 29, 1, 3072, 4), (6, 34, 0, 9000, 2)])
+def test_encode_two_pass_many_blocks(oracle_lib, knob, levels, C, order, T, hkv):
     """The two-pass lane encoder over several 8192-vector ranges of its
-    second pass (12288 vectors, heavy-tailed data so that many need the
-    drift search): bytes, norms and stats equal to the one-pass kernel's and
-    to the oracle's."""
+    second pass (12288 or 18000 vectors, heavy-tailed data so that many need
+    the drift search; heads shorter than a range, and longer, so that a
+    range starts inside a head and spans two): bytes, norms and stats equal
+    to the one-pass kernel's and to the oracle's."""
     O = oracle_lib
-    _say(f"two-pass {levels}/{C} order {order}")
-    T, hkv = 3072, 4
+    _say(f"two-pass {levels}/{C} order {order} T {T} hkv {hkv}")
     gc, oc = _codecs(O, levels, C, seed=211 + levels, hkv=hkv, order=order)
     x = synth.kv_tensor("student_t5", T, hkv, seed=212, device=DEV)
     slots = torch.randperm(T + 100, generator=torch.Generator().manual_seed(213))[:T].to(DEV)
