@@ -194,52 +194,53 @@ def summarize_profiles(d):
     with open(os.path.join(out_dir, f"all_kernels_{wl}_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    # ---- HBM counters (of that kernel)
-    def per_kernel(kind, counter):
-        rows = _csv(_find(os.path.join(d, kind), "counter_collection.csv"))
-        rows = [r for r in rows if r["Counter_Name"] == counter]
-        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        cal = max(copies, key=lambda r: float(r["Counter_Value"]))
-        att = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]]
-        bl = _bench_line(os.path.join(d, f"{kind}_bench.json"))
-        if bl.get("attn_source_sha256_16") != src:
-            raise SystemExit(f"{kind} run was made on a different attention source")
-        return float(cal["Counter_Value"]), att
-    f_cal, f_att = per_kernel("fetch", "FETCH_SIZE")
-    w_cal, w_att = per_kernel("write", "WRITE_SIZE")
-    gib_kib = float(1 << 20)
-    f_scale, w_scale = gib_kib / f_cal, gib_kib / w_cal
-    fetch_b = sum(f_att) / len(f_att) * 1024 * f_scale
-    write_b = sum(w_att) / len(w_att) * 1024 * w_scale
-    alg = rl["alg_bytes_per_launch"]
-    rec = {"kernel": kname, "workload": wl, "source_sha256_16": src,
-           "fetch_kib_per_launch_raw": sum(f_att) / len(f_att), "write_kib_per_launch_raw": sum(w_att) / len(w_att),
-           "launches": [len(f_att), len(w_att)],
-           "copy_1gib_fetch_kib": f_cal, "copy_1gib_write_kib": w_cal,
-           "fetch_scale": f_scale, "write_scale": w_scale,
-           "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
-           "traffic_bytes_per_launch": fetch_b + write_b,
-           "alg_bytes_per_launch": alg, "traffic_over_alg": (fetch_b + write_b) / alg,
-           "commands": [PROFILE_CMDS["fetch"], PROFILE_CMDS["write"]]}
-    with open(os.path.join(out_dir, f"attn_splitk_{wl}_counters.json"), "w") as f:
-        json.dump(rec, f, indent=1)
-        f.write("\n")
-    md = [f"# HBM counters: {kname}, {wl}", "",
-          "Commands (from the repository root), one counter per run:", "", "```",
-          PROFILE_CMDS["fetch"], PROFILE_CMDS["write"], "```", "",
-          "| | FETCH_SIZE | WRITE_SIZE |", "|---|---:|---:|",
-          f"| 1 GiB device copy (KiB) | {f_cal:.0f} | {w_cal:.0f} |",
-          f"| scale to bytes moved | {f_scale:.3f} | {w_scale:.3f} |",
-          f"| split-K kernel, raw KiB per launch | {rec['fetch_kib_per_launch_raw']:.0f} | "
-          f"{rec['write_kib_per_launch_raw']:.0f} |",
-          f"| split-K kernel, scaled MB per launch | {fetch_b / 1e6:.1f} | {write_b / 1e6:.1f} |", "",
-          f"Algorithmic bytes per launch (containers + fp16 norms of every context token, K and V): "
-          f"{alg / 1e6:.1f} MB.  Measured traffic {(fetch_b + write_b) / 1e6:.1f} MB = "
-          f"{rec['traffic_over_alg']:.3f} x algorithmic; the writes are the split-K partial results and the "
-          f"appended tokens' containers.", ""]
-    with open(os.path.join(out_dir, f"attn_splitk_{wl}_counters.md"), "w") as f:
-        f.write("\n".join(md) + "\n")
-    print(f"wrote profiles for source {src}: traffic {(fetch_b + write_b) / 1e6:.1f} MB per launch")
+    # ---- HBM counters (of that kernel); kept as they are when this run has none
+    if os.path.isdir(os.path.join(d, "fetch")) and os.path.isdir(os.path.join(d, "write")):
+        def per_kernel(kind, counter):
+            rows = _csv(_find(os.path.join(d, kind), "counter_collection.csv"))
+            rows = [r for r in rows if r["Counter_Name"] == counter]
+            copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+            cal = max(copies, key=lambda r: float(r["Counter_Value"]))
+            att = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]]
+            bl = _bench_line(os.path.join(d, f"{kind}_bench.json"))
+            if bl.get("attn_source_sha256_16") != src:
+                raise SystemExit(f"{kind} run was made on a different attention source")
+            return float(cal["Counter_Value"]), att
+        f_cal, f_att = per_kernel("fetch", "FETCH_SIZE")
+        w_cal, w_att = per_kernel("write", "WRITE_SIZE")
+        gib_kib = float(1 << 20)
+        f_scale, w_scale = gib_kib / f_cal, gib_kib / w_cal
+        fetch_b = sum(f_att) / len(f_att) * 1024 * f_scale
+        write_b = sum(w_att) / len(w_att) * 1024 * w_scale
+        alg = rl["alg_bytes_per_launch"]
+        rec = {"kernel": kname, "workload": wl, "source_sha256_16": src,
+               "fetch_kib_per_launch_raw": sum(f_att) / len(f_att), "write_kib_per_launch_raw": sum(w_att) / len(w_att),
+               "launches": [len(f_att), len(w_att)],
+               "copy_1gib_fetch_kib": f_cal, "copy_1gib_write_kib": w_cal,
+               "fetch_scale": f_scale, "write_scale": w_scale,
+               "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+               "traffic_bytes_per_launch": fetch_b + write_b,
+               "alg_bytes_per_launch": alg, "traffic_over_alg": (fetch_b + write_b) / alg,
+               "commands": [PROFILE_CMDS["fetch"], PROFILE_CMDS["write"]]}
+        with open(os.path.join(out_dir, f"attn_splitk_{wl}_counters.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        md = [f"# HBM counters: {kname}, {wl}", "",
+              "Commands (from the repository root), one counter per run:", "", "```",
+              PROFILE_CMDS["fetch"], PROFILE_CMDS["write"], "```", "",
+              "| | FETCH_SIZE | WRITE_SIZE |", "|---|---:|---:|",
+              f"| 1 GiB device copy (KiB) | {f_cal:.0f} | {w_cal:.0f} |",
+              f"| scale to bytes moved | {f_scale:.3f} | {w_scale:.3f} |",
+              f"| split-K kernel, raw KiB per launch | {rec['fetch_kib_per_launch_raw']:.0f} | "
+              f"{rec['write_kib_per_launch_raw']:.0f} |",
+              f"| split-K kernel, scaled MB per launch | {fetch_b / 1e6:.1f} | {write_b / 1e6:.1f} |", "",
+              f"Algorithmic bytes per launch (containers + fp16 norms of every context token, K and V): "
+              f"{alg / 1e6:.1f} MB.  Measured traffic {(fetch_b + write_b) / 1e6:.1f} MB = "
+              f"{rec['traffic_over_alg']:.3f} x algorithmic; the writes are the split-K partial results and the "
+              f"appended tokens' containers.", ""]
+        with open(os.path.join(out_dir, f"attn_splitk_{wl}_counters.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
+        print(f"wrote profiles for source {src}: traffic {(fetch_b + write_b) / 1e6:.1f} MB per launch")
     if os.path.isdir(os.path.join(d, "sq")):
         summarize_sq(d, kname, wl, src)
     if os.path.isdir(os.path.join(d, "trace_c4")):
