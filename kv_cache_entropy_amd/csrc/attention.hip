@@ -271,10 +271,15 @@ __device__ __forceinline__ void renorm(uint32_t &x, lds_u8 *&p, uint32_t byte) {
 // byte is k, the number of bytes the group has taken so far.
 typedef const volatile __attribute__((address_space(3))) u32x2_a4 lds_u32x2_a4;
 constexpr uint32_t kSel0 = 0x06050400u;
-__device__ __forceinline__ uint32_t byte_window(lds_u8 *p) {
+// (The two dwords are loaded first and shifted later, so the caller can
+// issue other loads before waiting for them.)
+__device__ __forceinline__ uint2 byte_window_load(lds_u8 *p) {
   const uint32_t a = (uint32_t)(uintptr_t)p;
   const u32x2_a4 d = *(lds_u32x2_a4 *)(uintptr_t)(a & ~3u);
-  return __builtin_amdgcn_alignbyte(d.y, d.x, a);  // bytes a .. a + 3
+  return make_uint2(d.x, d.y);
+}
+__device__ __forceinline__ uint32_t byte_window_shift(uint2 d, lds_u8 *p) {
+  return __builtin_amdgcn_alignbyte(d.y, d.x, (uint32_t)(uintptr_t)p);  // bytes p .. p + 3
 }
 __device__ __forceinline__ void renorm_window(uint32_t &x, uint32_t w, uint32_t &sel) {
   const bool need = x < kLow;
@@ -391,27 +396,39 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
       constexpr int gq = decltype(gc)::value;
       constexpr int G = p * (kDPass / 4) + gq;
       uint32_t lv[4];
-      // the group's renormalisation bytes (volatile loads, issued first)
       uint32_t wk = 0, wv = 0, selk = kSel0, selv = kSel0;
-      if (DK) wk = byte_window(pk);
-      if (DV) wv = byte_window(pv);
+      uint2 dwk = make_uint2(0, 0), dwv = make_uint2(0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // the two chains' loads are issued in this order (volatile), so
-        // each LDS round trip of one chain overlaps the other's
+        // each LDS round trip of one chain overlaps the other's.  The
+        // group's renormalisation bytes are read in its first step, after
+        // the table read that step's renorm waits for anyway: in the order
+        // results are used (LDS returns in order), never on their own.
         uint32_t ak = 0, av = 0;
         uint2 ek = make_uint2(0, 0), ev = make_uint2(0, 0);
         if (SLOT) {
           if (DK) ak = slot_of(xk);
           if (DV) av = slot_of(xv);
           if (DK) ek = lookup_slot(tk, ak);
+          if (DK && j == 0) dwk = byte_window_load(pk);
           if (DV) ev = lookup_slot(tv, av);
+          if (DV && j == 0) dwv = byte_window_load(pv);
         } else {
           uint32_t sk = 0, sv = 0;
           if (DK) sk = lookup_sym8(tk, xk);
           if (DV) sv = lookup_sym8(tv, xv);
+          if (DK && j == 0) dwk = byte_window_load(pk);
+          if (DV && j == 0) dwv = byte_window_load(pv);
           if (DK) ek = lookup_symtab(tk, sk);
           if (DV) ev = lookup_symtab(tv, sv);
+        }
+        if (j == 0) {
+          // the windows' byte shifts (and so their waits) stay below the
+          // step's loads
+          __builtin_amdgcn_sched_barrier(0);
+          if (DK) wk = byte_window_shift(dwk, pk);
+          if (DV) wv = byte_window_shift(dwv, pv);
         }
         if (DK) {
           xk = SLOT ? rans_advance_slot(xk, ak, ek) : rans_advance(xk, ek);
