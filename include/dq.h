@@ -51,7 +51,7 @@ const char *dq_status_string(int status);
 
 /* ABI version: 100 * major + minor (101: dq_codec_desc.drift_order; 102: decode
  * with append; 103: dq_set_knob, dq_attn_decode_noalloc; 104:
- * DQ_KNOB_ENCODE_TWO_PASS). */
+ * DQ_KNOB_ENCODE_TWO_PASS; 105: DQ_KNOB_QK_VALU). */
 int dq_version(void);
 
 /* Path overrides, for tests and tuning.  Every value the library can pick by
@@ -84,6 +84,14 @@ int dq_version(void);
  *                            a first kernel encodes the vectors that need no
  *                            drift and a second runs the search on the rest
  *                            (same bytes, norms and stats)
+ *   DQ_KNOB_QK_VALU          1: decode attention's query-key products as fp32
+ *                            fused multiply-adds on the vector ALU (the
+ *                            rotated query read from global memory, four
+ *                            dims at a time) instead of 4x4x4 MFMAs; a
+ *                            measurement variant of the per-slot-table
+ *                            kernel without appended encodes (other
+ *                            launches ignore it).  Scores differ from the
+ *                            MFMA path by fp32 rounding only.
  * dq_set_knob returns DQ_ERR_INVALID for an unknown knob or a value below
  * -1; dq_get_knob returns the value (or DQ_ERR_INVALID). */
 enum {
@@ -96,7 +104,8 @@ enum {
   DQ_KNOB_WORK_QUEUE = 7,
   DQ_KNOB_SLOT_TABLE = 8,
   DQ_KNOB_ENCODE_TWO_PASS = 9,
-  DQ_KNOB_COUNT = 10
+  DQ_KNOB_QK_VALU = 10,
+  DQ_KNOB_COUNT = 11
 };
 int dq_set_knob(int knob, int64_t value);
 int64_t dq_get_knob(int knob);

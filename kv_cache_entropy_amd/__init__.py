@@ -51,7 +51,7 @@ def _check(status: int, what: str):
 # except for the split length (floating-point order of the attention sums).
 KNOBS = {"split_tokens": 1, "latency_mode": 2, "append_fuse": 3, "encode_wave_max": 4,
          "encode_key_span": 5, "splitk_waves": 6, "work_queue": 7, "slot_table": 8,
-         "encode_two_pass": 9}
+         "encode_two_pass": 9, "qk_valu": 10}
 
 
 def set_knob(name: str, value) -> None:

@@ -166,6 +166,29 @@ __device__ __forceinline__ void rotate_q_wave(const AttnArgs &a, uint64_t kseed,
   qreg[1] = t4[64 + lane];
 }
 
+// The rotated query of kv group g of sequence b in fp32 for the VALU QK
+// variant: dst[4 d + h] = q~_h[d] (2 KB, heads past the group size zero),
+// visible to the whole wave when this returns.
+__device__ __forceinline__ void rotate_q_global(const AttnArgs &a, uint64_t kseed, int b, int g, float *dst,
+                                                int lane) {
+  const uint64_t w0 = dev_splitmix64(kseed, 2ull * (uint64_t)g);
+  const uint64_t w1 = dev_splitmix64(kseed, 2ull * (uint64_t)g + 1ull);
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    float v0 = 0.0f, v1 = 0.0f;
+    if (hh < a.group) rotate_q_head(a.q + ((int64_t)b * a.Hq + g * a.group + hh) * kD, w0, w1, lane, v0, v1);
+    dst[4 * lane + hh] = v0;
+    dst[4 * (lane + 64) + hh] = v1;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");  // stores done, stale L1 lines dropped
+}
+
+// Four floats at one address for the whole wave (a typed global load, so it
+// waits on the vector-memory counter, not the LDS one).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) f32x4 global_f32x4;
+__device__ __forceinline__ f32x4 load_global_f4(const float *p) { return *(global_f32x4 *)p; }
+
 __device__ __forceinline__ uint32_t load_le32(const uint8_t *p) {
   return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
 }
@@ -372,10 +395,18 @@ __device__ __forceinline__ void load_p(const uint16_t *pl, int lane, half4 &Ph, 
 // FULLV (latency mode): K and V of the same tile; the V levels of all 128
 // dims stay in the V tile for pv_full after the tile's softmax, and no PV
 // runs inside the pass.
-template <bool DK, bool DV, bool FULLV = false, bool SLOT = false>
+//
+// VQK (measurement variant): the K scores as fp32 fused multiply-adds on the
+// vector ALU, sc[h] += level * q~_h[d] in dim order, with q~ read from
+// global memory (qg, [dim][head]) one group of 4 dims ahead: qb holds the
+// first group's values on entry and, on return, those the next pass starts
+// with (loaded before the caller's next tile fetch, which they then need
+// not wait for).
+template <bool DK, bool DV, bool FULLV = false, bool SLOT = false, bool VQK = false>
 __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, const uint8_t *kb,
                                           const uint8_t *vb, const uint4 (&qreg)[2], const uint16_t *pl,
-                                          uint16_t *vt, floatx4 &sc, floatx4 (&acc)[8], int lane) {
+                                          uint16_t *vt, floatx4 &sc, floatx4 (&acc)[8], int lane,
+                                          const float *qg = nullptr, f32x4 *qb = nullptr) {
   half4 Ph = {}, Pl = {};
   if (DV && !FULLV) load_p(pl, lane, Ph, Pl);
   const uint32_t *vrow = reinterpret_cast<const uint32_t *>(vt) + (lane & 15) * (kVtStride / 2) + (lane >> 4) * 8;
@@ -443,7 +474,18 @@ __device__ __forceinline__ void tile_pass(const DecTab tk, const DecTab tv, cons
       }
       if (DK) pk += selk - kSel0;
       if (DV) pv += selv - kSel0;
-      if (DK) {
+      if (DK && VQK) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float l = (float)__builtin_bit_cast(_Float16, (uint16_t)(lv[j] >> 16));
+#pragma unroll
+          for (int h = 0; h < 4; ++h) sc[h] = __builtin_fmaf(l, qb[j][h], sc[h]);
+        }
+        // the next group's q~ (after the last group: the next pass's first)
+        constexpr int Gn = (G + 1) % (kD / 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qb[j] = load_global_f4(qg + 4 * (4 * Gn + j));
+      } else if (DK) {
         const uint32_t b01 = __builtin_amdgcn_perm(lv[1], lv[0], 0x07060302u);
         const uint32_t b23 = __builtin_amdgcn_perm(lv[3], lv[2], 0x07060302u);
         const half4 Bk = __builtin_bit_cast(half4, make_uint2(b01, b23));
@@ -639,9 +681,10 @@ __device__ __forceinline__ void append_vector(const AttnArgs &a, const Tables &t
 // arithmetic and its order are those of the pipelined mode.
 // SLOT: the per-slot decode tables (64 KB for K and V), so a decode step is
 // one LDS round trip; otherwise the byte table and the symbol entries.
-template <int NQ, bool APPEND, bool LAT = false, bool SLOT = false>
+template <int NQ, bool APPEND, bool LAT = false, bool SLOT = false, bool VQK = false>
 __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnArgs a, Tables tk, Tables tv) {
   static_assert(!(LAT && SLOT), "latency mode keeps the byte tables: its whole V tiles leave no room");
+  static_assert(!VQK || (SLOT && !APPEND), "the VALU QK variant is built for the plain per-slot-table kernel");
   // decode tables at fixed LDS addresses (static), per-wave slices after them
   __shared__ uint2 slot_ent[2][SLOT ? kM : 1];
   __shared__ uint8_t sym8[2][SLOT ? 1 : kM];
@@ -732,17 +775,31 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
     const int64_t plane0 = (int64_t)g * a.S;
     // pool index of the first token of tile `tile` of this item: a page is
     // one tile, so a tile's containers are contiguous in either layout
+    // (the sequence's start is read once per item: a read per tile would
+    // follow the tile prefetch, and waiting for it would wait for that too)
+    const int64_t seq0 = a.pages ? 0 : a.seq_start[b];
     auto tile_base = [&](int tile) -> int64_t {
       const int t = t0 + tile * kTile;
       return a.pages ? plane0 + (int64_t)a.pages[(int64_t)b * a.max_pages + t / kTile] * kTile
-                     : plane0 + a.seq_start[b] + t;
+                     : plane0 + seq0 + t;
     };
 
     wave_sync();  // the previous item's LDS reads are done
     // rotated query of this (sequence, kv head): lane l holds dim groups
     // l / 4 and 16 + l / 4 of head l mod 4 (8 VGPRs for the whole item)
-    uint4 qreg[2];
-    rotate_q_wave(a, tk.seed, b, g, vt, qreg, lane);
+    uint4 qreg[2] = {};
+    const float *qg = nullptr;
+    f32x4 qb[4];  // VQK: the q~ group a K pass starts with
+    if (VQK) {
+      // the item's partial slot holds q~ until the partial overwrites it
+      float *qs = a.part + pidx * 4 * kPart;
+      rotate_q_global(a, tk.seed, b, g, qs, lane);
+      qg = qs;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qb[j] = load_global_f4(qg + 4 * j);
+    } else {
+      rotate_q_wave(a, tk.seed, b, g, vt, qreg, lane);
+    }
 
     // this lane's token norms for a tile (0 outside the pool plane)
     auto norms = [&](int64_t tbase, uint32_t &nk, uint32_t &nv) {
@@ -817,7 +874,8 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
 #pragma unroll
     for (int p = 0; p < 8; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
     floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-    tile_pass<true, false, false, SLOT>(dk, dv, kst + koff0 + tok * Ck, nullptr, qreg, pl, vt, sc, acc, lane);
+    tile_pass<true, false, false, SLOT, VQK>(dk, dv, kst + koff0 + tok * Ck, nullptr, qreg, pl, vt, sc, acc, lane,
+                                             qg, qb);
     softmax_tile(sc, nk0, nv0, tok < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
 
     for (int j = 0; j < ntiles; ++j) {
@@ -831,22 +889,25 @@ __global__ void __launch_bounds__(NQ == 3 ? 768 : 256) attn_splitk_kernel(AttnAr
         koff = rk.off;
       }
       wave_sync();
-      // prefetch the next iteration's tiles into registers
+      // prefetch the next iteration's tiles into registers; the K tile's
+      // base first (in a paged pool a page-table read, which would otherwise
+      // wait for the V tile's loads issued before it)
       uint32_t nk2 = 0, nv2 = 0;
+      const int64_t base2 = j + 2 < ntiles ? tile_base(j + 2) : 0;
       if (next) fetch<NQ>(rv, a.vc + vbase * Cv, kTile * Cv, a.vc, vpool_end, lane);
       if (j + 2 < ntiles) {
-        const int64_t base2 = tile_base(j + 2);
         fetch<NQ>(rk, a.kc + base2 * Ck, kTile * Ck, a.kc, kpool_end, lane);
         norms(base2, nk2, nv2);
         vbase = base2;
       }
       if (next) {
         sc = floatx4{0.f, 0.f, 0.f, 0.f};
-        tile_pass<true, true, false, SLOT>(dk, dv, kst + koff + tok * Ck, vst + voff + tok * Cv, qreg, pl, vt, sc,
-                                           acc, lane);
+        tile_pass<true, true, false, SLOT, VQK>(dk, dv, kst + koff + tok * Ck, vst + voff + tok * Cv, qreg, pl, vt,
+                                                sc, acc, lane, qg, qb);
         softmax_tile(sc, nk1, nv1, (j + 1) * kTile + tok < t1 - t0, a.qk_scale, m_run, l_lane, pl, acc, lane);
       } else {
-        tile_pass<false, true, false, SLOT>(dk, dv, nullptr, vst + voff + tok * Cv, qreg, pl, vt, sc, acc, lane);
+        tile_pass<false, true, false, SLOT, VQK>(dk, dv, nullptr, vst + voff + tok * Cv, qreg, pl, vt, sc, acc, lane,
+                                                 qg, qb);
       }
       nk1 = nk2;
       nv1 = nv2;
@@ -1285,7 +1346,8 @@ __global__ void __launch_bounds__(NQ == 3 ? 512 : 256) attn_prefill_kernel(AttnA
     const int t1 = min(t0 + a.chunk, pmax + 1);
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
     const int64_t plane0 = (int64_t)g * a.S;
-    auto tile_base = [&](int tile) -> int64_t { return plane0 + a.seq_start[b] + t0 + tile * kTile; };
+    const int64_t seq0 = a.seq_start[b];  // read once per item, not after each tile prefetch
+    auto tile_base = [&](int tile) -> int64_t { return plane0 + seq0 + t0 + tile * kTile; };
 
     wave_sync();
     const uint4 *qr = reinterpret_cast<const uint4 *>(a.qrot + ((bg * a.nqb) + qb) * kQrotPrefill);
@@ -1339,9 +1401,9 @@ __global__ void __launch_bounds__(NQ == 3 ? 512 : 256) attn_prefill_kernel(AttnA
       }
       wave_sync();
       uint32_t nk2 = 0, nv2 = 0;
+      const int64_t base2 = j + 2 < ntiles ? tile_base(j + 2) : 0;
       if (next) fetch<NQ>(rv, a.vc + vbase * Cv, kTile * Cv, a.vc, vpool_end, lane);
       if (j + 2 < ntiles) {
-        const int64_t base2 = tile_base(j + 2);
         fetch<NQ>(rk, a.kc + base2 * Ck, kTile * Ck, a.kc, kpool_end, lane);
         norms(base2, nk2, nv2);
         vbase = base2;
@@ -1800,18 +1862,18 @@ int make_plan(int B, int Hq, int Hkv, int64_t max_len, int Ck, int Cv, Plan *pl)
   return DQ_OK;
 }
 
-template <int NQ, bool APPEND, bool LAT = false, bool SLOT = false>
+template <int NQ, bool APPEND, bool LAT = false, bool SLOT = false, bool VQK = false>
 hipError_t launch_splitk(const Plan &pl, const AttnArgs &a, const Tables &tk, const Tables &tv, hipStream_t s) {
   // dynamic LDS beyond the default limit, requested once (thread-safe static)
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ, APPEND, LAT, SLOT>),
+      hipFuncSetAttribute(reinterpret_cast<const void *>(attn_splitk_kernel<NQ, APPEND, LAT, SLOT, VQK>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - (SLOT ? kSlotLds : kStaticLds));
   if (attr != hipSuccess) return attr;
   // the append's encode items (if this launch runs them) come first, one per wave
   const int64_t n = a.n_items + (APPEND ? a.n_enc : 0);
   const int64_t want = (n + pl.waves_per_block - 1) / pl.waves_per_block;
   const int blocks = (int)(want < pl.blocks_cap ? want : pl.blocks_cap);
-  hipLaunchKernelGGL((attn_splitk_kernel<NQ, APPEND, LAT, SLOT>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((attn_splitk_kernel<NQ, APPEND, LAT, SLOT, VQK>), dim3((unsigned)blocks),
                      dim3(64 * pl.waves_per_block), pl.lds, s, a, tk, tv);
   return hipGetLastError();
 }
@@ -2125,8 +2187,9 @@ static int attn_decode(dq_codec_t ck, dq_codec_t cv, const void *q, int32_t B, i
     e = app && a.n_enc > 0 ? dq::launch_splitk<3, true, true>(pl, a, ck->t, cv->t, s)
                            : dq::launch_splitk<3, false, true>(pl, a, ck->t, cv->t, s);
   else if (pl.slot)  // three-piece tile fetch with the per-slot tables
-    e = app && a.n_enc > 0 ? dq::launch_splitk<3, true, false, true>(pl, a, ck->t, cv->t, s)
-                           : dq::launch_splitk<3, false, false, true>(pl, a, ck->t, cv->t, s);
+    e = app && a.n_enc > 0            ? dq::launch_splitk<3, true, false, true>(pl, a, ck->t, cv->t, s)
+        : dq::knob(DQ_KNOB_QK_VALU) == 1 ? dq::launch_splitk<3, false, false, true, true>(pl, a, ck->t, cv->t, s)
+                                         : dq::launch_splitk<3, false, false, true>(pl, a, ck->t, cv->t, s);
   else if (app && a.n_enc > 0)  // the variant with the encode loop only when it has encodes to run
     e = pl.nq == 3   ? dq::launch_splitk<3, true>(pl, a, ck->t, cv->t, s)
         : pl.nq == 5 ? dq::launch_splitk<5, true>(pl, a, ck->t, cv->t, s)

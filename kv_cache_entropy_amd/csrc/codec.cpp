@@ -19,8 +19,8 @@ namespace dq {
 
 // Path overrides set through dq_set_knob: one relaxed atomic load per use,
 // so hot calls read no environment and race with nothing.
-static std::atomic<int64_t> g_knobs[DQ_KNOB_COUNT] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
-static_assert(DQ_KNOB_COUNT == 10, "one initialiser per knob");
+static std::atomic<int64_t> g_knobs[DQ_KNOB_COUNT] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+static_assert(DQ_KNOB_COUNT == 11, "one initialiser per knob");
 
 int64_t knob(int k) { return g_knobs[k].load(std::memory_order_relaxed); }
 
@@ -151,7 +151,7 @@ const char *dq_status_string(int status) {
   }
 }
 
-int dq_version(void) { return 104; }
+int dq_version(void) { return 105; }
 
 int dq_set_knob(int knob, int64_t value) {
   if (knob < 1 || knob >= DQ_KNOB_COUNT || value < -1) return DQ_ERR_INVALID;

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     L = _lib.lib()
-    assert L.dq_version() == 104
+    assert L.dq_version() == 105
     assert L.dq_status_string(0) == b"ok"
     for code in (-1, -2, -3, -4, -5):
         assert L.dq_status_string(code) not in (b"ok", b"unknown status")

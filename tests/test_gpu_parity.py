@@ -555,6 +555,39 @@ def test_attention_slot_tables_bit_identical(oracle_lib, knob, Hq, hkv, lens, C,
     _assert_close(res[1][0].cpu().numpy(), _oracle_attn(O, c), f"slot tables Hq={Hq} hkv={hkv}")
 
 
+@pytest.mark.parametrize("Hq,hkv,lens,C,step64,split", [
+    (8, 2, [1, 63, 64, 65, 300, 129, 2000], (34, 34), (0, 0), None),
+    (4, 4, [5000, 70], (29, 29), (0, 0), 640),
+    (1, 1, [128, 1], (34, 29), (0, 0), 64),
+    (4, 2, [3000, 4097], (38, 29), (66, 0), None),
+])
+def test_attention_qk_valu_variant(oracle_lib, knob, Hq, hkv, lens, C, step64, split):
+    """The measurement variant with the query-key products as fp32 fused
+    multiply-adds on the vector ALU (the rotated query read from global
+    memory) instead of MFMAs: within the tolerance of the fp64 oracle, plain
+    and over a paged pool, and within fp32 rounding of the MFMA path."""
+    O = oracle_lib
+    knob("latency_mode", 0)
+    knob("slot_table", 1)
+    if split:
+        knob("split_tokens", split)
+    c = _attn_case(O, len(lens), Hq, hkv, lens, C=C, step64=step64, seed=211 + Hq, gap=64)
+    pools, pages = _paged_copy(c, np.random.default_rng(9))
+    pg = torch.from_numpy(pages).to(DEV)
+    res = {}
+    for mode in (0, 1):
+        knob("qk_valu", mode)
+        plain = _gpu_attn(c)
+        paged = dq.attn_decode_paged(c["ck"], c["cv"], c["q"], *pools["K"], *pools["V"], pg, c["sl"],
+                                     int(c["lens"].max()))
+        torch.cuda.synchronize()
+        res[mode] = (plain, paged)
+    assert torch.equal(res[1][0], res[1][1]), "paged and contiguous differ"
+    ref = _oracle_attn(O, c)
+    _assert_close(res[1][0].cpu().numpy(), ref, f"qk on valu Hq={Hq} hkv={hkv}")
+    assert float((res[1][0] - res[0][0]).abs().max()) <= 1e-4, "VALU and MFMA scores differ beyond fp32 rounding"
+
+
 def test_decode_step_graph_replay(oracle_lib):
     """A decode step with append captured once in a HIP graph
     (torch.cuda.CUDAGraph over the library's launches, which go to the
