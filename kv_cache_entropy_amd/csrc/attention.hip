@@ -966,6 +966,51 @@ __global__ void __launch_bounds__(64 * kAppendWaves) append_encode_kernel(AttnAr
 // and weights are taken 128 partials at a time, one per thread, so the
 // latency is that of a few loads, not of n dependent ones; each thread then
 // sums its dim in partial order.
+// The same merge for n <= kFewParts partials (a decode step over a few long
+// chunks per sequence): every thread loads the few (m, l) pairs itself, so
+// there is no exchange, no barrier and no loop over kD slots.  Weights as
+// above; acc and l summed in partial order, the extra partial last.
+constexpr int kFewParts = 4;
+__device__ __forceinline__ float lse_merge_few(const float *src, int64_t stride, int n, const float *pe) {
+  const int d = threadIdx.x;
+  float av[kFewParts], mv[kFewParts], lv[kFewParts];
+#pragma unroll
+  for (int j = 0; j < kFewParts; ++j) {
+    av[j] = 0.0f;
+    mv[j] = -__builtin_inff();
+    lv[j] = 0.0f;
+    if (j < n) {  // n is the same for the whole block
+      av[j] = src[(int64_t)j * stride + d];
+      mv[j] = src[(int64_t)j * stride + 128];
+      lv[j] = src[(int64_t)j * stride + 129];
+    }
+  }
+  float ae = 0.0f, me = -__builtin_inff(), le = 0.0f;
+  if (pe) {
+    ae = pe[d];
+    me = pe[128];
+    le = pe[129];
+  }
+  float M = me;
+#pragma unroll
+  for (int j = 0; j < kFewParts; ++j) M = fmaxf(M, mv[j]);
+  float o = 0.0f, L = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kFewParts; ++j) {
+    const float w = mv[j] != -__builtin_inff() ? exp2f(mv[j] - M) : 0.0f;
+    if (w != 0.0f) {
+      o += w * av[j];
+      L += w * lv[j];
+    }
+  }
+  if (pe) {
+    const float w = exp2f(me - M);
+    o += w * ae;
+    L += w * le;
+  }
+  return L > 0.0f ? o / L : 0.0f;  // an empty row (a caller error) gives zeros
+}
+
 __device__ __forceinline__ float lse_merge(const float *src, int64_t stride, int n, const float *pe, float *red,
                                            float *wts) {
   const int d = threadIdx.x;
@@ -1059,7 +1104,8 @@ __global__ void __launch_bounds__(128) combine_kernel(AttnArgs a, uint64_t vseed
   const int n = min(a.nc, L <= big ? (L + a.cq) / (a.cq + 1) : a.cr + (L - big + a.cq - 1) / a.cq);
   const float *src = a.part + (((int64_t)b * a.Hkv + g) * a.nc) * 4 * kPart + hh * kPart;
   const float *pe = extra ? a.part_new + ((int64_t)b * a.Hkv + g) * 4 * kPart + hh * kPart : nullptr;
-  buf[d] = lse_merge(src, 4 * kPart, n, pe, red, wts);  // an empty sequence (a caller error) gives a zero row
+  // an empty sequence (a caller error) gives a zero row
+  buf[d] = n <= kFewParts ? lse_merge_few(src, 4 * kPart, n, pe) : lse_merge(src, 4 * kPart, n, pe, red, wts);
   // inverse rotation: o = D_V * H * o' / 128 (H * H = 128 I)
 #pragma unroll
   for (int w = 1; w < kD; w <<= 1) {
