@@ -968,8 +968,9 @@ __global__ void __launch_bounds__(64 * kAppendWaves) append_encode_kernel(AttnAr
 // sums its dim in partial order.
 // The same merge for n <= kFewParts partials (a decode step over a few long
 // chunks per sequence): every thread loads the few (m, l) pairs itself, so
-// there is no exchange, no barrier and no loop over kD slots.  Weights as
-// above; acc and l summed in partial order, the extra partial last.
+// there is no exchange, no barrier and no loop over kD slots.  The weights
+// are lse_merge's (below); acc and l are summed in partial order, the extra
+// partial last.
 constexpr int kFewParts = 4;
 __device__ __forceinline__ float lse_merge_few(const float *src, int64_t stride, int n, const float *pe) {
   const int d = threadIdx.x;
